@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of routed exact-token attention (HGA) on one MI355X.
+
+One step = one pass of the whole hot path over the Qwen3-30B-A3B-shaped
+prefill layer (batch 1, 32 query / 4 KV heads, d=128, 32768 tokens, bf16,
+C=64, g_s=16, F=2, L=8, K_c=16, K_g=32): hga_build_summaries (rotated key
+cache + chunk / group summaries), hga_route (chunk and group top-K, visible
+granule lists) and hga_attend (exact-token attention over those granules).
+Inputs are resident in HBM before the timed region.
+
+Also measured in the same run (extra fields of the one JSON line):
+  decode  -- one decode step for 16 sequences x 65536 cached tokens
+             (route + attend at position 65536, summaries precomputed);
+  smalllm -- the SmallLM-shaped prefill (batch 4, 8/8 heads, d=64, 4096 tokens);
+  cpu_baseline -- the CPU oracle on a bounded sample of the prefill step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--only prefill|decode|smalllm|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "routed-attn prefill Mtok/s + decode us/step at 64K ctx; % of HBM/MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Pipeline:
+    """Device buffers and the three calls of one step."""
+
+    def __init__(self, w, seed=0):
+        import torch
+        import hierarchical_kv_routing_amd as H
+        self.H, self.torch, self.w = H, torch, w
+        self.cfg = H.Config.from_workload(w)
+        t0 = time.time()
+        q, k, v = W.make_inputs(w, seed, threads=16)
+        log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s")
+        dev = torch.device("cuda:0")
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.q = torch.from_numpy(q).to(dev).to(dt)
+        self.k = torch.from_numpy(k).to(dev).to(dt)
+        self.v = torch.from_numpy(v).to(dev).to(dt)
+        self.q_np, self.k_np, self.v_np = q, k, v
+        del q, k, v
+        B, Hkv, cap, d = self.k.shape
+        c = self.cfg
+        self.k_rot = torch.empty_like(self.k)
+        self.csum = torch.empty((B, Hkv, cap // c.chunk_size, d), dtype=torch.float32, device=dev)
+        self.gsum = torch.empty((B, Hkv, cap // c.group_size, d), dtype=torch.float32, device=dev)
+        self.ro = H.route_outputs(c, B, w.q_pos0, w.n_q, dev)
+        self.out = torch.empty_like(self.q)
+        aw = H.attend_workspace_bytes(c, B, w.q_pos0, w.n_q)
+        self.aws = torch.empty(max(aw, 16), dtype=torch.uint8, device=dev)
+
+    def build(self, lo=0, hi=None):
+        self.H.build_summaries(self.cfg, self.k, lo, self.w.n_ctx if hi is None else hi,
+                               self.k_rot, self.csum, self.gsum)
+
+    def route(self):
+        r = self.ro
+        self.H.route(self.cfg, self.q, self.w.q_pos0, self.csum, self.gsum, self.k.shape[2],
+                     r["chunk_idx"], r["group_idx"], r["granules"], r["granule_count"],
+                     r["workspace"])
+
+    def attend(self):
+        r = self.ro
+        self.H.attend(self.cfg, self.q, self.w.q_pos0, self.k_rot, self.v, r["granules"],
+                      r["granule_count"], self.out, None, self.aws)
+
+
+def timed_steps(torch, stages, steps, warmup):
+    """Run ``warmup`` then ``steps`` steps of the stage list; events bracket the
+    whole timed region and every stage (same stream as the launches)."""
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(steps):
+        for i, (_, fn) in enumerate(stages):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_stage = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+                 for i, (name, _) in enumerate(stages)}
+    return total_ms / steps, per_stage
+
+
+def visible_pairs(w, counts_np):
+    """Sum over query rows (query, head) of the visible keys, from the
+    granule counts (keys j <= i inside the current chunk are counted exactly)."""
+    C, gs, G = w.chunk_size, w.group_size, w.group_ratio
+    total = 0
+    t0 = w.q_pos0 // C
+    for u in range(counts_np.shape[2]):
+        t = t0 + u
+        qlo = max(t * C, w.q_pos0)
+        qhi = min((t + 1) * C, w.q_pos0 + w.n_q)
+        nq = qhi - qlo
+        cnt = counts_np[:, :, u].astype(np.int64)
+        # keys of the current chunk's granules come last in each list
+        cur = (qhi - 1) // gs - (t * C) // gs + 1
+        other = (cnt - cur) * gs
+        causal = sum(i - t * C + 1 for i in range(qlo, qhi))
+        total += int(G * (nq * other.sum() + causal * cnt.size))
+    return total
+
+
+def bench_prefill(args):
+    import torch
+    w = W.QWEN3_PREFILL
+    pipe = Pipeline(w)
+    ms, stage = timed_steps(torch, [("build_summaries", pipe.build), ("route", pipe.route),
+                                    ("attend", pipe.attend)], args.steps, args.warmup)
+    counts = pipe.ro["granule_count"].cpu().numpy()
+    pairs = visible_pairs(w, counts)
+    flops = 4.0 * w.head_dim * pairs              # QK^T and PV, 2 flops per MAC
+    attend_tflops = flops / (stage["attend"] * 1e-3) / 1e12
+    res = dict(ms=ms, stage_ms=stage, pairs=pairs, attend_flops=flops,
+               attend_tflops=attend_tflops, tokens=w.n_q)
+    return pipe, res
+
+
+def bench_decode(args):
+    import torch
+    w = W.DECODE_64K
+    pipe = Pipeline(w)
+    pipe.build()  # cache + summaries of the 65536 cached tokens and the new token (untimed)
+    torch.cuda.synchronize()
+    ms, stage = timed_steps(torch, [("route", pipe.route), ("attend", pipe.attend)],
+                            max(args.steps * 10, 50), args.warmup)
+    counts = pipe.ro["granule_count"].cpu().numpy().astype(np.int64)
+    B, Hkv, d = w.batch, w.n_kv_heads, w.head_dim
+    t = w.q_pos0 // w.chunk_size
+    n_mid = t - w.n_sink_chunks - max(w.n_recent_chunks, 1)
+    n_groups = min(w.top_groups, w.top_chunks * (w.chunk_size // w.group_size))
+    # algorithmic bytes: scanned chunk summaries, fetched group summaries,
+    # gathered K and V of the visible tokens, q in and o out
+    keys = (counts - 1) * w.group_size + 1  # the current chunk holds one token
+    bytes_step = (B * Hkv * n_mid * d * 4 + B * Hkv * w.top_chunks * (w.chunk_size // w.group_size) * d * 4
+                  + int(keys.sum()) * d * 2 * 2 + 2 * B * w.n_q_heads * d * 2)
+    del n_groups
+    us = ms * 1e3
+    return pipe, dict(us_per_step=us, stage_us={k: v * 1e3 for k, v in stage.items()},
+                      bytes_per_step=bytes_step,
+                      achieved_gbs=bytes_step / (ms * 1e-3) / 1e9)
+
+
+def bench_smalllm(args):
+    import torch
+    w = W.SMALLLM_PREFILL
+    pipe = Pipeline(w)
+    ms, stage = timed_steps(torch, [("build_summaries", pipe.build), ("route", pipe.route),
+                                    ("attend", pipe.attend)], args.steps, args.warmup)
+    return pipe, dict(ms=ms, stage_ms=stage, mtok_s=w.batch * w.n_q / (ms * 1e-3) / 1e6)
+
+
+def cpu_baseline(pipe, budget_s=12.0):
+    """Time the CPU oracle on a bounded, unbiased sample of the prefill step
+    and scale to the whole step: summaries of one (sequence, KV head) slab
+    and the route + attention of randomly ordered units of that slab."""
+    from oracle import hga_ref as R
+    w = pipe.w
+    p = R.params_from_workload(w)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q, k, v = pipe.q_np, pipe.k_np, pipe.v_np
+    t0 = time.time()
+    cs, gs = R.summaries(k[0, 0].astype(np.float64), w.n_ctx, p)
+    t_sum = time.time() - t0
+    csum = np.zeros((1, w.n_kv_heads) + cs.shape)
+    gsum = np.zeros((1, w.n_kv_heads) + gs.shape)
+    csum[0, 0], gsum[0, 0] = cs, gs
+    nqc = w.n_q // w.chunk_size
+    order = np.random.default_rng(0).permutation(nqc)
+    done = 0
+    t1 = time.time()
+    for t in order:
+        unit = [(0, 0, int(t))]
+        rt = R.route(q, w.q_pos0, w.n_q, csum, gsum, p, units=unit)
+        R.attend_given(q, w.q_pos0, w.n_q, k, v, rt["granules"], rt["count"], p, t0=0, units=unit)
+        done += 1
+        if time.time() - t1 > budget_s:
+            break
+    t_units = time.time() - t1
+    units_total = w.batch * w.n_kv_heads * nqc
+    est_s = t_sum * w.batch * w.n_kv_heads + t_units * units_total / done
+    return dict(value=w.n_q / est_s / 1e6, unit="Mtok/s", cores=int(cores), kind="oracle",
+                sample=(f"{w.name}: summaries of 1 of {w.batch * w.n_kv_heads} (sequence, kv head) "
+                        f"slabs ({t_sum:.2f}s) + route and attention of {done} of {units_total} units "
+                        f"in random query-chunk order ({t_units:.2f}s); scaled to the whole step "
+                        f"= {est_s:.1f}s per step"))
+
+
+def copy_calibration(args):
+    """A plain device copy of known size (for scaling HBM byte counters)."""
+    import torch
+    n = 1 << 28  # 256 Mi bf16 elements = 512 MiB
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {2 * n} bytes read and written per launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "copy"], default=None)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the routed-attention hot path runs per (sequence, KV head) unit on one device "
+              "and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import hierarchical_kv_routing_amd as H
+    H.lib()
+
+    if args.only == "copy":
+        copy_calibration(args)
+        return
+    if args.only == "decode":
+        _, dec = bench_decode(args)
+        print(json.dumps(dict(decode=dec)), flush=True)
+        return
+    if args.only == "smalllm":
+        _, sm = bench_smalllm(args)
+        print(json.dumps(dict(smalllm=sm)), flush=True)
+        return
+
+    pipe, pre = bench_prefill(args)
+    log(f"[bench] prefill: {pre['ms']:.3f} ms/step, stages {pre['stage_ms']}")
+    w = pipe.w
+    value = pre["tokens"] / (pre["ms"] * 1e-3) / 1e6
+    line = dict(
+        metric=METRIC, value=value, unit="Mtok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=pre["ms"], higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=w.name, batch=w.batch, seq_len=w.n_ctx, q_heads=w.n_q_heads,
+                    kv_heads=w.n_kv_heads, head_dim=w.head_dim, C=w.chunk_size, g_s=w.group_size,
+                    F=w.n_sink_chunks, L=w.n_recent_chunks, K_c=w.top_chunks, K_g=w.top_groups,
+                    rope_theta=w.rope_theta),
+        roofline=dict(bound="mfma", kernel="attend_mfma_kernel", achieved=pre["attend_tflops"],
+                      peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=pre["attend_tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                      flops_per_launch=pre["attend_flops"], visible_pairs=pre["pairs"],
+                      avg_launch_ms=pre["stage_ms"]["attend"]),
+        stage_ms=pre["stage_ms"],
+    )
+    if args.only is None:
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(pipe)
+        del pipe
+        torch.cuda.empty_cache()
+        _, dec = bench_decode(args)
+        line["decode"] = dict(workload=W.DECODE_64K.name, us_per_step=dec["us_per_step"],
+                              stage_us=dec["stage_us"],
+                              roofline=dict(bound="hbm", achieved=dec["achieved_gbs"], peak=PEAK_HBM_GBS,
+                                            unit="GB/s", frac=dec["achieved_gbs"] / PEAK_HBM_GBS,
+                                            bytes_per_step=dec["bytes_per_step"]))
+        _, sm = bench_smalllm(args)
+        line["smalllm"] = dict(workload=W.SMALLLM_PREFILL.name, mtok_s=sm["mtok_s"], ms=sm["ms"],
+                               stage_ms=sm["stage_ms"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,283 @@
+"""MI355X (gfx950) routed exact-token attention -- Hierarchical Global Attention.
+
+A thin ctypes binding over ``libhga.so`` (built from ``csrc/`` by
+``python -m hierarchical_kv_routing_amd.build``).  Every step of the path
+runs in the library's HIP kernels; this module only checks tensor shapes and
+passes device pointers and the current HIP stream.  PyTorch provides device
+memory and streams.  There is no fallback: a missing or unloadable library
+raises ``HGAError``.
+
+Entry points (same names as the C ABI in include/hga.h):
+  build_summaries  -- rotated key cache + mixed-RoPE chunk / group summaries
+  route            -- chunk top-K_c, group top-K_g, visible granule lists
+  attend           -- exact-token softmax attention over the granule lists
+  dense_causal     -- Eq. (1) dense causal attention (reference path)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhga.so")
+
+HGA_OK = 0
+_STATUS = {0: "HGA_OK", 1: "HGA_ERR_INVALID_ARGUMENT", 2: "HGA_ERR_UNSUPPORTED",
+           3: "HGA_ERR_WORKSPACE_TOO_SMALL", 4: "HGA_ERR_HIP"}
+HGA_F32, HGA_BF16 = 0, 1
+
+# Every symbol include/hga.h declares.
+ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_bytes",
+               "hga_route", "hga_attend_workspace_bytes", "hga_attend", "hga_dense_causal",
+               "hga_status_string", "hga_last_hip_error")
+
+
+class HGAError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+class hga_config(ctypes.Structure):
+    _fields_ = [("chunk_size", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("n_sink_chunks", ctypes.c_int32), ("n_recent_chunks", ctypes.c_int32),
+                ("top_chunks", ctypes.c_int32), ("top_groups", ctypes.c_int32),
+                ("n_hf_pairs", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class Config:
+    """Routing / attention parameters (names of the pages: C, g_s, F, L, K_c, K_g)."""
+    chunk_size: int
+    group_size: int
+    n_sink_chunks: int
+    n_recent_chunks: int
+    top_chunks: int
+    top_groups: int
+    n_hf_pairs: int
+    head_dim: int
+    n_q_heads: int
+    n_kv_heads: int
+    rope_theta: float
+    softmax_scale: float = 0.0
+
+    @classmethod
+    def from_workload(cls, w, **over) -> "Config":
+        kw = dict(chunk_size=w.chunk_size, group_size=w.group_size,
+                  n_sink_chunks=w.n_sink_chunks, n_recent_chunks=w.n_recent_chunks,
+                  top_chunks=w.top_chunks, top_groups=w.top_groups, n_hf_pairs=w.n_hf_pairs,
+                  head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                  rope_theta=w.rope_theta)
+        kw.update(over)
+        return cls(**kw)
+
+    def c(self) -> hga_config:
+        return hga_config(self.chunk_size, self.group_size, self.n_sink_chunks,
+                          self.n_recent_chunks, self.top_chunks, self.top_groups,
+                          self.n_hf_pairs, self.head_dim, self.n_q_heads, self.n_kv_heads,
+                          float(self.rope_theta), float(self.softmax_scale))
+
+    def n_query_chunks(self, q_pos0: int, n_q: int) -> int:
+        if n_q <= 0:
+            return 0
+        return (q_pos0 + n_q - 1) // self.chunk_size - q_pos0 // self.chunk_size + 1
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhga.so (raises HGAError when it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise HGAError(f"{LIB_PATH} is not built; run: python -m hierarchical_kv_routing_amd.build")
+    try:
+        l = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise HGAError(f"cannot load {LIB_PATH}: {e}") from e
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CP = ctypes.POINTER(hga_config)
+    sig = {
+        "hga_build_summaries": (I32, [CP, I32, I32, P, I64, I64, I64, P, P, P, P]),
+        "hga_max_granules": (I32, [CP]),
+        "hga_route_workspace_bytes": (SZ, [CP, I32, I64, I64]),
+        "hga_route": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, SZ, P]),
+        "hga_attend_workspace_bytes": (SZ, [CP, I32, I64, I64]),
+        "hga_attend": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, SZ, P]),
+        "hga_dense_causal": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, SZ, P]),
+        "hga_status_string": (ctypes.c_char_p, [I32]),
+        "hga_last_hip_error": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(l, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = l
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != HGA_OK:
+        extra = ""
+        if status == 4:
+            extra = f" (hipError {lib().hga_last_hip_error()})"
+        raise HGAError(f"{what}: {_STATUS.get(status, status)}{extra}", status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HGA_BF16
+    if t.dtype == torch.float32:
+        return HGA_F32
+    raise HGAError(f"unsupported dtype {t.dtype}: q/k/v/out must be bfloat16 or float32")
+
+
+def _dev(t, name, shape=None, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise HGAError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise HGAError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise HGAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise HGAError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def max_granules(cfg: Config) -> int:
+    return int(lib().hga_max_granules(ctypes.byref(cfg.c())))
+
+
+def route_workspace_bytes(cfg: Config, batch: int, q_pos0: int, n_q: int) -> int:
+    return int(lib().hga_route_workspace_bytes(ctypes.byref(cfg.c()), batch, q_pos0, n_q))
+
+
+def attend_workspace_bytes(cfg: Config, batch: int, q_pos0: int, n_q: int) -> int:
+    return int(lib().hga_attend_workspace_bytes(ctypes.byref(cfg.c()), batch, q_pos0, n_q))
+
+
+def build_summaries(cfg: Config, k_raw, tok_begin: int, tok_end: int, k_rot, chunk_sum,
+                    group_sum=None, stream=None):
+    """Rotate keys [tok_begin, tok_end) into k_rot and write the summaries of
+    every chunk / group that closes inside the range (the store's append)."""
+    torch = _torch()
+    B, Hkv, cap, d = k_raw.shape
+    _dev(k_raw, "k_raw")
+    _dev(k_rot, "k_rot", k_raw.shape, k_raw.dtype)
+    _dev(chunk_sum, "chunk_sum", (B, Hkv, cap // cfg.chunk_size, d), torch.float32)
+    _dev(group_sum, "group_sum", (B, Hkv, cap // cfg.group_size, d), torch.float32)
+    st = lib().hga_build_summaries(
+        ctypes.byref(cfg.c()), _dtype_code(k_raw), B, k_raw.data_ptr(), cap, tok_begin, tok_end,
+        k_rot.data_ptr() if k_rot is not None else None, chunk_sum.data_ptr(),
+        group_sum.data_ptr() if group_sum is not None else None, _stream(k_raw, stream))
+    _check(st, "hga_build_summaries")
+
+
+def route_outputs(cfg: Config, batch: int, q_pos0: int, n_q: int, device):
+    """Allocate chunk_idx, group_idx, granules, granule_count and the workspace."""
+    torch = _torch()
+    nqc = cfg.n_query_chunks(q_pos0, n_q)
+    H = cfg.n_kv_heads
+    out = dict(
+        chunk_idx=torch.empty((batch, H, nqc, max(cfg.top_chunks, 1)), dtype=torch.int32, device=device),
+        group_idx=torch.empty((batch, H, nqc, max(cfg.top_groups, 1)), dtype=torch.int32, device=device),
+        granules=torch.empty((batch, H, nqc, max_granules(cfg)), dtype=torch.int32, device=device),
+        granule_count=torch.empty((batch, H, nqc), dtype=torch.int32, device=device))
+    ws = route_workspace_bytes(cfg, batch, q_pos0, n_q)
+    out["workspace"] = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+    return out
+
+
+def route(cfg: Config, q, q_pos0: int, chunk_sum, group_sum, kv_cap: int, chunk_idx, group_idx,
+          granules, granule_count, workspace=None, stream=None):
+    """Two-level routing of every (sequence, KV head, query chunk) unit."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    nqc = cfg.n_query_chunks(q_pos0, n_q)
+    Hkv = cfg.n_kv_heads
+    _dev(q, "q")
+    _dev(chunk_sum, "chunk_sum", (B, Hkv, kv_cap // cfg.chunk_size, d), torch.float32)
+    _dev(group_sum, "group_sum", (B, Hkv, kv_cap // cfg.group_size, d), torch.float32)
+    _dev(chunk_idx, "chunk_idx", (B, Hkv, nqc, max(cfg.top_chunks, 1)), torch.int32)
+    _dev(group_idx, "group_idx", (B, Hkv, nqc, max(cfg.top_groups, 1)), torch.int32)
+    _dev(granules, "granules", (B, Hkv, nqc, max_granules(cfg)), torch.int32)
+    _dev(granule_count, "granule_count", (B, Hkv, nqc), torch.int32)
+    _dev(workspace, "workspace")
+    st = lib().hga_route(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q,
+        chunk_sum.data_ptr(), group_sum.data_ptr() if group_sum is not None else None, kv_cap,
+        chunk_idx.data_ptr(), group_idx.data_ptr() if group_idx is not None else None,
+        granules.data_ptr(), granule_count.data_ptr(),
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(q, stream))
+    _check(st, "hga_route")
+
+
+def attend(cfg: Config, q, q_pos0: int, k_rot, v, granules, granule_count, out, lse=None,
+           workspace=None, stream=None):
+    """Exact-token attention of every query over its unit's granule list."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    kv_cap = k_rot.shape[2]
+    nqc = cfg.n_query_chunks(q_pos0, n_q)
+    _dev(q, "q")
+    _dev(k_rot, "k_rot", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(v, "v", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(granules, "granules", (B, cfg.n_kv_heads, nqc, max_granules(cfg)), torch.int32)
+    _dev(granule_count, "granule_count", (B, cfg.n_kv_heads, nqc), torch.int32)
+    _dev(out, "out", q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, n_q), torch.float32)
+    _dev(workspace, "workspace")
+    st = lib().hga_attend(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q, k_rot.data_ptr(),
+        v.data_ptr(), kv_cap, granules.data_ptr(), granule_count.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(q, stream))
+    _check(st, "hga_attend")
+
+
+def dense_causal(cfg: Config, q, q_pos0: int, k_rot, v, out, lse=None, workspace=None, stream=None):
+    """Eq. (1): every query attends to all keys at positions <= its own."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    kv_cap = k_rot.shape[2]
+    _dev(q, "q")
+    _dev(k_rot, "k_rot", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(v, "v", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(out, "out", q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, n_q), torch.float32)
+    _dev(workspace, "workspace")
+    st = lib().hga_dense_causal(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q, k_rot.data_ptr(),
+        v.data_ptr(), kv_cap, out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(q, stream))
+    _check(st, "hga_dense_causal")
+
+
+def default_scale(cfg: Config) -> float:
+    return cfg.softmax_scale if cfg.softmax_scale else 1.0 / math.sqrt(cfg.head_dim)

@@ -1,0 +1,48 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel
+// translation units.  Not installed; the public interface is include/hga.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hga.h"
+
+namespace hga {
+
+constexpr int kMaxHalfDim = 64;  // d <= 128
+
+// theta_i = rope_theta^(-2i/d), computed once on the host in double.
+struct RopeFreqs {
+  double f[kMaxHalfDim];
+};
+
+// A validated call shape.  Built by api.cpp, read by the launchers.
+struct Geometry {
+  int B, Hq, Hkv, G, d, C, gs, r;  // r = C / gs granules per chunk
+  int F, L, Kc, Kg, n_hf;
+  int64_t kv_cap, q_pos0, n_q;
+  int64_t t0, nqc;  // first query chunk, number of query chunks
+  int gmax;         // granules per unit at most
+  float scale;      // softmax scale
+  bool bf16;
+  RopeFreqs rope;
+};
+
+hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_begin,
+                            int64_t tok_end, void* k_rot, float* chunk_sum,
+                            float* group_sum, hipStream_t stream);
+
+size_t route_workspace(const Geometry& g);
+bool route_supported(const Geometry& g);
+hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum,
+                        const float* group_sum, int32_t* chunk_idx, int32_t* group_idx,
+                        int32_t* granules, int32_t* granule_count, void* ws,
+                        hipStream_t stream);
+
+size_t attend_workspace(const Geometry& g, bool dense);
+hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,
+                         const int32_t* granules, const int32_t* granule_count, bool dense,
+                         void* out, float* lse, void* ws, hipStream_t stream);
+
+}  // namespace hga

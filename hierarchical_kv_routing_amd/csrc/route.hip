@@ -1,0 +1,529 @@
+// Two-level content routing: chunk scores, top-K_c, group scores inside the
+// selected chunks, top-K_g, and the visible-granule list of every unit.
+//
+// Source: xllm-io paper-review page of "Hierarchical Global Attention",
+// section 3: routing policy (fixed sink / recent / previous-chunk windows,
+// middle context competes), score_m = q^T c_m, the selection equation
+// M_sel = topK_c, G_sel = topK_g over the groups of M_sel, and the exact-token
+// output paragraph (which tokens are opened).  Scores of a unit are the max
+// over its query rows (query chunk x GQA group of the KV head).
+//
+// Scoring is a small dense contraction (rows x d) . (d x candidates) done on
+// bf16 matrix cores with both operands split hi + lo (hi*hi + hi*lo + lo*hi,
+// f32 accumulation), about 1e-5 relative to f64, so routing decisions agree
+// with an f64 evaluation except at near-ties.  Selection is an exact block
+// radix select on order-preserving 32-bit keys; equal keys go to the lowest
+// index.
+//
+// Two launch shapes:
+//  * fused: one workgroup per unit (sequence, KV head, query chunk) scores
+//    every middle chunk, selects, scores the groups and writes the lists.
+//    Units run longest (largest t) first.
+//  * segmented (few units with long middle contexts, e.g. a decode step):
+//    score_kernel spreads each unit's middle chunks over many workgroups and
+//    writes raw scores to the workspace; the fused kernel then runs with
+//    FROM_WS and skips chunk scoring.
+#include "hga_device.h"
+
+namespace hga {
+namespace {
+
+constexpr int kRouteThreads = 512;      // 8 waves
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kScoreThreads = 256;      // segmented scoring: 4 waves
+constexpr int kRowsPerWave = 64;        // 4 row blocks of 16
+constexpr int kMaxRows = kRowsPerWave * kRouteWaves;
+constexpr int kMaxCand = 4096;          // middle chunks per unit held in LDS
+constexpr int kMaxSel = 256;            // K_c, K_g upper bound
+constexpr int kMaxTableQ = 64;          // queries per unit (C <= 64)
+
+struct RouteParams {
+  const void* q;
+  const float* csum;
+  const float* gsum;
+  int32_t* cidx;
+  int32_t* gidx;
+  int32_t* gran;
+  int32_t* gcnt;
+  float* ws;  // segmented scores [unit][ws_stride]
+  int64_t ws_stride;
+  int64_t q_pos0, n_q, t0, nqc, nchunk_cap, ngroup_cap;
+  int B, Hq, Hkv, G, d, C, gs, r, F, L, Kc, Kg, gmax;
+  int seg_chunks, nseg;
+  RopeFreqs rope;
+};
+
+struct Unit {
+  int b, kvh;
+  int64_t t, qlo, mid_lo, mid_hi, sink_hi, rec_lo, slot;
+  int nq, R;
+};
+
+// Unit u in [0, B*Hkv*nqc): largest query chunk first; (b, kvh) fastest so
+// that units sharing a summary table stay on the same XCD's L2.
+__device__ __forceinline__ Unit make_unit(const RouteParams& p, int64_t u) {
+  Unit w;
+  const int64_t bh = static_cast<int64_t>(p.B) * p.Hkv;
+  const int64_t trel = p.nqc - 1 - u / bh;
+  const int64_t rem = u % bh;
+  w.b = static_cast<int>(rem / p.Hkv);
+  w.kvh = static_cast<int>(rem % p.Hkv);
+  w.t = p.t0 + trel;
+  const int64_t c0 = w.t * p.C;
+  w.qlo = c0 > p.q_pos0 ? c0 : p.q_pos0;
+  const int64_t qend = p.q_pos0 + p.n_q;
+  const int64_t qhi = (c0 + p.C) < qend ? (c0 + p.C) : qend;
+  w.nq = static_cast<int>(qhi - w.qlo);
+  w.R = w.nq * p.G;
+  const int64_t lp = p.L > 1 ? p.L : 1;
+  w.sink_hi = w.t < p.F ? w.t : p.F;
+  const int64_t rl = w.t - lp;
+  w.rec_lo = rl > w.sink_hi ? rl : w.sink_hi;
+  w.mid_lo = w.sink_hi;
+  w.mid_hi = w.rec_lo;
+  w.slot = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nqc + trel;
+  return w;
+}
+
+// cos/sin of every (query of the unit, pair) into LDS.
+__device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit& w, float2* cs) {
+  const int h = p.d >> 1;
+  for (int i = threadIdx.x; i < w.nq * h; i += blockDim.x) {
+    const int qi = i / h, pr = i - qi * h;
+    float c, s;
+    rope_cs(static_cast<double>(w.qlo + qi), p.rope.f[pr], c, s);
+    cs[i] = make_float2(c, s);
+  }
+}
+
+// The wave's 4 row blocks of 16 rotated query rows as split-bf16 A operands
+// (16x16x32 layout: lane -> row lane%16, d slots ks*32 + 8*(lane/16) + i).
+// Rows past the unit's last row repeat the last row, which leaves every max
+// unchanged.  Row r of a unit is (query r / G, head r % G).
+template <bool BF16, int KS>
+__device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, int rbase,
+                                          const float2* cs, Pack8 (&ahi)[4][KS],
+                                          Pack8 (&alo)[4][KS]) {
+  const int lane = threadIdx.x & 63;
+  const int h = p.d >> 1;
+  const int sub = lane >> 4;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    int r = rbase + blk * 16 + (lane & 15);
+    if (r >= w.R) r = w.R - 1;
+    const int qi = r / p.G;
+    const int hl = r - qi * p.G;
+    const int64_t base =
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0)) * p.d;
+    float x[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8<BF16>(p.q, base + ks * 32 + sub * 8, x[ks]);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float2 t = cs[qi * h + ks * 32 + sub * 8 + i];
+        const float a = x[ks][i], b = x[ks + KS / 2][i];
+        x[ks][i] = a * t.x - b * t.y;
+        x[ks + KS / 2][i] = a * t.y + b * t.x;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) split_bf16(x[ks][i], ahi[blk][ks].h[i], alo[blk][ks].h[i]);
+    }
+  }
+}
+
+// Max over the wave's rows of q~ . s for 16 summary rows (one per lane%16).
+template <int KS>
+__device__ __forceinline__ float score16(const float* srow, int d, const Pack8 (&ahi)[4][KS],
+                                         const Pack8 (&alo)[4][KS]) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4;
+  Pack8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float x[8];
+    load8<false>(srow, ks * 32 + sub * 8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(x[i], bhi[ks].h[i], blo[ks].h[i]);
+  }
+  (void)d;
+  float best = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mfma16x16x32(ahi[blk][ks].v, bhi[ks].v, acc);
+      acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
+      acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
+    }
+    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+  }
+  best = fmaxf(best, __shfl_xor(best, 16));
+  best = fmaxf(best, __shfl_xor(best, 32));
+  return best;
+}
+
+struct SelScratch {
+  int hist[256];
+  int wsum[16];
+  int bcast[4];
+};
+
+__device__ __forceinline__ int block_excl_scan(int v, SelScratch& s, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) s.wsum[wave] = inc;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = s.wsum[w];
+    if (w < wave) pre += x;
+    total += x;
+  }
+  __syncthreads();
+  return pre + inc - v;
+}
+
+// Indices of the k largest keys[0..n) (ties to the lower index), ascending,
+// into out[].  Exact radix select over the 32-bit keys, then a stable
+// compaction in index order.  Block-wide; every thread must call it.
+__device__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (k <= 0 || n <= 0) return 0;
+  if (n <= k) {
+    for (int i = tid; i < n; i += nt) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += nt) s.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += nt) {
+      const uint32_t kk = keys[i];
+      if ((kk & pmask) == prefix) atomicAdd(&s.hist[(kk >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s.hist[255 - 4 * tid - j];
+        tot += c[j];
+      }
+      int inc = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (tid >= off) inc += y;
+      }
+      const int excl = inc - tot;
+      if (excl < need && need <= inc) {
+        int above = excl;
+        for (int j = 0; j < 4; ++j) {
+          if (above + c[j] >= need) {
+            s.bcast[0] = 255 - 4 * tid - j;
+            s.bcast[1] = above;
+            break;
+          }
+          above += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    const int digit = s.bcast[0];
+    need -= s.bcast[1];
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;
+  const int per = (n + nt - 1) / nt;
+  const int lo = tid * per;
+  const int hi = lo + per < n ? lo + per : n;
+  int n_eq = 0;
+  for (int i = lo; i < hi; ++i) n_eq += keys[i] == thr;
+  int total;
+  int eq_before = block_excl_scan(n_eq, s, total);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t kk = keys[i];
+      if (kk > thr) {
+        ++n_sel;
+      } else if (kk == thr) {
+        if (e < need) ++n_sel;
+        ++e;
+      }
+    }
+  }
+  int pos = block_excl_scan(n_sel, s, total);
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t kk = keys[i];
+      bool take = kk > thr;
+      if (kk == thr) {
+        take = e < need;
+        ++e;
+      }
+      if (take) out[pos++] = i;
+    }
+  }
+  __syncthreads();
+  return k;
+}
+
+// Segmented chunk scoring: raw max-scores of one segment of a unit's middle
+// chunks into the workspace.
+template <bool BF16, int KS>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
+  __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
+  const int64_t u = blockIdx.x / p.nseg;
+  const int sg = blockIdx.x - static_cast<int>(u * p.nseg);
+  const Unit w = make_unit(p, u);
+  const int64_t m0 = w.mid_lo + static_cast<int64_t>(sg) * p.seg_chunks;
+  int64_t m1 = m0 + p.seg_chunks;
+  if (m1 > w.mid_hi) m1 = w.mid_hi;
+  if (m0 >= m1 || p.Kc <= 0 || w.R <= 0) return;  // uniform
+  fill_rope_table(p, w, cs);
+  __syncthreads();
+  Pack8 ahi[4][KS], alo[4][KS];
+  load_rows<BF16, KS>(p, w, 0, cs, ahi, alo);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+  const int ntile = static_cast<int>((m1 - m0 + 15) / 16);
+  for (int tile = wave; tile < ntile; tile += kScoreThreads / 64) {
+    int64_t m = m0 + tile * 16 + (lane & 15);
+    const bool valid = m < m1;
+    if (!valid) m = m1 - 1;
+    const float v = score16<KS>(p.csum + (cbase + m) * p.d, p.d, ahi, alo);
+    if (lane < 16 && valid) p.ws[w.slot * p.ws_stride + (m - w.mid_lo)] = v;
+  }
+}
+
+template <bool BF16, int KS, bool FROM_WS>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
+  __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
+  __shared__ uint32_t keys[kMaxCand];
+  __shared__ int selc[kMaxSel];
+  __shared__ int selg[kMaxSel];
+  __shared__ SelScratch scr;
+
+  const Unit w = make_unit(p, blockIdx.x);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_mid = static_cast<int>(w.mid_hi - w.mid_lo);
+  const bool route = p.Kc > 0 && n_mid > 0 && w.R > 0;
+
+  // Work split inside the block: RG row groups x TG tile groups.
+  const int RG = (w.R + kRowsPerWave - 1) / kRowsPerWave;
+  const int TG = RG > 0 ? kRouteWaves / RG : 1;
+  const int rg = RG > 0 ? wave % RG : 0;
+  const int tg = RG > 0 ? wave / RG : kRouteWaves;
+  const bool has_rows = route && tg < TG;
+
+  Pack8 ahi[4][KS], alo[4][KS];
+  if (route) {
+    fill_rope_table(p, w, cs);
+    __syncthreads();
+    if (has_rows) load_rows<BF16, KS>(p, w, rg * kRowsPerWave, cs, ahi, alo);
+  }
+
+  int nselc = 0;
+  if (route) {
+    if constexpr (FROM_WS) {
+      for (int i = threadIdx.x; i < n_mid; i += blockDim.x)
+        keys[i] = order_key(p.ws[w.slot * p.ws_stride + i]);
+    } else {
+      for (int i = threadIdx.x; i < n_mid; i += blockDim.x) keys[i] = 0u;
+      __syncthreads();
+      if (has_rows) {
+        const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+        const int ntile = (n_mid + 15) / 16;
+        for (int tile = tg; tile < ntile; tile += TG) {
+          int c = tile * 16 + (lane & 15);
+          const bool valid = c < n_mid;
+          if (!valid) c = n_mid - 1;
+          const float v = score16<KS>(p.csum + (cbase + w.mid_lo + c) * p.d, p.d, ahi, alo);
+          if (lane < 16 && valid) atomicMax(&keys[c], order_key(v));
+        }
+      }
+    }
+    __syncthreads();
+    nselc = block_select(keys, n_mid, p.Kc, selc, scr);
+    for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] += static_cast<int>(w.mid_lo);
+    __syncthreads();
+  }
+
+  int nselg = 0;
+  if (p.Kg > 0 && nselc > 0) {
+    const int nc = nselc * p.r;
+    for (int i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = 0u;
+    __syncthreads();
+    if (has_rows) {
+      const int64_t gbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.ngroup_cap;
+      const int ntile = (nc + 15) / 16;
+      for (int tile = tg; tile < ntile; tile += TG) {
+        int c = tile * 16 + (lane & 15);
+        const bool valid = c < nc;
+        if (!valid) c = nc - 1;
+        const int cr = c / p.r;
+        const int64_t gid = static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r);
+        const float v = score16<KS>(p.gsum + (gbase + gid) * p.d, p.d, ahi, alo);
+        if (lane < 16 && valid) atomicMax(&keys[c], order_key(v));
+      }
+    }
+    __syncthreads();
+    nselg = block_select(keys, nc, p.Kg, selg, scr);
+    for (int i = threadIdx.x; i < nselg; i += blockDim.x) {
+      const int c = selg[i];
+      const int cr = c / p.r;
+      selg[i] = selc[cr] * p.r + (c - cr * p.r);
+    }
+    __syncthreads();
+  }
+
+  // Outputs.  The visible list is: sink granules, routed granules, recent
+  // granules, current-chunk granules up to the last query; the routed ones
+  // lie in [sink_hi, rec_lo) so the concatenation is ascending and unique.
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int32_t* ci = p.cidx + w.slot * p.Kc;
+  for (int i = tid; i < p.Kc; i += nt) ci[i] = i < nselc ? selc[i] : -1;
+  if (p.Kg > 0 && p.gidx != nullptr) {
+    int32_t* gi = p.gidx + w.slot * p.Kg;
+    for (int i = tid; i < p.Kg; i += nt) gi[i] = i < nselg ? selg[i] : -1;
+  }
+  const int r = p.r;
+  const int n1 = static_cast<int>(w.sink_hi) * r;
+  const int n2 = p.Kg > 0 ? nselg : nselc * r;
+  const int64_t rec0 = w.rec_lo * r;
+  const int n3 = static_cast<int>(w.t - w.rec_lo) * r;
+  const int64_t cur0 = w.t * r;
+  const int64_t qlast = w.qlo + w.nq - 1;
+  const int n4 = static_cast<int>(qlast / p.gs - cur0 + 1);
+  const int total = n1 + n2 + n3 + n4;
+  int32_t* gl = p.gran + w.slot * p.gmax;
+  for (int i = tid; i < p.gmax; i += nt) {
+    int32_t v = -1;
+    if (i < n1) {
+      v = i;
+    } else if (i < n1 + n2) {
+      const int j = i - n1;
+      v = p.Kg > 0 ? selg[j] : selc[j / r] * r + (j - (j / r) * r);
+    } else if (i < n1 + n2 + n3) {
+      v = static_cast<int32_t>(rec0 + (i - n1 - n2));
+    } else if (i < total) {
+      v = static_cast<int32_t>(cur0 + (i - n1 - n2 - n3));
+    }
+    gl[i] = v;
+  }
+  if (tid == 0) p.gcnt[w.slot] = total;
+}
+
+template <bool BF16, int KS>
+hipError_t launch_route_t(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
+  if (segmented) {
+    hipLaunchKernelGGL((score_kernel<BF16, KS>), dim3(static_cast<unsigned>(units * p.nseg)),
+                       dim3(kScoreThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_kernel<BF16, KS, true>), dim3(static_cast<unsigned>(units)),
+                       dim3(kRouteThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((route_kernel<BF16, KS, false>), dim3(static_cast<unsigned>(units)),
+                       dim3(kRouteThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+int64_t max_middle(const Geometry& g) {
+  const int64_t t = g.t0 + g.nqc - 1;
+  const int64_t lp = g.L > 1 ? g.L : 1;
+  const int64_t sink = t < g.F ? t : g.F;
+  const int64_t rec = t - lp > sink ? t - lp : sink;
+  return rec - sink;
+}
+
+bool use_segmented(const Geometry& g) {
+  const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  return units < 512 && max_middle(g) > 256 && g.nqc == 1 &&
+         g.n_q * static_cast<int64_t>(g.G) <= kRowsPerWave;
+}
+
+constexpr int kSegChunks = 64;
+
+}  // namespace
+
+bool route_supported(const Geometry& g) {
+  return (g.d == 64 || g.d == 128) && g.C <= kMaxTableQ && g.C * g.G <= kMaxRows &&
+         max_middle(g) <= kMaxCand && g.Kc <= kMaxSel && g.Kg <= kMaxSel &&
+         static_cast<int64_t>(g.Kc) * g.r <= kMaxCand;
+}
+
+size_t route_workspace(const Geometry& g) {
+  if (!use_segmented(g)) return 0;
+  return static_cast<size_t>(g.B) * g.Hkv * g.nqc * static_cast<size_t>(max_middle(g)) * sizeof(float);
+}
+
+hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum,
+                        const float* group_sum, int32_t* chunk_idx, int32_t* group_idx,
+                        int32_t* granules, int32_t* granule_count, void* ws,
+                        hipStream_t stream) {
+  RouteParams p;
+  p.q = q;
+  p.csum = chunk_sum;
+  p.gsum = group_sum;
+  p.cidx = chunk_idx;
+  p.gidx = group_idx;
+  p.gran = granules;
+  p.gcnt = granule_count;
+  p.ws = static_cast<float*>(ws);
+  p.ws_stride = max_middle(g);
+  p.q_pos0 = g.q_pos0;
+  p.n_q = g.n_q;
+  p.t0 = g.t0;
+  p.nqc = g.nqc;
+  p.nchunk_cap = g.kv_cap / g.C;
+  p.ngroup_cap = g.kv_cap / g.gs;
+  p.B = g.B;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.G;
+  p.d = g.d;
+  p.C = g.C;
+  p.gs = g.gs;
+  p.r = g.r;
+  p.F = g.F;
+  p.L = g.L;
+  p.Kc = g.Kc;
+  p.Kg = g.Kg;
+  p.gmax = g.gmax;
+  p.rope = g.rope;
+  const bool seg = use_segmented(g);
+  p.seg_chunks = kSegChunks;
+  p.nseg = static_cast<int>((max_middle(g) + kSegChunks - 1) / kSegChunks);
+  if (p.nseg < 1) p.nseg = 1;
+  const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  if (g.bf16) {
+    return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)
+                      : launch_route_t<true, 2>(p, units, seg, stream);
+  }
+  return g.d == 128 ? launch_route_t<false, 4>(p, units, seg, stream)
+                    : launch_route_t<false, 2>(p, units, seg, stream);
+}
+
+}  // namespace hga

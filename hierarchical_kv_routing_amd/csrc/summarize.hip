@@ -1,0 +1,150 @@
+// Mixed-RoPE chunk and group key summaries plus the rotated key cache.
+//
+// Source: xllm-io paper-review page of "Hierarchical Global Attention",
+// section 3, Mixed-RoPE routing summaries (summary equation) and the
+// framework paragraph (chunks of C tokens split into groups of g_s tokens;
+// closed chunks carry a chunk summary and group summaries).
+//
+// One workgroup per (chunk, kv head, sequence), 4 waves.  Lane p owns RoPE
+// pair p = (k[p], k[p + d/2]); wave w walks groups w, w+4, ... of the chunk
+// token by token (each token row is read once, coalesced across lanes), so
+// the group sums live in registers.  The chunk sum is the sum of the group
+// sums taken over the 4 waves in a fixed order, so results are bitwise
+// reproducible.  Work is HBM-streaming: d*elem bytes read per token plus the
+// k_rot write.
+#include "hga_device.h"
+
+namespace hga {
+namespace {
+
+constexpr int kSumWaves = 4;
+
+struct SumParams {
+  const void* k_raw;
+  void* k_rot;
+  float* chunk_sum;
+  float* group_sum;
+  int64_t kv_cap, tok_begin, tok_end, chunk_first;
+  int Hkv, d, C, gs, r, n_hf;
+  RopeFreqs rope;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = p.d >> 1;
+  const int64_t m = p.chunk_first + blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t slab = (static_cast<int64_t>(b) * p.Hkv + kvh) * p.kv_cap;
+  const int64_t c0 = m * p.C;
+  const int64_t c1 = c0 + p.C;
+  const int64_t tend = c1 < p.tok_end ? c1 : p.tok_end;
+  const bool active = lane < h;
+  const double freq = active ? p.rope.f[lane] : 0.0;
+  const bool high = lane < p.n_hf;
+
+  float cx = 0.f, cy = 0.f;  // chunk partial sums of this wave (rotated or raw per pair kind)
+  for (int g = wave; g < p.r; g += kSumWaves) {
+    const int64_t g0 = c0 + static_cast<int64_t>(g) * p.gs;
+    const int64_t g1 = g0 + p.gs;
+    const int64_t jend = g1 < tend ? g1 : tend;
+    float sx = 0.f, sy = 0.f;
+    if (active) {
+      for (int64_t j = g0; j < jend; ++j) {
+        const int64_t e = (slab + j) * p.d + lane;
+        const float x = load1<BF16>(p.k_raw, e);
+        const float y = load1<BF16>(p.k_raw, e + h);
+        float c, s;
+        rope_cs(static_cast<double>(j), freq, c, s);
+        const float rx = x * c - y * s;
+        const float ry = x * s + y * c;
+        if (p.k_rot != nullptr && j >= p.tok_begin) {
+          store1<BF16>(p.k_rot, e, rx);
+          store1<BF16>(p.k_rot, e + h, ry);
+        }
+        // high-frequency pairs average rotated keys, low-frequency pairs raw keys
+        sx += high ? rx : x;
+        sy += high ? ry : y;
+      }
+      const bool done = g1 <= p.tok_end && g1 > p.tok_begin;
+      if (done && p.group_sum != nullptr) {
+        const float inv_n = static_cast<float>(p.gs);
+        float ox = sx / inv_n, oy = sy / inv_n;
+        if (!high) {
+          float c, s;
+          rope_cs(static_cast<double>(g0) + 0.5 * (p.gs - 1), freq, c, s);
+          const float mx = ox, my = oy;
+          ox = mx * c - my * s;
+          oy = mx * s + my * c;
+        }
+        const int64_t row = (static_cast<int64_t>(b) * p.Hkv + kvh) * (p.kv_cap / p.gs) + g0 / p.gs;
+        p.group_sum[row * p.d + lane] = ox;
+        p.group_sum[row * p.d + lane + h] = oy;
+      }
+    }
+    cx += sx;
+    cy += sy;
+  }
+
+  const bool chunk_done = c1 <= p.tok_end && c1 > p.tok_begin;  // uniform over the block
+  if (!chunk_done) return;
+  __shared__ float part[kSumWaves][64][2];
+  part[wave][lane][0] = cx;
+  part[wave][lane][1] = cy;
+  __syncthreads();
+  if (wave == 0 && active) {
+    float sx = 0.f, sy = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSumWaves; ++w) {
+      sx += part[w][lane][0];
+      sy += part[w][lane][1];
+    }
+    const float n = static_cast<float>(p.C);
+    float ox = sx / n, oy = sy / n;
+    if (!high) {
+      float c, s;
+      rope_cs(static_cast<double>(c0) + 0.5 * (p.C - 1), freq, c, s);
+      const float mx = ox, my = oy;
+      ox = mx * c - my * s;
+      oy = mx * s + my * c;
+    }
+    const int64_t row = (static_cast<int64_t>(b) * p.Hkv + kvh) * (p.kv_cap / p.C) + m;
+    p.chunk_sum[row * p.d + lane] = ox;
+    p.chunk_sum[row * p.d + lane + h] = oy;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_begin,
+                            int64_t tok_end, void* k_rot, float* chunk_sum,
+                            float* group_sum, hipStream_t stream) {
+  SumParams p;
+  p.k_raw = k_raw;
+  p.k_rot = k_rot;
+  p.chunk_sum = chunk_sum;
+  p.group_sum = group_sum;
+  p.kv_cap = g.kv_cap;
+  p.tok_begin = tok_begin;
+  p.tok_end = tok_end;
+  p.chunk_first = tok_begin / g.C;
+  p.Hkv = g.Hkv;
+  p.d = g.d;
+  p.C = g.C;
+  p.gs = g.gs;
+  p.r = g.r;
+  p.n_hf = g.n_hf;
+  p.rope = g.rope;
+  const int64_t chunk_last = (tok_end - 1) / g.C;
+  dim3 grid(static_cast<unsigned>(chunk_last - p.chunk_first + 1), g.Hkv, g.B);
+  dim3 block(kSumWaves * 64);
+  if (g.bf16)
+    hipLaunchKernelGGL(summarize_kernel<true>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(summarize_kernel<false>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace hga

@@ -1,0 +1,202 @@
+/*
+ * hga.h -- C ABI of the MI355X (gfx950) routed exact-token attention library
+ * (Hierarchical Global Attention, arXiv:2606.30709).
+ *
+ * The pages that define the method (the xllm-io paper-review page, section 3
+ * "technical architecture") describe a key/value store with four operations:
+ * append a closed chunk, read the chunk summaries for routing, fetch the group
+ * summaries for the second routing level, and gather the exact token K/V of
+ * the selected chunks or groups; routing is kept apart from storage.  The
+ * entry points below map onto them:
+ *
+ *   append               -> hga_build_summaries
+ *   read + fetch (route) -> hga_route
+ *   gather + attend      -> hga_attend, hga_attend_host_tiered
+ *   Eq. (1) reference    -> hga_dense_causal
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Positions are absolute token indices starting at 0.  Chunk m covers tokens
+ * [m*C, (m+1)*C); group (granule) g covers tokens [g*g_s, (g+1)*g_s).  Query
+ * chunk t covers query positions [t*C, (t+1)*C).
+ *
+ * Layouts (row-major, innermost last):
+ *   k_raw, k_rot, v : [B][Hkv][kv_cap][d]   element dtype (f32 or bf16);
+ *                     slot j holds the token at position j.
+ *   q_raw, out      : [B][Hq][n_q][d]       query qi sits at q_pos0 + qi.
+ *   lse             : [B][Hq][n_q]          f32, natural-log sum-exp.
+ *   chunk_sum       : [B][Hkv][kv_cap/C][d]   f32
+ *   group_sum       : [B][Hkv][kv_cap/g_s][d] f32
+ *   NQC (query chunks of a call) = (q_pos0+n_q-1)/C - q_pos0/C + 1; unit
+ *   (b, kvh, t) is stored at index [b][kvh][t - q_pos0/C].
+ *   chunk_idx       : [B][Hkv][NQC][K_c]    int32 ascending, -1 padded
+ *   group_idx       : [B][Hkv][NQC][K_g]    int32 ascending, -1 padded
+ *   granules        : [B][Hkv][NQC][G_max]  int32 ascending unique, -1 padded
+ *   granule_count   : [B][Hkv][NQC]         int32
+ *
+ * RoPE: theta_i = rope_theta^(-2i/d) for pair i < d/2; pair i is the
+ * elements (i, i + d/2) (half-split layout); R_p turns a pair by p*theta_i.
+ * Angles are formed in double precision and reduced before an f32 sincos.
+ *
+ * Ownership: the caller owns every buffer and allocates it; the library never
+ * allocates device memory and keeps no mutable global state apart from a
+ * per-thread last-HIP-error code.  All device pointers must be 16-byte
+ * aligned device (or managed) memory.
+ *
+ * Asynchrony: every entry point enqueues work on `stream` (a hipStream_t,
+ * NULL = the default stream) and returns without synchronising, except
+ * hga_attend_host_tiered which is documented as host-blocking.
+ *
+ * Errors: all arguments are validated on the host before anything is
+ * enqueued; on an error nothing is enqueued and the outputs are untouched.
+ * No C++ exception crosses the ABI.  HGA_ERR_HIP means a HIP launch or
+ * runtime call failed; hga_last_hip_error() returns its hipError_t code.
+ *
+ * Thread safety: the entry points are re-entrant given distinct workspaces.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_INVALID_ARGUMENT = 1,
+  HGA_ERR_UNSUPPORTED = 2,
+  HGA_ERR_WORKSPACE_TOO_SMALL = 3,
+  HGA_ERR_HIP = 4
+} hga_status;
+
+/* q, k, v and out share one element type. */
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+
+typedef struct hga_config {
+  int32_t chunk_size;      /* C: tokens per chunk (framework paragraph)           */
+  int32_t group_size;      /* g_s: tokens per group; C % g_s == 0                 */
+  int32_t n_sink_chunks;   /* F: first chunks always visible (routing policy)    */
+  int32_t n_recent_chunks; /* L: last closed chunks always visible               */
+  int32_t top_chunks;      /* K_c: routed middle chunks (selection equation)     */
+  int32_t top_groups;      /* K_g: routed groups; 0 = routed chunks open whole   */
+  int32_t n_hf_pairs;      /* RoPE pairs [0, n_hf) are high frequency (Mixed-RoPE) */
+  int32_t head_dim;        /* d in {64, 128}                                      */
+  int32_t n_q_heads;       /* Hq; Hq % Hkv == 0, query head h reads KV head h/(Hq/Hkv) */
+  int32_t n_kv_heads;      /* Hkv                                                 */
+  double rope_theta;       /* RoPE base, > 0                                      */
+  float softmax_scale;     /* 0 => 1/sqrt(d) (Eq. 1)                              */
+} hga_config;
+
+/*
+ * hga_build_summaries -- "append closed chunk".
+ *
+ * Mixed-RoPE summary equation (xllm-io page, section 3): for a closed chunk
+ * (or group) G with first token f and middle position p_mid = f + (|G|-1)/2,
+ *   pairs i <  n_hf : (1/|G|) sum_{j in G} R_j k_j        (rotate, then mean)
+ *   pairs i >= n_hf : R_{p_mid}((1/|G|) sum_{j in G} k_j)  (mean, then rotate)
+ *
+ * Rotates the raw keys of tokens [tok_begin, tok_end) into k_rot (when k_rot
+ * is not NULL; stored in the input dtype, round-to-nearest-even for bf16) and
+ * writes the summary of every chunk and group whose last token lies in
+ * [tok_begin, tok_end).  Summaries read every token of their block from
+ * k_raw, so k_raw must already hold the earlier tokens of a block that
+ * completes in the range.  Used both for prefill (0, n) and for the decode
+ * append of one token (p, p+1).
+ *
+ * group_sum may be NULL iff top_groups == 0.  Requires kv_cap % C == 0 and
+ * 0 <= tok_begin < tok_end <= kv_cap.
+ */
+hga_status hga_build_summaries(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                               const void* k_raw, int64_t kv_cap,
+                               int64_t tok_begin, int64_t tok_end,
+                               void* k_rot, float* chunk_sum, float* group_sum,
+                               void* stream);
+
+/* Granules one unit can attend to at most:
+ * (C/g_s)(1 + F + max(L,1)) + (K_g if K_g > 0 else K_c C/g_s).  -1 on a bad config. */
+int32_t hga_max_granules(const hga_config* cfg);
+
+/* Workspace bytes hga_route needs for this call shape (may be 0). */
+size_t hga_route_workspace_bytes(const hga_config* cfg, int32_t batch,
+                                 int64_t q_pos0, int64_t n_q);
+
+/*
+ * hga_route -- "read chunk summaries" and "fetch group summaries".
+ *
+ * Routing policy and selection equation (xllm-io page, section 3).  For each
+ * unit (sequence b, KV head kvh, query chunk t):
+ *   Fixed(t)  = first min(F,t) chunks  U  last L closed chunks  U  {t-1}
+ *   Middle(t) = closed chunks m < t not in Fixed(t)
+ *   s[m]      = max over the unit's query rows (queries of chunk t inside
+ *               [q_pos0, q_pos0+n_q) x the G query heads of kvh) of q~ . c_m
+ *               (q~ = RoPE-rotated query, no 1/sqrt(d))
+ *   M_sel     = first min(K_c, |Middle|) of Middle by (s descending, m ascending)
+ *   G_sel     = when K_g > 0: the same over the C/g_s groups of each chunk in
+ *               M_sel (global id m*C/g_s + g), scored against group_sum
+ *   granules  = Fixed(t) granules U routed groups (or the granules of the
+ *               chunks in M_sel when K_g == 0) U the granules of chunk t whose
+ *               first token is <= the unit's last query (sorted, unique)
+ * Scores are evaluated with split-bf16 matrix-core products (hi*hi + hi*lo +
+ * lo*hi, f32 accumulation), about 1e-5 relative to an f64 evaluation; exact
+ * ties go to the lowest index.
+ *
+ * chunk_sum must hold every chunk < the last query chunk; group_sum every
+ * group of those chunks (group_sum / group_idx may be NULL iff K_g == 0).
+ * Requires kv_cap % C == 0 and q_pos0 + n_q <= kv_cap.
+ */
+hga_status hga_route(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                     const void* q_raw, int64_t q_pos0, int64_t n_q,
+                     const float* chunk_sum, const float* group_sum, int64_t kv_cap,
+                     int32_t* chunk_idx, int32_t* group_idx,
+                     int32_t* granules, int32_t* granule_count,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes hga_attend / hga_dense_causal need for this call shape. */
+size_t hga_attend_workspace_bytes(const hga_config* cfg, int32_t batch,
+                                  int64_t q_pos0, int64_t n_q);
+
+/*
+ * hga_attend -- "gather exact token K/V" + exact-token softmax attention.
+ *
+ * Exact-token output paragraph and Eq. (1) (xllm-io page, section 3): the
+ * query at position i with head h attends, with softmax over exactly these
+ * tokens, to every token j of its unit's granule list with j < t*C or
+ * j <= i (causal inside the current chunk):
+ *   out[i,h] = sum_j softmax_j(scale * q~_{i,h} . k~_j) v_j
+ * granules / granule_count are those written by hga_route (or any ascending
+ * list of granules inside [0, kv_cap/g_s) with count <= G_max; lists must
+ * not repeat a granule).  k_rot holds RoPE-rotated keys (hga_build_summaries).
+ * bf16 runs QK^T and PV on bf16 matrix cores (P rounded to bf16) with f32
+ * online softmax; f32 runs on f32 vector ALUs.  lse may be NULL.
+ */
+hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                      const void* q_raw, int64_t q_pos0, int64_t n_q,
+                      const void* k_rot, const void* v, int64_t kv_cap,
+                      const int32_t* granules, const int32_t* granule_count,
+                      void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hga_dense_causal -- Eq. (1): every query i attends to all keys j <= i.
+ * The reference the routed path reduces to when the budgets cover every
+ * middle chunk.  Same layouts and numerics as hga_attend.
+ */
+hga_status hga_dense_causal(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                            const void* q_raw, int64_t q_pos0, int64_t n_q,
+                            const void* k_rot, const void* v, int64_t kv_cap,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+const char* hga_status_string(hga_status status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int hga_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

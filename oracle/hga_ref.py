@@ -173,12 +173,13 @@ def query_chunks(q_pos0: int, n_q: int, C: int) -> range:
     return range(q_pos0 // C, (q_pos0 + n_q - 1) // C + 1)
 
 
-def unit_rows(q_rot_b: np.ndarray, kvh: int, qpos: np.ndarray, q_pos0: int, p: Params) -> np.ndarray:
-    """Rotated query rows (query, head) of one unit: heads h with h // G == kvh
-    (standard GQA).  Returns [len(qpos) * G, d]."""
+def unit_rows(q_b: np.ndarray, kvh: int, qpos: np.ndarray, q_pos0: int, p: Params) -> np.ndarray:
+    """RoPE-rotated query rows (query, head) of one unit, from the raw
+    queries q_b [Hq][n_q][d] of one sequence: heads h with h // G == kvh
+    (standard GQA).  Returns [G * len(qpos), d]."""
     G = p.Hq // p.Hkv
-    rows = q_rot_b[kvh * G:(kvh + 1) * G, qpos - q_pos0, :]   # [G, nq, d]
-    return rows.reshape(-1, p.d)
+    raw = np.asarray(q_b[kvh * G:(kvh + 1) * G][:, qpos - q_pos0, :], dtype=np.float64)
+    return rope(raw, qpos, p.theta).reshape(-1, p.d)
 
 
 def route_unit(rows: np.ndarray, t: int, csum: np.ndarray, gsum: np.ndarray, p: Params) -> dict:
@@ -243,8 +244,7 @@ def route(q_raw, q_pos0: int, n_q: int, csum, gsum, p: Params, units=None) -> di
     (index lists ascending, -1 padded) and ``info[(b,kvh,t)]`` with the
     per-unit route_unit() result.  Units not routed hold -1 / 0.
     """
-    q = np.asarray(q_raw, dtype=np.float64)
-    B = q.shape[0]
+    B = q_raw.shape[0]
     tq = list(query_chunks(q_pos0, n_q, p.C))
     t0 = tq[0]
     nqc = len(tq)
@@ -256,12 +256,9 @@ def route(q_raw, q_pos0: int, n_q: int, csum, gsum, p: Params, units=None) -> di
     info = {}
     if units is None:
         units = [(b, h, t) for b in range(B) for h in range(p.Hkv) for t in tq]
-    qrot = {}
     for (b, kvh, t) in units:
-        if b not in qrot:
-            qrot[b] = rope(q[b], q_pos0 + np.arange(n_q), p.theta)
         qpos = unit_queries(t, q_pos0, n_q, p.C)
-        rows = unit_rows(qrot[b], kvh, qpos, q_pos0, p)
+        rows = unit_rows(q_raw[b], kvh, qpos, q_pos0, p)
         res = route_unit(rows, t, np.asarray(csum[b, kvh], np.float64),
                          np.asarray(gsum[b, kvh], np.float64) if gsum is not None else None, p)
         gl = visible_granules(t, int(qpos[-1]), res["sel_chunks"], res["sel_groups"], p)
@@ -301,20 +298,16 @@ def attend_given(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, p: Par
     Returns out [B,Hq,n_q,d], lse [B,Hq,n_q]; rows of units not listed in
     ``units`` are NaN.
     """
-    q = np.asarray(q_raw, dtype=np.float64)
-    B = q.shape[0]
+    B = q_raw.shape[0]
     G = p.Hq // p.Hkv
     tq = list(query_chunks(q_pos0, n_q, p.C))
     if t0 is None:
         t0 = tq[0]
-    out = np.full(q.shape, np.nan)
-    lse = np.full(q.shape[:3], np.nan)
+    out = np.full(q_raw.shape, np.nan)
+    lse = np.full(q_raw.shape[:3], np.nan)
     if units is None:
         units = [(b, h, t) for b in range(B) for h in range(p.Hkv) for t in tq]
-    qrot = {}
     for (b, kvh, t) in units:
-        if b not in qrot:
-            qrot[b] = rope(q[b], q_pos0 + np.arange(n_q), p.theta)
         gl = np.asarray(granules[b, kvh, t - t0, : int(count[b, kvh, t - t0])], np.int64)
         tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
         kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta)
@@ -323,7 +316,7 @@ def attend_given(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, p: Par
         mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
         for hl in range(G):
             h = kvh * G + hl
-            rows = qrot[b][h, qpos - q_pos0, :]
+            rows = rope(np.asarray(q_raw[b, h, qpos - q_pos0, :], np.float64), qpos, p.theta)
             o, ls = _softmax_attend(rows, kk, vv, mask, p.softmax_scale)
             out[b, h, qpos - q_pos0] = o
             lse[b, h, qpos - q_pos0] = ls

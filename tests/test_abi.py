@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/hga.h declares, and rejects bad arguments on the host before any
+HIP call (nothing is enqueued on an error)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_kv_routing_amd as H
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(H.LIB_PATH):
+        pytest.skip("libhga.so not built (python -m hierarchical_kv_routing_amd.build)")
+    return H.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "hga.h")).read()
+    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert set(names) == set(H.ABI_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in H._STATUS.items():
+        assert lib.hga_status_string(code).decode() == name
+    assert lib.hga_last_hip_error() == 0
+
+
+def test_max_granules(lib):
+    # (C/g_s)(1 + F + max(L,1)) + routed
+    assert H.max_granules(H.Config.from_workload(W.QWEN3_PREFILL)) == 4 * 11 + 32
+    assert H.max_granules(H.Config.from_workload(W.HOST_TIERED_CHUNK)) == 4 * 11 + 24 * 4
+    assert H.max_granules(H.Config.from_workload(W.TINY_F32)) == 4 * 5 + 4
+    assert H.max_granules(H.Config.from_workload(W.TINY_F32, n_recent_chunks=0)) == 4 * 4 + 4
+    assert H.max_granules(H.Config.from_workload(W.TINY_F32, group_size=48)) == -1
+
+
+def _route(lib, cfg, dtype=1, B=1, q=16, q_pos0=0, n_q=64, cs=16, gs=16, cap=64,
+           ci=16, gi=16, gr=16, gc=16, ws=None, wsb=0):
+    return lib.hga_route(ctypes.byref(cfg.c()), dtype, B, q, q_pos0, n_q, cs, gs, cap, ci, gi, gr, gc,
+                         ws, wsb, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(group_size=48), 1),          # C % g_s != 0
+    (dict(group_size=0), 1),
+    (dict(n_q_heads=6, n_kv_heads=4), 1),
+    (dict(n_hf_pairs=65), 1),
+    (dict(n_hf_pairs=-1), 1),
+    (dict(top_chunks=-1), 1),
+    (dict(rope_theta=0.0), 1),
+    (dict(rope_theta=float("nan")), 1),
+    (dict(softmax_scale=-1.0), 1),
+    (dict(head_dim=96), 2),            # d in {64, 128}
+    (dict(chunk_size=128, group_size=16), 2),
+])
+def test_bad_config_rejected(lib, over, status):
+    cfg = H.Config.from_workload(W.QWEN3_PREFILL, **over)
+    # Pointers here are never dereferenced: validation fails first.
+    assert _route(lib, cfg) == status
+    assert lib.hga_build_summaries(ctypes.byref(cfg.c()), 1, 1, 16, 64, 0, 64, None, 16, 16, None) == status
+    assert lib.hga_attend(ctypes.byref(cfg.c()), 1, 1, 16, 0, 64, 16, 16, 64, 16, 16, 16, None,
+                          None, 0, None) == status
+
+
+def test_bad_arguments_rejected(lib):
+    cfg = H.Config.from_workload(W.QWEN3_PREFILL)
+    assert _route(lib, cfg, dtype=7) == 1
+    assert _route(lib, cfg, B=0) == 1
+    assert _route(lib, cfg, cap=100) == 1              # kv_cap % C
+    assert _route(lib, cfg, n_q=65) == 1               # q_pos0 + n_q > kv_cap
+    assert _route(lib, cfg, q_pos0=-1) == 1
+    assert _route(lib, cfg, q=None) == 1
+    assert _route(lib, cfg, q=18) == 1                 # misaligned
+    assert _route(lib, cfg, gr=None) == 1
+    assert _route(lib, cfg, gs=None) == 1              # K_g > 0 needs group summaries
+    assert _route(lib, cfg, n_q=0) == 0                # empty call: a no-op
+    # summaries: empty / reversed / out-of-range token ranges
+    c = ctypes.byref(cfg.c())
+    assert lib.hga_build_summaries(c, 1, 1, 16, 64, 10, 10, None, 16, 16, None) == 1
+    assert lib.hga_build_summaries(c, 1, 1, 16, 64, 0, 65, None, 16, 16, None) == 1
+    assert lib.hga_build_summaries(c, 1, 1, 16, 64, 0, 64, None, 16, None, None) == 1
+    # dense / attend null pointers
+    assert lib.hga_dense_causal(c, 1, 1, 16, 0, 64, None, 16, 64, 16, None, None, 0, None) == 1
+    assert lib.hga_attend(c, 1, 1, 16, 0, 64, 16, 16, 64, None, 16, 16, None, None, 0, None) == 1
+
+
+def test_workspace_checks(lib):
+    cfg = H.Config.from_workload(W.DECODE_64K)
+    need = H.route_workspace_bytes(cfg, 16, 65536, 1)
+    # segmented decode routing: one f32 score per middle chunk per unit
+    assert need == 16 * 4 * 1014 * 4
+    assert _route(lib, cfg, B=16, q_pos0=65536, n_q=1, cap=65600, ws=16, wsb=need - 4) == 3
+    assert _route(lib, cfg, B=16, q_pos0=65536, n_q=1, cap=65600, ws=None, wsb=0) == 3
+    assert H.attend_workspace_bytes(cfg, 16, 65536, 1) > 0
+    big = H.Config.from_workload(W.QWEN3_PREFILL)
+    assert H.route_workspace_bytes(big, 1, 0, 32768) == 0

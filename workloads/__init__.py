@@ -211,18 +211,33 @@ def q_slab(w: Workload, seed: int, b: int, hq: int) -> np.ndarray:
     return _finish(w, q)
 
 
-def make_inputs(w: Workload, seed: int = 0):
-    """Whole tensors: q [B,Hq,n_q,d], k [B,Hkv,kv_cap,d], v [B,Hkv,kv_cap,d] (float32)."""
+def make_inputs(w: Workload, seed: int = 0, threads: int = 1):
+    """Whole tensors: q [B,Hq,n_q,d], k [B,Hkv,kv_cap,d], v [B,Hkv,kv_cap,d]
+    (float32; bf16 workloads hold exact bfloat16 values).  Slabs are
+    independent streams, so ``threads`` > 1 gives the same values."""
+    from concurrent.futures import ThreadPoolExecutor
     B, Hq, Hkv, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     q = np.empty((B, Hq, w.n_q, d), dtype=np.float32)
     k = np.empty((B, Hkv, w.kv_cap, d), dtype=np.float32)
     v = np.empty((B, Hkv, w.kv_cap, d), dtype=np.float32)
+    jobs = []
     for b in range(B):
         for h in range(Hq):
-            q[b, h] = q_slab(w, seed, b, h)
+            jobs.append((q, b, h, q_slab))
         for h in range(Hkv):
-            k[b, h] = k_slab(w, seed, b, h)
-            v[b, h] = v_slab(w, seed, b, h)
+            jobs.append((k, b, h, k_slab))
+            jobs.append((v, b, h, v_slab))
+
+    def run(job):
+        arr, b, h, fn = job
+        arr[b, h] = fn(w, seed, b, h)
+
+    if threads <= 1:
+        for j in jobs:
+            run(j)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, jobs))
     return q, k, v
 
 
