@@ -15,7 +15,7 @@ Also measured in the same run (extra fields of the one JSON line):
   cpu_baseline -- the CPU oracle on a bounded sample of the prefill step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prefill|decode|smalllm|copy]
+       [--only prefill|decode|smalllm|host|copy]
 """
 from __future__ import annotations
 
@@ -180,6 +180,62 @@ def bench_smalllm(args):
     return pipe, dict(ms=ms, stage_ms=stage, mtok_s=w.batch * w.n_q / (ms * 1e-3) / 1e6)
 
 
+def pinned_copy_gbs(torch, nbytes=256 << 20, reps=5):
+    """Measured host->device rate of one large pinned-memory copy."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8):
+    """Prefill with token K/V in pinned host RAM: route + host packing + H2D of
+    the routed granules on a side stream + attention, one call per step."""
+    import torch
+    import hierarchical_kv_routing_amd as H
+    pipe = Pipeline(w)
+    pipe.build()
+    torch.cuda.synchronize()
+    # attention alone on device-resident K/V (same granules): the overlap reference
+    pipe.route()
+    _, st = timed_steps(torch, [("attend", pipe.attend)], 3, 1)
+    store = H.host_store(pipe.cfg, pipe.k_rot, pipe.v)
+    dev_b, host_b = H.host_tiered_buffer_bytes(pipe.cfg, torch.bfloat16, w.batch, w.q_pos0, w.n_q,
+                                               wmax, slots)
+    dev = torch.empty(dev_b, dtype=torch.uint8, device="cuda:0")
+    host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
+    lse = torch.empty(pipe.q.shape[:3], dtype=torch.float32, device="cuda:0")
+    xs = torch.cuda.Stream()
+
+    def call():
+        return H.attend_host_tiered(pipe.cfg, pipe.q, w.q_pos0, store, pipe.k.shape[2], pipe.csum,
+                                    pipe.gsum, pipe.out, lse, dev, host, wmax, slots, threads,
+                                    copy_stream=xs)
+
+    call()
+    torch.cuda.synchronize()
+    steps = max(2, min(args.steps, 4))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stats = call()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    t_copy = stats["bytes_h2d"] / (copy_gbs * 1e9)
+    t_attn = st["attend"] * 1e-3
+    return dict(workload=w.name, ms=t * 1e3, mtok_s=w.n_q / t / 1e6,
+                h2d_gb=stats["bytes_h2d"] / 1e9, h2d_gbs=stats["bytes_h2d"] / t / 1e9,
+                pinned_copy_peak_gbs=copy_gbs, windows=stats["windows"],
+                granules_copied=stats["granules_copied"], host_pack_s=stats["pack_seconds"],
+                attend_device_ms=st["attend"], overlap=(t_copy + t_attn) / t)
+
+
 def cpu_baseline(pipe, budget_s=12.0):
     """Time the CPU oracle on a bounded, unbiased sample of the prefill step
     and scale to the whole step: summaries of one (sequence, KV head) slab
@@ -238,7 +294,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "copy"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -257,6 +313,11 @@ def main():
     if args.only == "decode":
         _, dec = bench_decode(args)
         print(json.dumps(dict(decode=dec)), flush=True)
+        return
+    if args.only == "host":
+        gbs = pinned_copy_gbs(torch)
+        res = {w.name: bench_host_tier(args, w, gbs) for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP)}
+        print(json.dumps(dict(host_tiered=res)), flush=True)
         return
     if args.only == "smalllm":
         _, sm = bench_smalllm(args)
@@ -296,6 +357,13 @@ def main():
         _, sm = bench_smalllm(args)
         line["smalllm"] = dict(workload=W.SMALLLM_PREFILL.name, mtok_s=sm["mtok_s"], ms=sm["ms"],
                                stage_ms=sm["stage_ms"])
+        torch.cuda.empty_cache()
+        gbs = pinned_copy_gbs(torch)
+        line["host_tiered"] = {}
+        for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP):
+            line["host_tiered"][w.name] = bench_host_tier(args, w, gbs)
+            log(f"[bench] host tier {w.name}: {line['host_tiered'][w.name]}")
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 

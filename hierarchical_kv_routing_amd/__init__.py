@@ -31,6 +31,7 @@ HGA_F32, HGA_BF16 = 0, 1
 # Every symbol include/hga.h declares.
 ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_bytes",
                "hga_route", "hga_attend_workspace_bytes", "hga_attend", "hga_dense_causal",
+               "hga_host_tiered_buffer_bytes", "hga_attend_host_tiered",
                "hga_status_string", "hga_last_hip_error")
 
 
@@ -47,6 +48,12 @@ class hga_config(ctypes.Structure):
                 ("n_hf_pairs", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+
+
+class hga_tier_stats(ctypes.Structure):
+    _fields_ = [("windows", ctypes.c_int64), ("granules_copied", ctypes.c_int64),
+                ("bytes_h2d", ctypes.c_int64), ("pack_seconds", ctypes.c_double),
+                ("host_seconds", ctypes.c_double)]
 
 
 @dataclass(frozen=True)
@@ -111,6 +118,10 @@ def lib() -> ctypes.CDLL:
         "hga_attend_workspace_bytes": (SZ, [CP, I32, I64, I64]),
         "hga_attend": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, SZ, P]),
         "hga_dense_causal": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, SZ, P]),
+        "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64,
+                                               ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
+                                         I32, I64, I32, P, P, ctypes.POINTER(hga_tier_stats)]),
         "hga_status_string": (ctypes.c_char_p, [I32]),
         "hga_last_hip_error": (ctypes.c_int, []),
     }
@@ -277,6 +288,65 @@ def dense_causal(cfg: Config, q, q_pos0: int, k_rot, v, out, lse=None, workspace
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(q, stream))
     _check(st, "hga_dense_causal")
+
+
+def host_tiered_buffer_bytes(cfg: Config, dtype, batch: int, q_pos0: int, n_q: int,
+                             max_window_chunks: int, slots_per_window: int):
+    """(device_bytes, host_bytes) of the staging buffers the host tier needs."""
+    torch = _torch()
+    code = HGA_BF16 if dtype == torch.bfloat16 else HGA_F32
+    dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib().hga_host_tiered_buffer_bytes(ctypes.byref(cfg.c()), code, batch, q_pos0, n_q,
+                                            max_window_chunks, slots_per_window,
+                                            ctypes.byref(dev), ctypes.byref(host))
+    _check(st, "hga_host_tiered_buffer_bytes")
+    return dev.value, host.value
+
+
+def host_store(cfg: Config, k_rot, v):
+    """Pinned host copy of (rotated K, V) in the granule-major layout the host
+    tier reads: [B][Hkv][kv_cap/g_s][2][g_s][d]."""
+    torch = _torch()
+    B, Hkv, cap, d = k_rot.shape
+    gs = cfg.group_size
+    ng = cap // gs
+    store = torch.empty((B, Hkv, ng, 2, gs, d), dtype=k_rot.dtype, pin_memory=True)
+    both = torch.stack([k_rot.view(B, Hkv, ng, gs, d), v.view(B, Hkv, ng, gs, d)], dim=3)
+    store.copy_(both)
+    return store
+
+
+def attend_host_tiered(cfg: Config, q, q_pos0: int, kv_host, kv_cap: int, chunk_sum, group_sum,
+                       out, lse, dev_staging, host_staging, max_window_chunks: int,
+                       slots_per_window: int, n_threads: int = 8, compute_stream=None,
+                       copy_stream=None) -> dict:
+    """Route + attention with token K/V in pinned host RAM (host-blocking until
+    the last attention launch is enqueued).  Returns the call's statistics."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    _dev(q, "q")
+    _dev(out, "out", q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, n_q), torch.float32)
+    _dev(chunk_sum, "chunk_sum", (B, cfg.n_kv_heads, kv_cap // cfg.chunk_size, d), torch.float32)
+    _dev(group_sum, "group_sum", (B, cfg.n_kv_heads, kv_cap // cfg.group_size, d), torch.float32)
+    _dev(dev_staging, "dev_staging")
+    if kv_host.is_cuda or not kv_host.is_pinned() or not host_staging.is_pinned():
+        raise HGAError("kv_host and host_staging must be pinned host tensors")
+    if tuple(kv_host.shape) != (B, cfg.n_kv_heads, kv_cap // cfg.group_size, 2, cfg.group_size, d):
+        raise HGAError(f"kv_host has shape {tuple(kv_host.shape)}")
+    cs = compute_stream if compute_stream is not None else torch.cuda.current_stream(q.device)
+    xs = copy_stream if copy_stream is not None else cs
+    stats = hga_tier_stats()
+    st = lib().hga_attend_host_tiered(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q, kv_host.data_ptr(),
+        kv_cap, chunk_sum.data_ptr(), group_sum.data_ptr() if group_sum is not None else None,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        dev_staging.data_ptr(), dev_staging.numel() * dev_staging.element_size(),
+        host_staging.data_ptr(), host_staging.numel() * host_staging.element_size(),
+        max_window_chunks, slots_per_window, n_threads, ctypes.c_void_p(cs.cuda_stream),
+        ctypes.c_void_p(xs.cuda_stream), ctypes.byref(stats))
+    _check(st, "hga_attend_host_tiered")
+    return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}
 
 
 def default_scale(cfg: Config) -> float:

@@ -10,10 +10,15 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-hga_status hip_fail(hipError_t e) {
+}  // namespace
+
+hga_status hga::hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
   return HGA_ERR_HIP;
 }
+
+namespace {
+using hga::hip_fail;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -41,8 +46,10 @@ int32_t max_granules(const hga_config* c) {
   return r * (1 + c->n_sink_chunks + lp) + routed;
 }
 
-hga_status make_geometry(const hga_config* c, hga_dtype dt, int32_t batch, int64_t kv_cap,
-                         int64_t q_pos0, int64_t n_q, hga::Geometry& g) {
+}  // namespace
+
+hga_status hga::make_geometry(const hga_config* c, hga_dtype dt, int32_t batch, int64_t kv_cap,
+                              int64_t q_pos0, int64_t n_q, hga::Geometry& g) {
   hga_status st = check_config(c);
   if (st != HGA_OK) return st;
   if (dt != HGA_F32 && dt != HGA_BF16) return HGA_ERR_INVALID_ARGUMENT;
@@ -77,6 +84,8 @@ hga_status make_geometry(const hga_config* c, hga_dtype dt, int32_t batch, int64
   return HGA_OK;
 }
 
+namespace {
+using hga::make_geometry;
 }  // namespace
 
 extern "C" {

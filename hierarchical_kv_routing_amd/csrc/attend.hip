@@ -44,9 +44,17 @@ struct AttendParams {
   float* lse;
   const int32_t* gran;
   const int32_t* gcnt;
+  // Pool mode (host tier): K and V of granule-list entry i of a unit live in
+  // a granule-major staging pool [slot][2][g_s][D] at slot pool_slot[i];
+  // k and v then both point at the pool.
+  const int32_t* pool_slot;
+  int64_t pool_slots;
   float* ws_o;   // [slot][split][Rcap][D]
   float* ws_ml;  // [slot][split][Rcap][2]
   int64_t q_pos0, n_q, kv_cap, t0, nqc;
+  // q / out / lse rows: row r of a (sequence, head) holds position q_row0 + r
+  // and rows are q_stride apart (a window call covers part of the array).
+  int64_t q_stride, q_row0;
   int B, Hq, Hkv, G, d, C, gs, gmax, Rcap;
   int nw, slices, splits, keys_per_split;
   int dense;
@@ -84,12 +92,32 @@ __device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
 }
 
 // Token held by key slot s of a unit (slot order = ascending granules), or
-// -1 when a caller-supplied granule id lies outside [0, kv_cap / g_s).
+// -1 when a caller-supplied granule id lies outside [0, kv_cap / g_s) (or,
+// in pool mode, its pool slot lies outside the pool).
 __device__ __forceinline__ int64_t slot_token(const AttendParams& p, const AUnit& w, int s) {
   if (p.dense) return s;
   const int gi = s / p.gs;
   const int64_t tok = static_cast<int64_t>(p.gran[w.slot * p.gmax + gi]) * p.gs + (s - gi * p.gs);
+  if (p.pool_slot != nullptr) {
+    const int64_t ps = p.pool_slot[w.slot * p.gmax + gi];
+    if (ps < 0 || ps >= p.pool_slots) return -1;
+  }
   return (tok >= 0 && tok < p.kv_cap) ? tok : -1;
+}
+
+// Element offsets (from p.k and p.v) of the K and V rows of key slot s
+// holding token tok.
+template <int D>
+__device__ __forceinline__ void kv_offsets(const AttendParams& p, const AUnit& w, int s, int64_t tok,
+                                           int64_t slab, int64_t& ko, int64_t& vo) {
+  if (p.pool_slot != nullptr) {
+    const int gi = s / p.gs;
+    const int64_t ps = p.pool_slot[w.slot * p.gmax + gi];
+    ko = (ps * 2 * p.gs + (s - gi * p.gs)) * D;
+    vo = ko + static_cast<int64_t>(p.gs) * D;
+  } else {
+    ko = vo = (slab + tok) * D;
+  }
 }
 
 // K row index read by MFMA row m: bits 2 and 3 swapped (an involution).
@@ -119,9 +147,10 @@ __device__ __forceinline__ void load_tile(const AttendParams& p, const AUnit& w,
       const int gs = kbase + s;
       const int64_t tok = gs < kend ? slot_token(p, w, gs) : -1;
       if (tok >= 0) {
-        const int64_t e = (slab + tok) * D + sl * 8;
-        kk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e);
+        int64_t ko, vo;
+        kv_offsets<D>(p, w, gs, tok, slab, ko, vo);
+        kk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + ko + sl * 8);
+        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + vo + sl * 8);
       }
     }
     tr.k[i] = kk;
@@ -210,7 +239,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   {
     float x[KS][8];
     const int64_t base =
-        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (qpos - p.q_pos0)) * D;
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (row_ok) {
@@ -311,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
 
   if (!row_ok) return;
   // O^T register j of block db is d = db*32 + 8*(j/4) + 4*hsub + (j%4).
-  const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (qpos - p.q_pos0);
+  const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0);
   if (p.splits == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     uint16_t* out = static_cast<uint16_t*>(p.out) + orow * D;
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   float q[D];
   {
     const float* src = static_cast<const float*>(p.q) +
-        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (qpos - p.q_pos0)) * D;
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0)) * D;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
       const float a = row_ok ? src[i] : 0.f, b = row_ok ? src[i + H] : 0.f;
@@ -398,8 +427,10 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       const int64_t tok = kb + s < kend ? slot_token(p, w, kb + s) : -1;
       if (tok >= 0) {
-        kk =reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + (slab + tok) * D)[c4];
-        vv = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + (slab + tok) * D)[c4];
+        int64_t ko, vo;
+        kv_offsets<D>(p, w, kb + s, tok, slab, ko, vo);
+        kk = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + ko)[c4];
+        vv = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + vo)[c4];
       }
       reinterpret_cast<float4*>(&kt[s][0])[c4] = kk;
       reinterpret_cast<float4*>(&vt[s][0])[c4] = vv;
@@ -433,7 +464,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     m_run = m_new;
   }
   if (!row_ok) return;
-  const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (qpos - p.q_pos0);
+  const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0);
   if (p.splits == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* out = static_cast<float*>(p.out) + orow * D;
@@ -480,7 +511,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
   }
   const int qloc = row / p.G, hl = row - qloc * p.G;
   const int64_t orow =
-      (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qloc - p.q_pos0);
+      (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (w.qlo + qloc - p.q_row0);
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) store1<BF16>(p.out, orow * D + lane + 64 * i, acc[i] * inv);
@@ -501,7 +532,7 @@ int64_t max_keys(const Geometry& g, bool dense) {
   return std::min<int64_t>(static_cast<int64_t>(g.gmax) * g.gs, causal);
 }
 
-Plan make_plan(const Geometry& g, bool dense) {
+Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   Plan pl;
   pl.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   // Rows of the largest unit: a query chunk holds at most min(C, n_q) queries.
@@ -519,7 +550,7 @@ Plan make_plan(const Geometry& g, bool dense) {
   const int64_t keys = max_keys(g, dense);
   pl.splits = 1;
   pl.kps = static_cast<int>(keys);
-  if (wgs < 512 && keys > 256) {
+  if (allow_split && wgs < 512 && keys > 256) {
     int64_t sp = (keys + 127) / 128;
     const int64_t want = (1024 + wgs - 1) / wgs;
     if (sp > want) sp = want;
@@ -557,8 +588,8 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
 
 }  // namespace
 
-size_t attend_workspace(const Geometry& g, bool dense) {
-  const Plan pl = make_plan(g, dense);
+size_t attend_workspace(const Geometry& g, bool dense, bool allow_split) {
+  const Plan pl = make_plan(g, dense, allow_split);
   if (pl.splits == 1) return 0;
   const size_t rows = static_cast<size_t>(pl.units) * pl.splits * pl.rcap;
   return rows * (static_cast<size_t>(g.d) + 2) * sizeof(float);
@@ -566,8 +597,11 @@ size_t attend_workspace(const Geometry& g, bool dense) {
 
 hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,
                          const int32_t* granules, const int32_t* granule_count, bool dense,
-                         void* out, float* lse, void* ws, hipStream_t stream) {
-  const Plan pl = make_plan(g, dense);
+                         void* out, float* lse, void* ws, hipStream_t stream,
+                         const AttendExtra* extra) {
+  const AttendExtra none;
+  const AttendExtra& ex = extra != nullptr ? *extra : none;
+  const Plan pl = make_plan(g, dense, ex.allow_split);
   AttendParams p;
   p.q = q;
   p.k = k_rot;
@@ -576,11 +610,15 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
   p.lse = lse;
   p.gran = granules;
   p.gcnt = granule_count;
+  p.pool_slot = ex.pool_slot;
+  p.pool_slots = ex.pool_slots;
   const size_t rows = static_cast<size_t>(pl.units) * pl.splits * pl.rcap;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = pl.splits > 1 ? static_cast<float*>(ws) + rows * g.d : nullptr;
   p.q_pos0 = g.q_pos0;
   p.n_q = g.n_q;
+  p.q_stride = ex.q_stride >= 0 ? ex.q_stride : g.n_q;
+  p.q_row0 = ex.q_row0 >= 0 ? ex.q_row0 : g.q_pos0;
   p.kv_cap = g.kv_cap;
   p.t0 = g.t0;
   p.nqc = g.nqc;

@@ -29,6 +29,12 @@ struct Geometry {
   RopeFreqs rope;
 };
 
+// Validates a config and call shape and fills the geometry (api.cpp).
+hga_status make_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, int64_t kv_cap,
+                         int64_t q_pos0, int64_t n_q, Geometry& g);
+// Records a failed HIP call as this thread's last error; returns HGA_ERR_HIP.
+hga_status hip_fail(hipError_t e);
+
 hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_begin,
                             int64_t tok_end, void* k_rot, float* chunk_sum,
                             float* group_sum, hipStream_t stream);
@@ -40,9 +46,21 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
                         int32_t* granules, int32_t* granule_count, void* ws,
                         hipStream_t stream);
 
-size_t attend_workspace(const Geometry& g, bool dense);
+// Options of the host tier: K/V read from a granule-major staging pool
+// ([slot][2][g_s][d], K then V) through per-entry pool slots, and no key
+// splitting (so no workspace).
+struct AttendExtra {
+  const int32_t* pool_slot = nullptr;
+  int64_t pool_slots = 0;
+  bool allow_split = true;
+  int64_t q_stride = -1;  // rows per (sequence, head) of q/out/lse; -1 = n_q
+  int64_t q_row0 = -1;    // position of row 0; -1 = q_pos0
+};
+
+size_t attend_workspace(const Geometry& g, bool dense, bool allow_split = true);
 hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,
                          const int32_t* granules, const int32_t* granule_count, bool dense,
-                         void* out, float* lse, void* ws, hipStream_t stream);
+                         void* out, float* lse, void* ws, hipStream_t stream,
+                         const AttendExtra* extra = nullptr);
 
 }  // namespace hga

@@ -1,0 +1,352 @@
+// Host-tiered exact-token attention: the token K/V live in pinned host RAM,
+// the chunk / group summary tables in HBM.
+//
+// Source: xllm-io paper-review page of "Hierarchical Global Attention",
+// section 3, tiered K/V store: summaries and routing stay on the device, the
+// full token K/V history sits in host RAM and only what the router selects
+// is moved to the device for the exact-token attention.
+//
+// Pipeline (one call = one prefill over [q_pos0, q_pos0 + n_q)):
+//   1. route every unit on the device (summaries in HBM);
+//   2. one device-to-host copy of the granule lists and counts;
+//   3. windows of consecutive query chunks: the union of the granules their
+//      units attend to (fixed windows + routed groups or chunks, each granule
+//      once per (sequence, KV head)) is gathered by host threads from the
+//      granule-major store into pinned staging, moved with one
+//      hipMemcpyAsync on the copy stream, and an event gates the window's
+//      attention on the compute stream;
+//   4. two window buffers alternate, so window w+1 is packed and copied
+//      while window w is attended.
+// The call returns after the last attention launch is enqueued.
+#include <algorithm>
+#include <chrono>
+#include <condition_variable>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "hga_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of every buffer carved from the caller's staging memory.
+struct Layout {
+  int64_t units = 0, wunits = 0, slots = 0;
+  size_t granule_bytes = 0;
+  size_t cidx = 0, gidx = 0, gran = 0, gcnt = 0, rws = 0, win[2] = {0, 0}, dev_total = 0;
+  size_t pool_bytes = 0, wgran = 0, wslot = 0, wcnt = 0, win_bytes = 0;  // inside one window buffer
+  size_t hgran = 0, hcnt = 0, hwin[2] = {0, 0}, host_total = 0;
+};
+
+Layout make_layout(const hga::Geometry& g, int32_t wmax, int64_t slots) {
+  Layout L;
+  const size_t elem = g.bf16 ? 2 : 4;
+  L.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  L.wunits = static_cast<int64_t>(g.B) * g.Hkv * wmax;
+  L.slots = slots;
+  L.granule_bytes = static_cast<size_t>(2) * g.gs * g.d * elem;
+  const size_t u = static_cast<size_t>(L.units);
+  size_t off = 0;
+  L.cidx = off; off = align_up(off + u * std::max(g.Kc, 1) * 4);
+  L.gidx = off; off = align_up(off + u * std::max(g.Kg, 1) * 4);
+  L.gran = off; off = align_up(off + u * g.gmax * 4);
+  L.gcnt = off; off = align_up(off + u * 4);
+  L.rws = off; off = align_up(off + hga::route_workspace(g));
+  L.pool_bytes = align_up(static_cast<size_t>(slots) * L.granule_bytes);
+  L.wgran = L.pool_bytes;
+  L.wslot = align_up(L.wgran + static_cast<size_t>(L.wunits) * g.gmax * 4);
+  L.wcnt = align_up(L.wslot + static_cast<size_t>(L.wunits) * g.gmax * 4);
+  L.win_bytes = align_up(L.wcnt + static_cast<size_t>(L.wunits) * 4);
+  L.win[0] = off; off += L.win_bytes;
+  L.win[1] = off; off += L.win_bytes;
+  L.dev_total = off;
+  size_t h = 0;
+  L.hgran = h; h = align_up(h + u * g.gmax * 4);
+  L.hcnt = h; h = align_up(h + u * 4);
+  L.hwin[0] = h; h += L.win_bytes;
+  L.hwin[1] = h; h += L.win_bytes;
+  L.host_total = h;
+  return L;
+}
+
+// A fixed set of host threads that run one job (thread i of n) per run().
+class Packer {
+ public:
+  explicit Packer(int n) {
+    for (int i = 0; i < n; ++i) th_.emplace_back([this, i, n] { loop(i, n); });
+  }
+  ~Packer() {
+    {
+      std::lock_guard<std::mutex> l(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  void run(const std::function<void(int, int)>& job) {
+    if (th_.empty()) {
+      job(0, 1);
+      return;
+    }
+    std::unique_lock<std::mutex> l(mu_);
+    job_ = &job;
+    pending_ = static_cast<int>(th_.size());
+    ++gen_;
+    cv_.notify_all();
+    done_.wait(l, [this] { return pending_ == 0; });
+    job_ = nullptr;
+  }
+
+ private:
+  void loop(int i, int n) {
+    int64_t seen = 0;
+    for (;;) {
+      const std::function<void(int, int)>* job;
+      {
+        std::unique_lock<std::mutex> l(mu_);
+        cv_.wait(l, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        job = job_;
+      }
+      (*job)(i, n);
+      {
+        std::lock_guard<std::mutex> l(mu_);
+        if (--pending_ == 0) done_.notify_one();
+      }
+    }
+  }
+  std::vector<std::thread> th_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_;
+  const std::function<void(int, int)>* job_ = nullptr;
+  int pending_ = 0;
+  int64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+bool pinned_host(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query must not poison later launches
+    return false;
+  }
+  return a.type == hipMemoryTypeHost;
+}
+
+struct Events {
+  hipEvent_t e[4] = {nullptr, nullptr, nullptr, nullptr};
+  ~Events() {
+    for (hipEvent_t x : e)
+      if (x != nullptr) (void)hipEventDestroy(x);
+  }
+};
+
+hga_status tier_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, int64_t q_pos0,
+                         int64_t n_q, int64_t kv_cap, int32_t wmax, int64_t slots, hga::Geometry& g) {
+  hga_status st = hga::make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
+  if (st != HGA_OK) return st;
+  if (n_q <= 0 || wmax <= 0) return HGA_ERR_INVALID_ARGUMENT;
+  // one query chunk of every (sequence, KV head) must fit a window
+  if (slots < static_cast<int64_t>(g.B) * g.Hkv * g.gmax) return HGA_ERR_INVALID_ARGUMENT;
+  if (!hga::route_supported(g)) return HGA_ERR_UNSUPPORTED;
+  return HGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                        int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
+                                        int64_t slots_per_window, size_t* device_bytes,
+                                        size_t* host_bytes) {
+  if (device_bytes == nullptr || host_bytes == nullptr || cfg == nullptr || cfg->chunk_size <= 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  const int64_t cap = ((q_pos0 + n_q + cfg->chunk_size - 1) / cfg->chunk_size) * cfg->chunk_size;
+  hga::Geometry g;
+  hga_status st = tier_geometry(cfg, dtype, batch, q_pos0, n_q, cap > 0 ? cap : cfg->chunk_size,
+                                max_window_chunks, slots_per_window, g);
+  if (st != HGA_OK) return st;
+  const Layout L = make_layout(g, max_window_chunks, slots_per_window);
+  *device_bytes = L.dev_total;
+  *host_bytes = L.host_total;
+  return HGA_OK;
+}
+
+hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                  const void* q_raw, int64_t q_pos0, int64_t n_q,
+                                  const void* kv_host, int64_t kv_cap, const float* chunk_sum,
+                                  const float* group_sum, void* out, float* lse,
+                                  void* dev_staging, size_t dev_bytes, void* host_staging,
+                                  size_t host_bytes, int32_t max_window_chunks,
+                                  int64_t slots_per_window, int32_t n_threads,
+                                  void* compute_stream, void* copy_stream,
+                                  hga_tier_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  hga::Geometry g;
+  hga_status st = tier_geometry(cfg, dtype, batch, q_pos0, n_q, kv_cap, max_window_chunks,
+                                slots_per_window, g);
+  if (st != HGA_OK) return st;
+  if (q_raw == nullptr || kv_host == nullptr || out == nullptr || chunk_sum == nullptr ||
+      dev_staging == nullptr || host_staging == nullptr || n_threads < 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (g.Kg > 0 && group_sum == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(dev_staging) | reinterpret_cast<uintptr_t>(host_staging)) % kAlign)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (!pinned_host(kv_host) || !pinned_host(host_staging)) return HGA_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(g, max_window_chunks, slots_per_window);
+  if (dev_bytes < L.dev_total || host_bytes < L.host_total) return HGA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  hipStream_t xs = static_cast<hipStream_t>(copy_stream);
+  char* dev = static_cast<char*>(dev_staging);
+  char* host = static_cast<char*>(host_staging);
+  int32_t* d_cidx = reinterpret_cast<int32_t*>(dev + L.cidx);
+  int32_t* d_gidx = reinterpret_cast<int32_t*>(dev + L.gidx);
+  int32_t* d_gran = reinterpret_cast<int32_t*>(dev + L.gran);
+  int32_t* d_gcnt = reinterpret_cast<int32_t*>(dev + L.gcnt);
+  const int32_t* h_gran = reinterpret_cast<const int32_t*>(host + L.hgran);
+  const int32_t* h_gcnt = reinterpret_cast<const int32_t*>(host + L.hcnt);
+
+  // 1-2. route on the device, bring the granule lists to the host
+  hipError_t e = hga::launch_route(g, q_raw, chunk_sum, group_sum, d_cidx, g.Kg > 0 ? d_gidx : nullptr,
+                                   d_gran, d_gcnt, dev + L.rws, cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  e = hipMemcpyAsync(host + L.hgran, d_gran, static_cast<size_t>(L.units) * g.gmax * 4,
+                     hipMemcpyDeviceToHost, cs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host + L.hcnt, d_gcnt, static_cast<size_t>(L.units) * 4, hipMemcpyDeviceToHost, cs);
+  if (e == hipSuccess) e = hipStreamSynchronize(cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+
+  Events ev;  // copied[0..1], attended[0..1]
+  for (auto& x : ev.e) {
+    e = hipEventCreateWithFlags(&x, hipEventDisableTiming);
+    if (e != hipSuccess) return hga::hip_fail(e);
+  }
+  hipEvent_t* copied = ev.e;
+  hipEvent_t* attended = ev.e + 2;
+
+  const int64_t ngran = g.kv_cap / g.gs;
+  const int64_t bh = static_cast<int64_t>(g.B) * g.Hkv;
+  std::vector<int32_t> stamp(static_cast<size_t>(bh * ngran), -1);
+  std::vector<int32_t> slotmap(static_cast<size_t>(bh * ngran), 0);
+  std::vector<std::pair<const char*, char*>> jobs;
+  jobs.reserve(static_cast<size_t>(slots_per_window));
+  const char* store = static_cast<const char*>(kv_host);
+  Packer packer(n_threads);
+  double pack_s = 0.0;
+  int64_t copied_granules = 0, bytes_h2d = 0;
+  const int64_t t_end = g.t0 + g.nqc;
+  int32_t w = 0;
+  for (int64_t ta = g.t0; ta < t_end; ++w) {
+    const int buf = w & 1;
+    char* hw = host + L.hwin[buf];
+    char* dw = dev + L.win[buf];
+    if (w >= 2) {  // the copy that last read this host buffer must be done
+      e = hipEventSynchronize(copied[buf]);
+      if (e != hipSuccess) return hga::hip_fail(e);
+    }
+    // Grow the window one query chunk at a time while its granule union fits.
+    int64_t next = 0, tb = ta;
+    jobs.clear();
+    while (tb < t_end && tb - ta < max_window_chunks) {
+      int64_t add = 0;
+      for (int64_t x = 0; x < bh; ++x) {
+        const int64_t u = x * g.nqc + (tb - g.t0);
+        for (int32_t i = 0; i < h_gcnt[u]; ++i) {
+          const int64_t gid = h_gran[u * g.gmax + i];
+          add += stamp[static_cast<size_t>(x * ngran + gid)] != w;
+        }
+      }
+      if (next + add > slots_per_window) break;
+      for (int64_t x = 0; x < bh; ++x) {
+        const int64_t u = x * g.nqc + (tb - g.t0);
+        for (int32_t i = 0; i < h_gcnt[u]; ++i) {
+          const int64_t gid = h_gran[u * g.gmax + i];
+          const size_t k = static_cast<size_t>(x * ngran + gid);
+          if (stamp[k] != w) {
+            stamp[k] = w;
+            slotmap[k] = static_cast<int32_t>(next);
+            jobs.emplace_back(store + (x * ngran + gid) * L.granule_bytes, hw + next * L.granule_bytes);
+            ++next;
+          }
+        }
+      }
+      ++tb;
+    }
+    const int64_t nw = tb - ta;
+    int32_t* wgran = reinterpret_cast<int32_t*>(hw + L.wgran);
+    int32_t* wslot = reinterpret_cast<int32_t*>(hw + L.wslot);
+    int32_t* wcnt = reinterpret_cast<int32_t*>(hw + L.wcnt);
+    for (int64_t x = 0; x < bh; ++x) {
+      for (int64_t t = ta; t < tb; ++t) {
+        const int64_t u = x * g.nqc + (t - g.t0);
+        const int64_t wu = x * nw + (t - ta);
+        wcnt[wu] = h_gcnt[u];
+        for (int32_t i = 0; i < g.gmax; ++i) {
+          const int32_t gid = i < h_gcnt[u] ? h_gran[u * g.gmax + i] : -1;
+          wgran[wu * g.gmax + i] = gid;
+          wslot[wu * g.gmax + i] = gid >= 0 ? slotmap[static_cast<size_t>(x * ngran + gid)] : -1;
+        }
+      }
+    }
+    // 3. pack on the host threads
+    const auto p0 = std::chrono::steady_clock::now();
+    const size_t nj = jobs.size();
+    const size_t gb = L.granule_bytes;
+    packer.run([&](int i, int n) {
+      const size_t lo = nj * i / n, hi = nj * (i + 1) / n;
+      for (size_t j = lo; j < hi; ++j) std::memcpy(jobs[j].second, jobs[j].first, gb);
+    });
+    pack_s += std::chrono::duration<double>(std::chrono::steady_clock::now() - p0).count();
+    // H2D on the copy stream once the attention that last read this device buffer is done
+    if (w >= 2) {
+      e = hipStreamWaitEvent(xs, attended[buf], 0);
+      if (e != hipSuccess) return hga::hip_fail(e);
+    }
+    const size_t pool_used = static_cast<size_t>(next) * L.granule_bytes;
+    const size_t idx_bytes = L.win_bytes - L.wgran;
+    e = hipMemcpyAsync(dw, hw, pool_used, hipMemcpyHostToDevice, xs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dw + L.wgran, hw + L.wgran, idx_bytes, hipMemcpyHostToDevice, xs);
+    if (e == hipSuccess) e = hipEventRecord(copied[buf], xs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, copied[buf], 0);
+    if (e != hipSuccess) return hga::hip_fail(e);
+    copied_granules += next;
+    bytes_h2d += static_cast<int64_t>(pool_used + idx_bytes);
+    // attention of the window's units over the staged pool
+    hga::Geometry gw = g;
+    gw.q_pos0 = std::max(ta * g.C, g.q_pos0);
+    gw.n_q = std::min(tb * g.C, g.q_pos0 + g.n_q) - gw.q_pos0;
+    gw.t0 = ta;
+    gw.nqc = nw;
+    hga::AttendExtra ex;
+    ex.pool_slot = reinterpret_cast<const int32_t*>(dw + L.wslot);
+    ex.pool_slots = slots_per_window;
+    ex.allow_split = false;
+    ex.q_stride = g.n_q;
+    ex.q_row0 = g.q_pos0;
+    e = hga::launch_attend(gw, q_raw, dw, dw, reinterpret_cast<const int32_t*>(dw + L.wgran),
+                           reinterpret_cast<const int32_t*>(dw + L.wcnt), false, out, lse, nullptr, cs, &ex);
+    if (e == hipSuccess) e = hipEventRecord(attended[buf], cs);
+    if (e != hipSuccess) return hga::hip_fail(e);
+    ta = tb;
+  }
+  if (stats != nullptr) {
+    stats->windows = w;
+    stats->granules_copied = copied_granules;
+    stats->bytes_h2d = bytes_h2d;
+    stats->pack_seconds = pack_s;
+    stats->host_seconds =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+  }
+  return HGA_OK;
+}
+
+}  // extern "C"

@@ -190,6 +190,61 @@ hga_status hga_dense_causal(const hga_config* cfg, hga_dtype dtype, int32_t batc
                             void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Host tier -- tiered K/V store of the xllm-io page, section 3: summaries
+ * and routing stay on the device; the full token K/V history lives in host
+ * RAM and only the routed working set is moved to the device.
+ *
+ * kv_host (pinned host memory, e.g. hipHostMalloc) holds the RoPE-rotated
+ * keys and the values granule-major: [B][Hkv][kv_cap/g_s][2][g_s][d] in the
+ * call dtype, K block then V block of each granule (g_s * d elements each).
+ *
+ * hga_attend_host_tiered computes the same outputs as hga_route followed by
+ * hga_attend on device-resident K/V (bitwise: the same granules in the same
+ * order), for queries [q_pos0, q_pos0 + n_q):
+ *   1. routes every unit on compute_stream (chunk_sum / group_sum in HBM);
+ *   2. copies the granule lists to the host (the call blocks for this);
+ *   3. walks windows of at most max_window_chunks query chunks whose union
+ *      of needed granules (one copy per granule per (sequence, KV head))
+ *      fits slots_per_window; n_threads host threads pack each union from
+ *      kv_host into pinned staging, one hipMemcpyAsync per window moves it
+ *      on copy_stream, and an event gates the window's attention on
+ *      compute_stream;
+ *   4. two window buffers alternate, so window w+1 is packed and copied
+ *      while window w is attended.
+ * It returns once the last attention is enqueued on compute_stream.
+ *
+ * dev_staging (device) and host_staging (pinned host) are caller-owned,
+ * 256-byte aligned, at least the sizes hga_host_tiered_buffer_bytes returns;
+ * slots_per_window >= B * Hkv * hga_max_granules(cfg).  Both streams must
+ * be distinct from work that uses the staging buffers concurrently.
+ * Returns HGA_ERR_INVALID_ARGUMENT when kv_host or host_staging is not
+ * pinned host memory.  stats may be NULL.
+ */
+typedef struct hga_tier_stats {
+  int64_t windows;          /* attention launches (windows)                       */
+  int64_t granules_copied;  /* granules moved host -> device (K and V together)    */
+  int64_t bytes_h2d;        /* bytes of all host -> device copies of the call      */
+  double pack_seconds;      /* host time spent packing granules into staging       */
+  double host_seconds;      /* host time of the whole call                         */
+} hga_tier_stats;
+
+hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                        int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
+                                        int64_t slots_per_window, size_t* device_bytes,
+                                        size_t* host_bytes);
+
+hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                  const void* q_raw, int64_t q_pos0, int64_t n_q,
+                                  const void* kv_host, int64_t kv_cap,
+                                  const float* chunk_sum, const float* group_sum,
+                                  void* out, float* lse,
+                                  void* dev_staging, size_t dev_bytes,
+                                  void* host_staging, size_t host_bytes,
+                                  int32_t max_window_chunks, int64_t slots_per_window,
+                                  int32_t n_threads, void* compute_stream, void* copy_stream,
+                                  hga_tier_stats* stats);
+
 const char* hga_status_string(hga_status status);
 
 /* hipError_t of the last failed HIP call made by this thread (0 if none). */

@@ -1,0 +1,86 @@
+"""GPU tests of the pinned-host K/V tier: its outputs equal the device-resident
+route + attend path bit for bit (same granules, same order), and match the
+oracle on sampled units."""
+import numpy as np
+import pytest
+
+import hierarchical_kv_routing_amd as H
+import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def run_host_tier(run, max_window_chunks, slots, threads=4, copy_stream=True):
+    import torch
+    w, cfg = run.w, run.cfg
+    store = H.host_store(cfg, run.k_rot, run.v)
+    dt = P.torch_dtype(w)
+    dev_b, host_b = H.host_tiered_buffer_bytes(cfg, dt, w.batch, w.q_pos0, w.n_q,
+                                               max_window_chunks, slots)
+    dev = torch.empty(dev_b, dtype=torch.uint8, device="cuda:0")
+    host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
+    out = torch.full_like(run.out, float("nan"))
+    lse = torch.full_like(run.lse, float("nan"))
+    xs = torch.cuda.Stream() if copy_stream else None
+    stats = H.attend_host_tiered(cfg, run.q, w.q_pos0, store, run.k.shape[2], run.csum, run.gsum,
+                                 out, lse, dev, host, max_window_chunks, slots, threads,
+                                 copy_stream=xs)
+    torch.cuda.synchronize()
+    return out, lse, stats
+
+
+@pytest.mark.parametrize("base", ["chunk_only", "group"])
+def test_host_tier_equals_device_path(base):
+    import torch
+    w0 = W.HOST_TIERED_CHUNK if base == "chunk_only" else W.HOST_TIERED_GROUP
+    w = w0.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=16)
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.GpuRun(w, q, k, v)
+    gmax = H.max_granules(run.cfg)
+    slots = w.batch * w.n_kv_heads * gmax + 64    # windows split on slot capacity
+    out, lse, stats = run_host_tier(run, max_window_chunks=16, slots=slots)
+    print(f"[gpu] host tier {base}: {stats}", flush=True)
+    assert stats["windows"] > 64 // 16
+    total = int(run.np("granule_count").sum())
+    assert 0 < stats["granules_copied"] <= total
+    same = (bool(torch.equal(out, run.out)), bool(torch.equal(lse, run.lse)))
+    assert all(same), same
+    units = P.sample_units(w, 6)
+    P.check_attention(run, q, k, v, units, out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+
+
+def test_host_tier_same_stream_and_no_threads():
+    """Copy and compute on one stream, packing on the calling thread."""
+    import torch
+    w = W.HOST_TIERED_GROUP.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=8)
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.GpuRun(w, q, k, v)
+    slots = 2 * w.batch * w.n_kv_heads * H.max_granules(run.cfg)
+    out, lse, stats = run_host_tier(run, 8, slots, threads=0, copy_stream=False)
+    same = bool(torch.equal(out, run.out))
+    assert same
+
+
+def test_host_tier_rejects_pageable_memory():
+    import torch
+    w = W.HOST_TIERED_GROUP.scaled(n_ctx=1024, kv_cap=1024, n_q=1024, planted=0)
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.GpuRun(w, q, k, v, attend=False)
+    cfg = run.cfg
+    B, Hkv, cap, d = run.k.shape
+    pageable = torch.zeros((B, Hkv, cap // w.group_size, 2, w.group_size, d), dtype=torch.bfloat16)
+    slots = B * Hkv * H.max_granules(cfg)
+    dev_b, host_b = H.host_tiered_buffer_bytes(cfg, torch.bfloat16, B, 0, w.n_q, 4, slots)
+    dev = torch.empty(dev_b, dtype=torch.uint8, device="cuda:0")
+    host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
+    import ctypes
+    stats = H.hga_tier_stats()
+    st = H.lib().hga_attend_host_tiered(
+        ctypes.byref(cfg.c()), H.HGA_BF16, B, run.q.data_ptr(), 0, w.n_q, pageable.data_ptr(), cap,
+        run.csum.data_ptr(), run.gsum.data_ptr(), run.out.data_ptr(), None, dev.data_ptr(), dev_b,
+        host.data_ptr(), host_b, 4, slots, 2, None, None, ctypes.byref(stats))
+    assert st == 1
+    # the failed pointer query left no error behind for the next launch
+    run.attend()
+    torch.cuda.synchronize()
