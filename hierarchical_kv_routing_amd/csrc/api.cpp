@@ -188,6 +188,7 @@ static hga_status attend_common(const hga_config* cfg, hga_dtype dtype, int32_t 
   if (!aligned16(q_raw) || !aligned16(k_rot) || !aligned16(v) || !aligned16(out) ||
       !aligned16(workspace))
     return HGA_ERR_INVALID_ARGUMENT;
+  if (!hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
   const size_t need = hga::attend_workspace(g, dense);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   hipError_t e = hga::launch_attend(g, q_raw, k_rot, v, granules, granule_count, dense, out, lse,

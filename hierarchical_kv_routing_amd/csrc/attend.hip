@@ -6,20 +6,27 @@
 // current chunk's causal part, the fixed windows and the routed groups or
 // chunks, with no summary tokens) and Eq. (1) (dense causal attention).
 //
-// bf16 path (attend_mfma_kernel): one workgroup holds NW waves x 32 query
-// rows of one unit (sequence, KV head, query chunk); a row is (query, head)
-// with the G query heads of the KV head interleaved, so all GQA heads share
-// every K/V tile.  K/V tiles of 32 gathered tokens are staged in LDS (K
-// row-major, V transposed) and double-buffered; each wave computes
+// bf16 path (attend_mfma_kernel): a workgroup holds NW waves, each with RB
+// blocks of 32 query rows of one unit (sequence, KV head, query chunk); a
+// row is (query, head) with the G query heads of the KV head interleaved, so
+// all GQA heads share every K/V stage.  Stages of 64 gathered tokens are
+// staged in LDS (K row-major, V transposed, written as packed key pairs) and
+// double-buffered from registers.  Per 32-key sub-tile each wave computes
 //   S^T = K Q^T      (32x32x16 bf16 MFMA, keys on M, query rows on N)
-//   online softmax   (f32, base 2, Q pre-scaled by scale*log2(e))
+//   softmax          (f32, base 2, Q pre-scaled by scale*log2(e))
 //   O^T += V^T P^T   (32x32x16 bf16 MFMA, P rounded to bf16)
-// With rows on N each lane owns one row, so row max / sum need one lane
-// exchange.  K rows are read into the MFMA in the order pi(m) (bits 2 and 3
-// of m swapped), which makes the S^T accumulator registers of a lane cover
-// exactly the 8 consecutive keys the PV product wants from it: P never goes
-// through LDS.  Few-unit calls (decode) split each unit's keys over several
-// workgroups and merge (m, l, O) partials in combine_kernel.
+// With rows on N each lane owns one row.  K rows are read into the MFMA in
+// the order pi(m) (bits 2 and 3 of m swapped), which makes the S^T
+// accumulator registers of a lane cover exactly the 8 consecutive keys the
+// PV product wants from it: P never goes through LDS.
+//
+// Softmax keeps a per-row reference r and accumulates 2^(s - r): r moves
+// only when a stage's scores exceed it by more than 2^8 (a wave-uniform
+// branch), so the common stage does one subtraction, one exp2, one max and
+// one add per score.  Row sums stay lane-local until the end.  Causal /
+// validity masks are evaluated only in stages that hold current-chunk or
+// out-of-range keys.  Few-unit calls (decode) split each unit's keys over
+// several workgroups and merge (m, l, O) partials in combine_kernel.
 //
 // f32 path (attend_f32_kernel): one wave per 64 rows, one lane per row,
 // K/V tiles in LDS, f32 vector ALU; exact to f32 rounding.
@@ -27,14 +34,23 @@
 
 #include "hga_device.h"
 
+#ifndef HGA_ATTEND_RB
+#define HGA_ATTEND_RB 1
+#endif
+
 namespace hga {
 namespace {
 
-constexpr int kTK = 32;           // keys per tile
-constexpr int kVPitch = kTK * 2 + 16;  // bytes per transposed V row
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kTK = 64;                // keys per LDS stage (bf16 path)
+constexpr int kVP = kTK * 2 + 16;      // bytes per transposed V row in LDS
+constexpr int kTKf = 32;               // keys per LDS tile (f32 path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
+constexpr float kRescale = 8.0f;       // move the reference when scores exceed it by 2^8
 
 struct AttendParams {
   const void* q;
@@ -51,12 +67,12 @@ struct AttendParams {
   int64_t pool_slots;
   float* ws_o;   // [slot][split][Rcap][D]
   float* ws_ml;  // [slot][split][Rcap][2]
-  int64_t q_pos0, n_q, kv_cap, t0, nqc;
+  int64_t q_pos0, n_q, kv_cap, t0, nqc, units;
   // q / out / lse rows: row r of a (sequence, head) holds position q_row0 + r
   // and rows are q_stride apart (a window call covers part of the array).
   int64_t q_stride, q_row0;
-  int B, Hq, Hkv, G, d, C, gs, gmax, Rcap;
-  int nw, slices, splits, keys_per_split;
+  int B, Hq, Hkv, G, d, C, gs, lg_gs, gmax, Rcap;
+  int slices, splits, keys_per_split, per_unit;
   int dense;
   float scale_log2;
   RopeFreqs rope;
@@ -91,30 +107,45 @@ __device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
   return w;
 }
 
+// Work item of this block.  Units are taken 8 at a time, one per XCD
+// (consecutive blocks go to consecutive XCDs), and every item (row slice x
+// key split) of a unit lands on the same XCD, whose L2 then serves the
+// unit's K/V to all of them.
+__device__ __forceinline__ bool block_item(const AttendParams& p, int64_t& u, int& item) {
+  const int64_t bx = blockIdx.x;
+  const int64_t per = 8 * static_cast<int64_t>(p.per_unit);
+  const int64_t grp = bx / per;
+  const int rem = static_cast<int>(bx - grp * per);
+  item = rem >> 3;
+  u = grp * 8 + (rem & 7);
+  return u < p.units;
+}
+
 // Token held by key slot s of a unit (slot order = ascending granules), or
 // -1 when a caller-supplied granule id lies outside [0, kv_cap / g_s) (or,
 // in pool mode, its pool slot lies outside the pool).
-__device__ __forceinline__ int64_t slot_token(const AttendParams& p, const AUnit& w, int s) {
+__device__ __forceinline__ int slot_token(const AttendParams& p, const AUnit& w, int s) {
   if (p.dense) return s;
-  const int gi = s / p.gs;
-  const int64_t tok = static_cast<int64_t>(p.gran[w.slot * p.gmax + gi]) * p.gs + (s - gi * p.gs);
+  const int gi = s >> p.lg_gs;
+  const int64_t g = p.gran[w.slot * p.gmax + gi];
   if (p.pool_slot != nullptr) {
     const int64_t ps = p.pool_slot[w.slot * p.gmax + gi];
     if (ps < 0 || ps >= p.pool_slots) return -1;
   }
-  return (tok >= 0 && tok < p.kv_cap) ? tok : -1;
+  const int64_t tok = (g << p.lg_gs) + (s & ((1 << p.lg_gs) - 1));
+  return (tok >= 0 && tok < p.kv_cap) ? static_cast<int>(tok) : -1;
 }
 
 // Element offsets (from p.k and p.v) of the K and V rows of key slot s
 // holding token tok.
 template <int D>
-__device__ __forceinline__ void kv_offsets(const AttendParams& p, const AUnit& w, int s, int64_t tok,
+__device__ __forceinline__ void kv_offsets(const AttendParams& p, const AUnit& w, int s, int tok,
                                            int64_t slab, int64_t& ko, int64_t& vo) {
   if (p.pool_slot != nullptr) {
-    const int gi = s / p.gs;
+    const int gi = s >> p.lg_gs;
     const int64_t ps = p.pool_slot[w.slot * p.gmax + gi];
-    ko = (ps * 2 * p.gs + (s - gi * p.gs)) * D;
-    vo = ko + static_cast<int64_t>(p.gs) * D;
+    ko = ((ps << (p.lg_gs + 1)) + (s & ((1 << p.lg_gs) - 1))) * D;
+    vo = ko + (static_cast<int64_t>(1) << p.lg_gs) * D;
   } else {
     ko = vo = (slab + tok) * D;
   }
@@ -125,98 +156,202 @@ __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// One 64-key stage in registers: thread item = (key pair, 16-byte d slice).
 template <int D, int NW>
-struct TileRegs {
-  static constexpr int kSlots = kTK * (D / 8);
-  static constexpr int kPer = (kSlots + NW * 64 - 1) / (NW * 64);
-  uint4 k[kPer];
-  uint4 v[kPer];
-  int tok;  // token of key slot threadIdx.x (threads < kTK), -1 = none
+struct StageRegs {
+  static constexpr int SL = D / 8;
+  static constexpr int kItems = (kTK / 2) * SL;
+  static constexpr int kPer = (kItems + NW * 64 - 1) / (NW * 64);
+  uint4 k0[kPer], k1[kPer], v0[kPer], v1[kPer];
+  int t0[kPer], t1[kPer];
+  bool masked;
 };
 
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(const AttendParams& p, const AUnit& w, int kbase,
-                                          int kend, int64_t slab, TileRegs<D, NW>& tr) {
-  constexpr int SL = D / 8;
+template <int D, int NW, bool POOL>
+__device__ __forceinline__ void load_stage(const AttendParams& p, const AUnit& w, int kb, int kend,
+                                           int64_t slab, int cur0, StageRegs<D, NW>& r) {
+  constexpr int SL = StageRegs<D, NW>::SL;
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
 #pragma unroll
-  for (int i = 0; i < TileRegs<D, NW>::kPer; ++i) {
+  for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
-    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (idx < TileRegs<D, NW>::kSlots) {
-      const int s = idx / SL, sl = idx - s * SL;
-      const int gs = kbase + s;
-      const int64_t tok = gs < kend ? slot_token(p, w, gs) : -1;
-      if (tok >= 0) {
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+    int t0 = -1, t1 = -1;
+    if (idx < StageRegs<D, NW>::kItems) {
+      const int kp = idx / SL, sl = idx - kp * SL;
+      const int s0 = kb + 2 * kp;
+      if (p.lg_gs > 0) {
+        // s0 is even, so both keys of the pair sit in one granule
+        t0 = s0 < kend ? slot_token(p, w, s0) : -1;
+        t1 = (t0 >= 0 && s0 + 1 < kend) ? t0 + 1 : -1;
+      } else {
+        t0 = s0 < kend ? slot_token(p, w, s0) : -1;
+        t1 = s0 + 1 < kend ? slot_token(p, w, s0 + 1) : -1;
+      }
+      if constexpr (POOL) {
         int64_t ko, vo;
-        kv_offsets<D>(p, w, gs, tok, slab, ko, vo);
-        kk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + ko + sl * 8);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + vo + sl * 8);
+        if (t0 >= 0) {
+          kv_offsets<D>(p, w, s0, t0, slab, ko, vo);
+          a0 = *reinterpret_cast<const uint4*>(kbase + ko + sl * 8);
+          b0 = *reinterpret_cast<const uint4*>(vbase + vo + sl * 8);
+        }
+        if (t1 >= 0) {
+          kv_offsets<D>(p, w, s0 + 1, t1, slab, ko, vo);
+          a1 = *reinterpret_cast<const uint4*>(kbase + ko + sl * 8);
+          b1 = *reinterpret_cast<const uint4*>(vbase + vo + sl * 8);
+        }
+      } else {
+        const uint16_t* kr = kbase + slab * D + sl * 8;
+        const uint16_t* vr = vbase + slab * D + sl * 8;
+        if (t0 >= 0) {
+          a0 = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(t0) * D);
+          b0 = *reinterpret_cast<const uint4*>(vr + static_cast<int64_t>(t0) * D);
+        }
+        if (t1 >= 0) {
+          a1 = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(t1) * D);
+          b1 = *reinterpret_cast<const uint4*>(vr + static_cast<int64_t>(t1) * D);
+        }
       }
     }
-    tr.k[i] = kk;
-    tr.v[i] = vv;
+    r.k0[i] = a0;
+    r.k1[i] = a1;
+    r.v0[i] = b0;
+    r.v1[i] = b1;
+    r.t0[i] = t0;
+    r.t1[i] = t1;
   }
-  tr.tok = -1;
-  if (threadIdx.x < kTK) {
-    const int gs = kbase + threadIdx.x;
-    if (gs < kend) tr.tok = static_cast<int>(slot_token(p, w, gs));
-  }
+  // Tokens ascend along a list, so the stage needs masks iff it runs past the
+  // end of the key range or its last key lies in the current chunk.
+  const int stop = kb + kTK < kend ? kb + kTK : kend;
+  const int tl = slot_token(p, w, stop - 1);
+  r.masked = (kb + kTK > kend) || tl < 0 || tl >= cur0;
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void store_tile(const TileRegs<D, NW>& tr, char* kl, char* vl, int* tl) {
-  constexpr int SL = D / 8;
+__device__ __forceinline__ void store_stage(const StageRegs<D, NW>& r, char* kl, char* vl, int* tl) {
+  constexpr int SL = StageRegs<D, NW>::SL;
   constexpr int KP = D * 2 + 16;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D, NW>::kPer; ++i) {
+  for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
-    if (idx < TileRegs<D, NW>::kSlots) {
-      const int s = idx / SL, sl = idx - s * SL;
-      *reinterpret_cast<uint4*>(kl + s * KP + sl * 16) = tr.k[i];
-      const uint32_t u[4] = {tr.v[i].x, tr.v[i].y, tr.v[i].z, tr.v[i].w};
+    if (idx < StageRegs<D, NW>::kItems) {
+      const int kp = idx / SL, sl = idx - kp * SL;
+      *reinterpret_cast<uint4*>(kl + (2 * kp) * KP + sl * 16) = r.k0[i];
+      *reinterpret_cast<uint4*>(kl + (2 * kp + 1) * KP + sl * 16) = r.k1[i];
+      const uint32_t x[4] = {r.v0[i].x, r.v0[i].y, r.v0[i].z, r.v0[i].w};
+      const uint32_t y[4] = {r.v1[i].x, r.v1[i].y, r.v1[i].z, r.v1[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(vl + (sl * 8 + 2 * e) * kVPitch + s * 2) =
-            static_cast<uint16_t>(u[e] & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(vl + (sl * 8 + 2 * e + 1) * kVPitch + s * 2) =
-            static_cast<uint16_t>(u[e] >> 16);
+        // element d of keys (2kp, 2kp+1) packed as one 32-bit LDS word
+        const uint32_t lo = (x[e] & 0xFFFFu) | (y[e] << 16);
+        const uint32_t hi = (x[e] >> 16) | (y[e] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e) * kVP + kp * 4) = lo;
+        *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e + 1) * kVP + kp * 4) = hi;
+      }
+      if (sl == 0) {
+        tl[2 * kp] = r.t0[i];
+        tl[2 * kp + 1] = r.t1[i];
       }
     }
   }
-  if (threadIdx.x < kTK) tl[threadIdx.x] = tr.tok;
 }
 
 template <int D>
-constexpr int tile_bytes() {
-  return kTK * (D * 2 + 16) + D * kVPitch + kTK * 4;
+constexpr int stage_bytes() {
+  return kTK * (D * 2 + 16) + D * kVP + kTK * 4;
 }
 
-template <int D, int NW>
+// Softmax of one 32-key half for one row: s[j] holds the score of key
+// 16*(j/8) + 8*hsub + (j%8) of the half (tokens tl[] when masked).  Scores
+// become 2^(s - ref); the reference moves (and o, lsum are rescaled) only
+// when the half's maximum exceeds it by more than kRescale.  Writes P as
+// bf16 MFMA operands (pb[0]: keys 0..15, pb[1]: keys 16..31).
+template <int DB>
+__device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* tl, int hsub,
+                                             int cur0, int qpos, float& ref, float& lsum,
+                                             bool& started, f32x16 (&o)[DB], Pack8 (&pb)[2]) {
+  float mx = -INFINITY;
+  if (masked) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int tok = tl[16 * (j >> 3) + 8 * hsub + (j & 7)];
+      const bool ok = (tok >= 0) & ((tok < cur0) | (tok <= qpos));
+      const float x = ok ? s[j] - ref : -INFINITY;
+      s[j] = x;
+      mx = fmaxf(mx, x);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x = s[j] - ref;
+      s[j] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  const bool chk = !started || mx > kRescale;
+  if (__builtin_amdgcn_ballot_w64(chk) != 0) {  // wave-uniform, rare
+    const float mrow = fmaxf(mx, __shfl_xor(mx, 32));
+    float delta = 0.f;
+    if (!started) {
+      if (mrow > -INFINITY) {  // first visible keys of the row set the reference
+        delta = mrow;
+        started = true;
+      }
+    } else if (mrow > kRescale) {
+      delta = mrow;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+    }
+    if (delta != 0.f) {
+      ref += delta;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] -= delta;
+    }
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(s[j]);
+    const float e1 = __builtin_amdgcn_exp2f(s[j + 1]);
+    ps += e0 + e1;
+    const f32x2 f = {e0, e1};
+    pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+  lsum += ps;
+}
+
+template <int D, int NW, int RB, bool POOL>
 __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   constexpr int KS = D / 16;    // k-steps of S^T over d
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int KP = D * 2 + 16;
-  constexpr int TB = tile_bytes<D>();
+  constexpr int SB = stage_bytes<D>();
   constexpr int H = D / 2;
   constexpr int kTable = 64 * H * 8;
-  constexpr int kSmem = (2 * TB) > kTable ? (2 * TB) : kTable;
+  constexpr int kSmem = (2 * SB) > kTable ? (2 * SB) : kTable;
+  constexpr int kRows = NW * 32 * RB;
   __shared__ __align__(16) char smem[kSmem];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int per_unit = p.slices * p.splits;
-  const int64_t u = blockIdx.x / per_unit;
-  const int rem = static_cast<int>(blockIdx.x - u * per_unit);
-  const int slice = rem / p.splits;
-  const int split = rem - slice * p.splits;
+  int64_t u;
+  int item;
+  if (!block_item(p, u, item)) return;  // uniform
+  const int slice = item / p.splits;
+  const int split = item - slice * p.splits;
   const AUnit w = make_aunit(p, u);
-  const int r0 = slice * NW * 32;
+  const int r0 = slice * kRows;
   if (r0 >= w.R) return;  // uniform
   const int kbeg = split * p.keys_per_split;
   int kend = kbeg + p.keys_per_split;
   if (kend > w.nkeys) kend = w.nkeys;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
   // RoPE table for the queries of this workgroup's rows.
-  const int rend = (r0 + NW * 32) < w.R ? (r0 + NW * 32) : w.R;
+  const int rend = (r0 + kRows) < w.R ? (r0 + kRows) : w.R;
   const int q_first = r0 / p.G;
   const int nqt = (rend - 1) / p.G - q_first + 1;
   float2* cs = reinterpret_cast<float2*>(smem);
@@ -228,21 +363,27 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   }
   __syncthreads();
 
-  // Query rows: lane -> row n = lane % 32, d slots ks*16 + 8*(lane/32) + i.
+  // Query rows: lane -> row n = lane % 32 of each row block, d slots
+  // ks*16 + 8*(lane/32) + i.
   const int n = lane & 31, hsub = lane >> 5;
-  const int row = r0 + wave * 32 + n;
-  const bool row_ok = row < w.R;
-  const int qloc = row_ok ? row / p.G : q_first;
-  const int hl = row_ok ? row - qloc * p.G : 0;
-  const int64_t qpos = w.qlo + qloc;
-  Pack8 qb[KS];
-  {
+  const int cur0 = static_cast<int>(w.t * p.C);
+  Pack8 qb[RB][KS];
+  int qpos[RB], hl[RB], row[RB];
+  bool rb_on[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    row[rb] = r0 + (wave * RB + rb) * 32 + n;
+    rb_on[rb] = (r0 + (wave * RB + rb) * 32) < w.R;
+    const bool ok = row[rb] < w.R;
+    const int qloc = ok ? row[rb] / p.G : q_first;
+    hl[rb] = ok ? row[rb] - qloc * p.G : 0;
+    qpos[rb] = static_cast<int>(w.qlo) + qloc;
     float x[KS][8];
     const int64_t base =
-        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0)) * D;
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl[rb]) * p.q_stride + (qpos[rb] - p.q_row0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (row_ok) {
+      if (ok) {
         load8<true>(p.q, base + ks * 16 + hsub * 8, x[ks]);
       } else {
 #pragma unroll
@@ -262,115 +403,128 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[ks].h[i] = f32_to_bf16(x[ks][i] * p.scale_log2);
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 f = {x[ks][2 * i] * p.scale_log2, x[ks][2 * i + 1] * p.scale_log2};
+        qb[rb][ks].u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+      }
     }
   }
-  __syncthreads();  // the table space becomes K/V tile buffers
+  __syncthreads();  // the table space becomes the K/V stage buffers
 
-  const bool wave_rows = (r0 + wave * 32) < w.R;
   const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
-  const int64_t cur0 = w.t * p.C;
-
-  f32x16 o[DB];
+  f32x16 o[RB][DB];
+  float ref[RB], lsum[RB];
+  bool started[RB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    ref[rb] = 0.f;
+    lsum[rb] = 0.f;
+    started[rb] = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[rb][db][j] = 0.f;
+  }
 
-  const int ntiles = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
-  TileRegs<D, NW> tr;
-  if (ntiles > 0) load_tile<D, NW>(p, w, kbeg, kend, slab, tr);
+  const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+  StageRegs<D, NW> sr;
+  if (nstages > 0) load_stage<D, NW, POOL>(p, w, kbeg, kend, slab, cur0, sr);
   const int prow = perm_row(n);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    char* kl = smem + (tile & 1) * TB;
+  for (int st = 0; st < nstages; ++st) {
+    char* kl = smem + (st & 1) * SB;
     char* vl = kl + kTK * KP;
-    int* tl = reinterpret_cast<int*>(vl + D * kVPitch);
-    store_tile<D, NW>(tr, kl, vl, tl);
+    int* tl = reinterpret_cast<int*>(vl + D * kVP);
+    store_stage<D, NW>(sr, kl, vl, tl);
+    const bool masked = sr.masked;
     __syncthreads();
-    if (tile + 1 < ntiles) load_tile<D, NW>(p, w, kbeg + (tile + 1) * kTK, kend, slab, tr);
-    if (wave_rows) {
-      f32x16 s;
+    if (st + 1 < nstages) load_stage<D, NW, POOL>(p, w, kbeg + (st + 1) * kTK, kend, slab, cur0, sr);
+    if (!rb_on[0]) continue;  // wave-uniform: this wave has no rows
+    // S^T for the two 32-key halves; each K operand serves every row block.
+    // s[rb][h][j] holds key 32h + 16*(j/8) + 8*hsub + (j%8).
+    f32x16 s[RB][2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = 0.f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[rb][h][j] = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + prow * KP + (ks * 16 + hsub * 8) * 2);
-        s = mfma32x32x16(a, qb[ks].v, s);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(kl + (h * 32 + prow) * KP + (ks * 16 + hsub * 8) * 2);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb_on[rb]) s[rb][h] = mfma32x32x16(a, qb[rb][ks].v, s[rb][h]);
       }
-      // s[j] holds key slot 16*(j/8) + 8*hsub + (j%8) of the tile for row n.
-      float mx = kNegBig;
+    }
+    // Per half: softmax (VALU) then O^T += V^T P^T; the second half's
+    // softmax is independent of the first half's PV products.
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int ks_ = 16 * (j >> 3) + 8 * hsub + (j & 7);
-        const int tok = tl[ks_];
-        const bool ok = tok >= 0 && (tok < cur0 || tok <= qpos);
-        s[j] = ok ? s[j] : -INFINITY;
-        mx = fmaxf(mx, s[j]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float psum = 0.f;
-      Pack8 pb[2];
+    for (int h = 0; h < 2; ++h) {
+      Pack8 pb[RB][2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = __builtin_amdgcn_exp2f(s[j] - m_new);
-        psum += e;
-        pb[j >> 3].h[j & 7] = f32_to_bf16(e);
-      }
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb])
+          softmax_half<DB>(s[rb][h], masked, tl + 32 * h, hsub, cur0, qpos[rb], ref[rb], lsum[rb],
+                           started[rb], o[rb], pb[rb]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              vl + (db * 32 + n) * kVP + ((2 * h + kk) * 16 + hsub * 8) * 2);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(vl + (db * 32 + n) * kVPitch + (kk * 16 + hsub * 8) * 2);
-          o[db] = mfma32x32x16(a, pb[kk].v, o[db]);
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb_on[rb]) o[rb][db] = mfma32x32x16(a, pb[rb][kk].v, o[rb][db]);
         }
       }
     }
   }
 
-  if (!row_ok) return;
   // O^T register j of block db is d = db*32 + 8*(j/4) + 4*hsub + (j%4).
-  const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0);
-  if (p.splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* out = static_cast<uint16_t*>(p.out) + orow * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rb_on[rb]) continue;
+    const float lrow = lsum[rb] + __shfl_xor(lsum[rb], 32);
+    if (row[rb] >= w.R) continue;
+    const int64_t orow =
+        (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl[rb]) * p.q_stride + (qpos[rb] - p.q_row0);
+    if (p.splits == 1) {
+      const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+      uint16_t* out = static_cast<uint16_t*>(p.out) + orow * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hsub;
-        uint2 pk;
-        pk.x = pack_bf16x2(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
-        pk.y = pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-        *reinterpret_cast<uint2*>(out + d0) = pk;
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * hsub;
+          const f32x2 f0 = {o[rb][db][4 * g4 + 0] * inv, o[rb][db][4 * g4 + 1] * inv};
+          const f32x2 f1 = {o[rb][db][4 * g4 + 2] * inv, o[rb][db][4 * g4 + 3] * inv};
+          uint2 pk;
+          pk.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f0, bf16x2));
+          pk.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f1, bf16x2));
+          *reinterpret_cast<uint2*>(out + d0) = pk;
+        }
       }
-    }
-    if (p.lse != nullptr && hsub == 0) p.lse[orow] = (m_run + log2f(l_run)) * kLn2;
-  } else {
-    const int64_t prow_i = (w.slot * p.splits + split) * p.Rcap + row;
-    float* wo = p.ws_o + prow_i * D;
+      if (p.lse != nullptr && hsub == 0)
+        p.lse[orow] = started[rb] ? (ref[rb] + log2f(lrow)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t pr = (w.slot * p.splits + split) * p.Rcap + row[rb];
+      float* wo = p.ws_o + pr * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hsub;
-        *reinterpret_cast<float4*>(wo + d0) =
-            make_float4(o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * hsub;
+          *reinterpret_cast<float4*>(wo + d0) =
+              make_float4(o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2], o[rb][db][4 * g4 + 3]);
+        }
       }
-    }
-    if (hsub == 0) {
-      p.ws_ml[prow_i * 2] = m_run;
-      p.ws_ml[prow_i * 2 + 1] = l_run;
+      if (hsub == 0) {
+        p.ws_ml[pr * 2] = started[rb] ? ref[rb] : kNegBig;
+        p.ws_ml[pr * 2 + 1] = lrow;
+      }
     }
   }
 }
@@ -378,17 +532,17 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
 // f32 inputs: one wave per 64 rows, one lane per row.
 template <int D>
 __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
-  constexpr int TK = 32;
+  constexpr int TK = kTKf;
   constexpr int H = D / 2;
   __shared__ __align__(16) float kt[TK][D];
   __shared__ __align__(16) float vt[TK][D];
   __shared__ int tk[TK];
   const int lane = threadIdx.x;
-  const int per_unit = p.slices * p.splits;
-  const int64_t u = blockIdx.x / per_unit;
-  const int rem = static_cast<int>(blockIdx.x - u * per_unit);
-  const int slice = rem / p.splits;
-  const int split = rem - slice * p.splits;
+  int64_t u;
+  int item;
+  if (!block_item(p, u, item)) return;
+  const int slice = item / p.splits;
+  const int split = item - slice * p.splits;
   const AUnit w = make_aunit(p, u);
   const int r0 = slice * 64;
   if (r0 >= w.R) return;
@@ -400,7 +554,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   const bool row_ok = row < w.R;
   const int qloc = row_ok ? row / p.G : 0;
   const int hl = row_ok ? row - qloc * p.G : 0;
-  const int64_t qpos = w.qlo + qloc;
+  const int qpos = static_cast<int>(w.qlo) + qloc;
   float q[D];
   {
     const float* src = static_cast<const float*>(p.q) +
@@ -419,13 +573,13 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   for (int i = 0; i < D; ++i) o[i] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
   const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
-  const int64_t cur0 = w.t * p.C;
+  const int cur0 = static_cast<int>(w.t * p.C);
   for (int kb = kbeg; kb < kend; kb += TK) {
     __syncthreads();
     for (int idx = lane; idx < TK * D / 4; idx += 64) {
       const int s = idx / (D / 4), c4 = idx - s * (D / 4);
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
-      const int64_t tok = kb + s < kend ? slot_token(p, w, kb + s) : -1;
+      const int tok = kb + s < kend ? slot_token(p, w, kb + s) : -1;
       if (tok >= 0) {
         int64_t ko, vo;
         kv_offsets<D>(p, w, kb + s, tok, slab, ko, vo);
@@ -435,7 +589,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
       reinterpret_cast<float4*>(&kt[s][0])[c4] = kk;
       reinterpret_cast<float4*>(&vt[s][0])[c4] = vv;
     }
-    if (lane < TK) tk[lane] = (kb + lane < kend) ? static_cast<int>(slot_token(p, w, kb + lane)) : -1;
+    if (lane < TK) tk[lane] = (kb + lane < kend) ? slot_token(p, w, kb + lane) : -1;
     __syncthreads();
     float sc[TK];
     float mx = kNegBig;
@@ -472,11 +626,11 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     for (int i = 0; i < D; ++i) out[i] = o[i] * inv;
     if (p.lse != nullptr) p.lse[orow] = (m_run + log2f(l_run)) * kLn2;
   } else {
-    const int64_t prow_i = (w.slot * p.splits + split) * p.Rcap + row;
+    const int64_t pr = (w.slot * p.splits + split) * p.Rcap + row;
 #pragma unroll
-    for (int i = 0; i < D; ++i) p.ws_o[prow_i * D + i] = o[i];
-    p.ws_ml[prow_i * 2] = m_run;
-    p.ws_ml[prow_i * 2 + 1] = l_run;
+    for (int i = 0; i < D; ++i) p.ws_o[pr * D + i] = o[i];
+    p.ws_ml[pr * 2] = m_run;
+    p.ws_ml[pr * 2 + 1] = l_run;
   }
 }
 
@@ -486,8 +640,7 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t gr = static_cast<int64_t>(blockIdx.x) * 4 + wave;  // (unit, row)
-  const int64_t units = static_cast<int64_t>(p.B) * p.Hkv * p.nqc;
-  if (gr >= units * p.Rcap) return;
+  if (gr >= p.units * p.Rcap) return;
   const int64_t u = gr / p.Rcap;
   const int row = static_cast<int>(gr - u * p.Rcap);
   const AUnit w = make_aunit(p, u);
@@ -519,7 +672,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
 }
 
 struct Plan {
-  int nw, slices, splits, kps, rcap;
+  int nw, rb, slices, splits, kps, rcap;
   int64_t units;
 };
 
@@ -538,10 +691,14 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   // Rows of the largest unit: a query chunk holds at most min(C, n_q) queries.
   const int64_t rows = std::min<int64_t>(g.C, g.n_q) * static_cast<int64_t>(g.G);
   pl.rcap = static_cast<int>(rows);
+  pl.rb = 1;
   if (g.bf16) {
     const int64_t blocks = (rows + 31) / 32;
-    pl.nw = blocks >= 8 ? 8 : (blocks >= 4 ? 4 : (blocks >= 2 ? 2 : 1));
-    pl.slices = static_cast<int>((blocks + pl.nw - 1) / pl.nw);
+    pl.rb = blocks >= 2 * HGA_ATTEND_RB ? HGA_ATTEND_RB : 1;
+    const int64_t wblocks = (blocks + pl.rb - 1) / pl.rb;  // waves needed
+    const int maxw = pl.rb == 2 ? 4 : 8;
+    pl.nw = wblocks >= maxw ? maxw : (wblocks >= 4 ? 4 : (wblocks >= 2 ? 2 : 1));
+    pl.slices = static_cast<int>((wblocks + pl.nw - 1) / pl.nw);
   } else {
     pl.nw = 1;
     pl.slices = static_cast<int>((rows + 63) / 64);
@@ -555,7 +712,6 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
     const int64_t want = (1024 + wgs - 1) / wgs;
     if (sp > want) sp = want;
     if (sp > 1) {
-      pl.splits = static_cast<int>(sp);
       pl.kps = static_cast<int>(((keys + sp - 1) / sp + kTK - 1) / kTK * kTK);
       pl.splits = static_cast<int>((keys + pl.kps - 1) / pl.kps);
     }
@@ -563,15 +719,37 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   return pl;
 }
 
+template <int D, int RB, bool POOL>
+void launch_mfma(int nw, unsigned grid, hipStream_t stream, const AttendParams& p) {
+  switch (nw) {
+    case 8: hipLaunchKernelGGL((attend_mfma_kernel<D, 8, RB, POOL>), dim3(grid), dim3(512), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RB, POOL>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2, RB, POOL>), dim3(grid), dim3(128), 0, stream, p); break;
+    default: hipLaunchKernelGGL((attend_mfma_kernel<D, 1, RB, POOL>), dim3(grid), dim3(64), 0, stream, p); break;
+  }
+}
+
+template <int D, int RB>
+void launch_mfma_pool(int nw, unsigned grid, hipStream_t stream, const AttendParams& p) {
+  if (p.pool_slot != nullptr)
+    launch_mfma<D, RB, true>(nw, grid, stream, p);
+  else
+    launch_mfma<D, RB, false>(nw, grid, stream, p);
+}
+
 template <int D>
 hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(pl.units * pl.slices * pl.splits);
+  const int64_t groups = (pl.units + 7) / 8;
+  const unsigned grid = static_cast<unsigned>(groups * 8 * p.per_unit);
   if (g.bf16) {
-    switch (pl.nw) {
-      case 8: hipLaunchKernelGGL((attend_mfma_kernel<D, 8>), dim3(grid), dim3(512), 0, stream, p); break;
-      case 4: hipLaunchKernelGGL((attend_mfma_kernel<D, 4>), dim3(grid), dim3(256), 0, stream, p); break;
-      case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2>), dim3(grid), dim3(128), 0, stream, p); break;
-      default: hipLaunchKernelGGL((attend_mfma_kernel<D, 1>), dim3(grid), dim3(64), 0, stream, p); break;
+    if constexpr (HGA_ATTEND_RB == 2) {
+      if (pl.rb == 2) {
+        launch_mfma_pool<D, 2>(pl.nw, grid, stream, p);
+      } else {
+        launch_mfma_pool<D, 1>(pl.nw, grid, stream, p);
+      }
+    } else {
+      launch_mfma_pool<D, 1>(pl.nw, grid, stream, p);
     }
   } else {
     hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(64), 0, stream, p);
@@ -587,6 +765,10 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
 }
 
 }  // namespace
+
+bool attend_supported(const Geometry& g) {
+  return (g.d == 64 || g.d == 128) && (g.gs & (g.gs - 1)) == 0 && g.C <= 64;
+}
 
 size_t attend_workspace(const Geometry& g, bool dense, bool allow_split) {
   const Plan pl = make_plan(g, dense, allow_split);
@@ -622,6 +804,7 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
   p.kv_cap = g.kv_cap;
   p.t0 = g.t0;
   p.nqc = g.nqc;
+  p.units = pl.units;
   p.B = g.B;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
@@ -629,12 +812,14 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
   p.d = g.d;
   p.C = g.C;
   p.gs = g.gs;
+  p.lg_gs = 0;
+  while ((1 << p.lg_gs) < g.gs) ++p.lg_gs;
   p.gmax = g.gmax;
   p.Rcap = pl.rcap;
-  p.nw = pl.nw;
   p.slices = pl.slices;
   p.splits = pl.splits;
   p.keys_per_split = pl.kps;
+  p.per_unit = pl.slices * pl.splits;
   p.dense = dense ? 1 : 0;
   p.scale_log2 = g.scale * kLog2e;
   p.rope = g.rope;

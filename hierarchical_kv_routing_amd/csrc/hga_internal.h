@@ -57,6 +57,7 @@ struct AttendExtra {
   int64_t q_row0 = -1;    // position of row 0; -1 = q_pos0
 };
 
+bool attend_supported(const Geometry& g);
 size_t attend_workspace(const Geometry& g, bool dense, bool allow_split = true);
 hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,
                          const int32_t* granules, const int32_t* granule_count, bool dense,

@@ -154,7 +154,7 @@ hga_status tier_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, 
   if (n_q <= 0 || wmax <= 0) return HGA_ERR_INVALID_ARGUMENT;
   // one query chunk of every (sequence, KV head) must fit a window
   if (slots < static_cast<int64_t>(g.B) * g.Hkv * g.gmax) return HGA_ERR_INVALID_ARGUMENT;
-  if (!hga::route_supported(g)) return HGA_ERR_UNSUPPORTED;
+  if (!hga::route_supported(g) || !hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
   return HGA_OK;
 }
 
