@@ -15,10 +15,12 @@
 //   S^T = K Q^T      (32x32x16 bf16 MFMA, keys on M, query rows on N)
 //   softmax          (f32, base 2, Q pre-scaled by scale*log2(e))
 //   O^T += V^T P^T   (32x32x16 bf16 MFMA, P rounded to bf16)
-// With rows on N each lane owns one row.  K rows are read into the MFMA in
-// the order pi(m) (bits 2 and 3 of m swapped), which makes the S^T
-// accumulator registers of a lane cover exactly the 8 consecutive keys the
-// PV product wants from it: P never goes through LDS.
+// With rows on N each lane owns one row.  MFMA row m of K is key pi(m)
+// (bits 2 and 3 of m swapped), which makes the S^T accumulator registers of
+// a lane cover exactly the 8 consecutive keys the PV product wants from it:
+// P never goes through LDS.  The permutation is applied when K is stored
+// (LDS row pi(s) holds key s), so the MFMA reads consecutive LDS rows and
+// both LDS reads and writes are free of bank conflicts.
 //
 // Softmax keeps a per-row reference r and accumulates 2^(s - r): r moves
 // only when a stage's scores exceed it by more than 2^8 (a wave-uniform
@@ -167,51 +169,61 @@ struct StageRegs {
   bool masked;
 };
 
+// Tokens of the key pair (s0, s0 + 1), -1 where absent.
+__device__ __forceinline__ void pair_tokens(const AttendParams& p, const AUnit& w, int s0, int kend,
+                                            int& t0, int& t1) {
+  t0 = s0 < kend ? slot_token(p, w, s0) : -1;
+  if (p.lg_gs > 0)  // s0 is even, so both keys of the pair sit in one granule
+    t1 = (t0 >= 0 && s0 + 1 < kend) ? t0 + 1 : -1;
+  else
+    t1 = s0 + 1 < kend ? slot_token(p, w, s0 + 1) : -1;
+}
+
+// 16 bytes (d slice sl) of the K (IS_V = false) or V row of key slot s.
+template <int D, bool POOL, bool IS_V>
+__device__ __forceinline__ uint4 load_row16(const AttendParams& p, const AUnit& w, int s, int tok,
+                                            int64_t slab, int sl) {
+  if (tok < 0) return make_uint4(0, 0, 0, 0);
+  const uint16_t* base = static_cast<const uint16_t*>(IS_V ? p.v : p.k);
+  int64_t off;
+  if constexpr (POOL) {
+    int64_t ko, vo;
+    kv_offsets<D>(p, w, s, tok, slab, ko, vo);
+    off = IS_V ? vo : ko;
+  } else {
+    off = (slab + tok) * D;
+  }
+  return *reinterpret_cast<const uint4*>(base + off + sl * 8);
+}
+
+// Item i of a stage covers one key pair and one 16-byte d slice.  K items
+// run slice-fastest (a half wave reads whole 256-byte rows); V items run
+// key-pair-fastest so that the transposed LDS stores of a wave land in 64
+// distinct banks.
 template <int D, int NW, bool POOL>
 __device__ __forceinline__ void load_stage(const AttendParams& p, const AUnit& w, int kb, int kend,
                                            int64_t slab, int cur0, StageRegs<D, NW>& r) {
   constexpr int SL = StageRegs<D, NW>::SL;
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
 #pragma unroll
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
     uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
     int t0 = -1, t1 = -1;
     if (idx < StageRegs<D, NW>::kItems) {
-      const int kp = idx / SL, sl = idx - kp * SL;
-      const int s0 = kb + 2 * kp;
-      if (p.lg_gs > 0) {
-        // s0 is even, so both keys of the pair sit in one granule
-        t0 = s0 < kend ? slot_token(p, w, s0) : -1;
-        t1 = (t0 >= 0 && s0 + 1 < kend) ? t0 + 1 : -1;
-      } else {
-        t0 = s0 < kend ? slot_token(p, w, s0) : -1;
-        t1 = s0 + 1 < kend ? slot_token(p, w, s0 + 1) : -1;
+      {
+        const int kp = idx / SL, sl = idx - kp * SL;
+        const int s0 = kb + 2 * kp;
+        pair_tokens(p, w, s0, kend, t0, t1);
+        a0 = load_row16<D, POOL, false>(p, w, s0, t0, slab, sl);
+        a1 = load_row16<D, POOL, false>(p, w, s0 + 1, t1, slab, sl);
       }
-      if constexpr (POOL) {
-        int64_t ko, vo;
-        if (t0 >= 0) {
-          kv_offsets<D>(p, w, s0, t0, slab, ko, vo);
-          a0 = *reinterpret_cast<const uint4*>(kbase + ko + sl * 8);
-          b0 = *reinterpret_cast<const uint4*>(vbase + vo + sl * 8);
-        }
-        if (t1 >= 0) {
-          kv_offsets<D>(p, w, s0 + 1, t1, slab, ko, vo);
-          a1 = *reinterpret_cast<const uint4*>(kbase + ko + sl * 8);
-          b1 = *reinterpret_cast<const uint4*>(vbase + vo + sl * 8);
-        }
-      } else {
-        const uint16_t* kr = kbase + slab * D + sl * 8;
-        const uint16_t* vr = vbase + slab * D + sl * 8;
-        if (t0 >= 0) {
-          a0 = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(t0) * D);
-          b0 = *reinterpret_cast<const uint4*>(vr + static_cast<int64_t>(t0) * D);
-        }
-        if (t1 >= 0) {
-          a1 = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(t1) * D);
-          b1 = *reinterpret_cast<const uint4*>(vr + static_cast<int64_t>(t1) * D);
-        }
+      {
+        const int kp = idx & 31, sl = idx >> 5;
+        const int s0 = kb + 2 * kp;
+        int u0, u1;
+        pair_tokens(p, w, s0, kend, u0, u1);
+        b0 = load_row16<D, POOL, true>(p, w, s0, u0, slab, sl);
+        b1 = load_row16<D, POOL, true>(p, w, s0 + 1, u1, slab, sl);
       }
     }
     r.k0[i] = a0;
@@ -236,9 +248,16 @@ __device__ __forceinline__ void store_stage(const StageRegs<D, NW>& r, char* kl,
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
     if (idx < StageRegs<D, NW>::kItems) {
-      const int kp = idx / SL, sl = idx - kp * SL;
-      *reinterpret_cast<uint4*>(kl + (2 * kp) * KP + sl * 16) = r.k0[i];
-      *reinterpret_cast<uint4*>(kl + (2 * kp + 1) * KP + sl * 16) = r.k1[i];
+      int kp = idx / SL, sl = idx - kp * SL;
+      // K row of key s goes to LDS row pi(s), so MFMA row m reads LDS row m
+      *reinterpret_cast<uint4*>(kl + perm_row(2 * kp) * KP + sl * 16) = r.k0[i];
+      *reinterpret_cast<uint4*>(kl + perm_row(2 * kp + 1) * KP + sl * 16) = r.k1[i];
+      if (sl == 0) {
+        tl[2 * kp] = r.t0[i];
+        tl[2 * kp + 1] = r.t1[i];
+      }
+      kp = idx & 31;
+      sl = idx >> 5;
       const uint32_t x[4] = {r.v0[i].x, r.v0[i].y, r.v0[i].z, r.v0[i].w};
       const uint32_t y[4] = {r.v1[i].x, r.v1[i].y, r.v1[i].z, r.v1[i].w};
 #pragma unroll
@@ -248,10 +267,6 @@ __device__ __forceinline__ void store_stage(const StageRegs<D, NW>& r, char* kl,
         const uint32_t hi = (x[e] >> 16) | (y[e] & 0xFFFF0000u);
         *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e) * kVP + kp * 4) = lo;
         *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e + 1) * kVP + kp * 4) = hi;
-      }
-      if (sl == 0) {
-        tl[2 * kp] = r.t0[i];
-        tl[2 * kp + 1] = r.t1[i];
       }
     }
   }
@@ -429,7 +444,6 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
   StageRegs<D, NW> sr;
   if (nstages > 0) load_stage<D, NW, POOL>(p, w, kbeg, kend, slab, cur0, sr);
-  const int prow = perm_row(n);
   for (int st = 0; st < nstages; ++st) {
     char* kl = smem + (st & 1) * SB;
     char* vl = kl + kTK * KP;
@@ -453,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kl + (h * 32 + prow) * KP + (ks * 16 + hsub * 8) * 2);
+            *reinterpret_cast<const bf16x8*>(kl + (h * 32 + n) * KP + (ks * 16 + hsub * 8) * 2);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           if (rb_on[rb]) s[rb][h] = mfma32x32x16(a, qb[rb][ks].v, s[rb][h]);
