@@ -47,6 +47,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kTK = 64;                // keys per LDS stage (bf16 path)
+constexpr int kTab = kAttendTable;     // granule-table entries per work item (bf16 path)
 constexpr int kVP = kTK * 2 + 16;      // bytes per transposed V row in LDS
 constexpr int kTKf = 32;               // keys per LDS tile (f32 path)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -169,74 +170,80 @@ struct StageRegs {
   bool masked;
 };
 
-// Tokens of the key pair (s0, s0 + 1), -1 where absent.
-__device__ __forceinline__ void pair_tokens(const AttendParams& p, const AUnit& w, int s0, int kend,
-                                            int& t0, int& t1) {
-  t0 = s0 < kend ? slot_token(p, w, s0) : -1;
-  if (p.lg_gs > 0)  // s0 is even, so both keys of the pair sit in one granule
-    t1 = (t0 >= 0 && s0 + 1 < kend) ? t0 + 1 : -1;
-  else
-    t1 = s0 + 1 < kend ? slot_token(p, w, s0 + 1) : -1;
+// Buffer resource over `bytes` bytes from `base`: a load whose offset is
+// at or beyond `bytes` returns zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+constexpr uint32_t kNoRow = 0x80000000u;  // beyond every K/V buffer (their sizes stay below 2^31)
+
+// (row, token) of key slot s: row counts D-element rows from the start of the
+// K (and V) buffer resource, token is the sequence position; both -1 when s
+// is at or past kend or its granule is invalid.  gtab holds the granules of
+// the work item from granule gfirst on (unused in dense mode).
+__device__ __forceinline__ int2 key_at(const AttendParams& p, const int2* gtab, int gfirst, int s,
+                                       int kend) {
+  if (s >= kend) return make_int2(-1, -1);
+  if (p.dense) return make_int2(s, s);
+  const int2 e = gtab[(s >> p.lg_gs) - gfirst];
+  const int lo = s & ((1 << p.lg_gs) - 1);
+  return e.x < 0 ? e : make_int2(e.x + lo, e.y + lo);
 }
 
-// 16 bytes (d slice sl) of the K (IS_V = false) or V row of key slot s.
-template <int D, bool POOL, bool IS_V>
-__device__ __forceinline__ uint4 load_row16(const AttendParams& p, const AUnit& w, int s, int tok,
-                                            int64_t slab, int sl) {
-  if (tok < 0) return make_uint4(0, 0, 0, 0);
-  const uint16_t* base = static_cast<const uint16_t*>(IS_V ? p.v : p.k);
-  int64_t off;
-  if constexpr (POOL) {
-    int64_t ko, vo;
-    kv_offsets<D>(p, w, s, tok, slab, ko, vo);
-    off = IS_V ? vo : ko;
-  } else {
-    off = (slab + tok) * D;
-  }
-  return *reinterpret_cast<const uint4*>(base + off + sl * 8);
+// Keys of the pair (s0, s0 + 1), s0 even.
+__device__ __forceinline__ void pair_keys(const AttendParams& p, const int2* gtab, int gfirst, int s0,
+                                          int kend, int2& a, int2& b) {
+  a = key_at(p, gtab, gfirst, s0, kend);
+  if (p.lg_gs > 0)  // both keys of the pair sit in one granule
+    b = (a.x >= 0 && s0 + 1 < kend) ? make_int2(a.x + 1, a.y + 1) : make_int2(-1, -1);
+  else
+    b = key_at(p, gtab, gfirst, s0 + 1, kend);
+}
+
+// 16 bytes (d slice sl) of row `row` of a K or V buffer; zero when row < 0.
+template <int D>
+__device__ __forceinline__ uint4 load_row16(__amdgpu_buffer_rsrc_t r, int row, int sl) {
+  const uint32_t off = row >= 0 ? static_cast<uint32_t>(row) * (D * 2) + sl * 16 : kNoRow;
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Item i of a stage covers one key pair and one 16-byte d slice.  K items
 // run slice-fastest (a half wave reads whole 256-byte rows); V items run
 // key-pair-fastest so that the transposed LDS stores of a wave land in 64
-// distinct banks.
-template <int D, int NW, bool POOL>
-__device__ __forceinline__ void load_stage(const AttendParams& p, const AUnit& w, int kb, int kend,
-                                           int64_t slab, int cur0, StageRegs<D, NW>& r) {
+// distinct banks.  Absent keys load zeros.
+template <int D, int NW>
+__device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffer_rsrc_t kr,
+                                           __amdgpu_buffer_rsrc_t vr, const int2* gtab, int gfirst,
+                                           int kb, int kend, int cur0, StageRegs<D, NW>& r) {
   constexpr int SL = StageRegs<D, NW>::SL;
 #pragma unroll
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-    int t0 = -1, t1 = -1;
     if (idx < StageRegs<D, NW>::kItems) {
       {
         const int kp = idx / SL, sl = idx - kp * SL;
-        const int s0 = kb + 2 * kp;
-        pair_tokens(p, w, s0, kend, t0, t1);
-        a0 = load_row16<D, POOL, false>(p, w, s0, t0, slab, sl);
-        a1 = load_row16<D, POOL, false>(p, w, s0 + 1, t1, slab, sl);
+        int2 a, b;
+        pair_keys(p, gtab, gfirst, kb + 2 * kp, kend, a, b);
+        r.k0[i] = load_row16<D>(kr, a.x, sl);
+        r.k1[i] = load_row16<D>(kr, b.x, sl);
+        r.t0[i] = a.y;
+        r.t1[i] = b.y;
       }
       {
         const int kp = idx & 31, sl = idx >> 5;
-        const int s0 = kb + 2 * kp;
-        int u0, u1;
-        pair_tokens(p, w, s0, kend, u0, u1);
-        b0 = load_row16<D, POOL, true>(p, w, s0, u0, slab, sl);
-        b1 = load_row16<D, POOL, true>(p, w, s0 + 1, u1, slab, sl);
+        int2 a, b;
+        pair_keys(p, gtab, gfirst, kb + 2 * kp, kend, a, b);
+        r.v0[i] = load_row16<D>(vr, a.x, sl);
+        r.v1[i] = load_row16<D>(vr, b.x, sl);
       }
     }
-    r.k0[i] = a0;
-    r.k1[i] = a1;
-    r.v0[i] = b0;
-    r.v1[i] = b1;
-    r.t0[i] = t0;
-    r.t1[i] = t1;
   }
   // Tokens ascend along a list, so the stage needs masks iff it runs past the
-  // end of the key range or its last key lies in the current chunk.
+  // end of the key range or its last key is absent or in the current chunk.
   const int stop = kb + kTK < kend ? kb + kTK : kend;
-  const int tl = slot_token(p, w, stop - 1);
+  const int tl = key_at(p, gtab, gfirst, stop - 1, kend).y;
   r.masked = (kb + kTK > kend) || tl < 0 || tl >= cur0;
 }
 
@@ -263,8 +270,8 @@ __device__ __forceinline__ void store_stage(const StageRegs<D, NW>& r, char* kl,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // element d of keys (2kp, 2kp+1) packed as one 32-bit LDS word
-        const uint32_t lo = (x[e] & 0xFFFFu) | (y[e] << 16);
-        const uint32_t hi = (x[e] >> 16) | (y[e] & 0xFFFF0000u);
+        const uint32_t lo = __builtin_amdgcn_perm(y[e], x[e], 0x05040100u);  // low halves
+        const uint32_t hi = __builtin_amdgcn_perm(y[e], x[e], 0x07060302u);  // high halves
         *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e) * kVP + kp * 4) = lo;
         *reinterpret_cast<uint32_t*>(vl + (sl * 8 + 2 * e + 1) * kVP + kp * 4) = hi;
       }
@@ -348,7 +355,8 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   constexpr int SB = stage_bytes<D>();
   constexpr int H = D / 2;
   constexpr int kTable = 64 * H * 8;
-  constexpr int kSmem = (2 * SB) > kTable ? (2 * SB) : kTable;
+  constexpr int kMain = (2 * SB) > kTable ? (2 * SB) : kTable;
+  constexpr int kSmem = kMain + kTab * 8;
   constexpr int kRows = NW * 32 * RB;
   __shared__ __align__(16) char smem[kSmem];
 
@@ -364,6 +372,30 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   int kend = kbeg + p.keys_per_split;
   if (kend > w.nkeys) kend = w.nkeys;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // Granule table of the item's key range (rows and tokens of each granule's
+  // first key), read once so that stage loads need no dependent global load.
+  int2* gtab = reinterpret_cast<int2*>(smem + kMain);
+  const int gfirst = kbeg >> p.lg_gs;
+  if (!p.dense && kend > kbeg) {
+    const int ng = ((kend - 1) >> p.lg_gs) - gfirst + 1;  // <= kTab (make_plan)
+    const int64_t gcap = p.kv_cap >> p.lg_gs;
+    for (int i = threadIdx.x; i < ng; i += NW * 64) {
+      const int64_t e = w.slot * p.gmax + gfirst + i;
+      const int64_t g = p.gran[e];
+      int2 t = make_int2(-1, -1);
+      if (g >= 0 && g < gcap) {
+        const int tok = static_cast<int>(g << p.lg_gs);
+        if constexpr (POOL) {
+          const int64_t ps = p.pool_slot[e];
+          if (ps >= 0 && ps < p.pool_slots) t = make_int2(static_cast<int>(ps << (p.lg_gs + 1)), tok);
+        } else {
+          t = make_int2(tok, tok);
+        }
+      }
+      gtab[i] = t;
+    }
+  }
 
   // RoPE table for the queries of this workgroup's rows.
   const int rend = (r0 + kRows) < w.R ? (r0 + kRows) : w.R;
@@ -426,7 +458,20 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   }
   __syncthreads();  // the table space becomes the K/V stage buffers
 
-  const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
+  // K and V buffer resources: the (sequence, KV head) slab, or the staging
+  // pool whose slot holds K then V of one granule.
+  __amdgpu_buffer_rsrc_t kr, vr;
+  if constexpr (POOL) {
+    const int64_t gbytes = static_cast<int64_t>(p.gs) * D * 2;
+    const uint32_t bytes = static_cast<uint32_t>(p.pool_slots * 2 * gbytes);
+    kr = buffer_rsrc(p.k, bytes);
+    vr = buffer_rsrc(static_cast<const char*>(p.v) + gbytes, bytes - static_cast<uint32_t>(gbytes));
+  } else {
+    const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap * D * 2;
+    const uint32_t bytes = static_cast<uint32_t>(p.kv_cap * D * 2);
+    kr = buffer_rsrc(static_cast<const char*>(p.k) + slab, bytes);
+    vr = buffer_rsrc(static_cast<const char*>(p.v) + slab, bytes);
+  }
   f32x16 o[RB][DB];
   float ref[RB], lsum[RB];
   bool started[RB];
@@ -443,7 +488,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
 
   const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
   StageRegs<D, NW> sr;
-  if (nstages > 0) load_stage<D, NW, POOL>(p, w, kbeg, kend, slab, cur0, sr);
+  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, sr);
   for (int st = 0; st < nstages; ++st) {
     char* kl = smem + (st & 1) * SB;
     char* vl = kl + kTK * KP;
@@ -451,7 +496,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
     store_stage<D, NW>(sr, kl, vl, tl);
     const bool masked = sr.masked;
     __syncthreads();
-    if (st + 1 < nstages) load_stage<D, NW, POOL>(p, w, kbeg + (st + 1) * kTK, kend, slab, cur0, sr);
+    if (st + 1 < nstages) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
     if (!rb_on[0]) continue;  // wave-uniform: this wave has no rows
     // S^T for the two 32-key halves; each K operand serves every row block.
     // s[rb][h][j] holds key 32h + 16*(j/8) + 8*hsub + (j%8).
@@ -730,6 +775,12 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
       pl.splits = static_cast<int>((keys + pl.kps - 1) / pl.kps);
     }
   }
+  // A routed bf16 item reads at most kTab granules (a multiple of kTK keys).
+  const int64_t cap = static_cast<int64_t>(kTab) * g.gs;
+  if (g.bf16 && !dense && allow_split && pl.kps > cap) {
+    pl.kps = static_cast<int>(cap);
+    pl.splits = static_cast<int>((keys + cap - 1) / cap);
+  }
   return pl;
 }
 
@@ -781,7 +832,9 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
 }  // namespace
 
 bool attend_supported(const Geometry& g) {
-  return (g.d == 64 || g.d == 128) && (g.gs & (g.gs - 1)) == 0 && g.C <= 64;
+  if (!((g.d == 64 || g.d == 128) && (g.gs & (g.gs - 1)) == 0 && g.C <= 64)) return false;
+  // bf16 K/V slabs are addressed through buffer resources with 32-bit offsets
+  return !g.bf16 || g.kv_cap * g.d * 2 < (int64_t{1} << 31);
 }
 
 size_t attend_workspace(const Geometry& g, bool dense, bool allow_split) {

@@ -57,6 +57,11 @@ struct AttendExtra {
   int64_t q_row0 = -1;    // position of row 0; -1 = q_pos0
 };
 
+// Granules one bf16 attention work item can read (an LDS table); longer
+// lists are split over several work items, which the host tier (no
+// splitting) cannot do, so it requires G_max <= kAttendTable.
+constexpr int kAttendTable = 2048;
+
 bool attend_supported(const Geometry& g);
 size_t attend_workspace(const Geometry& g, bool dense, bool allow_split = true);
 hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,

@@ -155,6 +155,9 @@ hga_status tier_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, 
   // one query chunk of every (sequence, KV head) must fit a window
   if (slots < static_cast<int64_t>(g.B) * g.Hkv * g.gmax) return HGA_ERR_INVALID_ARGUMENT;
   if (!hga::route_supported(g) || !hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
+  // the pool is read through 32-bit buffer offsets, every list by one work item
+  const int64_t pool = slots * 2 * g.gs * g.d * (g.bf16 ? 2 : 4);
+  if (g.bf16 && (pool >= (int64_t{1} << 31) || g.gmax > hga::kAttendTable)) return HGA_ERR_UNSUPPORTED;
   return HGA_OK;
 }
 
