@@ -87,6 +87,27 @@ struct AUnit {
   int nq, R, nkeys;
 };
 
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t v = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The unit's fields as scalars (the same on every lane of the block).
+__device__ __forceinline__ AUnit uniform_unit(const AUnit& a) {
+  AUnit w;
+  w.b = __builtin_amdgcn_readfirstlane(a.b);
+  w.kvh = __builtin_amdgcn_readfirstlane(a.kvh);
+  w.t = uniform64(a.t);
+  w.qlo = uniform64(a.qlo);
+  w.slot = uniform64(a.slot);
+  w.nq = __builtin_amdgcn_readfirstlane(a.nq);
+  w.R = __builtin_amdgcn_readfirstlane(a.R);
+  w.nkeys = __builtin_amdgcn_readfirstlane(a.nkeys);
+  return w;
+}
+
 __device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
   AUnit w;
   const int64_t bh = static_cast<int64_t>(p.B) * p.Hkv;
@@ -244,7 +265,8 @@ __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffe
   // end of the key range or its last key is absent or in the current chunk.
   const int stop = kb + kTK < kend ? kb + kTK : kend;
   const int tl = key_at(p, gtab, gfirst, stop - 1, kend).y;
-  r.masked = (kb + kTK > kend) || tl < 0 || tl >= cur0;
+  // the same value on every lane: make it a scalar so branches on it are uniform
+  r.masked = __builtin_amdgcn_readfirstlane(static_cast<int>((kb + kTK > kend) || tl < 0 || tl >= cur0)) != 0;
 }
 
 template <int D, int NW>
@@ -348,7 +370,7 @@ __device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* 
 }
 
 template <int D, int NW, int RB, bool POOL>
-__global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_mfma_kernel(AttendParams p) {
   constexpr int KS = D / 16;    // k-steps of S^T over d
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int KP = D * 2 + 16;
@@ -365,13 +387,13 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendParams p) {
   if (!block_item(p, u, item)) return;  // uniform
   const int slice = item / p.splits;
   const int split = item - slice * p.splits;
-  const AUnit w = make_aunit(p, u);
+  const AUnit w = uniform_unit(make_aunit(p, u));
   const int r0 = slice * kRows;
   if (r0 >= w.R) return;  // uniform
   const int kbeg = split * p.keys_per_split;
   int kend = kbeg + p.keys_per_split;
   if (kend > w.nkeys) kend = w.nkeys;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
   // Granule table of the item's key range (rows and tokens of each granule's
   // first key), read once so that stage loads need no dependent global load.

@@ -168,6 +168,83 @@ __device__ __forceinline__ float score16(const float* srow, int d, const Pack8 (
   return best;
 }
 
+// Summary rows staged in LDS, split into bf16 hi and lo halves, so that the
+// waves of a block that score the same rows for different query rows share
+// one load and one split.  Rows are padded by 16 bytes, which puts the 16
+// rows read by a quarter wave in distinct banks.
+constexpr int kStageRows = 64;
+constexpr int kStageStride = 4 * kMaxHalfDim + 16;  // bytes per staged row
+
+// Stages rows 0..kStageRows-1 given by row(i) (rows at or past n repeat row
+// n-1).  Block-wide.
+template <typename RowPtr>
+__device__ __forceinline__ void stage_rows(int n, int d, RowPtr row, char* shi, char* slo) {
+  const int segs = d / 8;
+  for (int i = threadIdx.x; i < kStageRows * segs; i += blockDim.x) {
+    const int r = i / segs, sg = i - r * segs;
+    float x[8];
+    load8<false>(row(r < n ? r : n - 1), sg * 8, x);
+    Pack8 h, l;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) split_bf16(x[k], h.h[k], l.h[k]);
+    *reinterpret_cast<uint4*>(shi + r * kStageStride + sg * 16) = h.q;
+    *reinterpret_cast<uint4*>(slo + r * kStageStride + sg * 16) = l.q;
+  }
+}
+
+// score16 for the 16 staged rows of tile `tile`.
+template <int KS>
+__device__ __forceinline__ float score16_staged(const char* shi, const char* slo, int tile,
+                                                const Pack8 (&ahi)[4][KS],
+                                                const Pack8 (&alo)[4][KS]) {
+  const int lane = threadIdx.x & 63;
+  const int off = (tile * 16 + (lane & 15)) * kStageStride + (lane >> 4) * 16;
+  Pack8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bhi[ks].q = *reinterpret_cast<const uint4*>(shi + off + ks * 64);
+    blo[ks].q = *reinterpret_cast<const uint4*>(slo + off + ks * 64);
+  }
+  float best = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mfma16x16x32(ahi[blk][ks].v, bhi[ks].v, acc);
+      acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
+      acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
+    }
+    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+  }
+  best = fmaxf(best, __shfl_xor(best, 16));
+  best = fmaxf(best, __shfl_xor(best, 32));
+  return best;
+}
+
+// Max-scores of n candidates (row(i) -> summary row) into keys[0..n), one
+// staged block of rows at a time; used when several row groups share tiles.
+template <int KS, typename RowPtr>
+__device__ __forceinline__ void score_staged(int n, int d, RowPtr row, bool has_rows, int tg,
+                                             int TG, const Pack8 (&ahi)[4][KS],
+                                             const Pack8 (&alo)[4][KS], char* shi, char* slo,
+                                             uint32_t* keys) {
+  const int lane = threadIdx.x & 63;
+  for (int b0 = 0; b0 < n; b0 += kStageRows) {
+    const int nb = n - b0 < kStageRows ? n - b0 : kStageRows;
+    stage_rows(nb, d, [&](int i) { return row(b0 + i); }, shi, slo);
+    __syncthreads();
+    if (has_rows) {
+      for (int tile = tg; tile * 16 < nb; tile += TG) {
+        const float v = score16_staged<KS>(shi, slo, tile, ahi, alo);
+        const int c = b0 + tile * 16 + (lane & 15);
+        if (lane < 16 && c < n) atomicMax(&keys[c], order_key(v));
+      }
+    }
+    __syncthreads();
+  }
+}
+
 struct SelScratch {
   int hist[256];
   int wsum[16];
@@ -323,6 +400,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
+  __shared__ __align__(16) char shi[kStageRows * kStageStride];
+  __shared__ __align__(16) char slo[kStageRows * kStageStride];
 
   const Unit w = make_unit(p, blockIdx.x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -351,8 +430,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     } else {
       for (int i = threadIdx.x; i < n_mid; i += blockDim.x) keys[i] = 0u;
       __syncthreads();
-      if (has_rows) {
-        const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+      const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+      if (RG > 1) {
+        const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
+        score_staged<KS>(n_mid, p.d, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
+                         has_rows, tg, TG, ahi, alo, shi, slo, keys);
+      } else if (has_rows) {
         const int ntile = (n_mid + 15) / 16;
         for (int tile = tg; tile < ntile; tile += TG) {
           int c = tile * 16 + (lane & 15);
@@ -374,8 +457,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     const int nc = nselc * p.r;
     for (int i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = 0u;
     __syncthreads();
-    if (has_rows) {
-      const int64_t gbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.ngroup_cap;
+    const int64_t gbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.ngroup_cap;
+    if (RG > 1) {
+      const float* g0 = p.gsum + gbase * p.d;
+      score_staged<KS>(nc, p.d, [&](int c) {
+        const int cr = c / p.r;
+        return g0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * p.d;
+      }, has_rows, tg, TG, ahi, alo, shi, slo, keys);
+    } else if (has_rows) {
       const int ntile = (nc + 15) / 16;
       for (int tile = tg; tile < ntile; tile += TG) {
         int c = tile * 16 + (lane & 15);
