@@ -777,8 +777,10 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
     const int64_t blocks = (rows + 31) / 32;
     pl.rb = blocks >= 2 * HGA_ATTEND_RB ? HGA_ATTEND_RB : 1;
     const int64_t wblocks = (blocks + pl.rb - 1) / pl.rb;  // waves needed
+    // Always 8 waves: the LDS stages hold one workgroup per CU, and waves
+    // without rows (few-row units such as decode) still share the loads.
     const int maxw = pl.rb == 2 ? 4 : 8;
-    pl.nw = wblocks >= maxw ? maxw : (wblocks >= 4 ? 4 : (wblocks >= 2 ? 2 : 1));
+    pl.nw = maxw;
     pl.slices = static_cast<int>((wblocks + pl.nw - 1) / pl.nw);
   } else {
     pl.nw = 1;
@@ -808,12 +810,10 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
 
 template <int D, int RB, bool POOL>
 void launch_mfma(int nw, unsigned grid, hipStream_t stream, const AttendParams& p) {
-  switch (nw) {
-    case 8: hipLaunchKernelGGL((attend_mfma_kernel<D, 8, RB, POOL>), dim3(grid), dim3(512), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RB, POOL>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2, RB, POOL>), dim3(grid), dim3(128), 0, stream, p); break;
-    default: hipLaunchKernelGGL((attend_mfma_kernel<D, 1, RB, POOL>), dim3(grid), dim3(64), 0, stream, p); break;
-  }
+  if (nw == 4)
+    hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RB, POOL>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attend_mfma_kernel<D, 8, RB, POOL>), dim3(grid), dim3(512), 0, stream, p);
 }
 
 template <int D, int RB>

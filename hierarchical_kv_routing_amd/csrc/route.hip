@@ -96,19 +96,19 @@ __device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit
   }
 }
 
-// The wave's 4 row blocks of 16 rotated query rows as split-bf16 A operands
+// The wave's NB row blocks of 16 rotated query rows as split-bf16 A operands
 // (16x16x32 layout: lane -> row lane%16, d slots ks*32 + 8*(lane/16) + i).
 // Rows past the unit's last row repeat the last row, which leaves every max
 // unchanged.  Row r of a unit is (query r / G, head r % G).
-template <bool BF16, int KS>
+template <bool BF16, int KS, int NB>
 __device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, int rbase,
-                                          const float2* cs, Pack8 (&ahi)[4][KS],
-                                          Pack8 (&alo)[4][KS]) {
+                                          const float2* cs, Pack8 (&ahi)[NB][KS],
+                                          Pack8 (&alo)[NB][KS]) {
   const int lane = threadIdx.x & 63;
   const int h = p.d >> 1;
   const int sub = lane >> 4;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
+  for (int blk = 0; blk < NB; ++blk) {
     int r = rbase + blk * 16 + (lane & 15);
     if (r >= w.R) r = w.R - 1;
     const int qi = r / p.G;
@@ -365,9 +365,38 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScr
   return k;
 }
 
+// Max over NB row blocks of q~ . s for the 16 summary rows whose f32 slices
+// (d slots ks*32 + 8*(lane/16) + i of row lane%16) a lane holds in x.
+template <int KS, int NB>
+__device__ __forceinline__ float score16_regs(const float (&x)[KS][8], const Pack8 (&ahi)[NB][KS],
+                                              const Pack8 (&alo)[NB][KS]) {
+  Pack8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(x[ks][i], bhi[ks].h[i], blo[ks].h[i]);
+  float best = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mfma16x16x32(ahi[blk][ks].v, bhi[ks].v, acc);
+      acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
+      acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
+    }
+    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+  }
+  best = fmaxf(best, __shfl_xor(best, 16));
+  best = fmaxf(best, __shfl_xor(best, 32));
+  return best;
+}
+
 // Segmented chunk scoring: raw max-scores of one segment of a unit's middle
-// chunks into the workspace.
-template <bool BF16, int KS>
+// chunks into the workspace.  NB row blocks of 16 rows cover the unit's rows;
+// each wave streams every fourth tile of 16 chunks, loading the next tile's
+// summary rows while the current one is multiplied.
+template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
   const int64_t u = blockIdx.x / p.nseg;
@@ -379,17 +408,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   if (m0 >= m1 || p.Kc <= 0 || w.R <= 0) return;  // uniform
   fill_rope_table(p, w, cs);
   __syncthreads();
-  Pack8 ahi[4][KS], alo[4][KS];
-  load_rows<BF16, KS>(p, w, 0, cs, ahi, alo);
+  Pack8 ahi[NB][KS], alo[NB][KS];
+  load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
+  constexpr int kWaves = kScoreThreads / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+  const float* base = p.csum + ((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap) * p.d;
   const int ntile = static_cast<int>((m1 - m0 + 15) / 16);
-  for (int tile = wave; tile < ntile; tile += kScoreThreads / 64) {
+  auto fetch = [&](int tile, float (&x)[KS][8]) {
     int64_t m = m0 + tile * 16 + (lane & 15);
-    const bool valid = m < m1;
-    if (!valid) m = m1 - 1;
-    const float v = score16<KS>(p.csum + (cbase + m) * p.d, p.d, ahi, alo);
-    if (lane < 16 && valid) p.ws[w.slot * p.ws_stride + (m - w.mid_lo)] = v;
+    if (m >= m1) m = m1 - 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8<false>(base + m * p.d, ks * 32 + (lane >> 4) * 8, x[ks]);
+  };
+  auto emit = [&](int tile, float v) {
+    const int64_t m = m0 + tile * 16 + (lane & 15);
+    if (lane < 16 && m < m1) p.ws[w.slot * p.ws_stride + (m - w.mid_lo)] = v;
+  };
+  float xa[KS][8], xb[KS][8];
+  int tile = wave;
+  if (tile < ntile) fetch(tile, xa);
+  while (tile < ntile) {
+    if (tile + kWaves < ntile) fetch(tile + kWaves, xb);
+    emit(tile, score16_regs<KS, NB>(xa, ahi, alo));
+    tile += kWaves;
+    if (tile >= ntile) break;
+    if (tile + kWaves < ntile) fetch(tile + kWaves, xa);
+    emit(tile, score16_regs<KS, NB>(xb, ahi, alo));
+    tile += kWaves;
   }
 }
 
@@ -419,7 +464,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   if (route) {
     fill_rope_table(p, w, cs);
     __syncthreads();
-    if (has_rows) load_rows<BF16, KS>(p, w, rg * kRowsPerWave, cs, ahi, alo);
+    if (has_rows) load_rows<BF16, KS, 4>(p, w, rg * kRowsPerWave, cs, ahi, alo);
   }
 
   int nselc = 0;
@@ -526,8 +571,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
 template <bool BF16, int KS>
 hipError_t launch_route_t(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
   if (segmented) {
-    hipLaunchKernelGGL((score_kernel<BF16, KS>), dim3(static_cast<unsigned>(units * p.nseg)),
-                       dim3(kScoreThreads), 0, stream, p);
+    const dim3 grid(static_cast<unsigned>(units * p.nseg));
+    const int rows = p.C * p.G < p.n_q * p.G ? p.C * p.G : static_cast<int>(p.n_q * p.G);
+    if (rows <= 16)
+      hipLaunchKernelGGL((score_kernel<BF16, KS, 1>), grid, dim3(kScoreThreads), 0, stream, p);
+    else if (rows <= 32)
+      hipLaunchKernelGGL((score_kernel<BF16, KS, 2>), grid, dim3(kScoreThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((score_kernel<BF16, KS, 4>), grid, dim3(kScoreThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_kernel<BF16, KS, true>), dim3(static_cast<unsigned>(units)),
@@ -603,10 +654,17 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   p.gmax = g.gmax;
   p.rope = g.rope;
   const bool seg = use_segmented(g);
-  p.seg_chunks = kSegChunks;
-  p.nseg = static_cast<int>((max_middle(g) + kSegChunks - 1) / kSegChunks);
-  if (p.nseg < 1) p.nseg = 1;
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  // about 512 scoring workgroups, each a multiple of 64 chunks
+  const int64_t mm = max_middle(g);
+  int64_t nseg = (512 + units - 1) / units;
+  const int64_t most = (mm + kSegChunks - 1) / kSegChunks;
+  if (nseg > most) nseg = most;
+  if (nseg < 1) nseg = 1;
+  p.seg_chunks = static_cast<int>(((mm + nseg - 1) / nseg + kSegChunks - 1) / kSegChunks * kSegChunks);
+  if (p.seg_chunks < kSegChunks) p.seg_chunks = kSegChunks;
+  p.nseg = static_cast<int>((mm + p.seg_chunks - 1) / p.seg_chunks);
+  if (p.nseg < 1) p.nseg = 1;
   if (g.bf16) {
     return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)
                       : launch_route_t<true, 2>(p, units, seg, stream);
