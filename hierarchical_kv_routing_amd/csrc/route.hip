@@ -136,38 +136,6 @@ __device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, i
   }
 }
 
-// Max over the wave's rows of q~ . s for 16 summary rows (one per lane%16).
-template <int KS>
-__device__ __forceinline__ float score16(const float* srow, int d, const Pack8 (&ahi)[4][KS],
-                                         const Pack8 (&alo)[4][KS]) {
-  const int lane = threadIdx.x & 63;
-  const int sub = lane >> 4;
-  Pack8 bhi[KS], blo[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    float x[8];
-    load8<false>(srow, ks * 32 + sub * 8, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) split_bf16(x[i], bhi[ks].h[i], blo[ks].h[i]);
-  }
-  (void)d;
-  float best = -INFINITY;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc = mfma16x16x32(ahi[blk][ks].v, bhi[ks].v, acc);
-      acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
-      acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
-    }
-    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-  }
-  best = fmaxf(best, __shfl_xor(best, 16));
-  best = fmaxf(best, __shfl_xor(best, 32));
-  return best;
-}
-
 // Summary rows staged in LDS, split into bf16 hi and lo halves, so that the
 // waves of a block that score the same rows for different query rows share
 // one load and one split.  Rows are padded by 16 bytes, which puts the 16
@@ -193,10 +161,10 @@ __device__ __forceinline__ void stage_rows(int n, int d, RowPtr row, char* shi, 
 }
 
 // score16 for the 16 staged rows of tile `tile`.
-template <int KS>
+template <int KS, int NB>
 __device__ __forceinline__ float score16_staged(const char* shi, const char* slo, int tile,
-                                                const Pack8 (&ahi)[4][KS],
-                                                const Pack8 (&alo)[4][KS]) {
+                                                const Pack8 (&ahi)[NB][KS],
+                                                const Pack8 (&alo)[NB][KS]) {
   const int lane = threadIdx.x & 63;
   const int off = (tile * 16 + (lane & 15)) * kStageStride + (lane >> 4) * 16;
   Pack8 bhi[KS], blo[KS];
@@ -207,7 +175,7 @@ __device__ __forceinline__ float score16_staged(const char* shi, const char* slo
   }
   float best = -INFINITY;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
+  for (int blk = 0; blk < NB; ++blk) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -224,10 +192,10 @@ __device__ __forceinline__ float score16_staged(const char* shi, const char* slo
 
 // Max-scores of n candidates (row(i) -> summary row) into keys[0..n), one
 // staged block of rows at a time; used when several row groups share tiles.
-template <int KS, typename RowPtr>
+template <int KS, int NB, typename RowPtr>
 __device__ __forceinline__ void score_staged(int n, int d, RowPtr row, bool has_rows, int tg,
-                                             int TG, const Pack8 (&ahi)[4][KS],
-                                             const Pack8 (&alo)[4][KS], char* shi, char* slo,
+                                             int TG, const Pack8 (&ahi)[NB][KS],
+                                             const Pack8 (&alo)[NB][KS], char* shi, char* slo,
                                              uint32_t* keys) {
   const int lane = threadIdx.x & 63;
   for (int b0 = 0; b0 < n; b0 += kStageRows) {
@@ -236,7 +204,7 @@ __device__ __forceinline__ void score_staged(int n, int d, RowPtr row, bool has_
     __syncthreads();
     if (has_rows) {
       for (int tile = tg; tile * 16 < nb; tile += TG) {
-        const float v = score16_staged<KS>(shi, slo, tile, ahi, alo);
+        const float v = score16_staged<KS, NB>(shi, slo, tile, ahi, alo);
         const int c = b0 + tile * 16 + (lane & 15);
         if (lane < 16 && c < n) atomicMax(&keys[c], order_key(v));
       }
@@ -392,6 +360,37 @@ __device__ __forceinline__ float score16_regs(const float (&x)[KS][8], const Pac
   return best;
 }
 
+// Max-scores of tiles tile0, tile0 + step, ... (16 candidates each) of n
+// candidates given by row(i), streamed by one wave with the next tile's
+// summary rows loaded while the current one is multiplied; emit(tile, v)
+// receives each tile's scores (lane%16 = candidate within the tile).
+template <int KS, int NB, typename RowPtr, typename Emit>
+__device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr row,
+                                             const Pack8 (&ahi)[NB][KS],
+                                             const Pack8 (&alo)[NB][KS], Emit emit) {
+  const int lane = threadIdx.x & 63;
+  const int ntile = (n + 15) / 16;
+  auto fetch = [&](int tile, float (&x)[KS][8]) {
+    int c = tile * 16 + (lane & 15);
+    if (c >= n) c = n - 1;
+    const float* src = row(c);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8<false>(src, ks * 32 + (lane >> 4) * 8, x[ks]);
+  };
+  float xa[KS][8], xb[KS][8];
+  int tile = tile0;
+  if (tile < ntile) fetch(tile, xa);
+  while (tile < ntile) {
+    if (tile + step < ntile) fetch(tile + step, xb);
+    emit(tile, score16_regs<KS, NB>(xa, ahi, alo));
+    tile += step;
+    if (tile >= ntile) break;
+    if (tile + step < ntile) fetch(tile + step, xa);
+    emit(tile, score16_regs<KS, NB>(xb, ahi, alo));
+    tile += step;
+  }
+}
+
 // Segmented chunk scoring: raw max-scores of one segment of a unit's middle
 // chunks into the workspace.  NB row blocks of 16 rows cover the unit's rows;
 // each wave streams every fourth tile of 16 chunks, loading the next tile's
@@ -410,35 +409,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   __syncthreads();
   Pack8 ahi[NB][KS], alo[NB][KS];
   load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
-  constexpr int kWaves = kScoreThreads / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* base = p.csum + ((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap) * p.d;
-  const int ntile = static_cast<int>((m1 - m0 + 15) / 16);
-  auto fetch = [&](int tile, float (&x)[KS][8]) {
-    int64_t m = m0 + tile * 16 + (lane & 15);
-    if (m >= m1) m = m1 - 1;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load8<false>(base + m * p.d, ks * 32 + (lane >> 4) * 8, x[ks]);
-  };
-  auto emit = [&](int tile, float v) {
-    const int64_t m = m0 + tile * 16 + (lane & 15);
-    if (lane < 16 && m < m1) p.ws[w.slot * p.ws_stride + (m - w.mid_lo)] = v;
-  };
-  float xa[KS][8], xb[KS][8];
-  int tile = wave;
-  if (tile < ntile) fetch(tile, xa);
-  while (tile < ntile) {
-    if (tile + kWaves < ntile) fetch(tile + kWaves, xb);
-    emit(tile, score16_regs<KS, NB>(xa, ahi, alo));
-    tile += kWaves;
-    if (tile >= ntile) break;
-    if (tile + kWaves < ntile) fetch(tile + kWaves, xa);
-    emit(tile, score16_regs<KS, NB>(xb, ahi, alo));
-    tile += kWaves;
-  }
+  const float* base = p.csum + ((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap + m0) * p.d;
+  const int n = static_cast<int>(m1 - m0);
+  score_stream<KS, NB>(n, wave, kScoreThreads / 64,
+                       [&](int c) { return base + static_cast<int64_t>(c) * p.d; }, ahi, alo,
+                       [&](int tile, float v) {
+                         const int c = tile * 16 + (lane & 15);
+                         if (lane < 16 && c < n) p.ws[w.slot * p.ws_stride + (m0 - w.mid_lo) + c] = v;
+                       });
 }
 
-template <bool BF16, int KS, bool FROM_WS>
+template <bool BF16, int KS, bool FROM_WS, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
   __shared__ uint32_t keys[kMaxCand];
@@ -453,18 +435,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   const int n_mid = static_cast<int>(w.mid_hi - w.mid_lo);
   const bool route = p.Kc > 0 && n_mid > 0 && w.R > 0;
 
-  // Work split inside the block: RG row groups x TG tile groups.
-  const int RG = (w.R + kRowsPerWave - 1) / kRowsPerWave;
+  // Work split inside the block: RG row groups (16*NB rows per wave) x TG
+  // tile groups.
+  constexpr int kRows = 16 * NB;
+  const int RG = (w.R + kRows - 1) / kRows;
   const int TG = RG > 0 ? kRouteWaves / RG : 1;
   const int rg = RG > 0 ? wave % RG : 0;
   const int tg = RG > 0 ? wave / RG : kRouteWaves;
   const bool has_rows = route && tg < TG;
 
-  Pack8 ahi[4][KS], alo[4][KS];
+  Pack8 ahi[NB][KS], alo[NB][KS];
   if (route) {
     fill_rope_table(p, w, cs);
     __syncthreads();
-    if (has_rows) load_rows<BF16, KS, 4>(p, w, rg * kRowsPerWave, cs, ahi, alo);
+    if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
   }
 
   int nselc = 0;
@@ -478,17 +462,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
       const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
       if (RG > 1) {
         const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
-        score_staged<KS>(n_mid, p.d, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
-                         has_rows, tg, TG, ahi, alo, shi, slo, keys);
+        score_staged<KS, NB>(n_mid, p.d, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
+                             has_rows, tg, TG, ahi, alo, shi, slo, keys);
       } else if (has_rows) {
-        const int ntile = (n_mid + 15) / 16;
-        for (int tile = tg; tile < ntile; tile += TG) {
-          int c = tile * 16 + (lane & 15);
-          const bool valid = c < n_mid;
-          if (!valid) c = n_mid - 1;
-          const float v = score16<KS>(p.csum + (cbase + w.mid_lo + c) * p.d, p.d, ahi, alo);
-          if (lane < 16 && valid) atomicMax(&keys[c], order_key(v));
-        }
+        const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
+        score_stream<KS, NB>(n_mid, tg, TG, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
+                             ahi, alo, [&](int tile, float v) {
+                               const int c = tile * 16 + (lane & 15);
+                               if (lane < 16 && c < n_mid) keys[c] = order_key(v);
+                             });
       }
     }
     __syncthreads();
@@ -503,23 +485,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     for (int i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = 0u;
     __syncthreads();
     const int64_t gbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.ngroup_cap;
+    const float* g0 = p.gsum + gbase * p.d;
+    auto grow = [&](int c) {
+      const int cr = c / p.r;
+      return g0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * p.d;
+    };
     if (RG > 1) {
-      const float* g0 = p.gsum + gbase * p.d;
-      score_staged<KS>(nc, p.d, [&](int c) {
-        const int cr = c / p.r;
-        return g0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * p.d;
-      }, has_rows, tg, TG, ahi, alo, shi, slo, keys);
+      score_staged<KS, NB>(nc, p.d, grow, has_rows, tg, TG, ahi, alo, shi, slo, keys);
     } else if (has_rows) {
-      const int ntile = (nc + 15) / 16;
-      for (int tile = tg; tile < ntile; tile += TG) {
-        int c = tile * 16 + (lane & 15);
-        const bool valid = c < nc;
-        if (!valid) c = nc - 1;
-        const int cr = c / p.r;
-        const int64_t gid = static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r);
-        const float v = score16<KS>(p.gsum + (gbase + gid) * p.d, p.d, ahi, alo);
-        if (lane < 16 && valid) atomicMax(&keys[c], order_key(v));
-      }
+      score_stream<KS, NB>(nc, tg, TG, grow, ahi, alo, [&](int tile, float v) {
+        const int c = tile * 16 + (lane & 15);
+        if (lane < 16 && c < nc) keys[c] = order_key(v);
+      });
     }
     __syncthreads();
     nselg = block_select(keys, nc, p.Kg, selg, scr);
@@ -568,26 +545,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   if (tid == 0) p.gcnt[w.slot] = total;
 }
 
-template <bool BF16, int KS>
-hipError_t launch_route_t(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
+template <bool BF16, int KS, int NB>
+hipError_t launch_route_nb(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
   if (segmented) {
-    const dim3 grid(static_cast<unsigned>(units * p.nseg));
-    const int rows = p.C * p.G < p.n_q * p.G ? p.C * p.G : static_cast<int>(p.n_q * p.G);
-    if (rows <= 16)
-      hipLaunchKernelGGL((score_kernel<BF16, KS, 1>), grid, dim3(kScoreThreads), 0, stream, p);
-    else if (rows <= 32)
-      hipLaunchKernelGGL((score_kernel<BF16, KS, 2>), grid, dim3(kScoreThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((score_kernel<BF16, KS, 4>), grid, dim3(kScoreThreads), 0, stream, p);
+    hipLaunchKernelGGL((score_kernel<BF16, KS, NB>), dim3(static_cast<unsigned>(units * p.nseg)),
+                       dim3(kScoreThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_kernel<BF16, KS, true>), dim3(static_cast<unsigned>(units)),
+    hipLaunchKernelGGL((route_kernel<BF16, KS, true, NB>), dim3(static_cast<unsigned>(units)),
                        dim3(kRouteThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((route_kernel<BF16, KS, false>), dim3(static_cast<unsigned>(units)),
+    hipLaunchKernelGGL((route_kernel<BF16, KS, false, NB>), dim3(static_cast<unsigned>(units)),
                        dim3(kRouteThreads), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+// Row blocks of 16 per wave: enough for the rows of one unit up to 64 (then
+// several waves split the rows).
+template <bool BF16, int KS>
+hipError_t launch_route_t(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
+  const int64_t rows = (p.C < p.n_q ? p.C : p.n_q) * static_cast<int64_t>(p.G);
+  if (rows <= 16) return launch_route_nb<BF16, KS, 1>(p, units, segmented, stream);
+  if (rows <= 32) return launch_route_nb<BF16, KS, 2>(p, units, segmented, stream);
+  return launch_route_nb<BF16, KS, 4>(p, units, segmented, stream);
 }
 
 int64_t max_middle(const Geometry& g) {
@@ -598,9 +579,12 @@ int64_t max_middle(const Geometry& g) {
   return rec - sink;
 }
 
+// Few units with long middle contexts: spread each unit's chunk scoring over
+// several workgroups.  From 64 units on, one workgroup per unit streams its
+// chunks fast enough and saves the second launch.
 bool use_segmented(const Geometry& g) {
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
-  return units < 512 && max_middle(g) > 256 && g.nqc == 1 &&
+  return units < 64 && max_middle(g) > 256 && g.nqc == 1 &&
          g.n_q * static_cast<int64_t>(g.G) <= kRowsPerWave;
 }
 
