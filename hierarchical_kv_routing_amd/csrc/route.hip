@@ -217,7 +217,110 @@ struct SelScratch {
   int hist[256];
   int wsum[16];
   int bcast[4];
+  uint64_t cand[128];
 };
+
+// 64-bit selection key: the score's order key above the inverted index, so
+// that a larger key means a larger score or, at equal scores, a lower index.
+__device__ __forceinline__ uint64_t sel_key(uint32_t k, int i) {
+  return (static_cast<uint64_t>(k) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const unsigned lo = __shfl_xor(static_cast<unsigned>(v), m);
+  const unsigned hi = __shfl_xor(static_cast<unsigned>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Bitonic sort of the wave's 64*M keys (element s*64 + lane in v[s]) into
+// descending order, entirely in registers.
+template <int M>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[M]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * M; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int s = 0; s < M; ++s) {
+        const bool up = ((s * 64 + lane) & size) == 0;  // this pair ends larger-first
+        if (stride >= 64) {
+          const int ps = s ^ (stride >> 6);
+          if (ps > s) {
+            const uint64_t a = v[s], b = v[ps];
+            const bool sw = up ? (a < b) : (a > b);
+            v[s] = sw ? b : a;
+            v[ps] = sw ? a : b;
+          }
+        } else {
+          const uint64_t o = shfl_xor64(v[s], stride);
+          const bool lower = (lane & stride) == 0;
+          const uint64_t mx = v[s] > o ? v[s] : o, mn = v[s] > o ? o : v[s];
+          v[s] = (lower == up) ? mx : mn;
+        }
+      }
+    }
+  }
+}
+
+// One wave: given its sorted keys (top k in lanes 0..k-1 of slot 0, k <= 64),
+// writes their indices to out[] in ascending order.
+__device__ __forceinline__ void wave_emit_ascending(uint64_t top, int k, int* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t idx = ~static_cast<uint32_t>(top);
+  uint64_t v[1] = {lane < k ? static_cast<uint64_t>(~idx) : 0ull};  // larger = lower index
+  wave_sort_desc<1>(v);
+  if (lane < k) out[lane] = static_cast<int>(~static_cast<uint32_t>(v[0]));
+}
+
+// Top-k selection for small inputs without the radix passes: n <= 128 with
+// k <= 64 (one wave sorts everything), or n <= 128 * waves with k <= 16 (each
+// wave sorts 128 keys and keeps its top k, one wave sorts the survivors).
+// Same result as block_select.  Block-wide; every thread must call it.
+__device__ __forceinline__ bool small_select_ok(int n, int k) {
+  return (n <= 128 && k <= 64) || (k <= 16 && n <= 128 * static_cast<int>(blockDim.x >> 6));
+}
+
+__device__ int small_select(const uint32_t* keys, int n, int k, int* out, SelScratch& sc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (n <= 128) {
+    if (wave == 0) {
+      uint64_t v[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i = s * 64 + lane;
+        v[s] = i < n ? sel_key(keys[i], i) : 0ull;
+      }
+      wave_sort_desc<2>(v);
+      wave_emit_ascending(v[0], k, out);
+    }
+    __syncthreads();
+    return k;
+  }
+  {
+    uint64_t v[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int i = wave * 128 + s * 64 + lane;
+      v[s] = i < n ? sel_key(keys[i], i) : 0ull;
+    }
+    wave_sort_desc<2>(v);
+    if (lane < 16) sc.cand[wave * 16 + lane] = lane < k ? v[0] : 0ull;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t v[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int i = s * 64 + lane;
+      v[s] = i < nw * 16 ? sc.cand[i] : 0ull;
+    }
+    wave_sort_desc<2>(v);
+    wave_emit_ascending(v[0], k, out);
+  }
+  __syncthreads();
+  return k;
+}
 
 __device__ __forceinline__ int block_excl_scan(int v, SelScratch& s, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -251,6 +354,7 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScr
     __syncthreads();
     return n;
   }
+  if (small_select_ok(n, k)) return small_select(keys, n, k, out, s);
   uint32_t prefix = 0, pmask = 0;
   int need = k;
   for (int pass = 0; pass < 4; ++pass) {
@@ -361,13 +465,14 @@ __device__ __forceinline__ float score16_regs(const float (&x)[KS][8], const Pac
 }
 
 // Max-scores of tiles tile0, tile0 + step, ... (16 candidates each) of n
-// candidates given by row(i), streamed by one wave with the next tile's
-// summary rows loaded while the current one is multiplied; emit(tile, v)
+// candidates given by row(i), streamed by one wave with DEPTH-1 tiles of
+// summary rows in flight ahead of the one being multiplied; emit(tile, v)
 // receives each tile's scores (lane%16 = candidate within the tile).
 template <int KS, int NB, typename RowPtr, typename Emit>
 __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr row,
                                              const Pack8 (&ahi)[NB][KS],
                                              const Pack8 (&alo)[NB][KS], Emit emit) {
+  constexpr int DEPTH = NB <= 2 ? 3 : 2;
   const int lane = threadIdx.x & 63;
   const int ntile = (n + 15) / 16;
   auto fetch = [&](int tile, float (&x)[KS][8]) {
@@ -377,17 +482,19 @@ __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load8<false>(src, ks * 32 + (lane >> 4) * 8, x[ks]);
   };
-  float xa[KS][8], xb[KS][8];
-  int tile = tile0;
-  if (tile < ntile) fetch(tile, xa);
-  while (tile < ntile) {
-    if (tile + step < ntile) fetch(tile + step, xb);
-    emit(tile, score16_regs<KS, NB>(xa, ahi, alo));
-    tile += step;
-    if (tile >= ntile) break;
-    if (tile + step < ntile) fetch(tile + step, xa);
-    emit(tile, score16_regs<KS, NB>(xb, ahi, alo));
-    tile += step;
+  float x[DEPTH][KS][8];
+#pragma unroll
+  for (int j = 0; j < DEPTH - 1; ++j)
+    if (tile0 + j * step < ntile) fetch(tile0 + j * step, x[j]);
+  for (int base = 0;; base += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      const int tile = tile0 + (base + j) * step;
+      if (tile >= ntile) return;
+      const int ahead = tile + (DEPTH - 1) * step;
+      if (ahead < ntile) fetch(ahead, x[(j + DEPTH - 1) % DEPTH]);
+      emit(tile, score16_regs<KS, NB>(x[j], ahi, alo));
+    }
   }
 }
 
