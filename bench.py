@@ -36,6 +36,29 @@ import workloads as W  # noqa: E402
 METRIC = "routed-attn prefill Mtok/s + decode us/step at 64K ctx; % of HBM/MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTEND_PROFILE = os.path.join(ROOT, "profiles", "attend_mfma_qwen3_prefill_n32768.md")
+ATTEND_SOURCES = ["attend.hip", "hga_device.h"]
+
+
+def recorded_traffic():
+    """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated), or None when the summary was taken
+    on another version of the kernel source than the one built here."""
+    import hashlib
+    import re
+    try:
+        text = open(ATTEND_PROFILE).read()
+    except OSError:
+        return None
+    t = re.search(r"attend traffic per launch: (\d+) bytes", text)
+    h = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    if t is None or h is None:
+        return None
+    cur = hashlib.sha256()
+    for f in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, "hierarchical_kv_routing_amd", "csrc", f), "rb") as fh:
+            cur.update(fh.read())
+    return int(t.group(1)) if cur.hexdigest() == h.group(1) else None
 
 
 def log(*a):
@@ -368,7 +391,8 @@ def main():
                     rope_theta=w.rope_theta),
         roofline=dict(bound="mfma", kernel="attend_mfma_kernel", achieved=pre["attend_tflops"],
                       peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=pre["attend_tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                      frac=pre["attend_tflops"] / PEAK_BF16_TFLOPS, traffic=recorded_traffic(),
+                      traffic_unit="bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                       flops_per_launch=pre["attend_flops"], visible_pairs=pre["pairs"],
                       avg_launch_ms=pre["stage_ms"]["attend"]),
         stage_ms=pre["stage_ms"],
