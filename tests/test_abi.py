@@ -99,11 +99,14 @@ def test_bad_arguments_rejected(lib):
 
 def test_workspace_checks(lib):
     cfg = H.Config.from_workload(W.DECODE_64K)
-    need = H.route_workspace_bytes(cfg, 16, 65536, 1)
-    # segmented decode routing: one f32 score per middle chunk per unit
-    assert need == 16 * 4 * 1014 * 4
-    assert _route(lib, cfg, B=16, q_pos0=65536, n_q=1, cap=65600, ws=16, wsb=need - 4) == 3
-    assert _route(lib, cfg, B=16, q_pos0=65536, n_q=1, cap=65600, ws=None, wsb=0) == 3
+    # 4 sequences x 4 KV heads = 16 units: segmented decode routing, one f32
+    # score per middle chunk per unit
+    need = H.route_workspace_bytes(cfg, 4, 65536, 1)
+    assert need == 4 * 4 * 1014 * 4
+    assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=16, wsb=need - 4) == 3
+    assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=None, wsb=0) == 3
+    # from 64 units on, one routing workgroup per unit: no workspace
+    assert H.route_workspace_bytes(cfg, 16, 65536, 1) == 0
     assert H.attend_workspace_bytes(cfg, 16, 65536, 1) > 0
     big = H.Config.from_workload(W.QWEN3_PREFILL)
     assert H.route_workspace_bytes(big, 1, 0, 32768) == 0
