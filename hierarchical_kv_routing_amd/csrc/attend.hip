@@ -53,7 +53,7 @@ constexpr int kTKf = 32;               // keys per LDS tile (f32 path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
-constexpr float kRescale = 8.0f;       // move the reference when scores exceed it by 2^8
+constexpr float kRescaleSum = 4096.0f; // move the reference when a lane's half sum exceeds 2^12
 
 struct AttendParams {
   const void* q;
@@ -76,6 +76,7 @@ struct AttendParams {
   int64_t q_stride, q_row0;
   int B, Hq, Hkv, G, d, C, gs, lg_gs, gmax, Rcap;
   int slices, splits, keys_per_split, per_unit;
+  int64_t nblocks;  // work items (bx) of the launch; a workgroup takes bx = blockIdx.x + k*gridDim.x
   int dense;
   float scale_log2;
   RopeFreqs rope;
@@ -135,8 +136,7 @@ __device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
 // (consecutive blocks go to consecutive XCDs), and every item (row slice x
 // key split) of a unit lands on the same XCD, whose L2 then serves the
 // unit's K/V to all of them.
-__device__ __forceinline__ bool block_item(const AttendParams& p, int64_t& u, int& item) {
-  const int64_t bx = blockIdx.x;
+__device__ __forceinline__ bool block_item(const AttendParams& p, int64_t bx, int64_t& u, int& item) {
   const int64_t per = 8 * static_cast<int64_t>(p.per_unit);
   const int64_t grp = bx / per;
   const int rem = static_cast<int>(bx - grp * per);
@@ -199,33 +199,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 constexpr uint32_t kNoRow = 0x80000000u;  // beyond every K/V buffer (their sizes stay below 2^31)
 
-// (row, token) of key slot s: row counts D-element rows from the start of the
-// K (and V) buffer resource, token is the sequence position; both -1 when s
-// is at or past kend or its granule is invalid.  gtab holds the granules of
-// the work item from granule gfirst on (unused in dense mode).
-__device__ __forceinline__ int2 key_at(const AttendParams& p, const int2* gtab, int gfirst, int s,
-                                       int kend) {
-  if (s >= kend) return make_int2(-1, -1);
-  if (p.dense) return make_int2(s, s);
-  const int2 e = gtab[(s >> p.lg_gs) - gfirst];
-  const int lo = s & ((1 << p.lg_gs) - 1);
-  return e.x < 0 ? e : make_int2(e.x + lo, e.y + lo);
-}
-
-// Keys of the pair (s0, s0 + 1), s0 even.
-__device__ __forceinline__ void pair_keys(const AttendParams& p, const int2* gtab, int gfirst, int s0,
-                                          int kend, int2& a, int2& b) {
-  a = key_at(p, gtab, gfirst, s0, kend);
-  if (p.lg_gs > 0)  // both keys of the pair sit in one granule
-    b = (a.x >= 0 && s0 + 1 < kend) ? make_int2(a.x + 1, a.y + 1) : make_int2(-1, -1);
-  else
-    b = key_at(p, gtab, gfirst, s0 + 1, kend);
-}
-
-// 16 bytes (d slice sl) of row `row` of a K or V buffer; zero when row < 0.
-template <int D>
-__device__ __forceinline__ uint4 load_row16(__amdgpu_buffer_rsrc_t r, int row, int sl) {
-  const uint32_t off = row >= 0 ? static_cast<uint32_t>(row) * (D * 2) + sl * 16 : kNoRow;
+// 16 bytes at byte offset off of a K or V buffer resource (zero when off is
+// kNoRow).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
@@ -233,38 +209,55 @@ __device__ __forceinline__ uint4 load_row16(__amdgpu_buffer_rsrc_t r, int row, i
 // Item i of a stage covers one key pair and one 16-byte d slice.  K items
 // run slice-fastest (a half wave reads whole 256-byte rows); V items run
 // key-pair-fastest so that the transposed LDS stores of a wave land in 64
-// distinct banks.  Absent keys load zeros.
+// distinct banks.  gtab holds the work item's granules from granule gfirst on
+// (entry: row of the granule's first key in the K/V resource, its first
+// token; -1 when invalid).  A key past kend or in an invalid granule gets
+// offset kNoRow (zeros) and token -1.  No branches: the stage's first key kb
+// is a multiple of g_s, so a key's table entry is the stage's first entry
+// plus a per-thread constant.
 template <int D, int NW>
 __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffer_rsrc_t kr,
                                            __amdgpu_buffer_rsrc_t vr, const int2* gtab, int gfirst,
                                            int kb, int kend, int cur0, StageRegs<D, NW>& r) {
   constexpr int SL = StageRegs<D, NW>::SL;
+  const int lg = p.lg_gs, gm = (1 << lg) - 1;
+  const int gbase = (kb >> lg) - gfirst;
+  const int rem = kend - kb;  // keys of the stage before kend
+  auto key = [&](int s, int sl, uint32_t& off, int& tok) {
+    int gi = gbase + (s >> lg);
+    gi = gi < kTab - 1 ? gi : kTab - 1;  // keys past kend may point past the table
+    const int2 e = gtab[gi];
+    const bool ok = (s < rem) & (e.x >= 0);
+    off = ok ? static_cast<uint32_t>(e.x + (s & gm)) * (D * 2) + sl * 16 : kNoRow;
+    tok = ok ? e.y + (s & gm) : -1;
+  };
 #pragma unroll
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
     if (idx < StageRegs<D, NW>::kItems) {
+      uint32_t o0, o1;
       {
         const int kp = idx / SL, sl = idx - kp * SL;
-        int2 a, b;
-        pair_keys(p, gtab, gfirst, kb + 2 * kp, kend, a, b);
-        r.k0[i] = load_row16<D>(kr, a.x, sl);
-        r.k1[i] = load_row16<D>(kr, b.x, sl);
-        r.t0[i] = a.y;
-        r.t1[i] = b.y;
+        key(2 * kp, sl, o0, r.t0[i]);
+        key(2 * kp + 1, sl, o1, r.t1[i]);
+        r.k0[i] = load16(kr, o0);
+        r.k1[i] = load16(kr, o1);
       }
       {
         const int kp = idx & 31, sl = idx >> 5;
-        int2 a, b;
-        pair_keys(p, gtab, gfirst, kb + 2 * kp, kend, a, b);
-        r.v0[i] = load_row16<D>(vr, a.x, sl);
-        r.v1[i] = load_row16<D>(vr, b.x, sl);
+        int u0, u1;
+        key(2 * kp, sl, o0, u0);
+        key(2 * kp + 1, sl, o1, u1);
+        r.v0[i] = load16(vr, o0);
+        r.v1[i] = load16(vr, o1);
       }
     }
   }
   // Tokens ascend along a list, so the stage needs masks iff it runs past the
   // end of the key range or its last key is absent or in the current chunk.
-  const int stop = kb + kTK < kend ? kb + kTK : kend;
-  const int tl = key_at(p, gtab, gfirst, stop - 1, kend).y;
+  const int last = (rem < kTK ? rem : kTK) - 1;
+  const int2 e = gtab[gbase + (last >> lg)];
+  const int tl = e.x >= 0 ? e.y + (last & gm) : -1;
   // the same value on every lane: make it a scalar so branches on it are uniform
   r.masked = __builtin_amdgcn_readfirstlane(static_cast<int>((kb + kTK > kend) || tl < 0 || tl >= cur0)) != 0;
 }
@@ -306,35 +299,48 @@ constexpr int stage_bytes() {
   return kTK * (D * 2 + 16) + D * kVP + kTK * 4;
 }
 
+// 2^x of the 16 scores of a half (x already relative to the reference):
+// P as bf16 MFMA operands (pb[0]: keys 0..15, pb[1]: keys 16..31) and the
+// lane's partial row sum.
+__device__ __forceinline__ float exp_pack(const f32x16& s, Pack8 (&pb)[2]) {
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(s[j]);
+    const float e1 = __builtin_amdgcn_exp2f(s[j + 1]);
+    ps += e0 + e1;
+    const f32x2 f = {e0, e1};
+    pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+  return ps;
+}
+
 // Softmax of one 32-key half for one row: s[j] holds the score of key
 // 16*(j/8) + 8*hsub + (j%8) of the half (tokens tl[] when masked).  Scores
-// become 2^(s - ref); the reference moves (and o, lsum are rescaled) only
-// when the half's maximum exceeds it by more than kRescale.  Writes P as
-// bf16 MFMA operands (pb[0]: keys 0..15, pb[1]: keys 16..31).
+// become 2^(s - ref).  The reference moves (and o, lsum are rescaled) only
+// when a lane's sum of the half's terms exceeds 2^12 (every term is then
+// bounded by 2^12), a wave-uniform branch taken rarely; the common case
+// costs one compare per half instead of a running maximum.
 template <int DB>
 __device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* tl, int hsub,
                                              int cur0, int qpos, float& ref, float& lsum,
                                              bool& started, f32x16 (&o)[DB], Pack8 (&pb)[2]) {
-  float mx = -INFINITY;
   if (masked) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int tok = tl[16 * (j >> 3) + 8 * hsub + (j & 7)];
       const bool ok = (tok >= 0) & ((tok < cur0) | (tok <= qpos));
-      const float x = ok ? s[j] - ref : -INFINITY;
-      s[j] = x;
-      mx = fmaxf(mx, x);
+      s[j] = ok ? s[j] - ref : -INFINITY;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float x = s[j] - ref;
-      s[j] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int j = 0; j < 16; ++j) s[j] -= ref;
   }
-  const bool chk = !started || mx > kRescale;
-  if (__builtin_amdgcn_ballot_w64(chk) != 0) {  // wave-uniform, rare
+  float ps = exp_pack(s, pb);
+  if (__builtin_amdgcn_ballot_w64(!started || ps > kRescaleSum) != 0) {  // wave-uniform, rare
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[j]);
     const float mrow = fmaxf(mx, __shfl_xor(mx, 32));
     float delta = 0.f;
     if (!started) {
@@ -342,7 +348,7 @@ __device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* 
         delta = mrow;
         started = true;
       }
-    } else if (mrow > kRescale) {
+    } else if (mrow > 0.f) {
       delta = mrow;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       lsum *= alpha;
@@ -355,36 +361,31 @@ __device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* 
       ref += delta;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[j] -= delta;
+      ps = exp_pack(s, pb);
     }
-  }
-  float ps = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const float e0 = __builtin_amdgcn_exp2f(s[j]);
-    const float e1 = __builtin_amdgcn_exp2f(s[j + 1]);
-    ps += e0 + e1;
-    const f32x2 f = {e0, e1};
-    pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   }
   lsum += ps;
 }
 
+template <int D>
+constexpr int attend_main_bytes() {
+  return (2 * stage_bytes<D>()) > (64 * (D / 2) * 8) ? (2 * stage_bytes<D>()) : (64 * (D / 2) * 8);
+}
+
+// One work item bx: a row slice and key split of one unit.
 template <int D, int NW, int RB, bool POOL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_mfma_kernel(AttendParams p) {
+__device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, char* smem) {
   constexpr int KS = D / 16;    // k-steps of S^T over d
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int KP = D * 2 + 16;
   constexpr int SB = stage_bytes<D>();
   constexpr int H = D / 2;
-  constexpr int kTable = 64 * H * 8;
-  constexpr int kMain = (2 * SB) > kTable ? (2 * SB) : kTable;
-  constexpr int kSmem = kMain + kTab * 8;
+  constexpr int kMain = attend_main_bytes<D>();
   constexpr int kRows = NW * 32 * RB;
-  __shared__ __align__(16) char smem[kSmem];
 
   int64_t u;
   int item;
-  if (!block_item(p, u, item)) return;  // uniform
+  if (!block_item(p, bx, u, item)) return;  // uniform
   const int slice = item / p.splits;
   const int split = item - slice * p.splits;
   const AUnit w = uniform_unit(make_aunit(p, u));
@@ -395,16 +396,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (kend > w.nkeys) kend = w.nkeys;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
+  // Query rows: lane -> row n = lane % 32 of each row block, d slots
+  // ks*16 + 8*(lane/32) + i.  Their loads are issued first, so that they are
+  // in flight while the granule and RoPE tables are built.
+  const int n = lane & 31, hsub = lane >> 5;
+  const int cur0 = static_cast<int>(w.t * p.C);
+  const int q_first = r0 / p.G;
+  Pack8 qraw[RB][KS];
+  int qpos[RB], hl[RB], row[RB];
+  bool rb_on[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    row[rb] = r0 + (wave * RB + rb) * 32 + n;
+    rb_on[rb] = (r0 + (wave * RB + rb) * 32) < w.R;
+    const bool ok = row[rb] < w.R;
+    const int qloc = ok ? row[rb] / p.G : q_first;
+    hl[rb] = ok ? row[rb] - qloc * p.G : 0;
+    qpos[rb] = static_cast<int>(w.qlo) + qloc;
+    const int64_t base =
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl[rb]) * p.q_stride + (qpos[rb] - p.q_row0)) * D;
+    const uint16_t* qsrc = static_cast<const uint16_t*>(p.q) + base + hsub * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[rb][ks].q = ok ? *reinterpret_cast<const uint4*>(qsrc + ks * 16) : make_uint4(0, 0, 0, 0);
+  }
+
   // Granule table of the item's key range (rows and tokens of each granule's
   // first key), read once so that stage loads need no dependent global load.
   int2* gtab = reinterpret_cast<int2*>(smem + kMain);
   const int gfirst = kbeg >> p.lg_gs;
-  if (!p.dense && kend > kbeg) {
+  if (kend > kbeg) {
     const int ng = ((kend - 1) >> p.lg_gs) - gfirst + 1;  // <= kTab (make_plan)
     const int64_t gcap = p.kv_cap >> p.lg_gs;
     for (int i = threadIdx.x; i < ng; i += NW * 64) {
       const int64_t e = w.slot * p.gmax + gfirst + i;
-      const int64_t g = p.gran[e];
+      const int64_t g = p.dense ? gfirst + i : p.gran[e];  // dense: every granule in order
       int2 t = make_int2(-1, -1);
       if (g >= 0 && g < gcap) {
         const int tok = static_cast<int>(g << p.lg_gs);
@@ -421,7 +447,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // RoPE table for the queries of this workgroup's rows.
   const int rend = (r0 + kRows) < w.R ? (r0 + kRows) : w.R;
-  const int q_first = r0 / p.G;
   const int nqt = (rend - 1) / p.G - q_first + 1;
   float2* cs = reinterpret_cast<float2*>(smem);
   for (int i = threadIdx.x; i < nqt * H; i += NW * 64) {
@@ -432,33 +457,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   __syncthreads();
 
-  // Query rows: lane -> row n = lane % 32 of each row block, d slots
-  // ks*16 + 8*(lane/32) + i.
-  const int n = lane & 31, hsub = lane >> 5;
-  const int cur0 = static_cast<int>(w.t * p.C);
+  // K and V buffer resources: the (sequence, KV head) slab, or the staging
+  // pool whose slot holds K then V of one granule.
+  __amdgpu_buffer_rsrc_t kr, vr;
+  if constexpr (POOL) {
+    const int64_t gbytes = static_cast<int64_t>(p.gs) * D * 2;
+    const uint32_t bytes = static_cast<uint32_t>(p.pool_slots * 2 * gbytes);
+    kr = buffer_rsrc(p.k, bytes);
+    vr = buffer_rsrc(static_cast<const char*>(p.v) + gbytes, bytes - static_cast<uint32_t>(gbytes));
+  } else {
+    const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap * D * 2;
+    const uint32_t bytes = static_cast<uint32_t>(p.kv_cap * D * 2);
+    kr = buffer_rsrc(static_cast<const char*>(p.k) + slab, bytes);
+    vr = buffer_rsrc(static_cast<const char*>(p.v) + slab, bytes);
+  }
+  // The first stage's loads go out before the query rows are rotated.
+  const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+  StageRegs<D, NW> sr;
+  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, sr);
+
+  // Rotate, scale by softmax_scale * log2(e) and round the query rows to
+  // bf16 MFMA operands.
   Pack8 qb[RB][KS];
-  int qpos[RB], hl[RB], row[RB];
-  bool rb_on[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    row[rb] = r0 + (wave * RB + rb) * 32 + n;
-    rb_on[rb] = (r0 + (wave * RB + rb) * 32) < w.R;
-    const bool ok = row[rb] < w.R;
-    const int qloc = ok ? row[rb] / p.G : q_first;
-    hl[rb] = ok ? row[rb] - qloc * p.G : 0;
-    qpos[rb] = static_cast<int>(w.qlo) + qloc;
+    const int qloc = qpos[rb] - static_cast<int>(w.qlo);
     float x[KS][8];
-    const int64_t base =
-        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl[rb]) * p.q_stride + (qpos[rb] - p.q_row0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ok) {
-        load8<true>(p.q, base + ks * 16 + hsub * 8, x[ks]);
-      } else {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[ks][i] = 0.f;
-      }
-    }
+      for (int i = 0; i < 8; ++i) x[ks][i] = bf16_to_f32(qraw[rb][ks].h[i]);
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks) {
 #pragma unroll
@@ -480,20 +508,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   __syncthreads();  // the table space becomes the K/V stage buffers
 
-  // K and V buffer resources: the (sequence, KV head) slab, or the staging
-  // pool whose slot holds K then V of one granule.
-  __amdgpu_buffer_rsrc_t kr, vr;
-  if constexpr (POOL) {
-    const int64_t gbytes = static_cast<int64_t>(p.gs) * D * 2;
-    const uint32_t bytes = static_cast<uint32_t>(p.pool_slots * 2 * gbytes);
-    kr = buffer_rsrc(p.k, bytes);
-    vr = buffer_rsrc(static_cast<const char*>(p.v) + gbytes, bytes - static_cast<uint32_t>(gbytes));
-  } else {
-    const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap * D * 2;
-    const uint32_t bytes = static_cast<uint32_t>(p.kv_cap * D * 2);
-    kr = buffer_rsrc(static_cast<const char*>(p.k) + slab, bytes);
-    vr = buffer_rsrc(static_cast<const char*>(p.v) + slab, bytes);
-  }
   f32x16 o[RB][DB];
   float ref[RB], lsum[RB];
   bool started[RB];
@@ -508,10 +522,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int j = 0; j < 16; ++j) o[rb][db][j] = 0.f;
   }
 
-  const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
-  StageRegs<D, NW> sr;
-  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, sr);
-  for (int st = 0; st < nstages; ++st) {
+  auto step = [&](int st) {
     char* kl = smem + (st & 1) * SB;
     char* vl = kl + kTK * KP;
     int* tl = reinterpret_cast<int*>(vl + D * kVP);
@@ -519,7 +530,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bool masked = sr.masked;
     __syncthreads();
     if (st + 1 < nstages) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
-    if (!rb_on[0]) continue;  // wave-uniform: this wave has no rows
+    if (!rb_on[0]) return;  // wave-uniform: this wave has no rows
     // S^T for the two 32-key halves; each K operand serves every row block.
     // s[rb][h][j] holds key 32h + 16*(j/8) + 8*hsub + (j%8).
     f32x16 s[RB][2];
@@ -562,7 +573,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
     }
-  }
+  };
+  for (int st = 0; st < nstages; ++st) step(st);
 
   // O^T register j of block db is d = db*32 + 8*(j/4) + 4*hsub + (j%4).
 #pragma unroll
@@ -610,6 +622,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Persistent launch: one resident workgroup per slot walks the work items
+// bx = blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is a multiple of 8,
+// so every item stays on the XCD that block_item intends for it, and no
+// workgroup dispatch separates one item from the next.
+template <int D, int NW, int RB, bool POOL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_mfma_kernel(AttendParams p) {
+  __shared__ __align__(16) char smem[attend_main_bytes<D>() + kTab * 8];
+  for (int64_t bx = blockIdx.x; bx < p.nblocks; bx += gridDim.x) {
+    attend_item<D, NW, RB, POOL>(p, bx, smem);
+    __syncthreads();  // the next item rewrites the LDS tables
+  }
+}
+
 // f32 inputs: one wave per 64 rows, one lane per row.
 template <int D>
 __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
@@ -621,7 +646,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   const int lane = threadIdx.x;
   int64_t u;
   int item;
-  if (!block_item(p, u, item)) return;
+  if (!block_item(p, blockIdx.x, u, item)) return;
   const int slice = item / p.splits;
   const int split = item - slice * p.splits;
   const AUnit w = make_aunit(p, u);
@@ -799,44 +824,66 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
       pl.splits = static_cast<int>((keys + pl.kps - 1) / pl.kps);
     }
   }
-  // A routed bf16 item reads at most kTab granules (a multiple of kTK keys).
+  // A bf16 item reads at most kTab granules (a multiple of kTK keys).
   const int64_t cap = static_cast<int64_t>(kTab) * g.gs;
-  if (g.bf16 && !dense && allow_split && pl.kps > cap) {
+  if (g.bf16 && allow_split && pl.kps > cap) {
     pl.kps = static_cast<int>(cap);
     pl.splits = static_cast<int>((keys + cap - 1) / cap);
   }
   return pl;
 }
 
+// Workgroups that fit on the device at once for kernel k (a multiple of 8,
+// so that blockIdx.x and every bx it takes sit on the same XCD), at most n.
+template <typename Kernel>
+unsigned resident_grid(Kernel k, int threads, int64_t n) {
+  static int slots[16] = {};  // per device, computed once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (slots[dev] == 0) {
+    int cus = 0, occ = 0;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), threads, 0);
+    int v = (cus > 0 ? cus : 8) * (occ > 0 ? occ : 1);
+    v -= v % 8;
+    slots[dev] = v >= 8 ? v : 8;
+  }
+  return static_cast<unsigned>(n < slots[dev] ? n : slots[dev]);
+}
+
 template <int D, int RB, bool POOL>
-void launch_mfma(int nw, unsigned grid, hipStream_t stream, const AttendParams& p) {
-  if (nw == 4)
-    hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RB, POOL>), dim3(grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attend_mfma_kernel<D, 8, RB, POOL>), dim3(grid), dim3(512), 0, stream, p);
+void launch_mfma(int nw, int64_t nblocks, hipStream_t stream, const AttendParams& p) {
+  if (nw == 4) {
+    auto k = attend_mfma_kernel<D, 4, RB, POOL>;
+    hipLaunchKernelGGL(k, dim3(resident_grid(k, 256, nblocks)), dim3(256), 0, stream, p);
+  } else {
+    auto k = attend_mfma_kernel<D, 8, RB, POOL>;
+    hipLaunchKernelGGL(k, dim3(resident_grid(k, 512, nblocks)), dim3(512), 0, stream, p);
+  }
 }
 
 template <int D, int RB>
-void launch_mfma_pool(int nw, unsigned grid, hipStream_t stream, const AttendParams& p) {
+void launch_mfma_pool(int nw, int64_t nblocks, hipStream_t stream, const AttendParams& p) {
   if (p.pool_slot != nullptr)
-    launch_mfma<D, RB, true>(nw, grid, stream, p);
+    launch_mfma<D, RB, true>(nw, nblocks, stream, p);
   else
-    launch_mfma<D, RB, false>(nw, grid, stream, p);
+    launch_mfma<D, RB, false>(nw, nblocks, stream, p);
 }
 
 template <int D>
 hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, hipStream_t stream) {
   const int64_t groups = (pl.units + 7) / 8;
-  const unsigned grid = static_cast<unsigned>(groups * 8 * p.per_unit);
+  p.nblocks = groups * 8 * p.per_unit;
+  const unsigned grid = static_cast<unsigned>(p.nblocks);
   if (g.bf16) {
     if constexpr (HGA_ATTEND_RB == 2) {
       if (pl.rb == 2) {
-        launch_mfma_pool<D, 2>(pl.nw, grid, stream, p);
+        launch_mfma_pool<D, 2>(pl.nw, p.nblocks, stream, p);
       } else {
-        launch_mfma_pool<D, 1>(pl.nw, grid, stream, p);
+        launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
       }
     } else {
-      launch_mfma_pool<D, 1>(pl.nw, grid, stream, p);
+      launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
     }
   } else {
     hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(64), 0, stream, p);
