@@ -202,10 +202,13 @@ def bench_decode(args):
     pipe = Pipeline(w)
     pipe.build()  # cache + summaries of the 65536 cached tokens and the new token (untimed)
     torch.cuda.synchronize()
+    # a decode step is short: 10x the steps, and warmup long enough (tens of
+    # ms) for the GPU to reach its steady clock
     eager_ms, stage = timed_steps(torch, [("route", pipe.route), ("attend", pipe.attend)],
-                                  max(args.steps * 10, 50), args.warmup)
+                                  max(args.steps * 10, 50), max(args.warmup * 10, 50))
     # the step as a serving loop runs it: route + attend replayed as one HIP graph
-    ms = graph_step_ms(torch, [pipe.route, pipe.attend], max(args.steps * 10, 50), args.warmup)
+    ms = graph_step_ms(torch, [pipe.route, pipe.attend], max(args.steps * 10, 50),
+                       max(args.warmup * 10, 50))
     counts = pipe.ro["granule_count"].cpu().numpy().astype(np.int64)
     B, Hkv, d = w.batch, w.n_kv_heads, w.head_dim
     t = w.q_pos0 // w.chunk_size
@@ -344,8 +347,8 @@ def copy_calibration(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "copy"], default=None)
     args = ap.parse_args()

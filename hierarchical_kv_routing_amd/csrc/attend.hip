@@ -223,39 +223,43 @@ __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffe
   const int lg = p.lg_gs, gm = (1 << lg) - 1;
   const int gbase = (kb >> lg) - gfirst;
   const int rem = kend - kb;  // keys of the stage before kend
-  auto key = [&](int s, int sl, uint32_t& off, int& tok) {
+  // Table entries as single 64-bit LDS reads, all issued before any is used.
+  auto entry = [&](int s) {
     int gi = gbase + (s >> lg);
     gi = gi < kTab - 1 ? gi : kTab - 1;  // keys past kend may point past the table
-    const int2 e = gtab[gi];
-    const bool ok = (s < rem) & (e.x >= 0);
-    off = ok ? static_cast<uint32_t>(e.x + (s & gm)) * (D * 2) + sl * 16 : kNoRow;
-    tok = ok ? e.y + (s & gm) : -1;
+    return *reinterpret_cast<const unsigned long long*>(gtab + gi);
+  };
+  auto key = [&](int s, unsigned long long ev, int sl, uint32_t& off, int& tok) {
+    const int ex = static_cast<int>(static_cast<uint32_t>(ev));
+    const int ey = static_cast<int>(static_cast<uint32_t>(ev >> 32));
+    const bool ok = (s < rem) & (ex >= 0);
+    off = ok ? static_cast<uint32_t>(ex + (s & gm)) * (D * 2) + sl * 16 : kNoRow;
+    tok = ok ? ey + (s & gm) : -1;
   };
 #pragma unroll
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
     const int idx = threadIdx.x + i * NW * 64;
     if (idx < StageRegs<D, NW>::kItems) {
+      const int kpk = idx / SL, slk = idx - kpk * SL;
+      const int kpv = idx & 31, slv = idx >> 5;
+      const unsigned long long k0 = entry(2 * kpk), k1 = entry(2 * kpk + 1);
+      const unsigned long long v0 = entry(2 * kpv), v1 = entry(2 * kpv + 1);
       uint32_t o0, o1;
-      {
-        const int kp = idx / SL, sl = idx - kp * SL;
-        key(2 * kp, sl, o0, r.t0[i]);
-        key(2 * kp + 1, sl, o1, r.t1[i]);
-        r.k0[i] = load16(kr, o0);
-        r.k1[i] = load16(kr, o1);
-      }
-      {
-        const int kp = idx & 31, sl = idx >> 5;
-        int u0, u1;
-        key(2 * kp, sl, o0, u0);
-        key(2 * kp + 1, sl, o1, u1);
-        r.v0[i] = load16(vr, o0);
-        r.v1[i] = load16(vr, o1);
-      }
+      key(2 * kpk, k0, slk, o0, r.t0[i]);
+      key(2 * kpk + 1, k1, slk, o1, r.t1[i]);
+      r.k0[i] = load16(kr, o0);
+      r.k1[i] = load16(kr, o1);
+      int u0, u1;
+      key(2 * kpv, v0, slv, o0, u0);
+      key(2 * kpv + 1, v1, slv, o1, u1);
+      r.v0[i] = load16(vr, o0);
+      r.v1[i] = load16(vr, o1);
     }
   }
   // Tokens ascend along a list, so the stage needs masks iff it runs past the
   // end of the key range or its last key is absent or in the current chunk.
-  const int last = (rem < kTK ? rem : kTK) - 1;
+  int last = (rem < kTK ? rem : kTK) - 1;
+  last = last > 0 ? last : 0;  // a stage past the end (rem <= 0) is masked anyway
   const int2 e = gtab[gbase + (last >> lg)];
   const int tl = e.x >= 0 ? e.y + (last & gm) : -1;
   // the same value on every lane: make it a scalar so branches on it are uniform
@@ -529,8 +533,10 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
     store_stage<D, NW>(sr, kl, vl, tl);
     const bool masked = sr.masked;
     __syncthreads();
-    if (st + 1 < nstages) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
-    if (!rb_on[0]) return;  // wave-uniform: this wave has no rows
+    if (!rb_on[0]) {  // wave-uniform: this wave has no rows, only loads
+      load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
+      return;
+    }
     // S^T for the two 32-key halves; each K operand serves every row block.
     // s[rb][h][j] holds key 32h + 16*(j/8) + 8*hsub + (j%8).
     f32x16 s[RB][2];
@@ -551,6 +557,9 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
           if (rb_on[rb]) s[rb][h] = mfma32x32x16(a, qb[rb][ks].v, s[rb][h]);
       }
     }
+    // The next stage's loads go out behind the S products (past the last
+    // stage every key is absent: zeros, no memory traffic).
+    load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
     // Per half: softmax (VALU) then O^T += V^T P^T; the second half's
     // softmax is independent of the first half's PV products.
 #pragma unroll
