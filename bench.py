@@ -40,6 +40,52 @@ ATTEND_PROFILE = os.path.join(ROOT, "profiles", "attend_mfma_qwen3_prefill_n3276
 ATTEND_SOURCES = ["attend.hip", "hga_device.h"]
 
 
+def measured_peaks(torch):
+    """The device's reachable peaks, measured with libhga_peak.so: dense bf16
+    MFMA TFLOP/s (back-to-back 32x32x16 products, 8 workgroups per CU) and
+    copy GB/s (read + write of 1 GiB; the better of a plain grid-stride copy
+    kernel and torch's device copy)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_kv_routing_amd", "libhga_peak.so"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    blocks, iters = cus * 8, 2000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+
+    def mfma():
+        assert lib.hga_peak_mfma(ctypes.c_void_p(sink.data_ptr()), blocks, iters, stream) == 0
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+
+    def copy():
+        assert lib.hga_peak_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   ctypes.c_int64(nbytes), cus * 8, stream) == 0
+
+    def torch_copy():
+        dst.copy_(src)
+
+    out = {}
+    for name, fn, work in (("mfma_bf16_tflops", mfma, blocks * 4 * 4 * iters * 32768 / 1e12),
+                           ("hbm_copy_gbs", copy, 2 * nbytes / 1e9),
+                           ("torch_copy_gbs", torch_copy, 2 * nbytes / 1e9)):
+        for _ in range(30):  # tens of ms: the steady clock
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = work / (e0.elapsed_time(e1) / 10 * 1e-3)
+    del src, dst, sink
+    out["hbm_copy_gbs"] = max(out["hbm_copy_gbs"], out.pop("torch_copy_gbs"))  # the better copy
+    return out
+
+
 def recorded_traffic():
     """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary (copy-calibrated), or None when the summary was taken
@@ -350,7 +396,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "copy", "peaks"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -365,6 +411,9 @@ def main():
 
     if args.only == "copy":
         copy_calibration(args)
+        return
+    if args.only == "peaks":
+        print(json.dumps(dict(peaks_measured=measured_peaks(torch))), flush=True)
         return
     if args.only == "decode":
         _, dec = bench_decode(args)
@@ -401,6 +450,9 @@ def main():
         stage_ms=pre["stage_ms"],
     )
     if args.only is None:
+        peaks = measured_peaks(torch)
+        line["peaks_measured"] = peaks
+        line["roofline"]["frac_of_measured_peak"] = pre["attend_tflops"] / peaks["mfma_bf16_tflops"]
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(pipe)
         del pipe
@@ -412,6 +464,7 @@ def main():
                               stage_us_eager=dec["stage_us_eager"],
                               roofline=dict(bound="hbm", achieved=dec["achieved_gbs"], peak=PEAK_HBM_GBS,
                                             unit="GB/s", frac=dec["achieved_gbs"] / PEAK_HBM_GBS,
+                                            frac_of_measured_peak=dec["achieved_gbs"] / peaks["hbm_copy_gbs"],
                                             bytes_per_step=dec["bytes_per_step"]))
         _, sm = bench_smalllm(args)
         line["smalllm"] = dict(workload=W.SMALLLM_PREFILL.name, mtok_s=sm["mtok_s"], ms=sm["ms"],

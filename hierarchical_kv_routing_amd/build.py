@@ -13,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhga.so")
 SOURCES = ["summarize.hip", "route.hip", "attend.hip", "api.cpp", "host_tier.cpp"]
+PEAK_LIB = os.path.join(HERE, "libhga_peak.so")   # roofline microbenchmarks (bench.py)
+PEAK_SOURCES = ["peak.hip"]
 ARCH = "gfx950"
 
 
@@ -24,14 +26,20 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 into hierarchical_kv_routing_amd/libhga.so."""
-    tmp = LIB + f".tmp{os.getpid()}"
+    """Compile every source for gfx950: libhga.so (the path) and
+    libhga_peak.so (the peak microbenchmarks bench.py measures against)."""
+    _build_lib(PEAK_LIB, PEAK_SOURCES, verbose)
+    return _build_lib(LIB, SOURCES, verbose)
+
+
+def _build_lib(lib: str, sources, verbose: bool) -> str:
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            # packed f32 VALU forms stay off (hipcc forms them by itself otherwise)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(HERE, "..", "include"),
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+           "-o", tmp] + [os.path.join(CSRC, s) for s in sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,8 +51,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
