@@ -36,6 +36,9 @@ import workloads as W  # noqa: E402
 METRIC = "routed-attn prefill Mtok/s + decode us/step at 64K ctx; % of HBM/MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# warm tier of the host-tiered runs: a quarter of the 128K store's 32768
+# granules (64 MiB of bf16 K+V)
+WARM_TIER_SLOTS = 8192
 ATTEND_PROFILE = os.path.join(ROOT, "profiles", "attend_mfma_qwen3_prefill_n32768.md")
 ATTEND_SOURCES = ["attend.hip", "hga_device.h"]
 
@@ -297,9 +300,10 @@ def pinned_copy_gbs(torch, nbytes=256 << 20, reps=5):
     return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8):
+def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8, cache_slots=0):
     """Prefill with token K/V in pinned host RAM: route + host packing + H2D of
-    the routed granules on a side stream + attention, one call per step."""
+    the routed granules on a side stream + attention, one call per step
+    (with a warm tier of cache_slots granules when cache_slots > 0)."""
     import torch
     import hierarchical_kv_routing_amd as H
     pipe = Pipeline(w)
@@ -310,7 +314,7 @@ def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8):
     _, st = timed_steps(torch, [("attend", pipe.attend)], 3, 1)
     store = H.host_store(pipe.cfg, pipe.k_rot, pipe.v)
     dev_b, host_b = H.host_tiered_buffer_bytes(pipe.cfg, torch.bfloat16, w.batch, w.q_pos0, w.n_q,
-                                               wmax, slots)
+                                               wmax, slots, cache_slots)
     dev = torch.empty(dev_b, dtype=torch.uint8, device="cuda:0")
     host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
     lse = torch.empty(pipe.q.shape[:3], dtype=torch.float32, device="cuda:0")
@@ -319,7 +323,7 @@ def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8):
     def call():
         return H.attend_host_tiered(pipe.cfg, pipe.q, w.q_pos0, store, pipe.k.shape[2], pipe.csum,
                                     pipe.gsum, pipe.out, lse, dev, host, wmax, slots, threads,
-                                    copy_stream=xs)
+                                    copy_stream=xs, cache_slots=cache_slots)
 
     call()
     torch.cuda.synchronize()
@@ -331,11 +335,12 @@ def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8):
     t = (time.perf_counter() - t0) / steps
     t_copy = stats["bytes_h2d"] / (copy_gbs * 1e9)
     t_attn = st["attend"] * 1e-3
-    return dict(workload=w.name, ms=t * 1e3, mtok_s=w.n_q / t / 1e6,
+    return dict(workload=w.name, cache_slots=cache_slots, ms=t * 1e3, mtok_s=w.n_q / t / 1e6,
                 h2d_gb=stats["bytes_h2d"] / 1e9, h2d_gbs=stats["bytes_h2d"] / t / 1e9,
                 pinned_copy_peak_gbs=copy_gbs, windows=stats["windows"],
-                granules_copied=stats["granules_copied"], host_pack_s=stats["pack_seconds"],
-                attend_device_ms=st["attend"], overlap=(t_copy + t_attn) / t)
+                granules_copied=stats["granules_copied"], granules_hit=stats["granules_hit"],
+                host_pack_s=stats["pack_seconds"], attend_device_ms=st["attend"],
+                overlap=(t_copy + t_attn) / t)
 
 
 def cpu_baseline(pipe, budget_s=12.0):
@@ -421,7 +426,8 @@ def main():
         return
     if args.only == "host":
         gbs = pinned_copy_gbs(torch)
-        res = {w.name: bench_host_tier(args, w, gbs) for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP)}
+        res = {w.name + ("" if c == 0 else "_warm_tier"): bench_host_tier(args, w, gbs, cache_slots=c)
+               for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP) for c in (0, WARM_TIER_SLOTS)}
         print(json.dumps(dict(host_tiered=res)), flush=True)
         return
     if args.only == "smalllm":
@@ -473,9 +479,11 @@ def main():
         gbs = pinned_copy_gbs(torch)
         line["host_tiered"] = {}
         for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP):
-            line["host_tiered"][w.name] = bench_host_tier(args, w, gbs)
-            log(f"[bench] host tier {w.name}: {line['host_tiered'][w.name]}")
-            torch.cuda.empty_cache()
+            for cache in (0, WARM_TIER_SLOTS):
+                name = w.name + ("" if cache == 0 else "_warm_tier")
+                line["host_tiered"][name] = bench_host_tier(args, w, gbs, cache_slots=cache)
+                log(f"[bench] host tier {name}: {line['host_tiered'][name]}")
+                torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 

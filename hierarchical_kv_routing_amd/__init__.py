@@ -53,7 +53,7 @@ class hga_config(ctypes.Structure):
 class hga_tier_stats(ctypes.Structure):
     _fields_ = [("windows", ctypes.c_int64), ("granules_copied", ctypes.c_int64),
                 ("bytes_h2d", ctypes.c_int64), ("pack_seconds", ctypes.c_double),
-                ("host_seconds", ctypes.c_double)]
+                ("host_seconds", ctypes.c_double), ("granules_hit", ctypes.c_int64)]
 
 
 @dataclass(frozen=True)
@@ -118,10 +118,10 @@ def lib() -> ctypes.CDLL:
         "hga_attend_workspace_bytes": (SZ, [CP, I32, I64, I64]),
         "hga_attend": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, SZ, P]),
         "hga_dense_causal": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, SZ, P]),
-        "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64,
+        "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64, I64,
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
-                                         I32, I64, I32, P, P, ctypes.POINTER(hga_tier_stats)]),
+                                         I32, I64, I64, I32, P, P, ctypes.POINTER(hga_tier_stats)]),
         "hga_status_string": (ctypes.c_char_p, [I32]),
         "hga_last_hip_error": (ctypes.c_int, []),
     }
@@ -291,13 +291,14 @@ def dense_causal(cfg: Config, q, q_pos0: int, k_rot, v, out, lse=None, workspace
 
 
 def host_tiered_buffer_bytes(cfg: Config, dtype, batch: int, q_pos0: int, n_q: int,
-                             max_window_chunks: int, slots_per_window: int):
-    """(device_bytes, host_bytes) of the staging buffers the host tier needs."""
+                             max_window_chunks: int, slots_per_window: int, cache_slots: int = 0):
+    """(device_bytes, host_bytes) of the staging buffers the host tier needs
+    (cache_slots > 0: with a warm tier of that many granules)."""
     torch = _torch()
     code = HGA_BF16 if dtype == torch.bfloat16 else HGA_F32
     dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
     st = lib().hga_host_tiered_buffer_bytes(ctypes.byref(cfg.c()), code, batch, q_pos0, n_q,
-                                            max_window_chunks, slots_per_window,
+                                            max_window_chunks, slots_per_window, cache_slots,
                                             ctypes.byref(dev), ctypes.byref(host))
     _check(st, "hga_host_tiered_buffer_bytes")
     return dev.value, host.value
@@ -319,9 +320,10 @@ def host_store(cfg: Config, k_rot, v):
 def attend_host_tiered(cfg: Config, q, q_pos0: int, kv_host, kv_cap: int, chunk_sum, group_sum,
                        out, lse, dev_staging, host_staging, max_window_chunks: int,
                        slots_per_window: int, n_threads: int = 8, compute_stream=None,
-                       copy_stream=None) -> dict:
+                       copy_stream=None, cache_slots: int = 0) -> dict:
     """Route + attention with token K/V in pinned host RAM (host-blocking until
-    the last attention launch is enqueued).  Returns the call's statistics."""
+    the last attention launch is enqueued), with a warm tier of cache_slots
+    granules when cache_slots > 0.  Returns the call's statistics."""
     torch = _torch()
     B, Hq, n_q, d = q.shape
     _dev(q, "q")
@@ -343,7 +345,7 @@ def attend_host_tiered(cfg: Config, q, q_pos0: int, kv_host, kv_cap: int, chunk_
         out.data_ptr(), lse.data_ptr() if lse is not None else None,
         dev_staging.data_ptr(), dev_staging.numel() * dev_staging.element_size(),
         host_staging.data_ptr(), host_staging.numel() * host_staging.element_size(),
-        max_window_chunks, slots_per_window, n_threads, ctypes.c_void_p(cs.cuda_stream),
+        max_window_chunks, slots_per_window, cache_slots, n_threads, ctypes.c_void_p(cs.cuda_stream),
         ctypes.c_void_p(xs.cuda_stream), ctypes.byref(stats))
     _check(st, "hga_attend_host_tiered")
     return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}

@@ -17,6 +17,12 @@
 //      attention on the compute stream;
 //   4. two window buffers alternate, so window w+1 is packed and copied
 //      while window w is attended.
+// With a warm tier (cache_slots > 0) the device keeps a cache of granules
+// across the windows of the call (least recently used evicted first):
+// a window copies only the granules the cache lacks, into a landing buffer,
+// and a gather kernel on the compute stream moves them to their cache slots
+// before the window's attention; stream order makes every slot that the
+// window does not use safe to evict.
 // The call returns after the last attention launch is enqueued.
 #include <algorithm>
 #include <chrono>
@@ -36,19 +42,22 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Byte offsets of every buffer carved from the caller's staging memory.
 struct Layout {
-  int64_t units = 0, wunits = 0, slots = 0;
+  int64_t units = 0, wunits = 0, slots = 0, cache_slots = 0;
   size_t granule_bytes = 0;
-  size_t cidx = 0, gidx = 0, gran = 0, gcnt = 0, rws = 0, win[2] = {0, 0}, dev_total = 0;
-  size_t pool_bytes = 0, wgran = 0, wslot = 0, wcnt = 0, win_bytes = 0;  // inside one window buffer
+  size_t cidx = 0, gidx = 0, gran = 0, gcnt = 0, rws = 0, cache = 0, win[2] = {0, 0}, dev_total = 0;
+  // inside one window buffer: the pool (no cache) or the landing buffer of
+  // the window's misses (cache), then its index arrays
+  size_t pool_bytes = 0, wgran = 0, wslot = 0, wcnt = 0, wdst = 0, win_bytes = 0;
   size_t hgran = 0, hcnt = 0, hwin[2] = {0, 0}, host_total = 0;
 };
 
-Layout make_layout(const hga::Geometry& g, int32_t wmax, int64_t slots) {
+Layout make_layout(const hga::Geometry& g, int32_t wmax, int64_t slots, int64_t cache_slots) {
   Layout L;
   const size_t elem = g.bf16 ? 2 : 4;
   L.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   L.wunits = static_cast<int64_t>(g.B) * g.Hkv * wmax;
   L.slots = slots;
+  L.cache_slots = cache_slots;
   L.granule_bytes = static_cast<size_t>(2) * g.gs * g.d * elem;
   const size_t u = static_cast<size_t>(L.units);
   size_t off = 0;
@@ -57,11 +66,13 @@ Layout make_layout(const hga::Geometry& g, int32_t wmax, int64_t slots) {
   L.gran = off; off = align_up(off + u * g.gmax * 4);
   L.gcnt = off; off = align_up(off + u * 4);
   L.rws = off; off = align_up(off + hga::route_workspace(g));
+  L.cache = off; off = align_up(off + static_cast<size_t>(cache_slots) * L.granule_bytes);
   L.pool_bytes = align_up(static_cast<size_t>(slots) * L.granule_bytes);
   L.wgran = L.pool_bytes;
   L.wslot = align_up(L.wgran + static_cast<size_t>(L.wunits) * g.gmax * 4);
   L.wcnt = align_up(L.wslot + static_cast<size_t>(L.wunits) * g.gmax * 4);
-  L.win_bytes = align_up(L.wcnt + static_cast<size_t>(L.wunits) * 4);
+  L.wdst = align_up(L.wcnt + static_cast<size_t>(L.wunits) * 4);
+  L.win_bytes = align_up(L.wdst + (cache_slots > 0 ? static_cast<size_t>(slots) * 4 : 0));
   L.win[0] = off; off += L.win_bytes;
   L.win[1] = off; off += L.win_bytes;
   L.dev_total = off;
@@ -148,16 +159,214 @@ struct Events {
 };
 
 hga_status tier_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, int64_t q_pos0,
-                         int64_t n_q, int64_t kv_cap, int32_t wmax, int64_t slots, hga::Geometry& g) {
+                         int64_t n_q, int64_t kv_cap, int32_t wmax, int64_t slots,
+                         int64_t cache_slots, hga::Geometry& g) {
   hga_status st = hga::make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
   if (st != HGA_OK) return st;
-  if (n_q <= 0 || wmax <= 0) return HGA_ERR_INVALID_ARGUMENT;
-  // one query chunk of every (sequence, KV head) must fit a window
-  if (slots < static_cast<int64_t>(g.B) * g.Hkv * g.gmax) return HGA_ERR_INVALID_ARGUMENT;
+  if (n_q <= 0 || wmax <= 0 || cache_slots < 0) return HGA_ERR_INVALID_ARGUMENT;
+  // one query chunk of every (sequence, KV head) must fit a window (and the cache)
+  const int64_t chunk_need = static_cast<int64_t>(g.B) * g.Hkv * g.gmax;
+  if (slots < chunk_need) return HGA_ERR_INVALID_ARGUMENT;
+  if (cache_slots > 0 && cache_slots < chunk_need) return HGA_ERR_INVALID_ARGUMENT;
   if (!hga::route_supported(g) || !hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
-  // the pool is read through 32-bit buffer offsets, every list by one work item
-  const int64_t pool = slots * 2 * g.gs * g.d * (g.bf16 ? 2 : 4);
+  // the pool (or cache) is read through 32-bit buffer offsets, every list by one work item
+  const int64_t pool = std::max(slots, cache_slots) * 2 * g.gs * g.d * (g.bf16 ? 2 : 4);
   if (g.bf16 && (pool >= (int64_t{1} << 31) || g.gmax > hga::kAttendTable)) return HGA_ERR_UNSUPPORTED;
+  return HGA_OK;
+}
+
+// Copies granule j of the landing buffer to cache slot dst[j] (one
+// workgroup per granule, 16-byte words).
+__global__ __launch_bounds__(256) void land_granules(const uint4* landing, uint4* cache,
+                                                     const int32_t* dst, int64_t words) {
+  const uint4* src = landing + static_cast<int64_t>(blockIdx.x) * words;
+  uint4* out = cache + static_cast<int64_t>(dst[blockIdx.x]) * words;
+  for (int64_t i = threadIdx.x; i < words; i += blockDim.x) out[i] = src[i];
+}
+
+// Least-recently-used order of the cache slots (a doubly linked list; the
+// front is the most recent).  Slot owners are (sequence, KV head, granule)
+// keys, -1 when free.
+class Lru {
+ public:
+  explicit Lru(int64_t n) : prev_(n), next_(n), owner_(n, -1) {
+    for (int64_t i = 0; i < n; ++i) {
+      prev_[i] = i - 1;
+      next_[i] = i + 1 < n ? i + 1 : -1;
+    }
+    head_ = n > 0 ? 0 : -1;
+    tail_ = n - 1;
+  }
+  void touch(int64_t s) {  // move to the front
+    if (s == head_) return;
+    unlink(s);
+    prev_[s] = -1;
+    next_[s] = head_;
+    if (head_ >= 0) prev_[head_] = s;
+    head_ = s;
+    if (tail_ < 0) tail_ = s;
+  }
+  int64_t victim() const { return tail_; }
+  int64_t owner(int64_t s) const { return owner_[s]; }
+  void set_owner(int64_t s, int64_t key) { owner_[s] = key; }
+
+ private:
+  void unlink(int64_t s) {
+    if (prev_[s] >= 0) next_[prev_[s]] = next_[s]; else head_ = next_[s];
+    if (next_[s] >= 0) prev_[next_[s]] = prev_[s]; else tail_ = prev_[s];
+  }
+  std::vector<int64_t> prev_, next_, owner_;
+  int64_t head_ = -1, tail_ = -1;
+};
+
+// The window loop with a warm tier (see the file comment): L.cache holds
+// cache_slots granules; a window holds at most cache_slots distinct granules
+// and at most slots_per_window misses.
+hga_status tiered_cached(const hga::Geometry& g, const Layout& L, const void* q_raw,
+                         const void* kv_host, void* out, float* lse, char* dev, char* host,
+                         const int32_t* h_gran, const int32_t* h_gcnt, int32_t wmax,
+                         int64_t slots_per_window, int64_t cache_slots, int32_t n_threads,
+                         hipStream_t cs, hipStream_t xs, hipEvent_t* copied, hipEvent_t* attended,
+                         hga_tier_stats* stats, std::chrono::steady_clock::time_point t_start) {
+  const int64_t ngran = g.kv_cap / g.gs;
+  const int64_t bh = static_cast<int64_t>(g.B) * g.Hkv;
+  const size_t gb = L.granule_bytes;
+  char* cache = dev + L.cache;
+  Lru lru(cache_slots);
+  std::vector<int64_t> slot_of(static_cast<size_t>(bh * ngran), -1);
+  std::vector<int32_t> stamp(static_cast<size_t>(bh * ngran), -1);
+  std::vector<std::pair<const char*, char*>> jobs;
+  jobs.reserve(static_cast<size_t>(slots_per_window));
+  const char* store = static_cast<const char*>(kv_host);
+  Packer packer(n_threads);
+  double pack_s = 0.0;
+  int64_t copied_granules = 0, hits = 0, bytes_h2d = 0;
+  const int64_t t_end = g.t0 + g.nqc;
+  hipError_t e = hipSuccess;
+  int32_t w = 0;
+  for (int64_t ta = g.t0; ta < t_end; ++w) {
+    const int buf = w & 1;
+    char* hw = host + L.hwin[buf];
+    char* dw = dev + L.win[buf];
+    if (w >= 2) {  // the copy that last read this host buffer must be done
+      e = hipEventSynchronize(copied[buf]);
+      if (e != hipSuccess) return hga::hip_fail(e);
+    }
+    int32_t* wdst = reinterpret_cast<int32_t*>(hw + L.wdst);
+    // Grow the window one query chunk at a time while its distinct granules
+    // fit the cache and its misses the landing buffer; hits move to the
+    // front of the LRU order, misses take the least recently used slots.
+    int64_t need = 0, miss = 0, tb = ta;
+    jobs.clear();
+    while (tb < t_end && tb - ta < wmax) {
+      int64_t add_need = 0, add_miss = 0;
+      for (int64_t x = 0; x < bh; ++x) {
+        const int64_t u = x * g.nqc + (tb - g.t0);
+        for (int32_t i = 0; i < h_gcnt[u]; ++i) {
+          const size_t k = static_cast<size_t>(x * ngran + h_gran[u * g.gmax + i]);
+          if (stamp[k] != w) {
+            ++add_need;
+            add_miss += slot_of[k] < 0;
+          }
+        }
+      }
+      if (need + add_need > cache_slots || miss + add_miss > slots_per_window) break;
+      for (int64_t x = 0; x < bh; ++x) {
+        const int64_t u = x * g.nqc + (tb - g.t0);
+        for (int32_t i = 0; i < h_gcnt[u]; ++i) {
+          const int64_t k = x * ngran + h_gran[u * g.gmax + i];
+          if (stamp[static_cast<size_t>(k)] == w) continue;
+          stamp[static_cast<size_t>(k)] = w;
+          int64_t sl = slot_of[static_cast<size_t>(k)];
+          if (sl >= 0) {
+            ++hits;
+          } else {
+            sl = lru.victim();  // untouched in this window (need <= cache_slots)
+            const int64_t prev = lru.owner(sl);
+            if (prev >= 0) slot_of[static_cast<size_t>(prev)] = -1;
+            lru.set_owner(sl, k);
+            slot_of[static_cast<size_t>(k)] = sl;
+            wdst[miss] = static_cast<int32_t>(sl);
+            jobs.emplace_back(store + k * gb, hw + miss * gb);
+            ++miss;
+          }
+          lru.touch(sl);
+        }
+      }
+      need += add_need;
+      ++tb;
+    }
+    const int64_t nw = tb - ta;
+    int32_t* wgran = reinterpret_cast<int32_t*>(hw + L.wgran);
+    int32_t* wslot = reinterpret_cast<int32_t*>(hw + L.wslot);
+    int32_t* wcnt = reinterpret_cast<int32_t*>(hw + L.wcnt);
+    for (int64_t x = 0; x < bh; ++x) {
+      for (int64_t t = ta; t < tb; ++t) {
+        const int64_t u = x * g.nqc + (t - g.t0);
+        const int64_t wu = x * nw + (t - ta);
+        wcnt[wu] = h_gcnt[u];
+        for (int32_t i = 0; i < g.gmax; ++i) {
+          const int32_t gid = i < h_gcnt[u] ? h_gran[u * g.gmax + i] : -1;
+          wgran[wu * g.gmax + i] = gid;
+          wslot[wu * g.gmax + i] =
+              gid >= 0 ? static_cast<int32_t>(slot_of[static_cast<size_t>(x * ngran + gid)]) : -1;
+        }
+      }
+    }
+    const auto p0 = std::chrono::steady_clock::now();
+    const size_t nj = jobs.size();
+    packer.run([&](int i, int n) {
+      const size_t lo = nj * i / n, hi = nj * (i + 1) / n;
+      for (size_t j = lo; j < hi; ++j) std::memcpy(jobs[j].second, jobs[j].first, gb);
+    });
+    pack_s += std::chrono::duration<double>(std::chrono::steady_clock::now() - p0).count();
+    // the landing buffer and index arrays of this window buffer were last
+    // read by window w-2's gather and attention on the compute stream
+    if (w >= 2) {
+      e = hipStreamWaitEvent(xs, attended[buf], 0);
+      if (e != hipSuccess) return hga::hip_fail(e);
+    }
+    const size_t idx_bytes = L.win_bytes - L.wgran;
+    if (miss > 0) e = hipMemcpyAsync(dw, hw, static_cast<size_t>(miss) * gb, hipMemcpyHostToDevice, xs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dw + L.wgran, hw + L.wgran, idx_bytes, hipMemcpyHostToDevice, xs);
+    if (e == hipSuccess) e = hipEventRecord(copied[buf], xs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, copied[buf], 0);
+    if (e != hipSuccess) return hga::hip_fail(e);
+    if (miss > 0) {
+      hipLaunchKernelGGL(land_granules, dim3(static_cast<unsigned>(miss)), dim3(256), 0, cs,
+                         reinterpret_cast<const uint4*>(dw), reinterpret_cast<uint4*>(cache),
+                         reinterpret_cast<const int32_t*>(dw + L.wdst), static_cast<int64_t>(gb / 16));
+      e = hipGetLastError();
+      if (e != hipSuccess) return hga::hip_fail(e);
+    }
+    copied_granules += miss;
+    bytes_h2d += static_cast<int64_t>(static_cast<size_t>(miss) * gb + idx_bytes);
+    hga::Geometry gw = g;
+    gw.q_pos0 = std::max(ta * g.C, g.q_pos0);
+    gw.n_q = std::min(tb * g.C, g.q_pos0 + g.n_q) - gw.q_pos0;
+    gw.t0 = ta;
+    gw.nqc = nw;
+    hga::AttendExtra ex;
+    ex.pool_slot = reinterpret_cast<const int32_t*>(dw + L.wslot);
+    ex.pool_slots = cache_slots;
+    ex.allow_split = false;
+    ex.q_stride = g.n_q;
+    ex.q_row0 = g.q_pos0;
+    e = hga::launch_attend(gw, q_raw, cache, cache, reinterpret_cast<const int32_t*>(dw + L.wgran),
+                           reinterpret_cast<const int32_t*>(dw + L.wcnt), false, out, lse, nullptr, cs, &ex);
+    if (e == hipSuccess) e = hipEventRecord(attended[buf], cs);
+    if (e != hipSuccess) return hga::hip_fail(e);
+    ta = tb;
+  }
+  if (stats != nullptr) {
+    stats->windows = w;
+    stats->granules_copied = copied_granules;
+    stats->bytes_h2d = bytes_h2d;
+    stats->pack_seconds = pack_s;
+    stats->host_seconds =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+    stats->granules_hit = hits;
+  }
   return HGA_OK;
 }
 
@@ -167,16 +376,16 @@ extern "C" {
 
 hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                         int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
-                                        int64_t slots_per_window, size_t* device_bytes,
-                                        size_t* host_bytes) {
+                                        int64_t slots_per_window, int64_t cache_slots,
+                                        size_t* device_bytes, size_t* host_bytes) {
   if (device_bytes == nullptr || host_bytes == nullptr || cfg == nullptr || cfg->chunk_size <= 0)
     return HGA_ERR_INVALID_ARGUMENT;
   const int64_t cap = ((q_pos0 + n_q + cfg->chunk_size - 1) / cfg->chunk_size) * cfg->chunk_size;
   hga::Geometry g;
   hga_status st = tier_geometry(cfg, dtype, batch, q_pos0, n_q, cap > 0 ? cap : cfg->chunk_size,
-                                max_window_chunks, slots_per_window, g);
+                                max_window_chunks, slots_per_window, cache_slots, g);
   if (st != HGA_OK) return st;
-  const Layout L = make_layout(g, max_window_chunks, slots_per_window);
+  const Layout L = make_layout(g, max_window_chunks, slots_per_window, cache_slots);
   *device_bytes = L.dev_total;
   *host_bytes = L.host_total;
   return HGA_OK;
@@ -188,13 +397,13 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
                                   const float* group_sum, void* out, float* lse,
                                   void* dev_staging, size_t dev_bytes, void* host_staging,
                                   size_t host_bytes, int32_t max_window_chunks,
-                                  int64_t slots_per_window, int32_t n_threads,
-                                  void* compute_stream, void* copy_stream,
+                                  int64_t slots_per_window, int64_t cache_slots,
+                                  int32_t n_threads, void* compute_stream, void* copy_stream,
                                   hga_tier_stats* stats) {
   const auto t_start = std::chrono::steady_clock::now();
   hga::Geometry g;
   hga_status st = tier_geometry(cfg, dtype, batch, q_pos0, n_q, kv_cap, max_window_chunks,
-                                slots_per_window, g);
+                                slots_per_window, cache_slots, g);
   if (st != HGA_OK) return st;
   if (q_raw == nullptr || kv_host == nullptr || out == nullptr || chunk_sum == nullptr ||
       dev_staging == nullptr || host_staging == nullptr || n_threads < 0)
@@ -203,7 +412,7 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
   if ((reinterpret_cast<uintptr_t>(dev_staging) | reinterpret_cast<uintptr_t>(host_staging)) % kAlign)
     return HGA_ERR_INVALID_ARGUMENT;
   if (!pinned_host(kv_host) || !pinned_host(host_staging)) return HGA_ERR_INVALID_ARGUMENT;
-  const Layout L = make_layout(g, max_window_chunks, slots_per_window);
+  const Layout L = make_layout(g, max_window_chunks, slots_per_window, cache_slots);
   if (dev_bytes < L.dev_total || host_bytes < L.host_total) return HGA_ERR_WORKSPACE_TOO_SMALL;
 
   hipStream_t cs = static_cast<hipStream_t>(compute_stream);
@@ -238,6 +447,10 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
 
   const int64_t ngran = g.kv_cap / g.gs;
   const int64_t bh = static_cast<int64_t>(g.B) * g.Hkv;
+  if (cache_slots > 0)
+    return tiered_cached(g, L, q_raw, kv_host, out, lse, dev, host, h_gran, h_gcnt,
+                         max_window_chunks, slots_per_window, cache_slots, n_threads, cs, xs,
+                         copied, attended, stats, t_start);
   std::vector<int32_t> stamp(static_cast<size_t>(bh * ngran), -1);
   std::vector<int32_t> slotmap(static_cast<size_t>(bh * ngran), 0);
   std::vector<std::pair<const char*, char*>> jobs;
@@ -348,6 +561,7 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
     stats->pack_seconds = pack_s;
     stats->host_seconds =
         std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+    stats->granules_hit = 0;
   }
   return HGA_OK;
 }

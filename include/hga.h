@@ -214,6 +214,15 @@ hga_status hga_dense_causal(const hga_config* cfg, hga_dtype dtype, int32_t batc
  *      while window w is attended.
  * It returns once the last attention is enqueued on compute_stream.
  *
+ * Warm tier (the tiered store's VRAM cache, xllm-io page, section 3):
+ * with cache_slots > 0 the device keeps up to cache_slots granules across
+ * the windows of the call, evicting the least recently used; a window then
+ * holds at most cache_slots distinct granules and copies only its misses
+ * (at most slots_per_window), which a device gather moves into their cache
+ * slots before the window's attention.  Outputs are unchanged (bitwise);
+ * stats->granules_hit counts the reuses.  cache_slots = 0: no warm tier;
+ * otherwise cache_slots >= B * Hkv * hga_max_granules(cfg).
+ *
  * dev_staging (device) and host_staging (pinned host) are caller-owned,
  * 256-byte aligned, at least the sizes hga_host_tiered_buffer_bytes returns;
  * slots_per_window >= B * Hkv * hga_max_granules(cfg).  Both streams must
@@ -227,12 +236,13 @@ typedef struct hga_tier_stats {
   int64_t bytes_h2d;        /* bytes of all host -> device copies of the call      */
   double pack_seconds;      /* host time spent packing granules into staging       */
   double host_seconds;      /* host time of the whole call                         */
+  int64_t granules_hit;     /* granules a window found in the warm tier (cache)    */
 } hga_tier_stats;
 
 hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                         int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
-                                        int64_t slots_per_window, size_t* device_bytes,
-                                        size_t* host_bytes);
+                                        int64_t slots_per_window, int64_t cache_slots,
+                                        size_t* device_bytes, size_t* host_bytes);
 
 hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                   const void* q_raw, int64_t q_pos0, int64_t n_q,
@@ -242,7 +252,8 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
                                   void* dev_staging, size_t dev_bytes,
                                   void* host_staging, size_t host_bytes,
                                   int32_t max_window_chunks, int64_t slots_per_window,
-                                  int32_t n_threads, void* compute_stream, void* copy_stream,
+                                  int64_t cache_slots, int32_t n_threads,
+                                  void* compute_stream, void* copy_stream,
                                   hga_tier_stats* stats);
 
 const char* hga_status_string(hga_status status);

@@ -117,19 +117,28 @@ def test_host_tier_sizes_and_checks(lib):
     gmax = H.max_granules(cfg)
     dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
     c = ctypes.byref(cfg.c())
-    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384,
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, 0,
                                             ctypes.byref(dev), ctypes.byref(host)) == 0
     pool = 16384 * 2 * 16 * 128 * 2            # slots x (K + V) x g_s x d x bf16
     assert dev.value >= 2 * pool and host.value >= 2 * pool
-    # a window must hold one query chunk of every (sequence, KV head)
-    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 4 * gmax - 1,
+    no_cache = dev.value
+    # a warm tier adds its cache to the device buffer only
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, 20000,
+                                            ctypes.byref(dev), ctypes.byref(host)) == 0
+    assert dev.value >= no_cache + 20000 * 2 * 16 * 128 * 2
+    # a window must hold one query chunk of every (sequence, KV head); so must the cache
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 4 * gmax - 1, 0,
                                             ctypes.byref(dev), ctypes.byref(host)) == 1
-    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 0, 16384,
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, 4 * gmax - 1,
                                             ctypes.byref(dev), ctypes.byref(host)) == 1
-    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, None, None) == 1
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, -1,
+                                            ctypes.byref(dev), ctypes.byref(host)) == 1
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 0, 16384, 0,
+                                            ctypes.byref(dev), ctypes.byref(host)) == 1
+    assert lib.hga_host_tiered_buffer_bytes(c, 1, 1, 0, 131072, 64, 16384, 0, None, None) == 1
     # argument errors are reported before any pointer is touched
     stats = H.hga_tier_stats()
     assert lib.hga_attend_host_tiered(c, 1, 1, 16, 0, 131072, None, 131072, 16, 16, 16, None, 256, 0,
-                                      256, 0, 64, 16384, 4, None, None, ctypes.byref(stats)) == 1
+                                      256, 0, 64, 16384, 0, 4, None, None, ctypes.byref(stats)) == 1
     assert lib.hga_attend_host_tiered(c, 1, 1, 16, 0, 131072, 16, 131072, 16, 16, 16, None, 256, 0,
-                                      256, 0, 64, 16384, -1, None, None, ctypes.byref(stats)) == 1
+                                      256, 0, 64, 16384, 0, -1, None, None, ctypes.byref(stats)) == 1

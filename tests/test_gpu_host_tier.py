@@ -11,13 +11,13 @@ from tests import parity as P
 pytestmark = pytest.mark.gpu
 
 
-def run_host_tier(run, max_window_chunks, slots, threads=4, copy_stream=True):
+def run_host_tier(run, max_window_chunks, slots, threads=4, copy_stream=True, cache_slots=0):
     import torch
     w, cfg = run.w, run.cfg
     store = H.host_store(cfg, run.k_rot, run.v)
     dt = P.torch_dtype(w)
     dev_b, host_b = H.host_tiered_buffer_bytes(cfg, dt, w.batch, w.q_pos0, w.n_q,
-                                               max_window_chunks, slots)
+                                               max_window_chunks, slots, cache_slots)
     dev = torch.empty(dev_b, dtype=torch.uint8, device="cuda:0")
     host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
     out = torch.full_like(run.out, float("nan"))
@@ -25,7 +25,7 @@ def run_host_tier(run, max_window_chunks, slots, threads=4, copy_stream=True):
     xs = torch.cuda.Stream() if copy_stream else None
     stats = H.attend_host_tiered(cfg, run.q, w.q_pos0, store, run.k.shape[2], run.csum, run.gsum,
                                  out, lse, dev, host, max_window_chunks, slots, threads,
-                                 copy_stream=xs)
+                                 copy_stream=xs, cache_slots=cache_slots)
     torch.cuda.synchronize()
     return out, lse, stats
 
@@ -48,6 +48,28 @@ def test_host_tier_equals_device_path(base):
     assert all(same), same
     units = P.sample_units(w, 6)
     P.check_attention(run, q, k, v, units, out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("base", ["chunk_only", "group"])
+def test_warm_tier_equals_device_path(base):
+    """A warm tier small enough to evict: same outputs bit for bit, fewer
+    granules copied than without it, and the reuse counted."""
+    import torch
+    w0 = W.HOST_TIERED_CHUNK if base == "chunk_only" else W.HOST_TIERED_GROUP
+    w = w0.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=16)
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.GpuRun(w, q, k, v)
+    need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
+    cache = need + 64  # below the 1024 granules of the 4 (sequence, KV head) slabs
+    _, _, cold = run_host_tier(run, max_window_chunks=4, slots=need + 64)
+    out, lse, stats = run_host_tier(run, max_window_chunks=4, slots=need + 64, cache_slots=cache)
+    print(f"[gpu] warm tier {base}: {stats} (no cache: {cold})", flush=True)
+    same = (bool(torch.equal(out, run.out)), bool(torch.equal(lse, run.lse)))
+    assert all(same), same
+    assert stats["granules_hit"] > 0
+    assert stats["granules_copied"] < cold["granules_copied"]
+    assert stats["granules_copied"] > cache          # slots were evicted and reused
+    assert stats["windows"] >= w.n_q // w.chunk_size // 4
 
 
 def test_host_tier_same_stream_and_no_threads():
@@ -79,7 +101,7 @@ def test_host_tier_rejects_pageable_memory():
     st = H.lib().hga_attend_host_tiered(
         ctypes.byref(cfg.c()), H.HGA_BF16, B, run.q.data_ptr(), 0, w.n_q, pageable.data_ptr(), cap,
         run.csum.data_ptr(), run.gsum.data_ptr(), run.out.data_ptr(), None, dev.data_ptr(), dev_b,
-        host.data_ptr(), host_b, 4, slots, 2, None, None, ctypes.byref(stats))
+        host.data_ptr(), host_b, 4, slots, 0, 2, None, None, ctypes.byref(stats))
     assert st == 1
     # the failed pointer query left no error behind for the next launch
     run.attend()
