@@ -21,8 +21,18 @@ def _freq(i, d, theta):
     return float(theta) ** (-2.0 * i / d)
 
 
-def rotate(vec, pos, theta):
-    """R_pos on a d-vector: pair (vec[i], vec[i + d/2]) turned by pos*theta_i."""
+def wrap(pos, period):
+    """RoPE position index: pos itself, or pos taken modulo ``period`` for the
+    wrapped-position variant (xllm-io page, Sec. 5.5)."""
+    if not period:
+        return pos
+    return pos - period * math.floor(pos / period)
+
+
+def rotate(vec, pos, theta, period=0):
+    """R_pos on a d-vector: pair (vec[i], vec[i + d/2]) turned by p*theta_i,
+    p = wrap(pos, period)."""
+    pos = wrap(pos, period)
     d = len(vec)
     h = d // 2
     out = [0.0] * d
@@ -35,19 +45,22 @@ def rotate(vec, pos, theta):
     return out
 
 
-def block_summary(keys, first, n_hf, theta):
-    """Summary of the block of raw keys ``keys`` whose first position is first."""
+def block_summary(keys, first, n_hf, theta, period=0):
+    """Summary of the block of raw keys ``keys`` whose first position is first.
+
+    With wrapped positions the block's middle is the middle of its wrapped
+    positions (a block never straddles a multiple of the period)."""
     size = len(keys)
     d = len(keys[0])
     h = d // 2
     rot_sum = [0.0] * d
     raw_sum = [0.0] * d
     for j in range(size):
-        r = rotate(keys[j], first + j, theta)
+        r = rotate(keys[j], first + j, theta, period)
         for e in range(d):
             rot_sum[e] += r[e]
             raw_sum[e] += float(keys[j][e])
-    p_mid = first + (size - 1) / 2.0
+    p_mid = wrap(first, period) + (size - 1) / 2.0
     low = rotate([x / size for x in raw_sum], p_mid, theta)
     out = list(low)
     for i in range(n_hf):
@@ -56,8 +69,9 @@ def block_summary(keys, first, n_hf, theta):
     return out
 
 
-def all_summaries(keys, n_tokens, size, n_hf, theta):
-    return [block_summary([keys[j] for j in range(b * size, (b + 1) * size)], b * size, n_hf, theta)
+def all_summaries(keys, n_tokens, size, n_hf, theta, period=0):
+    return [block_summary([keys[j] for j in range(b * size, (b + 1) * size)], b * size, n_hf, theta,
+                          period)
             for b in range(n_tokens // size)]
 
 
@@ -128,7 +142,8 @@ def attend_row(qrot, keys_rot, vals, visible, scale):
     return [x / z for x in out], m + math.log(z)
 
 
-def routed_attention(q, k, v, q_pos0, C, gs, F, L, Kc, Kg, n_hf, theta, Hq, Hkv, scale=None):
+def routed_attention(q, k, v, q_pos0, C, gs, F, L, Kc, Kg, n_hf, theta, Hq, Hkv, scale=None,
+                     period=0):
     """Whole pipeline for one sequence: q [Hq][n_q][d], k, v [Hkv][n][d].
 
     Summaries are taken over the closed chunks before each query chunk.
@@ -143,24 +158,25 @@ def routed_attention(q, k, v, q_pos0, C, gs, F, L, Kc, Kg, n_hf, theta, Hq, Hkv,
     routes = {}
     out = [[None] * n_q for _ in range(Hq)]
     for kvh in range(Hkv):
-        keys_rot = [rotate(k[kvh][j], j, theta) for j in range(n_tok)]
-        csum = all_summaries(k[kvh], n_tok, C, n_hf, theta)
-        gsum = all_summaries(k[kvh], n_tok, gs, n_hf, theta)
+        keys_rot = [rotate(k[kvh][j], j, theta, period) for j in range(n_tok)]
+        csum = all_summaries(k[kvh], n_tok, C, n_hf, theta, period)
+        gsum = all_summaries(k[kvh], n_tok, gs, n_hf, theta, period)
         for t in range(q_pos0 // C, (n_tok - 1) // C + 1):
             qs = [i for i in range(max(t * C, q_pos0), min((t + 1) * C, n_tok))]
-            rows = [rotate(q[kvh * G + hl][i - q_pos0], i, theta) for hl in range(G) for i in qs]
+            rows = [rotate(q[kvh * G + hl][i - q_pos0], i, theta, period) for hl in range(G) for i in qs]
             selc, selg = route_one(rows, t, csum, gsum, C, gs, F, L, Kc, Kg)
             routes[(kvh, t)] = (selc, selg)
             for hl in range(G):
                 h = kvh * G + hl
                 for i in qs:
                     vis = visible_keys(i, t, selc, selg, C, gs, F, L, Kg)
-                    o, _ = attend_row(rotate(q[h][i - q_pos0], i, theta), keys_rot, v[kvh], vis, scale)
+                    o, _ = attend_row(rotate(q[h][i - q_pos0], i, theta, period), keys_rot, v[kvh], vis,
+                                      scale)
                     out[h][i - q_pos0] = o
     return out, routes
 
 
-def dense_attention(q, k, v, q_pos0, theta, Hq, Hkv, scale=None):
+def dense_attention(q, k, v, q_pos0, theta, Hq, Hkv, scale=None, period=0):
     d = len(q[0][0])
     n_q = len(q[0])
     G = Hq // Hkv
@@ -169,9 +185,10 @@ def dense_attention(q, k, v, q_pos0, theta, Hq, Hkv, scale=None):
     out = [[None] * n_q for _ in range(Hq)]
     for h in range(Hq):
         kvh = h // G
-        keys_rot = [rotate(k[kvh][j], j, theta) for j in range(q_pos0 + n_q)]
+        keys_rot = [rotate(k[kvh][j], j, theta, period) for j in range(q_pos0 + n_q)]
         for qi in range(n_q):
             i = q_pos0 + qi
-            o, _ = attend_row(rotate(q[h][qi], i, theta), keys_rot, v[kvh], list(range(i + 1)), scale)
+            o, _ = attend_row(rotate(q[h][qi], i, theta, period), keys_rot, v[kvh], list(range(i + 1)),
+                              scale)
             out[h][qi] = o
     return out

@@ -31,6 +31,7 @@ class Params:
     Hkv: int
     d: int
     scale: float = 0.0  # 0 -> 1/sqrt(d)
+    period: int = 0     # RoPE positions wrap modulo period; 0 = absolute
 
     @property
     def softmax_scale(self) -> float:
@@ -45,7 +46,7 @@ def params_from_workload(w) -> Params:
     return Params(C=w.chunk_size, gs=w.group_size, F=w.n_sink_chunks,
                   L=w.n_recent_chunks, Kc=w.top_chunks, Kg=w.top_groups,
                   n_hf=w.n_hf_pairs, theta=w.rope_theta, Hq=w.n_q_heads,
-                  Hkv=w.n_kv_heads, d=w.head_dim)
+                  Hkv=w.n_kv_heads, d=w.head_dim, period=w.rope_period)
 
 
 # --------------------------------------------------------------------------
@@ -69,16 +70,31 @@ def high_freq_pair_count(d: int, theta: float, C: int) -> int:
     return int(np.count_nonzero(wavelength < C))
 
 
-def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
+def rope_position(pos, period: int = 0) -> np.ndarray:
+    """The position index RoPE is given for position ``pos``.
+
+    xllm-io page, Sec. 5.5 (interaction with long-context positional
+    encoding): the variant that wraps the RoPE position index, p <- p mod
+    65536.  ``period`` = 0 keeps absolute positions.  The wrap is applied to
+    the value itself, also to a block's fractional middle position; callers
+    keep every block inside one period (period % C == 0), so the middle of a
+    block is the middle of its wrapped positions.
+    """
+    pos = np.asarray(pos, dtype=np.float64)
+    return np.mod(pos, float(period)) if period else pos
+
+
+def rope(x: np.ndarray, pos, theta: float, period: int = 0) -> np.ndarray:
     """Rotate x[..., n, d] by R_p at positions pos[n] (may be fractional).
 
     Pair i is (x[i], x[i + d/2]) (half-split layout, reading of the pages'
-    unprinted RoPE); R_p turns it counter-clockwise by p * theta_i.
+    unprinted RoPE); R_p turns it counter-clockwise by p * theta_i, with p
+    the position index of ``rope_position`` (wrapped when period > 0).
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = d // 2
-    ang = np.multiply.outer(np.asarray(pos, dtype=np.float64), rope_inv_freq(d, theta))
+    ang = np.multiply.outer(rope_position(pos, period), rope_inv_freq(d, theta))
     c, s = np.cos(ang), np.sin(ang)
     a, b = x[..., :h], x[..., h:]
     return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
@@ -89,7 +105,8 @@ def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
 # paragraph: closed chunks carry one chunk summary and C/g_s group summaries)
 # --------------------------------------------------------------------------
 
-def block_summaries(k_raw: np.ndarray, size: int, n_hf: int, theta: float) -> np.ndarray:
+def block_summaries(k_raw: np.ndarray, size: int, n_hf: int, theta: float,
+                    period: int = 0) -> np.ndarray:
     """Summaries of consecutive complete blocks of ``size`` tokens.
 
     k_raw [..., n, d] holds raw (pre-RoPE) keys at positions 0..n-1.  For a
@@ -98,17 +115,18 @@ def block_summaries(k_raw: np.ndarray, size: int, n_hf: int, theta: float) -> np
       pairs i <  n_hf: (1/|G|) sum_{j in G} R_j k_j      (rotate, then mean)
       pairs i >= n_hf: R_{p_mid}((1/|G|) sum_{j in G} k_j) (mean, then rotate)
     Only complete blocks are summarised (the pages route over closed chunks).
+    Every R_p takes its position through ``rope_position`` (``period``).
     """
     k_raw = np.asarray(k_raw, dtype=np.float64)
     n, d = k_raw.shape[-2], k_raw.shape[-1]
     h = d // 2
     nb = n // size
     k = k_raw[..., : nb * size, :]
-    rot_mean = rope(k, np.arange(nb * size), theta)
+    rot_mean = rope(k, np.arange(nb * size), theta, period)
     rot_mean = rot_mean.reshape(*k.shape[:-2], nb, size, d).mean(axis=-2)
     raw_mean = k.reshape(*k.shape[:-2], nb, size, d).mean(axis=-2)
     p_mid = np.arange(nb) * size + (size - 1) / 2.0
-    low = rope(raw_mean, p_mid, theta)
+    low = rope(raw_mean, p_mid, theta, period)
     out = low.copy()
     hf = np.r_[np.arange(n_hf), h + np.arange(n_hf)].astype(np.int64)
     out[..., hf] = rot_mean[..., hf]
@@ -118,8 +136,8 @@ def block_summaries(k_raw: np.ndarray, size: int, n_hf: int, theta: float) -> np
 def summaries(k_raw: np.ndarray, n_tokens: int, p: Params):
     """Chunk and group summaries of the first ``n_tokens`` keys."""
     k = np.asarray(k_raw, dtype=np.float64)[..., :n_tokens, :]
-    return (block_summaries(k, p.C, p.n_hf, p.theta),
-            block_summaries(k, p.gs, p.n_hf, p.theta))
+    return (block_summaries(k, p.C, p.n_hf, p.theta, p.period),
+            block_summaries(k, p.gs, p.n_hf, p.theta, p.period))
 
 
 # --------------------------------------------------------------------------
@@ -179,7 +197,7 @@ def unit_rows(q_b: np.ndarray, kvh: int, qpos: np.ndarray, q_pos0: int, p: Param
     (standard GQA).  Returns [G * len(qpos), d]."""
     G = p.Hq // p.Hkv
     raw = np.asarray(q_b[kvh * G:(kvh + 1) * G][:, qpos - q_pos0, :], dtype=np.float64)
-    return rope(raw, qpos, p.theta).reshape(-1, p.d)
+    return rope(raw, qpos, p.theta, p.period).reshape(-1, p.d)
 
 
 def route_unit(rows: np.ndarray, t: int, csum: np.ndarray, gsum: np.ndarray, p: Params) -> dict:
@@ -310,13 +328,13 @@ def attend_given(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, p: Par
     for (b, kvh, t) in units:
         gl = np.asarray(granules[b, kvh, t - t0, : int(count[b, kvh, t - t0])], np.int64)
         tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
-        kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta)
+        kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period)
         vv = np.asarray(v[b, kvh][tok], np.float64)
         qpos = unit_queries(t, q_pos0, n_q, p.C)
         mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
         for hl in range(G):
             h = kvh * G + hl
-            rows = rope(np.asarray(q_raw[b, h, qpos - q_pos0, :], np.float64), qpos, p.theta)
+            rows = rope(np.asarray(q_raw[b, h, qpos - q_pos0, :], np.float64), qpos, p.theta, p.period)
             o, ls = _softmax_attend(rows, kk, vv, mask, p.softmax_scale)
             out[b, h, qpos - q_pos0] = o
             lse[b, h, qpos - q_pos0] = ls
@@ -335,9 +353,9 @@ def dense_causal(q_raw, q_pos0: int, n_q: int, k_raw, v, p: Params, heads=None, 
     qi = np.arange(n_q) if q_index is None else np.asarray(q_index)
     nk = q_pos0 + int(qi.max()) + 1
     for b in range(B):
-        qrot = rope(q[b][:, qi, :], q_pos0 + qi, p.theta)
+        qrot = rope(q[b][:, qi, :], q_pos0 + qi, p.theta, p.period)
         for kvh in range(p.Hkv):
-            kk = rope(np.asarray(k_raw[b, kvh][:nk], np.float64), np.arange(nk), p.theta)
+            kk = rope(np.asarray(k_raw[b, kvh][:nk], np.float64), np.arange(nk), p.theta, p.period)
             vv = np.asarray(v[b, kvh][:nk], np.float64)
             mask = np.arange(nk)[None, :] <= (q_pos0 + qi)[:, None]
             for hl in range(G):

@@ -324,6 +324,116 @@ def test_value_shift_and_band_pattern():
     np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
 
 
+# ------------------------------------- wrapped RoPE positions (Sec. 5.5) ----
+# xllm-io page, Sec. 5.5: a variant feeds RoPE the position index modulo
+# 65536.  Every position that enters a rotation (queries, keys, and the
+# blocks' middle positions of the Mixed-RoPE summaries) is wrapped; causality
+# and routing keep absolute positions.
+
+
+def _prerotate(x, pos, period, theta):
+    """Turn pair i of x[..., n, d] by -period * floor(pos / period) * theta_i,
+    done as a complex product (independent of the oracle's rope)."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    freq = float(theta) ** (-2.0 * np.arange(h) / d)
+    shift = -period * np.floor(np.asarray(pos, np.float64) / period)
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * np.multiply.outer(shift, freq))
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rope_period=32),
+    dict(rope_period=16, top_groups=0),
+    dict(rope_period=24, q_pos0=37, n_q=59, n_ctx=96),
+])
+def test_wrapped_pipeline_matches_brute_force(kw):
+    """Summaries, routes and outputs with wrapped positions: the vectorised
+    oracle (np.mod of every position, fractional middles included) against
+    the brute force (floor-based wrap; a block's middle taken from its
+    wrapped first position)."""
+    w = _tiny_workload(**kw)
+    q, k, v = W.make_inputs(w, seed=11)
+    p, rt, out, _ = _oracle_pipeline(w, q, k, v)
+    for b in range(w.batch):
+        bout, routes = brute.routed_attention(
+            q[b].tolist(), k[b].tolist(), v[b].tolist(), w.q_pos0, w.chunk_size, w.group_size,
+            w.n_sink_chunks, w.n_recent_chunks, w.top_chunks, w.top_groups, w.n_hf_pairs,
+            w.rope_theta, w.n_q_heads, w.n_kv_heads, period=w.rope_period)
+        for (kvh, t), (selc, selg) in routes.items():
+            info = rt["info"][(b, kvh, t)]
+            assert info["sel_chunks"] == selc and info["sel_groups"] == selg
+        np.testing.assert_allclose(out[b], np.array(bout), atol=1e-12)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rope_period=32),
+    dict(rope_period=64, chunk_size=16, group_size=4, n_ctx=300, kv_cap=304, n_q=300,
+         head_dim=16, n_hf_pairs=3, top_chunks=3, top_groups=5),
+])
+def test_wrap_equals_prerotated_absolute(kw):
+    """R_{p mod P} = R_p R_{-P floor(p/P)}: wrapping the positions equals
+    absolute positions applied to inputs turned back by whole periods.  A
+    block lies inside one period, so its raw mean is turned by the same
+    angle as its tokens; summaries, routes, outputs and LSE must agree."""
+    w = _tiny_workload(**kw)
+    q, k, v = W.make_inputs(w, seed=12)
+    P_ = w.rope_period
+    qpos = w.q_pos0 + np.arange(w.n_q)
+    q2 = _prerotate(q, qpos, P_, w.rope_theta)
+    k2 = _prerotate(k, np.arange(w.kv_cap), P_, w.rope_theta)
+    p, rt, out, lse = _oracle_pipeline(w, q, k, v)
+    w0 = w.scaled(rope_period=0)
+    p0, rt0, out0, lse0 = _oracle_pipeline(w0, q2, k2, v)
+    cs, gsum = R.summaries(k, w.n_ctx, p)
+    cs0, gsum0 = R.summaries(k2, w.n_ctx, p0)
+    np.testing.assert_allclose(cs, cs0, atol=1e-12)
+    np.testing.assert_allclose(gsum, gsum0, atol=1e-12)
+    np.testing.assert_array_equal(rt["granules"], rt0["granules"])
+    np.testing.assert_allclose(out, out0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse0, atol=1e-12)
+    # and the wrap matters: absolute positions on the raw inputs differ
+    _, _, out_abs, _ = _oracle_pipeline(w0, q, k, v)
+    assert np.abs(out_abs - out).max() > 1e-3
+
+
+def test_wrap_beyond_context_is_absolute():
+    """A period at or beyond every position leaves the path unchanged."""
+    w = _tiny_workload(rope_period=96)
+    q, k, v = W.make_inputs(w, seed=13)
+    _, rt, out, lse = _oracle_pipeline(w, q, k, v)
+    _, rt0, out0, lse0 = _oracle_pipeline(w.scaled(rope_period=0), q, k, v)
+    np.testing.assert_array_equal(rt["granules"], rt0["granules"])
+    assert np.array_equal(out, out0) and np.array_equal(lse, lse0)
+
+
+def test_wrapped_dense_pattern_by_hand():
+    """Dense causal attention with wrapped positions: a query and a key in
+    the same period see their true distance; a key one period back is seen
+    at the same in-period offset as a key of the query's own period."""
+    d, theta, P_ = 8, 1e4, 16
+    p = R.Params(C=8, gs=4, F=0, L=0, Kc=0, Kg=0, n_hf=0, theta=theta, Hq=1, Hkv=1, d=d,
+                 period=P_)
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((1, 1, 40, d))
+    k = np.tile(rng.standard_normal(d), (1, 1, 40, 1))  # one key vector at every slot
+    v = rng.standard_normal((1, 1, 40, d))
+    out, lse = R.dense_causal(q, 0, 40, k, v, p)
+    # closed form for row i: logit_j = q_i . R_{(j mod P) - (i mod P)} k / sqrt(d)
+    for i in (3, 17, 39):
+        z = q[0, 0, i, : d // 2] + 1j * q[0, 0, i, d // 2:]
+        kz = k[0, 0, 0, : d // 2] + 1j * k[0, 0, 0, d // 2:]
+        freq = theta ** (-2.0 * np.arange(d // 2) / d)
+        lg = np.array([np.real(np.sum(np.conj(z) * kz *
+                                      np.exp(1j * ((j % P_) - (i % P_)) * freq)))
+                       for j in range(i + 1)]) / math.sqrt(d)
+        wts = np.exp(lg - lg.max())
+        ref = (wts[:, None] * v[0, 0, : i + 1]).sum(0) / wts.sum()
+        np.testing.assert_allclose(out[0, 0, i], ref, atol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, i], lg.max() + math.log(wts.sum()), atol=1e-12)
+
+
 # ---------------------------------------------------------------- Eq. 2 ----
 
 @pytest.mark.parametrize("kw", [{}, dict(top_groups=0), dict(q_pos0=21, n_q=75), dict(n_recent_chunks=0)])

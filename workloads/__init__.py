@@ -57,6 +57,7 @@ class Workload:
     planted_per_q_head: int = 0   # decode: planted matches per (batch, query head)
     key_rank: int = 0
     seed_offset: int = 0
+    rope_period: int = 0  # RoPE positions wrap modulo this (0 = absolute)
 
     @property
     def group_ratio(self) -> int:
