@@ -47,7 +47,8 @@ class hga_config(ctypes.Structure):
                 ("top_chunks", ctypes.c_int32), ("top_groups", ctypes.c_int32),
                 ("n_hf_pairs", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float)]
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("rope_period", ctypes.c_int64)]
 
 
 class hga_tier_stats(ctypes.Structure):
@@ -71,6 +72,7 @@ class Config:
     n_kv_heads: int
     rope_theta: float
     softmax_scale: float = 0.0
+    rope_period: int = 0  # RoPE positions wrap modulo this (0 = absolute)
 
     @classmethod
     def from_workload(cls, w, **over) -> "Config":
@@ -78,7 +80,7 @@ class Config:
                   n_sink_chunks=w.n_sink_chunks, n_recent_chunks=w.n_recent_chunks,
                   top_chunks=w.top_chunks, top_groups=w.top_groups, n_hf_pairs=w.n_hf_pairs,
                   head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
-                  rope_theta=w.rope_theta)
+                  rope_theta=w.rope_theta, rope_period=w.rope_period)
         kw.update(over)
         return cls(**kw)
 
@@ -86,7 +88,8 @@ class Config:
         return hga_config(self.chunk_size, self.group_size, self.n_sink_chunks,
                           self.n_recent_chunks, self.top_chunks, self.top_groups,
                           self.n_hf_pairs, self.head_dim, self.n_q_heads, self.n_kv_heads,
-                          float(self.rope_theta), float(self.softmax_scale))
+                          float(self.rope_theta), float(self.softmax_scale),
+                          int(self.rope_period))
 
     def n_query_chunks(self, q_pos0: int, n_q: int) -> int:
         if n_q <= 0:

@@ -34,6 +34,7 @@ hga_status check_config(const hga_config* c) {
   if (c->n_hf_pairs < 0 || c->n_hf_pairs > c->head_dim / 2) return HGA_ERR_INVALID_ARGUMENT;
   if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return HGA_ERR_INVALID_ARGUMENT;
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return HGA_ERR_INVALID_ARGUMENT;
+  if (c->rope_period < 0 || c->rope_period % c->chunk_size != 0) return HGA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return HGA_ERR_UNSUPPORTED;
   if (c->chunk_size > 64) return HGA_ERR_UNSUPPORTED;
   return HGA_OK;
@@ -79,6 +80,7 @@ hga_status hga::make_geometry(const hga_config* c, hga_dtype dt, int32_t batch, 
   g.bf16 = dt == HGA_BF16;
   for (int i = 0; i < hga::kMaxHalfDim; ++i)
     g.rope.f[i] = i < g.d / 2 ? std::pow(c->rope_theta, -2.0 * i / g.d) : 0.0;
+  g.rope.period = c->rope_period;
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   if (units * 64 > (int64_t{1} << 31) - 1) return HGA_ERR_UNSUPPORTED;
   return HGA_OK;

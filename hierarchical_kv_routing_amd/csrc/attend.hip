@@ -453,10 +453,11 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   const int rend = (r0 + kRows) < w.R ? (r0 + kRows) : w.R;
   const int nqt = (rend - 1) / p.G - q_first + 1;
   float2* cs = reinterpret_cast<float2*>(smem);
+  const int64_t q0 = rope_base(p.rope, w.qlo) + q_first;  // the unit's queries share one chunk
   for (int i = threadIdx.x; i < nqt * H; i += NW * 64) {
     const int qi = i / H, pr = i - qi * H;
     float c, s;
-    rope_cs(static_cast<double>(w.qlo + q_first + qi), p.rope.f[pr], c, s);
+    rope_cs(static_cast<double>(q0 + qi), p.rope.f[pr], c, s);
     cs[i] = make_float2(c, s);
   }
   __syncthreads();
@@ -670,6 +671,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   const int qloc = row_ok ? row / p.G : 0;
   const int hl = row_ok ? row - qloc * p.G : 0;
   const int qpos = static_cast<int>(w.qlo) + qloc;
+  const double qrot = static_cast<double>(rope_base(p.rope, w.qlo) + qloc);
   float q[D];
   {
     const float* src = static_cast<const float*>(p.q) +
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     for (int i = 0; i < H; ++i) {
       const float a = row_ok ? src[i] : 0.f, b = row_ok ? src[i + H] : 0.f;
       float c, s;
-      rope_cs(static_cast<double>(qpos), p.rope.f[i], c, s);
+      rope_cs(qrot, p.rope.f[i], c, s);
       q[i] = (a * c - b * s) * p.scale_log2;
       q[i + H] = (a * s + b * c) * p.scale_log2;
     }

@@ -87,6 +87,13 @@ __device__ __forceinline__ void rope_cs(double pos, double freq, float& c, float
   sincosf(static_cast<float>(r), &s, &c);
 }
 
+// Rotation position of the token at absolute position p: p mod period when
+// positions wrap.  Periods are multiples of C, so a caller wraps the first
+// position of a chunk or group once and adds in-block offsets to it.
+__device__ __forceinline__ int64_t rope_base(const RopeFreqs& r, int64_t p) {
+  return r.period > 0 ? p % r.period : p;
+}
+
 // Larger float -> larger unsigned key (total order on finite values).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -12,9 +12,11 @@ namespace hga {
 
 constexpr int kMaxHalfDim = 64;  // d <= 128
 
-// theta_i = rope_theta^(-2i/d), computed once on the host in double.
+// theta_i = rope_theta^(-2i/d), computed once on the host in double, and
+// the period positions wrap at before rotation (0 = absolute positions).
 struct RopeFreqs {
   double f[kMaxHalfDim];
+  int64_t period;
 };
 
 // A validated call shape.  Built by api.cpp, read by the launchers.

@@ -88,10 +88,11 @@ __device__ __forceinline__ Unit make_unit(const RouteParams& p, int64_t u) {
 // cos/sin of every (query of the unit, pair) into LDS.
 __device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit& w, float2* cs) {
   const int h = p.d >> 1;
+  const int64_t q0 = rope_base(p.rope, w.qlo);  // a unit's queries share one chunk
   for (int i = threadIdx.x; i < w.nq * h; i += blockDim.x) {
     const int qi = i / h, pr = i - qi * h;
     float c, s;
-    rope_cs(static_cast<double>(w.qlo + qi), p.rope.f[pr], c, s);
+    rope_cs(static_cast<double>(q0 + qi), p.rope.f[pr], c, s);
     cs[i] = make_float2(c, s);
   }
 }

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
     const int64_t g0 = c0 + static_cast<int64_t>(g) * p.gs;
     const int64_t g1 = g0 + p.gs;
     const int64_t jend = g1 < tend ? g1 : tend;
+    const int64_t gw = rope_base(p.rope, g0);  // rotation position of token g0
     float sx = 0.f, sy = 0.f;
     if (active) {
       for (int64_t j = g0; j < jend; ++j) {
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
         const float x = load1<BF16>(p.k_raw, e);
         const float y = load1<BF16>(p.k_raw, e + h);
         float c, s;
-        rope_cs(static_cast<double>(j), freq, c, s);
+        rope_cs(static_cast<double>(gw + (j - g0)), freq, c, s);
         const float rx = x * c - y * s;
         const float ry = x * s + y * c;
         if (p.k_rot != nullptr && j >= p.tok_begin) {
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
         float ox = sx / inv_n, oy = sy / inv_n;
         if (!high) {
           float c, s;
-          rope_cs(static_cast<double>(g0) + 0.5 * (p.gs - 1), freq, c, s);
+          rope_cs(static_cast<double>(gw) + 0.5 * (p.gs - 1), freq, c, s);
           const float mx = ox, my = oy;
           ox = mx * c - my * s;
           oy = mx * s + my * c;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
     float ox = sx / n, oy = sy / n;
     if (!high) {
       float c, s;
-      rope_cs(static_cast<double>(c0) + 0.5 * (p.C - 1), freq, c, s);
+      rope_cs(static_cast<double>(rope_base(p.rope, c0)) + 0.5 * (p.C - 1), freq, c, s);
       const float mx = ox, my = oy;
       ox = mx * c - my * s;
       oy = mx * s + my * c;

@@ -37,6 +37,11 @@
  * RoPE: theta_i = rope_theta^(-2i/d) for pair i < d/2; pair i is the
  * elements (i, i + d/2) (half-split layout); R_p turns a pair by p*theta_i.
  * Angles are formed in double precision and reduced before an f32 sincos.
+ * With rope_period = P > 0 (the wrapped-position variant of the xllm-io
+ * page, Sec. 5.5, P = 65536 there) every rotation uses p mod P instead of p:
+ * queries, keys and the middle positions of summaries.  P must be a multiple
+ * of C, so no chunk or group straddles a wrap.  Causality, chunk indices and
+ * routing keep absolute positions.
  *
  * Ownership: the caller owns every buffer and allocates it; the library never
  * allocates device memory and keeps no mutable global state apart from a
@@ -88,6 +93,7 @@ typedef struct hga_config {
   int32_t n_kv_heads;      /* Hkv                                                 */
   double rope_theta;       /* RoPE base, > 0                                      */
   float softmax_scale;     /* 0 => 1/sqrt(d) (Eq. 1)                              */
+  int64_t rope_period;     /* 0, or P: RoPE sees positions mod P (Sec. 5.5); P % C == 0 */
 } hga_config;
 
 /*

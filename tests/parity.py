@@ -109,7 +109,7 @@ def check_summaries(run: GpuRun, k, slabs=None):
         dc = np.abs(csum[b, h, : oc.shape[0]] - oc).max(initial=0.0)
         dg = np.abs(gsum[b, h, : og.shape[0]] - og).max(initial=0.0)
         assert dc <= SUM_ATOL and dg <= SUM_ATOL, (b, h, dc, dg)
-        ref = R.rope(kk[:n], np.arange(n), p.theta)
+        ref = R.rope(kk[:n], np.arange(n), p.theta, p.period)
         err = np.abs(krot[b, h, :n] - ref)
         if w.dtype == "bf16":
             assert np.all(err <= 2.0 ** -8 * np.abs(ref) + SUM_ATOL), (b, h, err.max())

@@ -32,6 +32,34 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of hga_config and hga_tier_stats have the C
+    compiler's size and field offsets for include/hga.h."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    fields = {"hga_config": [f for f, _ in H.hga_config._fields_],
+              "hga_tier_stats": [f for f, _ in H.hga_tier_stats._fields_]}
+    lines = []
+    for st, names in fields.items():
+        lines.append(f'  printf("%zu\\n", sizeof({st}));')
+        lines += [f'  printf("%zu\\n", offsetof({st}, {n}));' for n in names]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdint.h>\n#include <stdio.h>\n'
+                   '#include "hga.h"\nint main(void) {\n' + "\n".join(lines) + "\n  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = []
+    for cls in (H.hga_config, H.hga_tier_stats):
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, f).offset for f, _ in cls._fields_]
+    assert got == want
+
+
 def test_status_strings(lib):
     for code, name in H._STATUS.items():
         assert lib.hga_status_string(code).decode() == name
@@ -63,6 +91,8 @@ def _route(lib, cfg, dtype=1, B=1, q=16, q_pos0=0, n_q=64, cs=16, gs=16, cap=64,
     (dict(rope_theta=0.0), 1),
     (dict(rope_theta=float("nan")), 1),
     (dict(softmax_scale=-1.0), 1),
+    (dict(rope_period=-64), 1),
+    (dict(rope_period=100), 1),        # wrap period not a multiple of C
     (dict(head_dim=96), 2),            # d in {64, 128}
     (dict(chunk_size=128, group_size=16), 2),
 ])

@@ -41,15 +41,24 @@ def test_decode_64k_full():
     P.check_attention(run, q, k, v, units)
 
 
-@pytest.mark.parametrize("base", ["chunk_only", "group"])
+# "group_wrap64k": RoPE positions wrapped modulo 65536 (xllm-io page,
+# Sec. 5.5 variant) over 131072 tokens, through the warm tier (a device
+# cache of 8192 granules), so the second half of the sequence rotates as
+# the first.
+@pytest.mark.parametrize("base", ["chunk_only", "group", "group_wrap64k"])
 def test_host_tiered_128k_full(base):
     import torch
-    w = W.HOST_TIERED_CHUNK if base == "chunk_only" else W.HOST_TIERED_GROUP
+    w = {"chunk_only": W.HOST_TIERED_CHUNK, "group": W.HOST_TIERED_GROUP,
+         "group_wrap64k": W.HOST_TIERED_GROUP.scaled(rope_period=65536)}[base]
+    cache = 8192 if w.rope_period else 0
     q, k, v = P.make_inputs_parallel(w)
     print(f"[gpu] host tier 128k {base}: inputs ready", flush=True)
     run = P.GpuRun(w, q, k, v)
     slots = 16384
-    out, lse, stats = run_host_tier(run, max_window_chunks=64, slots=slots, threads=8)
+    if w.rope_period:
+        P.check_summaries(run, k, slabs=[(0, 2)])
+    out, lse, stats = run_host_tier(run, max_window_chunks=64, slots=slots, threads=8,
+                                    cache_slots=cache)
     print(f"[gpu] host tier 128k {base}: {stats}", flush=True)
     same = bool(torch.equal(out, run.out))
     assert same, "host tier differs from the device-resident path"

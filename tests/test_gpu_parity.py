@@ -140,6 +140,38 @@ def test_edge_cases(name):
     P.check_attention(run, q, k, v, units)
 
 
+# Wrapped RoPE positions (xllm-io page, Sec. 5.5 variant; period a multiple
+# of C).  Small periods make oracle-sized contexts wrap several times; the f32
+# case runs the f32 attention kernel, the ragged start a unit that begins
+# mid-chunk, and the decode case a query whose wrapped position is 0.
+WRAP = {
+    "f32_tiny_p256": _small(W.TINY_F32, rope_period=256),
+    "qwen3_ragged_p512": _small(W.QWEN3_PREFILL, n_ctx=2500, kv_cap=2560, n_q=2500, planted=16,
+                                rope_period=512),
+    "qwen3_ragged_start_p192": _small(W.QWEN3_PREFILL, n_ctx=1011, kv_cap=1024, q_pos0=200,
+                                      n_q=811, planted=8, rope_period=192),
+    "decode_p4096": _small(W.DECODE_64K, batch=3, n_ctx=20481, kv_cap=20544, q_pos0=20480,
+                           rope_period=4096),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WRAP))
+def test_rope_wrap(name):
+    w = WRAP[name]
+    q, k, v = _inputs(w, seed=5)
+    print(f"[gpu] rope wrap {name}: {w}", flush=True)
+    run = P.GpuRun(w, q, k, v)
+    P.check_summaries(run, k, slabs=[(0, 0), (w.batch - 1, w.n_kv_heads - 1)])
+    units = P.all_units(w)
+    orc = P.oracle_route(run, q, k, units)
+    exact, near = P.compare_routes(run, orc, units)
+    assert near <= max(2, len(units) // 50)
+    P.check_attention(run, q, k, v, units)
+    # the period reaches the kernels: absolute positions give other outputs
+    flat = P.GpuRun(w.scaled(rope_period=0), q, k, v)
+    assert not np.array_equal(flat.np("out"), run.np("out"))
+
+
 def test_empty_call_is_noop():
     w = _small(W.SMALLLM_PREFILL, batch=1, n_q_heads=1, n_kv_heads=1, n_ctx=128, kv_cap=128,
                n_q=128, planted=0)
