@@ -78,8 +78,7 @@ hga_status hga::make_geometry(const hga_config* c, hga_dtype dt, int32_t batch, 
   g.gmax = max_granules(c);
   g.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt(static_cast<float>(g.d));
   g.bf16 = dt == HGA_BF16;
-  for (int i = 0; i < hga::kMaxHalfDim; ++i)
-    g.rope.f[i] = i < g.d / 2 ? std::pow(c->rope_theta, -2.0 * i / g.d) : 0.0;
+  for (int b = 0; b < 6; ++b) g.rope.step[b] = std::pow(c->rope_theta, -2.0 * (1 << b) / g.d);
   g.rope.period = c->rope_period;
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   if (units * 64 > (int64_t{1} << 31) - 1) return HGA_ERR_UNSUPPORTED;

@@ -457,7 +457,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   for (int i = threadIdx.x; i < nqt * H; i += NW * 64) {
     const int qi = i / H, pr = i - qi * H;
     float c, s;
-    rope_cs(static_cast<double>(q0 + qi), p.rope.f[pr], c, s);
+    rope_cs(static_cast<double>(q0 + qi), rope_freq(p.rope, pr), c, s);
     cs[i] = make_float2(c, s);
   }
   __syncthreads();
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     for (int i = 0; i < H; ++i) {
       const float a = row_ok ? src[i] : 0.f, b = row_ok ? src[i + H] : 0.f;
       float c, s;
-      rope_cs(qrot, p.rope.f[i], c, s);
+      rope_cs(qrot, rope_freq(p.rope, i), c, s);
       q[i] = (a * c - b * s) * p.scale_log2;
       q[i + H] = (a * s + b * c) * p.scale_log2;
     }
@@ -762,22 +762,42 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
   const int row = static_cast<int>(gr - u * p.Rcap);
   const AUnit w = make_aunit(p, u);
   if (row >= w.R) return;
-  float m = kNegBig;
-  for (int s = 0; s < p.splits; ++s) {
-    if (s * p.keys_per_split >= w.nkeys) break;
-    m = fmaxf(m, p.ws_ml[((w.slot * p.splits + s) * p.Rcap + row) * 2]);
-  }
-  float l = 0.f;
-  float acc[D / 64 > 0 ? D / 64 : 1];
+  // Splits that hold keys of this unit; their partials are read eight at a
+  // time, every load of a group issued before any is used.
+  int ns = (w.nkeys + p.keys_per_split - 1) / p.keys_per_split;
+  ns = ns < p.splits ? ns : p.splits;
+  constexpr int kG = 8;
+  constexpr int kD = D / 64 > 0 ? D / 64 : 1;
+  float m = kNegBig, l = 0.f;
+  float acc[kD];
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) acc[i] = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    if (s * p.keys_per_split >= w.nkeys) break;
-    const int64_t pr = (w.slot * p.splits + s) * p.Rcap + row;
-    const float sc = exp2f(p.ws_ml[pr * 2] - m);
-    l += p.ws_ml[pr * 2 + 1] * sc;
+  for (int i = 0; i < kD; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kG) {
+    float2 ml[kG];
+    float o[kG][kD];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += p.ws_o[pr * D + lane + 64 * i] * sc;
+    for (int j = 0; j < kG; ++j) {
+      const bool on = s0 + j < ns;
+      const int64_t pr = (w.slot * p.splits + (on ? s0 + j : 0)) * p.Rcap + row;
+      ml[j] = on ? *reinterpret_cast<const float2*>(p.ws_ml + pr * 2) : make_float2(kNegBig, 0.f);
+#pragma unroll
+      for (int i = 0; i < kD; ++i) o[j][i] = on ? p.ws_o[pr * D + lane + 64 * i] : 0.f;
+    }
+    float mn = m;
+#pragma unroll
+    for (int j = 0; j < kG; ++j) mn = fmaxf(mn, ml[j].x);
+    const float c = exp2f(m - mn);
+    l *= c;
+#pragma unroll
+    for (int i = 0; i < kD; ++i) acc[i] *= c;
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const float sc = exp2f(ml[j].x - mn);
+      l += ml[j].y * sc;
+#pragma unroll
+      for (int i = 0; i < kD; ++i) acc[i] += o[j][i] * sc;
+    }
+    m = mn;
   }
   const int qloc = row / p.G, hl = row - qloc * p.G;
   const int64_t orow =
@@ -800,6 +820,19 @@ int64_t max_keys(const Geometry& g, bool dense) {
   const int64_t causal = (qlast / g.gs + 1) * g.gs;
   if (dense) return causal;
   return std::min<int64_t>(static_cast<int64_t>(g.gmax) * g.gs, causal);
+}
+
+// Compute units of the current device (queried once per device).
+int64_t device_cus() {
+  static int cus[16] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    cus[dev] = n > 0 ? n : 256;
+  }
+  return cus[dev];
 }
 
 Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
@@ -827,8 +860,17 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   pl.splits = 1;
   pl.kps = static_cast<int>(keys);
   if (allow_split && wgs < 512 && keys > 256) {
-    int64_t sp = (keys + 127) / 128;
-    const int64_t want = (1024 + wgs - 1) / wgs;
+    int64_t sp, want;
+    if (g.bf16) {
+      // About one work item per CU (the bf16 kernel keeps one workgroup per
+      // CU, so a second item per workgroup would run after the first), each
+      // at least one LDS stage of keys.
+      sp = (keys + kTK - 1) / kTK;
+      want = (device_cus() + wgs - 1) / wgs;
+    } else {
+      sp = (keys + 127) / 128;
+      want = (1024 + wgs - 1) / wgs;
+    }
     if (sp > want) sp = want;
     if (sp > 1) {
       pl.kps = static_cast<int>(((keys + sp - 1) / sp + kTK - 1) / kTK * kTK);

@@ -87,6 +87,15 @@ __device__ __forceinline__ void rope_cs(double pos, double freq, float& c, float
   sincosf(static_cast<float>(r), &s, &c);
 }
 
+// theta_i as the product of the factors of the set bits of i (fixed order,
+// so every kernel forms the same value).
+__device__ __forceinline__ double rope_freq(const RopeFreqs& r, int i) {
+  double f = 1.0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) f = ((i >> b) & 1) ? f * r.step[b] : f;
+  return f;
+}
+
 // Rotation position of the token at absolute position p: p mod period when
 // positions wrap.  Periods are multiples of C, so a caller wraps the first
 // position of a chunk or group once and adds in-block offsets to it.

@@ -12,10 +12,12 @@ namespace hga {
 
 constexpr int kMaxHalfDim = 64;  // d <= 128
 
-// theta_i = rope_theta^(-2i/d), computed once on the host in double, and
-// the period positions wrap at before rotation (0 = absolute positions).
+// RoPE frequencies theta_i = rope_theta^(-2i/d) for i < d/2 <= 64, kept as
+// the six factors step[b] = rope_theta^(-2^(b+1)/d) (host, double): a lane
+// forms theta_i as the product of the factors of the set bits of i, with no
+// memory access.  period: positions wrap modulo it before rotation (0 = no).
 struct RopeFreqs {
-  double f[kMaxHalfDim];
+  double step[6];
   int64_t period;
 };
 

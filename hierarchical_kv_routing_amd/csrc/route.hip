@@ -20,9 +20,13 @@
 //    every middle chunk, selects, scores the groups and writes the lists.
 //    Units run longest (largest t) first.
 //  * segmented (few units with long middle contexts, e.g. a decode step):
-//    score_kernel spreads each unit's middle chunks over many workgroups and
-//    writes raw scores to the workspace; the fused kernel then runs with
-//    FROM_WS and skips chunk scoring.
+//    score_kernel spreads each unit's middle chunks over many workgroups;
+//    each scores its segment and keeps the segment's own top-K_c (same order:
+//    score, then lower index), which it writes to the workspace.  The fused
+//    kernel then runs with FROM_WS: it selects the unit's top-K_c among the
+//    segments' survivors (every chunk of the global top-K_c is in its
+//    segment's top-K_c, so the result is the same set) and goes on with the
+//    group phase.
 #include "hga_device.h"
 
 namespace hga {
@@ -45,7 +49,9 @@ struct RouteParams {
   int32_t* gidx;
   int32_t* gran;
   int32_t* gcnt;
-  float* ws;  // segmented scores [unit][ws_stride]
+  // segmented: per unit, nseg*Kc segment winners' keys then their middle
+  // chunk offsets (both 32-bit words); ws_stride = 2*nseg*Kc
+  uint32_t* ws;
   int64_t ws_stride;
   int64_t q_pos0, n_q, t0, nqc, nchunk_cap, ngroup_cap;
   int B, Hq, Hkv, G, d, C, gs, r, F, L, Kc, Kg, gmax;
@@ -63,11 +69,15 @@ struct Unit {
 // that units sharing a summary table stay on the same XCD's L2.
 __device__ __forceinline__ Unit make_unit(const RouteParams& p, int64_t u) {
   Unit w;
-  const int64_t bh = static_cast<int64_t>(p.B) * p.Hkv;
-  const int64_t trel = p.nqc - 1 - u / bh;
-  const int64_t rem = u % bh;
-  w.b = static_cast<int>(rem / p.Hkv);
-  w.kvh = static_cast<int>(rem % p.Hkv);
+  // units < 2^31 (checked on the host): 32-bit division
+  const uint32_t bh = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.Hkv);
+  const uint32_t u32 = static_cast<uint32_t>(u);
+  const uint32_t q = u32 / bh;
+  const uint32_t rem = u32 - q * bh;
+  const int64_t trel = p.nqc - 1 - static_cast<int64_t>(q);
+  const uint32_t bq = rem / static_cast<uint32_t>(p.Hkv);
+  w.b = static_cast<int>(bq);
+  w.kvh = static_cast<int>(rem - bq * static_cast<uint32_t>(p.Hkv));
   w.t = p.t0 + trel;
   const int64_t c0 = w.t * p.C;
   w.qlo = c0 > p.q_pos0 ? c0 : p.q_pos0;
@@ -92,7 +102,7 @@ __device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit
   for (int i = threadIdx.x; i < w.nq * h; i += blockDim.x) {
     const int qi = i / h, pr = i - qi * h;
     float c, s;
-    rope_cs(static_cast<double>(q0 + qi), p.rope.f[pr], c, s);
+    rope_cs(static_cast<double>(q0 + qi), rope_freq(p.rope, pr), c, s);
     cs[i] = make_float2(c, s);
   }
 }
@@ -101,39 +111,59 @@ __device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit
 // (16x16x32 layout: lane -> row lane%16, d slots ks*32 + 8*(lane/16) + i).
 // Rows past the unit's last row repeat the last row, which leaves every max
 // unchanged.  Row r of a unit is (query r / G, head r % G).
+__device__ __forceinline__ int row_of_lane(const Unit& w, int rbase, int blk) {
+  const int r = rbase + blk * 16 + (threadIdx.x & 15);
+  return r < w.R ? r : w.R - 1;
+}
+
+// Raw query elements of one row block (issued early, rotated later).
+template <bool BF16, int KS>
+__device__ __forceinline__ void load_row_raw(const RouteParams& p, const Unit& w, int r,
+                                             float (&x)[KS][8]) {
+  const int sub = (threadIdx.x & 63) >> 4;
+  const int qi = r / p.G;
+  const int hl = r - qi * p.G;
+  const int64_t base =
+      ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0)) * p.d;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) load8<BF16>(p.q, base + ks * 32 + sub * 8, x[ks]);
+}
+
+// Rotates one row block's raw elements with the unit's RoPE table and splits
+// them into the bf16 hi / lo A operands.
+template <int KS>
+__device__ __forceinline__ void rotate_split(const RouteParams& p, int r, const float2* cs,
+                                             float (&x)[KS][8], Pack8 (&ahi)[KS], Pack8 (&alo)[KS]) {
+  const int sub = (threadIdx.x & 63) >> 4;
+  const int h = p.d >> 1;
+  const int qi = r / p.G;
+#pragma unroll
+  for (int ks = 0; ks < KS / 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float2 t = cs[qi * h + ks * 32 + sub * 8 + i];
+      const float a = x[ks][i], b = x[ks + KS / 2][i];
+      x[ks][i] = a * t.x - b * t.y;
+      x[ks + KS / 2][i] = a * t.y + b * t.x;
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(x[ks][i], ahi[ks].h[i], alo[ks].h[i]);
+  }
+}
+
 template <bool BF16, int KS, int NB>
 __device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, int rbase,
                                           const float2* cs, Pack8 (&ahi)[NB][KS],
                                           Pack8 (&alo)[NB][KS]) {
-  const int lane = threadIdx.x & 63;
-  const int h = p.d >> 1;
-  const int sub = lane >> 4;
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    int r = rbase + blk * 16 + (lane & 15);
-    if (r >= w.R) r = w.R - 1;
-    const int qi = r / p.G;
-    const int hl = r - qi * p.G;
-    const int64_t base =
-        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0)) * p.d;
+    const int r = row_of_lane(w, rbase, blk);
     float x[KS][8];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load8<BF16>(p.q, base + ks * 32 + sub * 8, x[ks]);
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 t = cs[qi * h + ks * 32 + sub * 8 + i];
-        const float a = x[ks][i], b = x[ks + KS / 2][i];
-        x[ks][i] = a * t.x - b * t.y;
-        x[ks + KS / 2][i] = a * t.y + b * t.x;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(x[ks][i], ahi[blk][ks].h[i], alo[blk][ks].h[i]);
-    }
+    load_row_raw<BF16, KS>(p, w, r, x);
+    rotate_split<KS>(p, r, cs, x, ahi[blk], alo[blk]);
   }
 }
 
@@ -214,11 +244,14 @@ __device__ __forceinline__ void score_staged(int n, int d, RowPtr row, bool has_
   }
 }
 
+constexpr int kRankMax = 512;  // rank_select: at most one candidate per thread
+
 struct SelScratch {
   int hist[256];
   int wsum[16];
   int bcast[4];
   uint64_t cand[128];
+  __attribute__((aligned(16))) uint64_t rk[kRankMax];
 };
 
 // 64-bit selection key: the score's order key above the inverted index, so
@@ -274,6 +307,38 @@ __device__ __forceinline__ void wave_emit_ascending(uint64_t top, int k, int* ou
   if (lane < k) out[lane] = static_cast<int>(~static_cast<uint32_t>(v[0]));
 }
 
+// Top-k for k < n <= blockDim.x: every thread ranks one key against all n
+// (broadcast LDS reads, eight keys per step; the list is padded with zero
+// keys, which rank below every real key); the k of rank < k are compacted
+// in index order with wave ballots.  Same result as block_select.
+// Block-wide.
+__device__ __forceinline__ int rank_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int n8 = (n + 7) & ~7;
+  uint64_t mine = 0;
+  if (tid < n) mine = sel_key(keys[tid], tid);
+  if (tid < n8) s.rk[tid] = mine;
+  __syncthreads();
+  int rank = 0;
+  if (tid < n) {
+    const ulonglong2* r2 = reinterpret_cast<const ulonglong2*>(s.rk);
+    for (int j = 0; j < n8 / 2; j += 4) {
+      const ulonglong2 a = r2[j], b = r2[j + 1], c = r2[j + 2], d = r2[j + 3];
+      rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) +
+              (c.y > mine) + (d.x > mine) + (d.y > mine);
+    }
+  }
+  const bool take = tid < n && rank < k;
+  const uint64_t m = __ballot(take);
+  if (lane == 0) s.wsum[wave] = __popcll(m);
+  __syncthreads();
+  int pos = __popcll(m & ((1ull << lane) - 1ull));
+  for (int w = 0; w < nw; ++w) pos += w < wave ? s.wsum[w] : 0;
+  if (take) out[pos] = tid;
+  __syncthreads();
+  return k;
+}
+
 // Top-k selection for small inputs without the radix passes: n <= 128 with
 // k <= 64 (one wave sorts everything), or n <= 128 * waves with k <= 16 (each
 // wave sorts 128 keys and keeps its top k, one wave sorts the survivors).
@@ -282,7 +347,7 @@ __device__ __forceinline__ bool small_select_ok(int n, int k) {
   return (n <= 128 && k <= 64) || (k <= 16 && n <= 128 * static_cast<int>(blockDim.x >> 6));
 }
 
-__device__ int small_select(const uint32_t* keys, int n, int k, int* out, SelScratch& sc) {
+__device__ __forceinline__ int small_select(const uint32_t* keys, int n, int k, int* out, SelScratch& sc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (n <= 128) {
     if (wave == 0) {
@@ -347,7 +412,7 @@ __device__ __forceinline__ int block_excl_scan(int v, SelScratch& s, int& total)
 // Indices of the k largest keys[0..n) (ties to the lower index), ascending,
 // into out[].  Exact radix select over the 32-bit keys, then a stable
 // compaction in index order.  Block-wide; every thread must call it.
-__device__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
+__device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (k <= 0 || n <= 0) return 0;
   if (n <= k) {
@@ -355,6 +420,7 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScr
     __syncthreads();
     return n;
   }
+  if (n <= static_cast<int>(blockDim.x) && n <= kRankMax) return rank_select(keys, n, k, out, s);
   if (small_select_ok(n, k)) return small_select(keys, n, k, out, s);
   uint32_t prefix = 0, pmask = 0;
   int need = k;
@@ -468,11 +534,13 @@ __device__ __forceinline__ float score16_regs(const float (&x)[KS][8], const Pac
 // Max-scores of tiles tile0, tile0 + step, ... (16 candidates each) of n
 // candidates given by row(i), streamed by one wave with DEPTH-1 tiles of
 // summary rows in flight ahead of the one being multiplied; emit(tile, v)
-// receives each tile's scores (lane%16 = candidate within the tile).
-template <int KS, int NB, typename RowPtr, typename Emit>
+// receives each tile's scores (lane%16 = candidate within the tile).  pro()
+// runs after the first tiles' loads are issued and before the first product
+// (it may fill ahi / alo; the wave must reach it even with no tiles).
+template <int KS, int NB, typename RowPtr, typename Emit, typename Pro>
 __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr row,
                                              const Pack8 (&ahi)[NB][KS],
-                                             const Pack8 (&alo)[NB][KS], Emit emit) {
+                                             const Pack8 (&alo)[NB][KS], Emit emit, Pro pro) {
   constexpr int DEPTH = NB <= 2 ? 3 : 2;
   const int lane = threadIdx.x & 63;
   const int ntile = (n + 15) / 16;
@@ -487,6 +555,7 @@ __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr 
 #pragma unroll
   for (int j = 0; j < DEPTH - 1; ++j)
     if (tile0 + j * step < ntile) fetch(tile0 + j * step, x[j]);
+  pro();
   for (int base = 0;; base += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
@@ -499,39 +568,78 @@ __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr 
   }
 }
 
-// Segmented chunk scoring: raw max-scores of one segment of a unit's middle
-// chunks into the workspace.  NB row blocks of 16 rows cover the unit's rows;
-// each wave streams every fourth tile of 16 chunks, loading the next tile's
-// summary rows while the current one is multiplied.
+template <int KS, int NB, typename RowPtr, typename Emit>
+__device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr row,
+                                             const Pack8 (&ahi)[NB][KS],
+                                             const Pack8 (&alo)[NB][KS], Emit emit) {
+  score_stream<KS, NB>(n, tile0, step, row, ahi, alo, emit, [] {});
+}
+
+// Segmented chunk scoring: one segment of a unit's middle chunks, reduced to
+// the segment's top-K_c (key and chunk offset, in ascending chunk order, key
+// 0 for missing entries: real keys are never 0) in the workspace.  NB row
+// blocks of 16 rows cover the unit's rows; each wave streams every fourth
+// tile of 16 chunks, loading the next tiles' summary rows while the current
+// one is multiplied.
 template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
+  __shared__ uint32_t keys[kMaxCand];
+  __shared__ int sel[kMaxSel];
+  __shared__ SelScratch scr;
+  if (p.Kc <= 0) return;  // uniform: the merge does not route either
   const int64_t u = blockIdx.x / p.nseg;
   const int sg = blockIdx.x - static_cast<int>(u * p.nseg);
   const Unit w = make_unit(p, u);
   const int64_t m0 = w.mid_lo + static_cast<int64_t>(sg) * p.seg_chunks;
   int64_t m1 = m0 + p.seg_chunks;
   if (m1 > w.mid_hi) m1 = w.mid_hi;
-  if (m0 >= m1 || p.Kc <= 0 || w.R <= 0) return;  // uniform
-  fill_rope_table(p, w, cs);
-  __syncthreads();
-  Pack8 ahi[NB][KS], alo[NB][KS];
-  load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* base = p.csum + ((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap + m0) * p.d;
-  const int n = static_cast<int>(m1 - m0);
-  score_stream<KS, NB>(n, wave, kScoreThreads / 64,
-                       [&](int c) { return base + static_cast<int64_t>(c) * p.d; }, ahi, alo,
-                       [&](int tile, float v) {
-                         const int c = tile * 16 + (lane & 15);
-                         if (lane < 16 && c < n) p.ws[w.slot * p.ws_stride + (m0 - w.mid_lo) + c] = v;
-                       });
+  const int n = m1 > m0 && w.R > 0 ? static_cast<int>(m1 - m0) : 0;  // uniform
+  if (n > 0) {
+    Pack8 ahi[NB][KS], alo[NB][KS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float* base = p.csum + ((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap + m0) * p.d;
+    auto rowp = [&](int c) { return base + static_cast<int64_t>(c) * p.d; };
+    auto emit = [&](int tile, float v) {
+      const int c = tile * 16 + (lane & 15);
+      if (lane < 16 && c < n) keys[c] = order_key(v);
+    };
+    if constexpr (NB <= 2) {
+      // the raw query rows and the first summary tiles are loaded while the
+      // RoPE table is computed
+      float xq[NB][KS][8];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) load_row_raw<BF16, KS>(p, w, row_of_lane(w, 0, blk), xq[blk]);
+      score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit, [&] {
+        fill_rope_table(p, w, cs);
+        __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          rotate_split<KS>(p, row_of_lane(w, 0, blk), cs, xq[blk], ahi[blk], alo[blk]);
+      });
+    } else {
+      fill_rope_table(p, w, cs);
+      __syncthreads();
+      load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
+      score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit);
+    }
+    __syncthreads();
+  }
+  const int nl = block_select(keys, n, p.Kc, sel, scr);
+  uint32_t* dk = p.ws + w.slot * p.ws_stride + static_cast<int64_t>(sg) * p.Kc;
+  uint32_t* di = dk + static_cast<int64_t>(p.nseg) * p.Kc;
+  const uint32_t off = static_cast<uint32_t>(m0 - w.mid_lo);
+  for (int i = threadIdx.x; i < p.Kc; i += blockDim.x) {
+    dk[i] = i < nl ? keys[sel[i]] : 0u;
+    di[i] = i < nl ? off + static_cast<uint32_t>(sel[i]) : 0u;
+  }
 }
 
 template <bool BF16, int KS, bool FROM_WS, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
   __shared__ uint32_t keys[kMaxCand];
+  __shared__ int coff[FROM_WS ? kMaxCand : 1];  // chunk offsets of the candidates
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
@@ -553,18 +661,58 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   const bool has_rows = route && tg < TG;
 
   Pack8 ahi[NB][KS], alo[NB][KS];
-  if (route) {
-    fill_rope_table(p, w, cs);
-    __syncthreads();
-    if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
-  }
-
   int nselc = 0;
   if (route) {
     if constexpr (FROM_WS) {
-      for (int i = threadIdx.x; i < n_mid; i += blockDim.x)
-        keys[i] = order_key(p.ws[w.slot * p.ws_stride + i]);
+      // The segments' winners (ascending chunk order) and the raw query rows
+      // are loaded first; the RoPE table is computed while they arrive.
+      constexpr int kPer = kMaxCand / kRouteThreads;
+      const int ncand = p.nseg * p.Kc;
+      const uint32_t* src = p.ws + w.slot * p.ws_stride;
+      uint32_t ck[kPer], co[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + j * kRouteThreads;
+        if (i < ncand) {
+          ck[j] = src[i];
+          co[j] = src[ncand + i];
+        }
+      }
+      float xq[NB <= 2 ? NB : 1][KS][8];
+      if constexpr (NB <= 2) {
+        if (has_rows) {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk)
+            load_row_raw<BF16, KS>(p, w, row_of_lane(w, rg * kRows, blk), xq[blk]);
+        }
+      }
+      fill_rope_table(p, w, cs);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + j * kRouteThreads;
+        if (i < ncand) {
+          keys[i] = ck[j];
+          coff[i] = static_cast<int>(co[j]);
+        }
+      }
+      __syncthreads();
+      if (has_rows) {
+        if constexpr (NB <= 2) {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk)
+            rotate_split<KS>(p, row_of_lane(w, rg * kRows, blk), cs, xq[blk], ahi[blk], alo[blk]);
+        } else {
+          load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
+        }
+      }
+      nselc = block_select(keys, ncand, p.Kc < n_mid ? p.Kc : n_mid, selc, scr);
+      for (int i = threadIdx.x; i < nselc; i += blockDim.x)
+        selc[i] = coff[selc[i]] + static_cast<int>(w.mid_lo);
+      __syncthreads();
     } else {
+      fill_rope_table(p, w, cs);
+      __syncthreads();
+      if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
       for (int i = threadIdx.x; i < n_mid; i += blockDim.x) keys[i] = 0u;
       __syncthreads();
       const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
@@ -580,11 +728,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
                                if (lane < 16 && c < n_mid) keys[c] = order_key(v);
                              });
       }
+      __syncthreads();
+      nselc = block_select(keys, n_mid, p.Kc, selc, scr);
+      for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] += static_cast<int>(w.mid_lo);
+      __syncthreads();
     }
-    __syncthreads();
-    nselc = block_select(keys, n_mid, p.Kc, selc, scr);
-    for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] += static_cast<int>(w.mid_lo);
-    __syncthreads();
   }
 
   int nselg = 0;
@@ -687,16 +835,37 @@ int64_t max_middle(const Geometry& g) {
   return rec - sink;
 }
 
-// Few units with long middle contexts: spread each unit's chunk scoring over
-// several workgroups.  From 64 units on, one workgroup per unit streams its
-// chunks fast enough and saves the second launch.
+// Few units with long middle contexts (decode-shaped calls): spread each
+// unit's chunk scoring over several workgroups.
+constexpr int64_t kSegUnits = 512;
 bool use_segmented(const Geometry& g) {
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
-  return units < 64 && max_middle(g) > 256 && g.nqc == 1 &&
+  return units < kSegUnits && max_middle(g) > 256 && g.nqc == 1 &&
          g.n_q * static_cast<int64_t>(g.G) <= kRowsPerWave;
 }
 
+// Segments of a segmented call: about kSegBlocks scoring workgroups, each
+// a multiple of kSegChunks chunks, and at most kMaxCand winners per unit.
 constexpr int kSegChunks = 64;
+constexpr int64_t kSegBlocks = 512;
+struct SegPlan {
+  int seg_chunks, nseg;
+};
+SegPlan seg_plan(const Geometry& g) {
+  const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  const int64_t mm = max_middle(g);
+  int64_t nseg = (kSegBlocks + units - 1) / units;
+  const int64_t most = (mm + kSegChunks - 1) / kSegChunks;
+  if (nseg > most) nseg = most;
+  if (g.Kc > 0 && nseg > kMaxCand / g.Kc) nseg = kMaxCand / g.Kc;
+  if (nseg < 1) nseg = 1;
+  SegPlan sp;
+  sp.seg_chunks = static_cast<int>(((mm + nseg - 1) / nseg + kSegChunks - 1) / kSegChunks * kSegChunks);
+  if (sp.seg_chunks < kSegChunks) sp.seg_chunks = kSegChunks;
+  sp.nseg = static_cast<int>((mm + sp.seg_chunks - 1) / sp.seg_chunks);
+  if (sp.nseg < 1) sp.nseg = 1;
+  return sp;
+}
 
 }  // namespace
 
@@ -707,8 +876,10 @@ bool route_supported(const Geometry& g) {
 }
 
 size_t route_workspace(const Geometry& g) {
-  if (!use_segmented(g)) return 0;
-  return static_cast<size_t>(g.B) * g.Hkv * g.nqc * static_cast<size_t>(max_middle(g)) * sizeof(float);
+  if (!use_segmented(g) || g.Kc <= 0) return 0;
+  const SegPlan sp = seg_plan(g);
+  return static_cast<size_t>(g.B) * g.Hkv * g.nqc * static_cast<size_t>(sp.nseg) * g.Kc *
+         2 * sizeof(uint32_t);
 }
 
 hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum,
@@ -723,8 +894,7 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   p.gidx = group_idx;
   p.gran = granules;
   p.gcnt = granule_count;
-  p.ws = static_cast<float*>(ws);
-  p.ws_stride = max_middle(g);
+  p.ws = static_cast<uint32_t*>(ws);
   p.q_pos0 = g.q_pos0;
   p.n_q = g.n_q;
   p.t0 = g.t0;
@@ -745,18 +915,12 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   p.Kg = g.Kg;
   p.gmax = g.gmax;
   p.rope = g.rope;
-  const bool seg = use_segmented(g);
+  const bool seg = use_segmented(g) && g.Kc > 0;
   const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
-  // about 512 scoring workgroups, each a multiple of 64 chunks
-  const int64_t mm = max_middle(g);
-  int64_t nseg = (512 + units - 1) / units;
-  const int64_t most = (mm + kSegChunks - 1) / kSegChunks;
-  if (nseg > most) nseg = most;
-  if (nseg < 1) nseg = 1;
-  p.seg_chunks = static_cast<int>(((mm + nseg - 1) / nseg + kSegChunks - 1) / kSegChunks * kSegChunks);
-  if (p.seg_chunks < kSegChunks) p.seg_chunks = kSegChunks;
-  p.nseg = static_cast<int>((mm + p.seg_chunks - 1) / p.seg_chunks);
-  if (p.nseg < 1) p.nseg = 1;
+  const SegPlan sp = seg_plan(g);
+  p.seg_chunks = sp.seg_chunks;
+  p.nseg = sp.nseg;
+  p.ws_stride = 2 * static_cast<int64_t>(sp.nseg) * g.Kc;
   if (g.bf16) {
     return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)
                       : launch_route_t<true, 2>(p, units, seg, stream);

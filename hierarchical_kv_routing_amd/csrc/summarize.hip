@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
   const int64_t c1 = c0 + p.C;
   const int64_t tend = c1 < p.tok_end ? c1 : p.tok_end;
   const bool active = lane < h;
-  const double freq = active ? p.rope.f[lane] : 0.0;
+  const double freq = active ? rope_freq(p.rope, lane) : 0.0;
   const bool high = lane < p.n_hf;
 
   float cx = 0.f, cy = 0.f;  // chunk partial sums of this wave (rotated or raw per pair kind)

@@ -129,15 +129,19 @@ def test_bad_arguments_rejected(lib):
 
 def test_workspace_checks(lib):
     cfg = H.Config.from_workload(W.DECODE_64K)
-    # 4 sequences x 4 KV heads = 16 units: segmented decode routing, one f32
-    # score per middle chunk per unit
+    # 4 sequences x 4 KV heads = 16 units: segmented decode routing over 1014
+    # middle chunks, 16 segments of 64 chunks, each keeping its top K_c = 8
+    # (a key and a chunk offset, 4 bytes each)
     need = H.route_workspace_bytes(cfg, 4, 65536, 1)
-    assert need == 4 * 4 * 1014 * 4
+    assert need == 4 * 4 * 16 * 8 * 8
     assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=16, wsb=need - 4) == 3
     assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=None, wsb=0) == 3
-    # from 64 units on, one routing workgroup per unit: no workspace
-    assert H.route_workspace_bytes(cfg, 16, 65536, 1) == 0
+    # 64 units: 8 segments of 128 chunks
+    assert H.route_workspace_bytes(cfg, 16, 65536, 1) == 16 * 4 * 8 * 8 * 8
     assert H.attend_workspace_bytes(cfg, 16, 65536, 1) > 0
+    # no routing (K_c = 0): nothing to keep
+    assert H.route_workspace_bytes(H.Config.from_workload(W.DECODE_64K, top_chunks=0), 16, 65536, 1) == 0
+    # many query chunks: one routing workgroup per unit
     big = H.Config.from_workload(W.QWEN3_PREFILL)
     assert H.route_workspace_bytes(big, 1, 0, 32768) == 0
 
