@@ -109,13 +109,19 @@ __device__ __forceinline__ AUnit uniform_unit(const AUnit& a) {
   return w;
 }
 
-__device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
+// Unit u (largest query chunk first, (sequence, KV head) fastest).  With
+// count = false the routed key count is left unread (nkeys = 0).
+__device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u, bool count = true) {
   AUnit w;
-  const int64_t bh = static_cast<int64_t>(p.B) * p.Hkv;
-  const int64_t trel = p.nqc - 1 - u / bh;
-  const int64_t rem = u % bh;
-  w.b = static_cast<int>(rem / p.Hkv);
-  w.kvh = static_cast<int>(rem % p.Hkv);
+  // units < 2^31 (checked on the host): 32-bit division
+  const uint32_t bh = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.Hkv);
+  const uint32_t u32 = static_cast<uint32_t>(u);
+  const uint32_t q = u32 / bh;
+  const uint32_t rem = u32 - q * bh;
+  const int64_t trel = p.nqc - 1 - static_cast<int64_t>(q);
+  const uint32_t bq = rem / static_cast<uint32_t>(p.Hkv);
+  w.b = static_cast<int>(bq);
+  w.kvh = static_cast<int>(rem - bq * static_cast<uint32_t>(p.Hkv));
   w.t = p.t0 + trel;
   const int64_t c0 = w.t * p.C;
   w.qlo = c0 > p.q_pos0 ? c0 : p.q_pos0;
@@ -127,7 +133,7 @@ __device__ __forceinline__ AUnit make_aunit(const AttendParams& p, int64_t u) {
   if (p.dense) {
     w.nkeys = static_cast<int>(((qhi - 1) / p.gs + 1) * p.gs);
   } else {
-    w.nkeys = p.gcnt[w.slot] * p.gs;
+    w.nkeys = count ? p.gcnt[w.slot] * p.gs : 0;
   }
   return w;
 }
@@ -808,8 +814,214 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
   if (p.lse != nullptr && lane == 0) p.lse[orow] = (m + log2f(l)) * kLn2;
 }
 
+// Decode-shaped calls (at most kDecRows query rows per unit: one query's
+// GQA group, or a few queries): one workgroup of four waves per (unit,
+// split of kDecKeys keys).  Each wave takes 32 keys: K rows go from HBM
+// straight into the A operands of 16x16x32 bf16 products (S^T = K Q^T,
+// query rows on N); the softmax runs in registers; P (bf16) and the wave's
+// V rows go through LDS, V read back transposed, for O = P V on the same
+// products.  The four waves' (m, l, O) are merged in LDS; the item writes its
+// partial to the workspace (several splits) or the normalised output.
+constexpr int kDecRows = 16;
+constexpr int kDecWaveKeys = 32;
+constexpr int kDecKeys = 4 * kDecWaveKeys;
+constexpr int kDecPP = kDecWaveKeys + 4;  // floats per P row in LDS (padded)
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
+  constexpr int KS = D / 32;        // k-steps of the QK product
+  constexpr int H = D / 2;
+  constexpr int DP = D / 64;        // V elements per lane as loaded
+  constexpr int NT = D / 16;        // output column tiles
+  constexpr int VP = D * 2 + 4;     // bytes per V row in LDS (padded)
+  constexpr int kVBuf = 4 * kDecWaveKeys * VP;
+  static_assert(kVBuf >= 4 * kDecRows * D * 4, "merge buffer aliases the V rows");
+  __shared__ float2 cs[kDecRows * H];
+  __shared__ __align__(16) float pw[4][kDecRows][kDecPP];
+  __shared__ __align__(16) char vbuf[kVBuf];
+  __shared__ float wm[4][kDecRows], wl[4][kDecRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t u = blockIdx.x / p.splits;
+  const int split = static_cast<int>(blockIdx.x - u * p.splits);
+  const AUnit w = uniform_unit(make_aunit(p, u, false));
+  const int64_t kw = static_cast<int64_t>(split) * kDecKeys + wave * kDecWaveKeys;  // wave's first key
+  const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
+  const int64_t qhi = w.qlo + w.nq;
+
+  // This lane's query row as the B operand column n = lane % 16 (rows past
+  // the unit's last repeat it; their outputs are never used).  Its loads go
+  // out first.
+  const int n = lane & 15, sub = lane >> 4;
+  const int rn = n < w.R ? n : w.R - 1;
+  const int qn = rn / p.G, hn = rn - qn * p.G;
+  float xq[KS][8];
+  {
+    const int64_t base =
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hn) * p.q_stride + (w.qlo + qn - p.q_row0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8<true>(p.q, base + ks * 32 + sub * 8, xq[ks]);
+  }
+  // Token of wave key kw + (lane % 32), or -1 (past the list or the causal end).
+  int tok = -1;
+  {
+    const int64_t k = kw + (lane & 31);
+    if (p.dense) {
+      tok = k < qhi ? static_cast<int>(k) : -1;
+    } else {
+      const int64_t gi = k >> p.lg_gs;
+      const int g = gi < p.gmax ? p.gran[w.slot * p.gmax + gi] : -1;
+      tok = g >= 0 ? g * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
+    }
+  }
+  // K rows of the two 16-key tiles (A operands: key lane % 16, d slots
+  // ks*32 + 8*(lane/16) + i) and the V elements of all 32 keys (lane owns
+  // columns DP*lane ...).
+  Pack8 ka[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int kt = __shfl(tok, t * 16 + n);
+    const int64_t e = (slab + (kt >= 0 ? kt : 0)) * D + sub * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[t][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e + ks * 32);
+  }
+  uint32_t vv[kDecWaveKeys];
+#pragma unroll
+  for (int j = 0; j < kDecWaveKeys; ++j) {
+    const int vt = __builtin_amdgcn_readlane(tok, j);
+    const int64_t e = (slab + (vt >= 0 ? vt : 0)) * D + lane * DP;
+    if constexpr (DP == 2) vv[j] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v) + e);
+    else vv[j] = static_cast<const uint16_t*>(p.v)[e];
+  }
+  // RoPE table of the unit's queries, then the rotated, scaled query
+  // operand (bf16).
+  for (int i = threadIdx.x; i < w.nq * H; i += 256) {
+    const int qi = i / H, pr = i - qi * H;
+    float c, s;
+    rope_cs(static_cast<double>(rope_base(p.rope, w.qlo) + qi), rope_freq(p.rope, pr), c, s);
+    cs[i] = make_float2(c, s);
+  }
+  __syncthreads();
+  Pack8 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS / 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float2 t = cs[qn * H + ks * 32 + sub * 8 + i];
+      const float a = xq[ks][i], b = xq[ks + KS / 2][i];
+      qb[ks].h[i] = f32_to_bf16((a * t.x - b * t.y) * p.scale_log2);
+      qb[ks + KS / 2].h[i] = f32_to_bf16((a * t.y + b * t.x) * p.scale_log2);
+    }
+  }
+  // S^T tiles: lane holds keys 16t + 4*(lane/16) + i of row n.
+  const int64_t qpos = w.qlo + qn;
+  float sv[2][4];
+  float mx = kNegBig;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(ka[t][ks].v, qb[ks].v, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kt = __shfl(tok, t * 16 + sub * 4 + i);
+      const bool ok = kt >= 0 && kt <= qpos;
+      sv[t][i] = ok ? acc[i] : -INFINITY;
+      mx = fmaxf(mx, sv[t][i]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // P (f32, rows x keys) and the wave's V rows into its LDS regions.
+  float ls = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float4 e4;
+    e4.x = exp2f(sv[t][0] - mx);  // 0 for masked keys
+    e4.y = exp2f(sv[t][1] - mx);
+    e4.z = exp2f(sv[t][2] - mx);
+    e4.w = exp2f(sv[t][3] - mx);
+    ls += (e4.x + e4.y) + (e4.z + e4.w);
+    *reinterpret_cast<float4*>(&pw[wave][n][t * 16 + sub * 4]) = e4;
+  }
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  char* vw = vbuf + wave * kDecWaveKeys * VP;
+#pragma unroll
+  for (int j = 0; j < kDecWaveKeys; ++j) {
+    if constexpr (DP == 2) *reinterpret_cast<uint32_t*>(vw + j * VP + lane * 4) = vv[j];
+    else *reinterpret_cast<uint16_t*>(vw + j * VP + lane * 2) = static_cast<uint16_t>(vv[j]);
+  }
+  // O = P V: A = P (row lane % 16, keys 8*(lane/16) + i), B = V (column
+  // lane % 16 of the tile, the same keys), read transposed from LDS.
+  Pack8 pa;
+  {
+    const float4 a = *reinterpret_cast<const float4*>(&pw[wave][n][sub * 8]);
+    const float4 b = *reinterpret_cast<const float4*>(&pw[wave][n][sub * 8 + 4]);
+    pa.h[0] = f32_to_bf16(a.x); pa.h[1] = f32_to_bf16(a.y);
+    pa.h[2] = f32_to_bf16(a.z); pa.h[3] = f32_to_bf16(a.w);
+    pa.h[4] = f32_to_bf16(b.x); pa.h[5] = f32_to_bf16(b.y);
+    pa.h[6] = f32_to_bf16(b.z); pa.h[7] = f32_to_bf16(b.w);
+  }
+  f32x4 ot[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    Pack8 vb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vb.h[i] = *reinterpret_cast<const uint16_t*>(vw + (sub * 8 + i) * VP + (c * 16 + n) * 2);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    ot[c] = mfma16x16x32(pa.v, vb.v, z);
+  }
+  // Merge the four waves (the merge buffer reuses the V rows' space).
+  __syncthreads();
+  float* wo = reinterpret_cast<float*>(vbuf);  // [4][kDecRows][D]
+  if (sub == 0) {
+    wm[wave][n] = mx;
+    wl[wave][n] = ls;
+  }
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = sub * 4 + i;
+      if (r < w.R) wo[(wave * kDecRows + r) * D + c * 16 + n] = ot[c][i];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < w.R * D; i += 256) {
+    const int r = i / D, d = i - r * D;
+    float m = kNegBig;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) m = fmaxf(m, wm[x][r]);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float sc = exp2f(wm[x][r] - m);
+      l += wl[x][r] * sc;
+      acc += wo[(x * kDecRows + r) * D + d] * sc;
+    }
+    if (p.splits > 1) {
+      const int64_t pr = (w.slot * p.splits + split) * p.Rcap + r;
+      p.ws_o[pr * D + d] = acc;
+      if (d == 0) {
+        p.ws_ml[pr * 2] = m;
+        p.ws_ml[pr * 2 + 1] = l;
+      }
+    } else {
+      const int qloc = r / p.G, hl = r - qloc * p.G;
+      const int64_t orow =
+          (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (w.qlo + qloc - p.q_row0);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      store1<true>(p.out, orow * D + d, acc * inv);
+      if (p.lse != nullptr && d == 0) p.lse[orow] = (m + log2f(l)) * kLn2;
+    }
+  }
+}
+
 struct Plan {
   int nw, rb, slices, splits, kps, rcap;
+  bool decode;
   int64_t units;
 };
 
@@ -842,6 +1054,18 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   const int64_t rows = std::min<int64_t>(g.C, g.n_q) * static_cast<int64_t>(g.G);
   pl.rcap = static_cast<int>(rows);
   pl.rb = 1;
+  pl.decode = false;
+  if (g.bf16 && allow_split && rows <= kDecRows) {
+    // decode kernel: kDecKeys keys per item
+    const int64_t keys = max_keys(g, dense);
+    pl.decode = true;
+    pl.nw = 4;
+    pl.slices = 1;
+    pl.kps = kDecKeys;
+    pl.splits = static_cast<int>((keys + kDecKeys - 1) / kDecKeys);
+    if (pl.splits < 1) pl.splits = 1;
+    return pl;
+  }
   if (g.bf16) {
     const int64_t blocks = (rows + 31) / 32;
     pl.rb = blocks >= 2 * HGA_ATTEND_RB ? HGA_ATTEND_RB : 1;
@@ -925,6 +1149,16 @@ void launch_mfma_pool(int nw, int64_t nblocks, hipStream_t stream, const AttendP
 
 template <int D>
 hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, hipStream_t stream) {
+  if (pl.decode) {
+    p.nblocks = pl.units * pl.splits;
+    hipLaunchKernelGGL((attend_decode_kernel<D>), dim3(static_cast<unsigned>(p.nblocks)), dim3(256), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || pl.splits == 1) return e;
+    const unsigned cgrid = static_cast<unsigned>((pl.units * pl.rcap + 3) / 4);
+    hipLaunchKernelGGL((combine_kernel<true, D>), dim3(cgrid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t groups = (pl.units + 7) / 8;
   p.nblocks = groups * 8 * p.per_unit;
   const unsigned grid = static_cast<unsigned>(p.nblocks);

@@ -21,12 +21,12 @@
 //    Units run longest (largest t) first.
 //  * segmented (few units with long middle contexts, e.g. a decode step):
 //    score_kernel spreads each unit's middle chunks over many workgroups;
-//    each scores its segment and keeps the segment's own top-K_c (same order:
-//    score, then lower index), which it writes to the workspace.  The fused
-//    kernel then runs with FROM_WS: it selects the unit's top-K_c among the
-//    segments' survivors (every chunk of the global top-K_c is in its
-//    segment's top-K_c, so the result is the same set) and goes on with the
-//    group phase.
+//    each scores its segment, keeps the segment's own top-K_c (same order:
+//    score, then lower index) and scores those chunks' groups, and writes
+//    all of it to the workspace.  merge_kernel then selects the unit's
+//    top-K_c among the segments' winners (every chunk of the unit's top-K_c
+//    is in its segment's top-K_c, so the result is the same set), the top-K_g
+//    among their groups, and writes the lists.
 #include "hga_device.h"
 
 namespace hga {
@@ -49,8 +49,8 @@ struct RouteParams {
   int32_t* gidx;
   int32_t* gran;
   int32_t* gcnt;
-  // segmented: per unit, nseg*Kc segment winners' keys then their middle
-  // chunk offsets (both 32-bit words); ws_stride = 2*nseg*Kc
+  // segmented: per unit, nseg*Kc segment winners' keys, their middle chunk
+  // offsets, and (group routing) nseg*Kc*r group keys, all 32-bit words
   uint32_t* ws;
   int64_t ws_stride;
   int64_t q_pos0, n_q, t0, nqc, nchunk_cap, ngroup_cap;
@@ -575,12 +575,15 @@ __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr 
   score_stream<KS, NB>(n, tile0, step, row, ahi, alo, emit, [] {});
 }
 
-// Segmented chunk scoring: one segment of a unit's middle chunks, reduced to
-// the segment's top-K_c (key and chunk offset, in ascending chunk order, key
-// 0 for missing entries: real keys are never 0) in the workspace.  NB row
-// blocks of 16 rows cover the unit's rows; each wave streams every fourth
-// tile of 16 chunks, loading the next tiles' summary rows while the current
-// one is multiplied.
+// Segmented routing, first kernel: one segment of a unit's middle chunks,
+// reduced to the segment's own top-K_c (keys and chunk offsets, ascending
+// chunk order, key 0 for missing entries: real keys are never 0) and, with
+// group routing, the scores of all groups of those K_c chunks (each
+// segment scores its winners' groups, so the merge needs no query rows).
+// NB row blocks of 16 rows cover the unit's rows; each wave streams every
+// fourth tile of 16 rows, loading the next tiles while the current one is
+// multiplied.  Workspace per unit: [nseg][K_c] keys, [nseg][K_c] offsets,
+// [nseg][K_c][C/g_s] group keys (32-bit words).
 template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
@@ -595,6 +598,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   int64_t m1 = m0 + p.seg_chunks;
   if (m1 > w.mid_hi) m1 = w.mid_hi;
   const int n = m1 > m0 && w.R > 0 ? static_cast<int>(m1 - m0) : 0;  // uniform
+  const int64_t ncand = static_cast<int64_t>(p.nseg) * p.Kc;
+  uint32_t* dk = p.ws + w.slot * p.ws_stride + static_cast<int64_t>(sg) * p.Kc;
+  uint32_t* di = dk + ncand;
+  uint32_t* dg = p.ws + w.slot * p.ws_stride + 2 * ncand + static_cast<int64_t>(sg) * p.Kc * p.r;
+  const int ng = p.Kg > 0 ? p.Kc * p.r : 0;  // group keys this segment writes
+  int nl = 0;
   if (n > 0) {
     Pack8 ahi[NB][KS], alo[NB][KS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -624,22 +633,122 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
       score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit);
     }
     __syncthreads();
+    nl = block_select(keys, n, p.Kc, sel, scr);
+    if (p.Kg > 0) {
+      // groups of the segment's winners: candidate c = i * r + g is group g
+      // of winner i (global id (m0 + sel[i]) * r + g)
+      const int nc = nl * p.r;
+      const float* g0 = p.gsum + (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.ngroup_cap * p.d;
+      score_stream<KS, NB>(nc, wave, kScoreThreads / 64,
+                           [&](int c) {
+                             const int i = c / p.r;
+                             return g0 + ((m0 + sel[i]) * p.r + (c - i * p.r)) * p.d;
+                           },
+                           ahi, alo, [&](int tile, float v) {
+                             const int c = tile * 16 + (lane & 15);
+                             if (lane < 16 && c < nc) dg[c] = order_key(v);
+                           });
+    }
   }
-  const int nl = block_select(keys, n, p.Kc, sel, scr);
-  uint32_t* dk = p.ws + w.slot * p.ws_stride + static_cast<int64_t>(sg) * p.Kc;
-  uint32_t* di = dk + static_cast<int64_t>(p.nseg) * p.Kc;
   const uint32_t off = static_cast<uint32_t>(m0 - w.mid_lo);
   for (int i = threadIdx.x; i < p.Kc; i += blockDim.x) {
     dk[i] = i < nl ? keys[sel[i]] : 0u;
     di[i] = i < nl ? off + static_cast<uint32_t>(sel[i]) : 0u;
   }
+  for (int c = nl * p.r + threadIdx.x; c < ng; c += blockDim.x) dg[c] = 0u;
 }
 
-template <bool BF16, int KS, bool FROM_WS, int NB>
+// Outputs of a unit.  The visible list is: sink granules, routed granules,
+// recent granules, current-chunk granules up to the last query; the routed
+// ones lie in [sink_hi, rec_lo) so the concatenation is ascending and
+// unique.  selc: chosen chunks (ascending); selg: chosen groups (ascending
+// global ids).  Block-wide.
+__device__ __forceinline__ void write_lists(const RouteParams& p, const Unit& w, const int* selc,
+                                            int nselc, const int* selg, int nselg) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int32_t* ci = p.cidx + w.slot * p.Kc;
+  for (int i = tid; i < p.Kc; i += nt) ci[i] = i < nselc ? selc[i] : -1;
+  if (p.Kg > 0 && p.gidx != nullptr) {
+    int32_t* gi = p.gidx + w.slot * p.Kg;
+    for (int i = tid; i < p.Kg; i += nt) gi[i] = i < nselg ? selg[i] : -1;
+  }
+  const int r = p.r;
+  const int n1 = static_cast<int>(w.sink_hi) * r;
+  const int n2 = p.Kg > 0 ? nselg : nselc * r;
+  const int64_t rec0 = w.rec_lo * r;
+  const int n3 = static_cast<int>(w.t - w.rec_lo) * r;
+  const int64_t cur0 = w.t * r;
+  const int64_t qlast = w.qlo + w.nq - 1;
+  const int n4 = static_cast<int>(qlast / p.gs - cur0 + 1);
+  const int total = n1 + n2 + n3 + n4;
+  int32_t* gl = p.gran + w.slot * p.gmax;
+  for (int i = tid; i < p.gmax; i += nt) {
+    int32_t v = -1;
+    if (i < n1) {
+      v = i;
+    } else if (i < n1 + n2) {
+      const int j = i - n1;
+      v = p.Kg > 0 ? selg[j] : selc[j / r] * r + (j - (j / r) * r);
+    } else if (i < n1 + n2 + n3) {
+      v = static_cast<int32_t>(rec0 + (i - n1 - n2));
+    } else if (i < total) {
+      v = static_cast<int32_t>(cur0 + (i - n1 - n2 - n3));
+    }
+    gl[i] = v;
+  }
+  if (tid == 0) p.gcnt[w.slot] = total;
+}
+
+// Segmented routing, second kernel: one workgroup per unit.
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(RouteParams p) {
+  __shared__ uint32_t keys[kMaxCand];
+  __shared__ int offs[kMaxCand];
+  __shared__ uint32_t gks[kMaxCand];
+  __shared__ int pos[kMaxSel];
+  __shared__ int selc[kMaxSel];
+  __shared__ int selg[kMaxSel];
+  __shared__ SelScratch scr;
+  const Unit w = make_unit(p, blockIdx.x);
+  const int n_mid = static_cast<int>(w.mid_hi - w.mid_lo);
+  int nselc = 0, nselg = 0;
+  if (p.Kc > 0 && n_mid > 0 && w.R > 0) {  // uniform
+    const int ncand = p.nseg * p.Kc;
+    const int ngk = p.Kg > 0 ? ncand * p.r : 0;
+    const uint32_t* src = p.ws + w.slot * p.ws_stride;
+    for (int i = threadIdx.x; i < ncand; i += blockDim.x) {
+      keys[i] = src[i];
+      offs[i] = static_cast<int>(src[ncand + i]);
+    }
+    for (int i = threadIdx.x; i < ngk; i += blockDim.x) gks[i] = src[2 * ncand + i];
+    __syncthreads();
+    nselc = block_select(keys, ncand, p.Kc < n_mid ? p.Kc : n_mid, pos, scr);
+    for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] = offs[pos[i]] + static_cast<int>(w.mid_lo);
+    if (p.Kg > 0) {
+      // candidate c = i * r + g: group g of the i-th chosen chunk (ascending
+      // global group ids)
+      const int nc = nselc * p.r;
+      for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+        const int i = c / p.r;
+        keys[c] = gks[pos[i] * p.r + (c - i * p.r)];
+      }
+      __syncthreads();
+      nselg = block_select(keys, nc, p.Kg, selg, scr);
+      for (int j = threadIdx.x; j < nselg; j += blockDim.x) {
+        const int c = selg[j];
+        const int i = c / p.r;
+        selg[j] = selc[i] * p.r + (c - i * p.r);
+      }
+    }
+    __syncthreads();
+  }
+  write_lists(p, w, selc, nselc, selg, nselg);
+}
+
+template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
   __shared__ uint32_t keys[kMaxCand];
-  __shared__ int coff[FROM_WS ? kMaxCand : 1];  // chunk offsets of the candidates
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
@@ -663,53 +772,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   Pack8 ahi[NB][KS], alo[NB][KS];
   int nselc = 0;
   if (route) {
-    if constexpr (FROM_WS) {
-      // The segments' winners (ascending chunk order) and the raw query rows
-      // are loaded first; the RoPE table is computed while they arrive.
-      constexpr int kPer = kMaxCand / kRouteThreads;
-      const int ncand = p.nseg * p.Kc;
-      const uint32_t* src = p.ws + w.slot * p.ws_stride;
-      uint32_t ck[kPer], co[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = threadIdx.x + j * kRouteThreads;
-        if (i < ncand) {
-          ck[j] = src[i];
-          co[j] = src[ncand + i];
-        }
-      }
-      float xq[NB <= 2 ? NB : 1][KS][8];
-      if constexpr (NB <= 2) {
-        if (has_rows) {
-#pragma unroll
-          for (int blk = 0; blk < NB; ++blk)
-            load_row_raw<BF16, KS>(p, w, row_of_lane(w, rg * kRows, blk), xq[blk]);
-        }
-      }
-      fill_rope_table(p, w, cs);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = threadIdx.x + j * kRouteThreads;
-        if (i < ncand) {
-          keys[i] = ck[j];
-          coff[i] = static_cast<int>(co[j]);
-        }
-      }
-      __syncthreads();
-      if (has_rows) {
-        if constexpr (NB <= 2) {
-#pragma unroll
-          for (int blk = 0; blk < NB; ++blk)
-            rotate_split<KS>(p, row_of_lane(w, rg * kRows, blk), cs, xq[blk], ahi[blk], alo[blk]);
-        } else {
-          load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
-        }
-      }
-      nselc = block_select(keys, ncand, p.Kc < n_mid ? p.Kc : n_mid, selc, scr);
-      for (int i = threadIdx.x; i < nselc; i += blockDim.x)
-        selc[i] = coff[selc[i]] + static_cast<int>(w.mid_lo);
-      __syncthreads();
-    } else {
+    {
       fill_rope_table(p, w, cs);
       __syncthreads();
       if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
@@ -764,42 +827,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __syncthreads();
   }
 
-  // Outputs.  The visible list is: sink granules, routed granules, recent
-  // granules, current-chunk granules up to the last query; the routed ones
-  // lie in [sink_hi, rec_lo) so the concatenation is ascending and unique.
-  const int tid = threadIdx.x, nt = blockDim.x;
-  int32_t* ci = p.cidx + w.slot * p.Kc;
-  for (int i = tid; i < p.Kc; i += nt) ci[i] = i < nselc ? selc[i] : -1;
-  if (p.Kg > 0 && p.gidx != nullptr) {
-    int32_t* gi = p.gidx + w.slot * p.Kg;
-    for (int i = tid; i < p.Kg; i += nt) gi[i] = i < nselg ? selg[i] : -1;
-  }
-  const int r = p.r;
-  const int n1 = static_cast<int>(w.sink_hi) * r;
-  const int n2 = p.Kg > 0 ? nselg : nselc * r;
-  const int64_t rec0 = w.rec_lo * r;
-  const int n3 = static_cast<int>(w.t - w.rec_lo) * r;
-  const int64_t cur0 = w.t * r;
-  const int64_t qlast = w.qlo + w.nq - 1;
-  const int n4 = static_cast<int>(qlast / p.gs - cur0 + 1);
-  const int total = n1 + n2 + n3 + n4;
-  int32_t* gl = p.gran + w.slot * p.gmax;
-  for (int i = tid; i < p.gmax; i += nt) {
-    int32_t v = -1;
-    if (i < n1) {
-      v = i;
-    } else if (i < n1 + n2) {
-      const int j = i - n1;
-      v = p.Kg > 0 ? selg[j] : selc[j / r] * r + (j - (j / r) * r);
-    } else if (i < n1 + n2 + n3) {
-      v = static_cast<int32_t>(rec0 + (i - n1 - n2));
-    } else if (i < total) {
-      v = static_cast<int32_t>(cur0 + (i - n1 - n2 - n3));
-    }
-    gl[i] = v;
-  }
-  if (tid == 0) p.gcnt[w.slot] = total;
+  write_lists(p, w, selc, nselc, selg, nselg);
 }
+
 
 template <bool BF16, int KS, int NB>
 hipError_t launch_route_nb(const RouteParams& p, int64_t units, bool segmented, hipStream_t stream) {
@@ -808,10 +838,9 @@ hipError_t launch_route_nb(const RouteParams& p, int64_t units, bool segmented, 
                        dim3(kScoreThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_kernel<BF16, KS, true, NB>), dim3(static_cast<unsigned>(units)),
-                       dim3(kRouteThreads), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(units)), dim3(kMergeThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((route_kernel<BF16, KS, false, NB>), dim3(static_cast<unsigned>(units)),
+    hipLaunchKernelGGL((route_kernel<BF16, KS, NB>), dim3(static_cast<unsigned>(units)),
                        dim3(kRouteThreads), 0, stream, p);
   }
   return hipGetLastError();
@@ -857,7 +886,9 @@ SegPlan seg_plan(const Geometry& g) {
   int64_t nseg = (kSegBlocks + units - 1) / units;
   const int64_t most = (mm + kSegChunks - 1) / kSegChunks;
   if (nseg > most) nseg = most;
-  if (g.Kc > 0 && nseg > kMaxCand / g.Kc) nseg = kMaxCand / g.Kc;
+  // winners (and their groups) of all segments fit the merge's LDS
+  const int64_t per = static_cast<int64_t>(g.Kc) * (g.Kg > 0 ? g.r : 1);
+  if (per > 0 && nseg > kMaxCand / per) nseg = kMaxCand / per;
   if (nseg < 1) nseg = 1;
   SegPlan sp;
   sp.seg_chunks = static_cast<int>(((mm + nseg - 1) / nseg + kSegChunks - 1) / kSegChunks * kSegChunks);
@@ -879,7 +910,7 @@ size_t route_workspace(const Geometry& g) {
   if (!use_segmented(g) || g.Kc <= 0) return 0;
   const SegPlan sp = seg_plan(g);
   return static_cast<size_t>(g.B) * g.Hkv * g.nqc * static_cast<size_t>(sp.nseg) * g.Kc *
-         2 * sizeof(uint32_t);
+         (2 + (g.Kg > 0 ? g.r : 0)) * sizeof(uint32_t);
 }
 
 hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum,
@@ -920,7 +951,7 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   const SegPlan sp = seg_plan(g);
   p.seg_chunks = sp.seg_chunks;
   p.nseg = sp.nseg;
-  p.ws_stride = 2 * static_cast<int64_t>(sp.nseg) * g.Kc;
+  p.ws_stride = static_cast<int64_t>(sp.nseg) * g.Kc * (2 + (g.Kg > 0 ? g.r : 0));
   if (g.bf16) {
     return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)
                       : launch_route_t<true, 2>(p, units, seg, stream);

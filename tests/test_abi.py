@@ -131,13 +131,17 @@ def test_workspace_checks(lib):
     cfg = H.Config.from_workload(W.DECODE_64K)
     # 4 sequences x 4 KV heads = 16 units: segmented decode routing over 1014
     # middle chunks, 16 segments of 64 chunks, each keeping its top K_c = 8
-    # (a key and a chunk offset, 4 bytes each)
+    # (a key and a chunk offset) and the scores of their 4 groups each, all
+    # 4-byte words
     need = H.route_workspace_bytes(cfg, 4, 65536, 1)
-    assert need == 4 * 4 * 16 * 8 * 8
+    assert need == 4 * 4 * 16 * 8 * (2 + 4) * 4
     assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=16, wsb=need - 4) == 3
     assert _route(lib, cfg, B=4, q_pos0=65536, n_q=1, cap=65600, ws=None, wsb=0) == 3
     # 64 units: 8 segments of 128 chunks
-    assert H.route_workspace_bytes(cfg, 16, 65536, 1) == 16 * 4 * 8 * 8 * 8
+    assert H.route_workspace_bytes(cfg, 16, 65536, 1) == 16 * 4 * 8 * 8 * (2 + 4) * 4
+    # chunk routing only: no group keys
+    chunk_only = H.Config.from_workload(W.DECODE_64K, top_groups=0)
+    assert H.route_workspace_bytes(chunk_only, 16, 65536, 1) == 16 * 4 * 8 * 8 * 2 * 4
     assert H.attend_workspace_bytes(cfg, 16, 65536, 1) > 0
     # no routing (K_c = 0): nothing to keep
     assert H.route_workspace_bytes(H.Config.from_workload(W.DECODE_64K, top_chunks=0), 16, 65536, 1) == 0
