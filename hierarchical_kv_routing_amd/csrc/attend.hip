@@ -78,6 +78,7 @@ struct AttendParams {
   int slices, splits, keys_per_split, per_unit;
   int64_t nblocks;  // work items (bx) of the launch; a workgroup takes bx = blockIdx.x + k*gridDim.x
   int dense;
+  int all_splits;   // every split wrote its partial (decode kernel)
   float scale_log2;
   RopeFreqs rope;
 };
@@ -766,12 +767,18 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
   if (gr >= p.units * p.Rcap) return;
   const int64_t u = gr / p.Rcap;
   const int row = static_cast<int>(gr - u * p.Rcap);
-  const AUnit w = make_aunit(p, u);
+  // The decode kernel writes every split's partial (empty ones as m = -big,
+  // l = 0), so it needs no key count; the other kernels skip splits past the
+  // unit's keys.
+  const AUnit w = make_aunit(p, u, !p.all_splits);
   if (row >= w.R) return;
-  // Splits that hold keys of this unit; their partials are read eight at a
-  // time, every load of a group issued before any is used.
-  int ns = (w.nkeys + p.keys_per_split - 1) / p.keys_per_split;
-  ns = ns < p.splits ? ns : p.splits;
+  // Splits that hold partials of this unit; they are read eight at a time,
+  // every load of a group issued before any is used.
+  int ns = p.splits;
+  if (!p.all_splits) {
+    ns = (w.nkeys + p.keys_per_split - 1) / p.keys_per_split;
+    ns = ns < p.splits ? ns : p.splits;
+  }
   constexpr int kG = 8;
   constexpr int kD = D / 64 > 0 ? D / 64 : 1;
   float m = kNegBig, l = 0.f;
@@ -1244,6 +1251,7 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
   p.keys_per_split = pl.kps;
   p.per_unit = pl.slices * pl.splits;
   p.dense = dense ? 1 : 0;
+  p.all_splits = pl.decode ? 1 : 0;
   p.scale_log2 = g.scale * kLog2e;
   p.rope = g.rope;
   return g.d == 128 ? launch_attend_d<128>(g, p, pl, stream) : launch_attend_d<64>(g, p, pl, stream);
