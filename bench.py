@@ -12,10 +12,14 @@ Also measured in the same run (extra fields of the one JSON line):
   decode  -- one decode step for 16 sequences x 65536 cached tokens
              (route + attend at position 65536, summaries precomputed);
   smalllm -- the SmallLM-shaped prefill (batch 4, 8/8 heads, d=64, 4096 tokens);
+  host_tiered -- prefill over 131072 tokens with K/V in pinned host RAM
+             (with and without the device cache of granules);
+  decode_host_tier_stream -- the decode shape streamed token by token with
+             its K/V history in pinned host RAM (DecodeSession);
   cpu_baseline -- the CPU oracle on a bounded sample of the prefill step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prefill|decode|smalllm|host|copy]
+       [--only prefill|decode|smalllm|host|stream|copy|peaks]
 """
 from __future__ import annotations
 
@@ -343,6 +347,72 @@ def bench_host_tier(args, w, copy_gbs, slots=16384, wmax=64, threads=8, cache_sl
                 overlap=(t_copy + t_attn) / t)
 
 
+STREAM_WARM_STEPS = 64   # one chunk of tokens streamed before the timed session
+STREAM_STEPS = 48
+STREAM_CACHE_SLOTS = 16384
+
+
+def bench_stream_decode(args):
+    """Decode with the K/V history in pinned host RAM (DecodeSession), one
+    token per sequence per step: append (rotate the key, store key and value
+    in the host tier, summaries of closed blocks) and step (route, granule
+    lists to the host, device-cache lookup, H2D of the misses, attention),
+    waited for at the end of every step as a serving loop would.  A first
+    session streams one chunk of tokens (untimed: first use of the host
+    threads and buffers); a second one, started where it ended, with a cold
+    device cache, streams the timed steps over new queries."""
+    import torch
+    import hierarchical_kv_routing_amd as H
+    n1, n2 = STREAM_WARM_STEPS, STREAM_STEPS
+    prefix = 65536
+    w = W.DECODE_64K.scaled(n_ctx=prefix + n1 + n2, kv_cap=prefix + 128, q_pos0=prefix, n_q=n1 + n2)
+    pipe = Pipeline(w)
+    pipe.build()
+    torch.cuda.synchronize()
+    cfg = pipe.cfg
+    store = H.host_store(cfg, pipe.k_rot, pipe.v)
+    store[:, :, prefix // cfg.group_size:] = 0  # the sessions append these tokens
+    pipe.csum[:, :, prefix // cfg.chunk_size:] = 0
+    pipe.gsum[:, :, prefix // cfg.group_size:] = 0
+    cap = pipe.k.shape[2]
+    ks = [pipe.k[:, :, p:p + 1].contiguous() for p in range(prefix, prefix + n1 + n2)]
+    vs = [pipe.v[:, :, p:p + 1].contiguous() for p in range(prefix, prefix + n1 + n2)]
+    qs = [pipe.q[:, :, s:s + 1].contiguous() for s in range(n1 + n2)]
+    del pipe.k_rot
+    torch.cuda.empty_cache()
+    out = torch.empty_like(qs[0])
+
+    def run(first, count):
+        sess = H.DecodeSession(cfg, w.batch, cap, prefix + first, STREAM_CACHE_SLOTS, store)
+        torch.cuda.synchronize()
+        times, stats = [], []
+        for s in range(first, first + count):
+            pos = prefix + s
+            t0 = time.perf_counter()
+            sess.append(ks[s], vs[s], pos, pipe.csum, pipe.gsum)
+            st = sess.step(qs[s], pos, pipe.csum, pipe.gsum, out, None)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            stats.append(st)
+        sess.close()
+        return np.array(times), stats
+
+    run(0, n1)
+    t, stats = run(n1, n2)
+    cp = np.array([x["granules_copied"] for x in stats], dtype=np.float64)
+    hit = np.array([x["granules_hit"] for x in stats], dtype=np.float64)
+    h2d = np.array([x["bytes_h2d"] for x in stats], dtype=np.float64)
+    look = np.array([x["pack_seconds"] for x in stats], dtype=np.float64)
+    return dict(workload=w.name + "_host_tier_stream", cache_slots=STREAM_CACHE_SLOTS, steps_timed=n2,
+                us_per_step_median=float(np.median(t) * 1e6), us_per_step_mean=float(t.mean() * 1e6),
+                us_per_step_after_first=float(np.median(t[1:]) * 1e6),
+                host_lookup_us_per_step=float(np.median(look) * 1e6),
+                granules_copied_per_step=float(cp[1:].mean()), granules_hit_per_step=float(hit[1:].mean()),
+                host_link_mb_per_step=float(h2d[1:].mean() / 1e6),
+                first_step_granules_copied=int(cp[0]),
+                timing="wall clock of append + step, synchronised every step")
+
+
 def cpu_baseline(pipe, budget_s=12.0):
     """Time the CPU oracle on a bounded, unbiased sample of the prefill step
     and scale to the whole step: summaries of one (sequence, KV head) slab
@@ -401,7 +471,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "copy", "peaks"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "stream", "copy", "peaks"],
+                    default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -429,6 +500,9 @@ def main():
         res = {w.name + ("" if c == 0 else "_warm_tier"): bench_host_tier(args, w, gbs, cache_slots=c)
                for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP) for c in (0, WARM_TIER_SLOTS)}
         print(json.dumps(dict(host_tiered=res)), flush=True)
+        return
+    if args.only == "stream":
+        print(json.dumps(dict(decode_host_tier_stream=bench_stream_decode(args))), flush=True)
         return
     if args.only == "smalllm":
         _, sm = bench_smalllm(args)
@@ -484,6 +558,9 @@ def main():
                 line["host_tiered"][name] = bench_host_tier(args, w, gbs, cache_slots=cache)
                 log(f"[bench] host tier {name}: {line['host_tiered'][name]}")
                 torch.cuda.empty_cache()
+        line["decode_host_tier_stream"] = bench_stream_decode(args)
+        log(f"[bench] streaming decode from the host tier: {line['decode_host_tier_stream']}")
+        torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 

@@ -32,7 +32,9 @@ HGA_F32, HGA_BF16 = 0, 1
 ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_bytes",
                "hga_route", "hga_attend_workspace_bytes", "hga_attend", "hga_dense_causal",
                "hga_host_tiered_buffer_bytes", "hga_attend_host_tiered",
-               "hga_status_string", "hga_last_hip_error")
+               "hga_decode_session_buffer_bytes", "hga_decode_session_create",
+               "hga_decode_session_destroy", "hga_decode_session_append",
+               "hga_decode_session_step", "hga_status_string", "hga_last_hip_error")
 
 
 class HGAError(RuntimeError):
@@ -125,6 +127,13 @@ def lib() -> ctypes.CDLL:
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
                                          I32, I64, I64, I32, P, P, ctypes.POINTER(hga_tier_stats)]),
+        "hga_decode_session_buffer_bytes": (I32, [CP, I32, I32, I64, I64, ctypes.POINTER(SZ),
+                                                  ctypes.POINTER(SZ)]),
+        "hga_decode_session_create": (I32, [CP, I32, I32, I64, I64, I64, P, P, SZ, P, SZ,
+                                            ctypes.POINTER(P)]),
+        "hga_decode_session_destroy": (None, [P]),
+        "hga_decode_session_append": (I32, [P, P, P, I64, P, P, P]),
+        "hga_decode_session_step": (I32, [P, P, I64, P, P, P, P, P, ctypes.POINTER(hga_tier_stats)]),
         "hga_status_string": (ctypes.c_char_p, [I32]),
         "hga_last_hip_error": (ctypes.c_int, []),
     }
@@ -352,6 +361,93 @@ def attend_host_tiered(cfg: Config, q, q_pos0: int, kv_host, kv_cap: int, chunk_
         ctypes.c_void_p(xs.cuda_stream), ctypes.byref(stats))
     _check(st, "hga_attend_host_tiered")
     return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}
+
+
+def decode_session_buffer_bytes(cfg: Config, dtype, batch: int, kv_cap: int, cache_slots: int):
+    """(device_bytes, host_bytes) of a streaming decode session's buffers."""
+    torch = _torch()
+    code = HGA_BF16 if dtype == torch.bfloat16 else HGA_F32
+    dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib().hga_decode_session_buffer_bytes(ctypes.byref(cfg.c()), code, batch, kv_cap, cache_slots,
+                                               ctypes.byref(dev), ctypes.byref(host))
+    _check(st, "hga_decode_session_buffer_bytes")
+    return dev.value, host.value
+
+
+class DecodeSession:
+    """Streaming decode from the host tier: K/V history in the pinned
+    granule-major store (host_store layout), a device cache of cache_slots
+    granules kept across steps.  The session allocates its device and pinned
+    host buffers with torch; the store and summary tables belong to the
+    caller."""
+
+    def __init__(self, cfg: Config, batch: int, kv_cap: int, first_pos: int, cache_slots: int,
+                 kv_host, device="cuda:0"):
+        torch = _torch()
+        if kv_host.is_cuda or not kv_host.is_pinned():
+            raise HGAError("kv_host must be a pinned host tensor")
+        d = cfg.head_dim
+        if tuple(kv_host.shape) != (batch, cfg.n_kv_heads, kv_cap // cfg.group_size, 2, cfg.group_size, d):
+            raise HGAError(f"kv_host has shape {tuple(kv_host.shape)}")
+        self.cfg, self.batch, self.kv_cap = cfg, batch, kv_cap
+        self._c = cfg.c()
+        dev_b, host_b = decode_session_buffer_bytes(cfg, kv_host.dtype, batch, kv_cap, cache_slots)
+        self.dev = torch.empty(max(dev_b, 256), dtype=torch.uint8, device=device)
+        self.host = torch.empty(max(host_b, 256), dtype=torch.uint8, pin_memory=True)
+        self.store = kv_host
+        h = ctypes.c_void_p(None)
+        st = lib().hga_decode_session_create(
+            ctypes.byref(self._c), _dtype_code(kv_host), batch, kv_cap, first_pos, cache_slots,
+            kv_host.data_ptr(), self.dev.data_ptr(), self.dev.numel(), self.host.data_ptr(),
+            self.host.numel(), ctypes.byref(h))
+        _check(st, "hga_decode_session_create")
+        self._h = h
+
+    def append(self, k_raw_new, v_new, pos: int, chunk_sum, group_sum, stream=None):
+        """Token pos of every sequence: k_raw_new / v_new [B][Hkv][1][d]."""
+        torch = _torch()
+        cfg = self.cfg
+        shape = (self.batch, cfg.n_kv_heads, 1, cfg.head_dim)
+        _dev(k_raw_new, "k_raw_new", shape, self.store.dtype)
+        _dev(v_new, "v_new", shape, self.store.dtype)
+        _dev(chunk_sum, "chunk_sum")
+        _dev(group_sum, "group_sum")
+        s = stream if stream is not None else torch.cuda.current_stream(k_raw_new.device)
+        st = lib().hga_decode_session_append(
+            self._h, k_raw_new.data_ptr(), v_new.data_ptr(), pos, chunk_sum.data_ptr(),
+            group_sum.data_ptr() if group_sum is not None else None, ctypes.c_void_p(s.cuda_stream))
+        _check(st, "hga_decode_session_append")
+
+    def step(self, q, pos: int, chunk_sum, group_sum, out, lse=None, stream=None) -> dict:
+        """One query per sequence at position pos: q, out [B][Hq][1][d]."""
+        torch = _torch()
+        cfg = self.cfg
+        shape = (self.batch, cfg.n_q_heads, 1, cfg.head_dim)
+        _dev(q, "q", shape, self.store.dtype)
+        _dev(out, "out", shape, self.store.dtype)
+        _dev(lse, "lse", shape[:3], torch.float32)
+        _dev(chunk_sum, "chunk_sum")
+        _dev(group_sum, "group_sum")
+        cs = stream if stream is not None else torch.cuda.current_stream(q.device)
+        stats = hga_tier_stats()
+        st = lib().hga_decode_session_step(
+            self._h, q.data_ptr(), pos, chunk_sum.data_ptr(),
+            group_sum.data_ptr() if group_sum is not None else None, out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, ctypes.c_void_p(cs.cuda_stream),
+            ctypes.byref(stats))
+        _check(st, "hga_decode_session_step")
+        return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            lib().hga_decode_session_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def default_scale(cfg: Config) -> float:

@@ -868,16 +868,26 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load8<true>(p.q, base + ks * 32 + sub * 8, xq[ks]);
   }
-  // Token of wave key kw + (lane % 32), or -1 (past the list or the causal end).
-  int tok = -1;
+  // Wave key kw + (lane % 32): its token, or -1 (past the list or the causal
+  // end), and the row of its K: the token in the (sequence, KV head) slab,
+  // or in pool mode row (2*slot)*g_s + offset of the granule's pool slot
+  // (its V row g_s further).
+  const bool pool = p.pool_slot != nullptr;
+  const int64_t kbase = pool ? 0 : slab;
+  const int64_t vshift = pool ? p.gs : 0;
+  int tok = -1, row = 0;
   {
     const int64_t k = kw + (lane & 31);
     if (p.dense) {
       tok = k < qhi ? static_cast<int>(k) : -1;
+      row = tok >= 0 ? tok : 0;
     } else {
       const int64_t gi = k >> p.lg_gs;
-      const int g = gi < p.gmax ? p.gran[w.slot * p.gmax + gi] : -1;
-      tok = g >= 0 ? g * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
+      const int64_t e = w.slot * p.gmax + gi;
+      const int g = gi < p.gmax ? p.gran[e] : -1;
+      const int off = static_cast<int>(k & (p.gs - 1));
+      tok = g >= 0 ? g * p.gs + off : -1;
+      if (g >= 0) row = pool ? 2 * p.pool_slot[e] * p.gs + off : tok;
     }
   }
   // K rows of the two 16-key tiles (A operands: key lane % 16, d slots
@@ -886,8 +896,8 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
   Pack8 ka[2][KS];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int kt = __shfl(tok, t * 16 + n);
-    const int64_t e = (slab + (kt >= 0 ? kt : 0)) * D + sub * 8;
+    const int kr = __shfl(row, t * 16 + n);
+    const int64_t e = (kbase + kr) * D + sub * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       ka[t][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e + ks * 32);
@@ -895,8 +905,8 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
   uint32_t vv[kDecWaveKeys];
 #pragma unroll
   for (int j = 0; j < kDecWaveKeys; ++j) {
-    const int vt = __builtin_amdgcn_readlane(tok, j);
-    const int64_t e = (slab + (vt >= 0 ? vt : 0)) * D + lane * DP;
+    const int vr = __builtin_amdgcn_readlane(row, j);
+    const int64_t e = (kbase + vshift + vr) * D + lane * DP;
     if constexpr (DP == 2) vv[j] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v) + e);
     else vv[j] = static_cast<const uint16_t*>(p.v)[e];
   }

@@ -39,9 +39,13 @@ hga_status make_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, 
 // Records a failed HIP call as this thread's last error; returns HGA_ERR_HIP.
 hga_status hip_fail(hipError_t e);
 
+// k_raw / k_rot hold tokens [k_first, k_first + k_rows) per (sequence, KV
+// head) (k_rows <= 0: the whole cache); every token the call reads or writes
+// must lie in that range.
 hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_begin,
                             int64_t tok_end, void* k_rot, float* chunk_sum,
-                            float* group_sum, hipStream_t stream);
+                            float* group_sum, hipStream_t stream, int64_t k_first = 0,
+                            int64_t k_rows = 0);
 
 size_t route_workspace(const Geometry& g);
 bool route_supported(const Geometry& g);

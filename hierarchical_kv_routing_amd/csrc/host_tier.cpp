@@ -567,3 +567,325 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Streaming decode from the host tier.
+//
+// Source: xllm-io paper-review page of "Hierarchical Global Attention",
+// section 3, tiered K/V store (RAM-cached decode): the token K/V history
+// stays in host RAM, summaries and routing on the device, and each decode
+// step moves only the granules its routes need; a device cache keeps
+// granules across steps (consecutive steps re-route mostly the same ones).
+//
+// A session holds, across steps, the device cache's slot map and LRU order
+// (host memory) and carves the caller's device / host buffers:
+//   device: route outputs, route and attention workspaces, the granule
+//           cache, a landing buffer for one step's misses, the per-entry
+//           cache slots, and the raw and rotated keys of the current chunk;
+//   host:   the granule lists, the landing staging and the slot arrays.
+// append() rotates a new token's key on the device (and builds the chunk /
+// group summaries a token closes, from the current chunk's raw keys), then
+// copies its rotated key and value into the host store.  step() routes the
+// step's queries, copies the lists to the host (a synchronisation), looks up
+// the cache (a granule copied when it held fewer tokens than the step needs,
+// i.e. the granule being filled, counts as a miss) and sends the miss list
+// to the device, where a gather kernel reads the missing granules straight
+// from the pinned store over the host link (no host-side packing) into their
+// cache slots; then the decode attention runs over the cache.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct SessionLayout {
+  int64_t units = 0, per_step = 0;
+  size_t granule_bytes = 0, row_bytes = 0;
+  // the slot map and the miss list (sources, then destinations) are
+  // contiguous on both sides: one host-to-device copy
+  size_t cidx = 0, gidx = 0, gran = 0, gcnt = 0, rws = 0, aws = 0, cache = 0, idx = 0,
+         win_raw = 0, win_rot = 0, dev_total = 0;
+  size_t hgran = 0, hcnt = 0, hidx = 0, host_total = 0;
+  size_t rws_bytes = 0, aws_bytes = 0, idx_bytes = 0, slots_off = 0, src_off = 0, dst_off = 0;
+};
+
+// Reads granule src[j] of the pinned host store (through its device
+// mapping, over the host link) into cache slot dst[j]; one workgroup per
+// granule, 16-byte words.
+__global__ __launch_bounds__(256) void fetch_granules(const uint4* store, const int64_t* src,
+                                                      const int32_t* dst, uint4* cache, int64_t words) {
+  const uint4* in = store + src[blockIdx.x] * words;
+  uint4* out = cache + static_cast<int64_t>(dst[blockIdx.x]) * words;
+  for (int64_t i = threadIdx.x; i < words; i += blockDim.x) out[i] = in[i];
+}
+
+// Geometry of a decode call at position pos (one query per sequence).
+hga_status session_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, int64_t kv_cap,
+                            int64_t pos, hga::Geometry& g) {
+  return hga::make_geometry(cfg, dtype, batch, kv_cap, pos, 1, g);
+}
+
+hga_status session_layout(const hga_config* cfg, hga_dtype dtype, int32_t batch, int64_t kv_cap,
+                          int64_t cache_slots, SessionLayout& L) {
+  hga::Geometry g;
+  // sizes at the last position: route and attention workspaces only grow
+  // with the context
+  hga_status st = session_geometry(cfg, dtype, batch, kv_cap, kv_cap - 1, g);
+  if (st != HGA_OK) return st;
+  if (dtype != HGA_BF16 || g.G > 16) return HGA_ERR_UNSUPPORTED;  // decode attention kernel
+  if (!hga::route_supported(g) || !hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
+  L.units = static_cast<int64_t>(g.B) * g.Hkv;
+  L.per_step = L.units * g.gmax;
+  if (cache_slots < L.per_step) return HGA_ERR_INVALID_ARGUMENT;
+  L.granule_bytes = static_cast<size_t>(2) * g.gs * g.d * 2;
+  L.row_bytes = static_cast<size_t>(g.d) * 2;
+  if (static_cast<double>(cache_slots) * 2 * g.gs >= 2147483647.0) return HGA_ERR_UNSUPPORTED;
+  L.rws_bytes = hga::route_workspace(g);
+  L.aws_bytes = hga::attend_workspace(g, false, true);
+  const size_t u = static_cast<size_t>(L.units);
+  size_t off = 0;
+  L.cidx = off; off = align_up(off + u * std::max(g.Kc, 1) * 4);
+  L.gidx = off; off = align_up(off + u * std::max(g.Kg, 1) * 4);
+  L.gran = off; off = align_up(off + u * g.gmax * 4);
+  L.gcnt = off; off = align_up(off + u * 4);
+  L.rws = off; off = align_up(off + L.rws_bytes);
+  L.aws = off; off = align_up(off + L.aws_bytes);
+  L.cache = off; off = align_up(off + static_cast<size_t>(cache_slots) * L.granule_bytes);
+  // index block: slots [per_step] int32, src [per_step] int64, dst [per_step] int32
+  L.slots_off = 0;
+  L.src_off = align_up(static_cast<size_t>(L.per_step) * 4);
+  L.dst_off = align_up(L.src_off + static_cast<size_t>(L.per_step) * 8);
+  L.idx_bytes = align_up(L.dst_off + static_cast<size_t>(L.per_step) * 4);
+  L.idx = off; off = align_up(off + L.idx_bytes);
+  L.win_raw = off; off = align_up(off + u * g.C * L.row_bytes);
+  L.win_rot = off; off = align_up(off + u * g.C * L.row_bytes);
+  L.dev_total = off;
+  size_t h = 0;
+  L.hgran = h; h = align_up(h + u * g.gmax * 4);
+  L.hcnt = h; h = align_up(h + u * 4);
+  L.hidx = h; h = align_up(h + L.idx_bytes);
+  L.host_total = h;
+  return HGA_OK;
+}
+
+}  // namespace
+
+struct hga_decode_session {
+  hga_config cfg;
+  hga_dtype dtype;
+  int32_t batch;
+  int64_t kv_cap, cache_slots, ngran;
+  SessionLayout L;
+  char* dev;
+  char* host;
+  char* store;
+  const uint4* store_dev;        // the store's device mapping
+  Lru lru;
+  std::vector<int64_t> slot_of;  // (sequence, KV head, granule) -> cache slot or -1
+  std::vector<int32_t> fill;     // cache slot -> tokens of its granule copy
+  int64_t next_pos;              // position append() expects next
+  explicit hga_decode_session(int64_t slots) : lru(slots) {}
+};
+
+extern "C" {
+
+hga_status hga_decode_session_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                           int64_t kv_cap, int64_t cache_slots,
+                                           size_t* device_bytes, size_t* host_bytes) {
+  if (cfg == nullptr || device_bytes == nullptr || host_bytes == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  SessionLayout L;
+  hga_status st = session_layout(cfg, dtype, batch, kv_cap, cache_slots, L);
+  if (st != HGA_OK) return st;
+  *device_bytes = L.dev_total;
+  *host_bytes = L.host_total;
+  return HGA_OK;
+}
+
+hga_status hga_decode_session_create(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                     int64_t kv_cap, int64_t first_pos, int64_t cache_slots,
+                                     void* kv_host, void* dev_buffer, size_t dev_bytes,
+                                     void* host_buffer, size_t host_bytes,
+                                     hga_decode_session** session) {
+  if (session == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  *session = nullptr;
+  if (cfg == nullptr || kv_host == nullptr || dev_buffer == nullptr || host_buffer == nullptr)
+    return HGA_ERR_INVALID_ARGUMENT;
+  SessionLayout L;
+  hga_status st = session_layout(cfg, dtype, batch, kv_cap, cache_slots, L);
+  if (st != HGA_OK) return st;
+  if (first_pos < 0 || first_pos >= kv_cap || first_pos % cfg->chunk_size != 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(dev_buffer) | reinterpret_cast<uintptr_t>(host_buffer)) % kAlign)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (!pinned_host(kv_host) || !pinned_host(host_buffer)) return HGA_ERR_INVALID_ARGUMENT;
+  if (dev_bytes < L.dev_total || host_bytes < L.host_total) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  void* store_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&store_dev, kv_host, 0);
+  if (e != hipSuccess || store_dev == nullptr) {
+    (void)hipGetLastError();
+    return HGA_ERR_UNSUPPORTED;  // the store must be mapped into the device's address space
+  }
+  hga_decode_session* s = nullptr;
+  try {
+    s = new hga_decode_session(cache_slots);
+    s->cfg = *cfg;
+    s->dtype = dtype;
+    s->batch = batch;
+    s->kv_cap = kv_cap;
+    s->cache_slots = cache_slots;
+    s->ngran = kv_cap / cfg->group_size;
+    s->L = L;
+    s->dev = static_cast<char*>(dev_buffer);
+    s->host = static_cast<char*>(host_buffer);
+    s->store = static_cast<char*>(kv_host);
+    s->store_dev = static_cast<const uint4*>(store_dev);
+    s->slot_of.assign(static_cast<size_t>(L.units * s->ngran), -1);
+    s->fill.assign(static_cast<size_t>(cache_slots), 0);
+    s->next_pos = first_pos;
+  } catch (...) {
+    delete s;
+    return HGA_ERR_INVALID_ARGUMENT;
+  }
+  *session = s;
+  return HGA_OK;
+}
+
+void hga_decode_session_destroy(hga_decode_session* session) { delete session; }
+
+hga_status hga_decode_session_append(hga_decode_session* s, const void* k_raw_new, const void* v_new,
+                                     int64_t pos, float* chunk_sum, float* group_sum,
+                                     void* compute_stream) {
+  if (s == nullptr || k_raw_new == nullptr || v_new == nullptr || chunk_sum == nullptr)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (s->cfg.top_groups > 0 && group_sum == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  if (pos != s->next_pos || pos >= s->kv_cap) return HGA_ERR_INVALID_ARGUMENT;
+  hga::Geometry g;
+  hga_status st = session_geometry(&s->cfg, s->dtype, s->batch, s->kv_cap, pos, g);
+  if (st != HGA_OK) return st;
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  const SessionLayout& L = s->L;
+  const int64_t w0 = pos / g.C * g.C;
+  const size_t row = static_cast<size_t>(pos - w0);
+  const size_t rb = L.row_bytes;
+  char* win_raw = s->dev + L.win_raw;
+  char* win_rot = s->dev + L.win_rot;
+  // raw key into the current chunk's window, then rotation (and the
+  // summaries of the blocks this token closes) on the device
+  hipError_t e = hipMemcpy2DAsync(win_raw + row * rb, g.C * rb, k_raw_new, rb, rb,
+                                  static_cast<size_t>(L.units), hipMemcpyDeviceToDevice, cs);
+  if (e == hipSuccess)
+    e = hga::launch_summarize(g, win_raw, pos, pos + 1, win_rot, chunk_sum, group_sum, cs, w0, g.C);
+  // rotated key and value into the granule-major host store
+  const size_t gb = L.granule_bytes;
+  const int64_t gid = pos / g.gs;
+  const size_t in_gran = static_cast<size_t>(pos % g.gs) * rb;
+  char* dst = s->store + static_cast<size_t>(gid) * gb + in_gran;
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(dst, static_cast<size_t>(s->ngran) * gb, win_rot + row * rb, g.C * rb, rb,
+                         static_cast<size_t>(L.units), hipMemcpyDeviceToHost, cs);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(dst + static_cast<size_t>(g.gs) * rb, static_cast<size_t>(s->ngran) * gb,
+                         v_new, rb, rb, static_cast<size_t>(L.units), hipMemcpyDeviceToHost, cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  s->next_pos = pos + 1;
+  return HGA_OK;
+}
+
+hga_status hga_decode_session_step(hga_decode_session* s, const void* q_raw, int64_t pos,
+                                   const float* chunk_sum, const float* group_sum, void* out,
+                                   float* lse, void* compute_stream, hga_tier_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  if (s == nullptr || q_raw == nullptr || chunk_sum == nullptr || out == nullptr)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (s->cfg.top_groups > 0 && group_sum == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  if (pos < 0 || pos >= s->next_pos) return HGA_ERR_INVALID_ARGUMENT;  // its token must be stored
+  hga::Geometry g;
+  hga_status st = session_geometry(&s->cfg, s->dtype, s->batch, s->kv_cap, pos, g);
+  if (st != HGA_OK) return st;
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+  const SessionLayout& L = s->L;
+  char* dev = s->dev;
+  char* host = s->host;
+  int32_t* d_gran = reinterpret_cast<int32_t*>(dev + L.gran);
+  int32_t* d_gcnt = reinterpret_cast<int32_t*>(dev + L.gcnt);
+  hipError_t e = hga::launch_route(g, q_raw, chunk_sum, group_sum, reinterpret_cast<int32_t*>(dev + L.cidx),
+                                   g.Kg > 0 ? reinterpret_cast<int32_t*>(dev + L.gidx) : nullptr, d_gran,
+                                   d_gcnt, dev + L.rws, cs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host + L.hgran, d_gran, static_cast<size_t>(L.per_step) * 4,
+                       hipMemcpyDeviceToHost, cs);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host + L.hcnt, d_gcnt, static_cast<size_t>(L.units) * 4, hipMemcpyDeviceToHost, cs);
+  // also orders every earlier step's gathers and attention, and every
+  // append's store copies, before the host rewrites the index block
+  if (e == hipSuccess) e = hipStreamSynchronize(cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+
+  const int32_t* h_gran = reinterpret_cast<const int32_t*>(host + L.hgran);
+  const int32_t* h_gcnt = reinterpret_cast<const int32_t*>(host + L.hcnt);
+  char* hidx = host + L.hidx;
+  int32_t* h_slots = reinterpret_cast<int32_t*>(hidx + L.slots_off);
+  int64_t* h_src = reinterpret_cast<int64_t*>(hidx + L.src_off);
+  int32_t* h_dst = reinterpret_cast<int32_t*>(hidx + L.dst_off);
+  int64_t miss = 0, hits = 0;
+  for (int64_t x = 0; x < L.units; ++x) {
+    const int32_t cnt = h_gcnt[x];
+    for (int32_t i = 0; i < g.gmax; ++i) {
+      if (i >= cnt) {
+        h_slots[x * g.gmax + i] = -1;
+        continue;
+      }
+      const int64_t gid = h_gran[x * g.gmax + i];
+      const int64_t k = x * s->ngran + gid;
+      const int64_t last = std::min<int64_t>(g.gs, pos + 1 - gid * g.gs);  // tokens this step needs
+      int64_t sl = s->slot_of[static_cast<size_t>(k)];
+      if (sl >= 0 && s->fill[static_cast<size_t>(sl)] >= last) {
+        ++hits;
+      } else {
+        if (sl < 0) {
+          sl = s->lru.victim();  // untouched in this step (per_step <= cache_slots)
+          const int64_t prev = s->lru.owner(sl);
+          if (prev >= 0) s->slot_of[static_cast<size_t>(prev)] = -1;
+          s->lru.set_owner(sl, k);
+          s->slot_of[static_cast<size_t>(k)] = sl;
+        }
+        s->fill[static_cast<size_t>(sl)] = static_cast<int32_t>(last);
+        h_src[miss] = k;
+        h_dst[miss] = static_cast<int32_t>(sl);
+        ++miss;
+      }
+      s->lru.touch(sl);
+      h_slots[x * g.gmax + i] = static_cast<int32_t>(sl);
+    }
+  }
+  const double lookup_s =
+      std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+  // the index block to the device, then the misses straight from the store
+  e = hipMemcpyAsync(dev + L.idx, hidx, L.idx_bytes, hipMemcpyHostToDevice, cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  const size_t gb = L.granule_bytes;
+  char* cache = dev + L.cache;
+  if (miss > 0) {
+    hipLaunchKernelGGL(fetch_granules, dim3(static_cast<unsigned>(miss)), dim3(256), 0, cs, s->store_dev,
+                       reinterpret_cast<const int64_t*>(dev + L.idx + L.src_off),
+                       reinterpret_cast<const int32_t*>(dev + L.idx + L.dst_off),
+                       reinterpret_cast<uint4*>(cache), static_cast<int64_t>(gb / 16));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hga::hip_fail(e);
+  }
+  hga::AttendExtra ex;
+  ex.pool_slot = reinterpret_cast<const int32_t*>(dev + L.idx + L.slots_off);
+  ex.pool_slots = s->cache_slots;
+  ex.allow_split = true;
+  e = hga::launch_attend(g, q_raw, cache, cache, d_gran, d_gcnt, false, out, lse, dev + L.aws, cs, &ex);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  if (stats != nullptr) {
+    stats->windows = 1;
+    stats->granules_copied = miss;
+    stats->bytes_h2d = static_cast<int64_t>(static_cast<size_t>(miss) * gb + L.idx_bytes);
+    stats->pack_seconds = lookup_s;
+    stats->host_seconds =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+    stats->granules_hit = hits;
+  }
+  return HGA_OK;
+}
+
+}  // extern "C"

@@ -25,6 +25,9 @@ struct SumParams {
   float* chunk_sum;
   float* group_sum;
   int64_t kv_cap, tok_begin, tok_end, chunk_first;
+  // k_raw / k_rot hold tokens [k_first, k_first + k_rows) of every
+  // (sequence, KV head), k_rows rows apart (the whole cache: 0, kv_cap)
+  int64_t k_first, k_rows;
   int Hkv, d, C, gs, r, n_hf;
   RopeFreqs rope;
 };
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
   const int64_t m = p.chunk_first + blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int64_t slab = (static_cast<int64_t>(b) * p.Hkv + kvh) * p.kv_cap;
+  const int64_t slab = (static_cast<int64_t>(b) * p.Hkv + kvh) * p.k_rows - p.k_first;
   const int64_t c0 = m * p.C;
   const int64_t c1 = c0 + p.C;
   const int64_t tend = c1 < p.tok_end ? c1 : p.tok_end;
@@ -121,8 +124,11 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
 
 hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_begin,
                             int64_t tok_end, void* k_rot, float* chunk_sum,
-                            float* group_sum, hipStream_t stream) {
+                            float* group_sum, hipStream_t stream, int64_t k_first,
+                            int64_t k_rows) {
   SumParams p;
+  p.k_first = k_first;
+  p.k_rows = k_rows > 0 ? k_rows : g.kv_cap;
   p.k_raw = k_raw;
   p.k_rot = k_rot;
   p.chunk_sum = chunk_sum;

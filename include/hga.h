@@ -262,6 +262,64 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
                                   void* compute_stream, void* copy_stream,
                                   hga_tier_stats* stats);
 
+/*
+ * Streaming decode from the host tier (xllm-io page, section 3, tiered K/V
+ * store, RAM-cached decode): the token K/V history stays in the pinned
+ * granule-major host store (layout of hga_attend_host_tiered), summaries and
+ * routing on the device, and a device cache of cache_slots granules keeps
+ * what earlier steps brought over (least recently used evicted first).
+ *
+ * A session (host object) owns the cache bookkeeping; the caller owns and
+ * allocates every buffer: kv_host (pinned, hipHostMalloc, mapped into the
+ * device's address space: the device reads missing granules from it
+ * directly over the host link), dev_buffer
+ * (device, 256-byte aligned, hga_decode_session_buffer_bytes), host_buffer
+ * (pinned, 256-byte aligned) and the summary tables chunk_sum / group_sum of
+ * hga_build_summaries.  bf16 only, at most 16 query heads per KV head,
+ * cache_slots >= batch * n_kv_heads * hga_max_granules(cfg).
+ *
+ * hga_decode_session_create: the store holds tokens [0, first_pos) and the
+ *   summary tables every chunk below first_pos; first_pos % C == 0.
+ * hga_decode_session_append: token pos (pos = the previous append + 1, the
+ *   first one first_pos) of every sequence: k_raw_new / v_new
+ *   [B][Hkv][1][d] device rows (raw key, value).  Rotates the key on the
+ *   device, writes the chunk and group summaries the token closes, and
+ *   copies the rotated key and the value into the host store (asynchronous on
+ *   compute_stream).  Unwritten store rows must hold finite values.
+ * hga_decode_session_step: one query per sequence at position pos (<= the
+ *   last appended position): q_raw [B][Hq][1][d], out [B][Hq][1][d], lse
+ *   [B][Hq][1] (may be NULL).  Same outputs as hga_route + hga_attend with
+ *   q_pos0 = pos, n_q = 1 over the device-resident cache.  Host-blocking: it
+ *   waits for the route's granule lists, looks the granules up in the cache,
+ *   then enqueues on compute_stream the gather of the misses from the store
+ *   and the attention.  A granule cached while it held fewer tokens than the
+ *   step needs is fetched again.  stats (may be NULL): granules fetched
+ *   (granules_copied) / found (granules_hit), bytes over the host link,
+ *   pack_seconds = host lookup time, host_seconds = whole call.
+ * Calls on one session must not overlap.
+ */
+typedef struct hga_decode_session hga_decode_session;
+
+hga_status hga_decode_session_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                           int64_t kv_cap, int64_t cache_slots,
+                                           size_t* device_bytes, size_t* host_bytes);
+
+hga_status hga_decode_session_create(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                     int64_t kv_cap, int64_t first_pos, int64_t cache_slots,
+                                     void* kv_host, void* dev_buffer, size_t dev_bytes,
+                                     void* host_buffer, size_t host_bytes,
+                                     hga_decode_session** session);
+
+void hga_decode_session_destroy(hga_decode_session* session);
+
+hga_status hga_decode_session_append(hga_decode_session* session, const void* k_raw_new,
+                                     const void* v_new, int64_t pos, float* chunk_sum,
+                                     float* group_sum, void* compute_stream);
+
+hga_status hga_decode_session_step(hga_decode_session* session, const void* q_raw, int64_t pos,
+                                   const float* chunk_sum, const float* group_sum, void* out,
+                                   float* lse, void* compute_stream, hga_tier_stats* stats);
+
 const char* hga_status_string(hga_status status);
 
 /* hipError_t of the last failed HIP call made by this thread (0 if none). */

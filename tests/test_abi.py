@@ -60,6 +60,32 @@ def test_struct_layouts_match_header(tmp_path):
     assert got == want
 
 
+def test_decode_session_sizes_and_checks(lib):
+    """Streaming decode sessions: buffer sizes, and argument checks that fail
+    before any HIP call (pointers here are never dereferenced)."""
+    cfg = H.Config.from_workload(W.DECODE_64K)
+    c = ctypes.byref(cfg.c())
+    cap = 65600
+    need = 16 * 4 * H.max_granules(cfg)
+    dev, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.hga_decode_session_buffer_bytes(c, 1, 16, cap, need, ctypes.byref(dev), ctypes.byref(host)) == 0
+    granule = 2 * 16 * 128 * 2
+    assert dev.value > need * granule and host.value > 0
+    # the cache must hold one step's granules; bf16 only
+    assert lib.hga_decode_session_buffer_bytes(c, 1, 16, cap, need - 1, ctypes.byref(dev), ctypes.byref(host)) == 1
+    assert lib.hga_decode_session_buffer_bytes(c, 0, 16, cap, need, ctypes.byref(dev), ctypes.byref(host)) == 2
+    h = ctypes.c_void_p(None)
+    # missing buffers, then a first position off a chunk boundary
+    assert lib.hga_decode_session_create(c, 1, 16, cap, 65536, need, None, 256, 1 << 30, 256, 1 << 20,
+                                         ctypes.byref(h)) == 1
+    assert lib.hga_decode_session_create(c, 1, 16, cap, 65537, need, 256, 256, 1 << 30, 256, 1 << 20,
+                                         ctypes.byref(h)) == 1
+    assert h.value is None
+    assert lib.hga_decode_session_append(None, 16, 16, 0, 16, 16, None) == 1
+    assert lib.hga_decode_session_step(None, 16, 0, 16, 16, 16, None, None, None) == 1
+    lib.hga_decode_session_destroy(None)
+
+
 def test_status_strings(lib):
     for code, name in H._STATUS.items():
         assert lib.hga_status_string(code).decode() == name

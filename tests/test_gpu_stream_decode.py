@@ -1,0 +1,117 @@
+"""Streaming decode from the host tier (DecodeSession) against the
+device-resident path: every step's output and LSE bit for bit, the session's
+summaries and host store after the appends, with a roomy cache and with the
+smallest allowed one (evictions on every step)."""
+import numpy as np
+import pytest
+
+import hierarchical_kv_routing_amd as H
+import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+PREFIX = 4096
+STEPS = 140   # crosses a chunk boundary; the closed chunk is routed later (L = 1)
+CAP = PREFIX + 192
+
+
+def _workload(**kw):
+    base = dict(batch=2, n_ctx=PREFIX + STEPS, kv_cap=CAP, q_pos0=PREFIX, n_q=STEPS,
+                n_recent_chunks=1, planted=0, planted_per_q_head=1)
+    base.update(kw)
+    return W.DECODE_64K.scaled(**base)
+
+
+def _reference(run, w, dev):
+    """Device-resident route + attend of every step's query."""
+    import torch
+    cfg = run.cfg
+    outs, lses = [], []
+    for s in range(w.n_q):
+        pos = w.q_pos0 + s
+        q = run.q[:, :, s:s + 1].contiguous()
+        ro = H.route_outputs(cfg, w.batch, pos, 1, dev)
+        H.route(cfg, q, pos, run.csum, run.gsum, CAP, ro["chunk_idx"], ro["group_idx"],
+                ro["granules"], ro["granule_count"], ro["workspace"])
+        aw = H.attend_workspace_bytes(cfg, w.batch, pos, 1)
+        ws = torch.empty(max(aw, 16), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        H.attend(cfg, q, pos, run.k_rot, run.v, ro["granules"], ro["granule_count"], out, lse, ws)
+        outs.append(out)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    return outs, lses
+
+
+def _session_run(run, w, cache_slots, dev):
+    import torch
+    cfg = run.cfg
+    # store and summary tables hold only the prefix; the session appends the rest
+    k_rot = run.k_rot.clone()
+    v = run.v.clone()
+    k_rot[:, :, PREFIX:] = 0
+    v[:, :, PREFIX:] = 0
+    store = H.host_store(cfg, k_rot, v)
+    csum = run.csum.clone()
+    gsum = run.gsum.clone()
+    csum[:, :, PREFIX // cfg.chunk_size:] = 0
+    gsum[:, :, PREFIX // cfg.group_size:] = 0
+    sess = H.DecodeSession(cfg, w.batch, CAP, PREFIX, cache_slots, store, device=dev)
+    outs, lses, stats = [], [], []
+    for s in range(w.n_q):
+        pos = w.q_pos0 + s
+        sess.append(run.k[:, :, pos:pos + 1].contiguous(), run.v[:, :, pos:pos + 1].contiguous(),
+                    pos, csum, gsum)
+        q = run.q[:, :, s:s + 1].contiguous()
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+        stats.append(sess.step(q, pos, csum, gsum, out, lse))
+        outs.append(out)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    sess.close()
+    return outs, lses, stats, csum, gsum, store
+
+
+@pytest.mark.parametrize("cache", ["roomy", "smallest"])
+def test_stream_decode_equals_device_path(cache):
+    import torch
+    w = _workload()
+    dev = torch.device("cuda:0")
+    q, k, v = P.make_inputs_parallel(w)
+    print(f"[gpu] stream decode ({cache}): {w}", flush=True)
+    run = P.GpuRun(w, q, k, v, route=False, attend=False)
+    ref_out, ref_lse = _reference(run, w, dev)
+    need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
+    slots = need if cache == "smallest" else 4 * need
+    outs, lses, stats, csum, gsum, store = _session_run(run, w, slots, dev)
+    bad = [s for s in range(w.n_q)
+           if not (torch.equal(outs[s], ref_out[s]) and torch.equal(lses[s], ref_lse[s]))]
+    assert not bad, f"steps differing from the device path: {bad[:10]}"
+    n_closed = (PREFIX + STEPS) // run.cfg.chunk_size
+    assert torch.equal(csum[:, :, :n_closed], run.csum[:, :, :n_closed])
+    ng_closed = (PREFIX + STEPS) // run.cfg.group_size
+    assert torch.equal(gsum[:, :, :ng_closed], run.gsum[:, :, :ng_closed])
+    ref_store = H.host_store(run.cfg, run.k_rot, run.v)
+    ng = (PREFIX + STEPS + run.cfg.group_size - 1) // run.cfg.group_size
+    got = store[:, :, :ng].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
+    want = ref_store[:, :, :ng].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
+    # token rows [0, PREFIX + STEPS) of both halves (K, V)
+    g = run.cfg.group_size
+    sel = np.arange(ng * 2 * g).reshape(ng, 2, g)
+    tok = (np.arange(ng)[:, None, None] * g + np.arange(g)[None, None, :]).repeat(2, axis=1)
+    rows = sel[tok < PREFIX + STEPS]
+    assert torch.equal(got[:, :, rows], want[:, :, rows])
+    copied = [st["granules_copied"] for st in stats]
+    hits = [st["granules_hit"] for st in stats]
+    print(f"[gpu] stream decode ({cache}): copied first {copied[0]} then mean "
+          f"{np.mean(copied[1:]):.1f}, hits mean {np.mean(hits[1:]):.1f}", flush=True)
+    assert copied[0] > 0 and hits[0] == 0
+    if cache == "roomy":
+        # later steps find the fixed windows (and any repeated routes) in the
+        # cache: only the granule being filled and new routes are copied
+        # (the synthetic queries are independent, so routes change a lot)
+        assert np.mean(copied[1:]) < 0.5 * copied[0]
+        assert min(hits[1:]) > 0
