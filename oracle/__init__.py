@@ -17,7 +17,9 @@ framework paragraph (chunks of C tokens split into groups of g_s), Eq. (1)
 summary equation, the routing-policy rules and the top-K_c / top-K_g
 selection equation, and the exact-token output paragraph; Sec. 5.5 as given
 there (RoPE position index wrapped modulo 65536, the ``period`` option of
-``hga_ref.rope_position``); RoPE itself follows RoFormer (cited by the pages).
+``hga_ref.rope_position``); the gradients of exact-token attention over fixed
+routes (``hga_ref.attend_backward``, the training path the pages time);
+RoPE itself follows RoFormer (cited by the pages).
 
 Readings where the pages are silent are listed in each function's docstring.
 Parity unpinned (conventions with no page value behind them, checked only as

@@ -341,6 +341,70 @@ def attend_given(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, p: Par
     return out, lse
 
 
+def unrope(x: np.ndarray, pos, theta: float, period: int = 0) -> np.ndarray:
+    """R_p^T x: the transpose (inverse) rotation, i.e. a turn by -p * theta_i
+    with p the (wrapped) position index."""
+    return rope(x, -rope_position(pos, period), theta)
+
+
+def attend_backward(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, d_out, p: Params,
+                    t0: int = None, units=None):
+    """Gradients of exact-token attention over fixed granule lists.
+
+    The routes are a discrete choice and stay fixed (no gradient flows
+    through summaries or selection); the gradient is that of the exact-token
+    softmax attention of each query row over its visible tokens (xllm-io
+    page, section 3, exact-token output; Eq. (1) restricted to the visible
+    set), with RoPE applied to the raw q and k.  For one row i with visible
+    set V_i, scale s, rotated q~_i, k~_j:
+      P_ij = softmax_j(s q~_i . k~_j),  O_i = sum_j P_ij v_j,
+      dv_j += P_ij dO_i,  dP_ij = dO_i . v_j,  D_i = dO_i . O_i,
+      dS_ij = P_ij (dP_ij - D_i),
+      dq~_i = s sum_j dS_ij k~_j,  dk~_j += s dS_ij q~_i,
+    and the raw gradients are the transposed rotations dq_i = R_i^T dq~_i,
+    dk_j = R_j^T dk~_j.  A KV head's K/V gradients sum over the G query heads
+    that read it.  Returns dq [B,Hq,n_q,d], dk, dv [B,Hkv,kv_cap,d] (float64;
+    rows of units not listed stay 0).
+    """
+    q = np.asarray(q_raw, np.float64)
+    do = np.asarray(d_out, np.float64)
+    B = q.shape[0]
+    G = p.Hq // p.Hkv
+    tq = list(query_chunks(q_pos0, n_q, p.C))
+    if t0 is None:
+        t0 = tq[0]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(np.asarray(k_raw).shape)
+    dv = np.zeros(np.asarray(v).shape)
+    if units is None:
+        units = [(b, h, t) for b in range(B) for h in range(p.Hkv) for t in tq]
+    sc = p.softmax_scale
+    for (b, kvh, t) in units:
+        gl = np.asarray(granules[b, kvh, t - t0, : int(count[b, kvh, t - t0])], np.int64)
+        tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
+        kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period)
+        vv = np.asarray(v[b, kvh][tok], np.float64)
+        qpos = unit_queries(t, q_pos0, n_q, p.C)
+        mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
+        dkk = np.zeros(kk.shape)
+        for hl in range(G):
+            h = kvh * G + hl
+            rows = rope(q[b, h, qpos - q_pos0, :], qpos, p.theta, p.period)
+            logits = np.where(mask, (rows @ kk.T) * sc, -np.inf)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            o = P @ vv
+            g = do[b, h, qpos - q_pos0, :]
+            dv[b, kvh][tok] += P.T @ g
+            dP = g @ vv.T
+            D = (g * o).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[b, h, qpos - q_pos0, :] = unrope(sc * (dS @ kk), qpos, p.theta, p.period)
+            dkk += sc * (dS.T @ rows)
+        dk[b, kvh][tok] += unrope(dkk, tok, p.theta, p.period)
+    return dq, dk, dv
+
+
 def dense_causal(q_raw, q_pos0: int, n_q: int, k_raw, v, p: Params, heads=None, q_index=None):
     """Eq. (1): each query i attends to every key j <= i (RoPE on q and k).
 

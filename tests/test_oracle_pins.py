@@ -434,6 +434,77 @@ def test_wrapped_dense_pattern_by_hand():
         np.testing.assert_allclose(lse[0, 0, i], lg.max() + math.log(wts.sum()), atol=1e-12)
 
 
+# ------------------------------------------------------------ backward ----
+# Gradients of exact-token attention with the routes held fixed.
+
+
+def _loss_and_grads(w, q, k, v, seed):
+    p, rt, out, _ = _oracle_pipeline(w, q, k, v)
+    do = np.random.default_rng(seed).standard_normal(out.shape)
+    dq, dk, dv = R.attend_backward(q, w.q_pos0, w.n_q, k, v, rt["granules"], rt["count"], do, p,
+                                   t0=rt["t0"])
+
+    def loss(qq, kk, vv):
+        o, _ = R.attend_given(qq, w.q_pos0, w.n_q, kk, vv, rt["granules"], rt["count"], p, t0=rt["t0"])
+        return float((o * do).sum())
+    return loss, dq, dk, dv
+
+
+@pytest.mark.parametrize("kw", [{}, dict(top_groups=0, q_pos0=21, n_q=75), dict(rope_period=32)])
+def test_backward_matches_finite_differences(kw):
+    """dL/dq, dL/dk, dL/dv of L = sum(dO * O) against central differences of
+    the oracle's forward (fp64, h = 1e-6), at random coordinates, including
+    keys seen through routed groups, sinks and the current chunk."""
+    w = _tiny_workload(**kw)
+    q, k, v = W.make_inputs(w, seed=21)
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    loss, dq, dk, dv = _loss_and_grads(w, q, k, v, seed=22)
+    rng = np.random.default_rng(23)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        n_tok = w.q_pos0 + w.n_q if name != "q" else w.n_q
+        for _ in range(8):
+            idx = (int(rng.integers(x.shape[0])), int(rng.integers(x.shape[1])),
+                   int(rng.integers(n_tok)), int(rng.integers(x.shape[3])))
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def test_backward_full_coverage_matches_torch_autograd():
+    """With budgets covering every middle chunk the routed backward is the
+    dense causal backward: torch fp64 autograd through its own RoPE (complex
+    rotation) and SDPA with is_causal gives the same raw-input gradients."""
+    torch = pytest.importorskip("torch")
+    w = _tiny_workload(n_ctx=128, kv_cap=128, n_q=128, top_chunks=16, top_groups=64)
+    q, k, v = W.make_inputs(w, seed=24)
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    _, dq, dk, dv = _loss_and_grads(w, q, k, v, seed=25)
+    do = np.random.default_rng(25).standard_normal(q.shape)
+    G = w.n_q_heads // w.n_kv_heads
+    d = w.head_dim
+    freq = torch.tensor(w.rope_theta ** (-2.0 * np.arange(d // 2) / d), dtype=torch.float64)
+    pos = torch.arange(128, dtype=torch.float64)
+    rot = torch.polar(torch.ones(128, d // 2, dtype=torch.float64), pos[:, None] * freq[None, :])
+
+    def rope_t(x):
+        z = torch.complex(x[..., : d // 2], x[..., d // 2:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        rope_t(qt), rope_t(kt).repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), is_causal=True)
+    (o * torch.tensor(do)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-10)
+
+
 # ---------------------------------------------------------------- Eq. 2 ----
 
 @pytest.mark.parametrize("kw", [{}, dict(top_groups=0), dict(q_pos0=21, n_q=75), dict(n_recent_chunks=0)])
