@@ -16,10 +16,11 @@ Also measured in the same run (extra fields of the one JSON line):
              (with and without the device cache of granules);
   decode_host_tier_stream -- the decode shape streamed token by token with
              its K/V history in pinned host RAM (DecodeSession);
+  backward -- hga_attend_backward (dq, dk, dv) on the prefill's routes;
   cpu_baseline -- the CPU oracle on a bounded sample of the prefill step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prefill|decode|smalllm|host|stream|copy|peaks]
+       [--only prefill|decode|smalllm|host|stream|backward|copy|peaks]
 """
 from __future__ import annotations
 
@@ -220,6 +221,40 @@ def bench_prefill(args):
     res = dict(ms=ms, stage_ms=stage, pairs=pairs, attend_flops=flops,
                attend_tflops=attend_tflops, tokens=w.n_q)
     return pipe, res
+
+
+def bench_backward(args, pipe=None, pairs=None):
+    """hga_attend_backward on the Qwen3-shaped prefill (routes and forward
+    outputs of one forward step held fixed, a random dO): dq, dk, dv."""
+    import torch
+    import hierarchical_kv_routing_amd as H
+    w = W.QWEN3_PREFILL
+    if pipe is None:
+        pipe = Pipeline(w)
+        pipe.build()
+        pipe.route()
+    lse = torch.empty(pipe.q.shape[:3], dtype=torch.float32, device="cuda:0")
+    H.attend(pipe.cfg, pipe.q, w.q_pos0, pipe.k_rot, pipe.v, pipe.ro["granules"],
+             pipe.ro["granule_count"], pipe.out, lse, pipe.aws)
+    if pairs is None:
+        pairs = visible_pairs(w, pipe.ro["granule_count"].cpu().numpy())
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7)
+    d_out = torch.randn(pipe.q.shape, generator=g, device="cuda:0").to(torch.bfloat16)
+    dq = torch.empty(pipe.q.shape, dtype=torch.float32, device="cuda:0")
+    dk = torch.empty(pipe.k.shape, dtype=torch.float32, device="cuda:0")
+    dv = torch.empty(pipe.k.shape, dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(H.attend_backward_workspace_bytes(pipe.cfg, w.batch, w.q_pos0, w.n_q), 16),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def bwd():
+        H.attend_backward(pipe.cfg, pipe.q, w.q_pos0, pipe.k_rot, pipe.v, pipe.ro["granules"],
+                          pipe.ro["granule_count"], pipe.out, lse, d_out, dq, dk, dv, ws)
+    ms, _ = timed_steps(torch, [("backward", bwd)], max(4, args.steps // 5), max(2, args.warmup // 5))
+    flops = 8.0 * w.head_dim * pairs  # dP, dQ, dK, dV: 2 flops per MAC, 4 products
+    return dict(workload=w.name, ms=ms, algorithmic_flops=flops, tflops=flops / (ms * 1e-3) / 1e12,
+                frac_of_peak=flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                timing="HIP events around hga_attend_backward (clear, D, dq, dk/dv, R^T kernels)")
 
 
 def graph_step_ms(torch, fns, steps, warmup=3):
@@ -471,8 +506,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "stream", "copy", "peaks"],
-                    default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "stream", "backward", "copy",
+                                       "peaks"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -500,6 +535,9 @@ def main():
         res = {w.name + ("" if c == 0 else "_warm_tier"): bench_host_tier(args, w, gbs, cache_slots=c)
                for w in (W.HOST_TIERED_CHUNK, W.HOST_TIERED_GROUP) for c in (0, WARM_TIER_SLOTS)}
         print(json.dumps(dict(host_tiered=res)), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps(dict(backward=bench_backward(args))), flush=True)
         return
     if args.only == "stream":
         print(json.dumps(dict(decode_host_tier_stream=bench_stream_decode(args))), flush=True)
@@ -535,6 +573,8 @@ def main():
         line["roofline"]["frac_of_measured_peak"] = pre["attend_tflops"] / peaks["mfma_bf16_tflops"]
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(pipe)
+        line["backward"] = bench_backward(args, pipe, pre["pairs"])
+        log(f"[bench] backward: {line['backward']}")
         del pipe
         torch.cuda.empty_cache()
         _, dec = bench_decode(args)

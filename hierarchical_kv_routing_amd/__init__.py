@@ -34,7 +34,8 @@ ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_b
                "hga_host_tiered_buffer_bytes", "hga_attend_host_tiered",
                "hga_decode_session_buffer_bytes", "hga_decode_session_create",
                "hga_decode_session_destroy", "hga_decode_session_append",
-               "hga_decode_session_step", "hga_status_string", "hga_last_hip_error")
+               "hga_decode_session_step", "hga_attend_backward_workspace_bytes",
+               "hga_attend_backward", "hga_status_string", "hga_last_hip_error")
 
 
 class HGAError(RuntimeError):
@@ -134,6 +135,9 @@ def lib() -> ctypes.CDLL:
         "hga_decode_session_destroy": (None, [P]),
         "hga_decode_session_append": (I32, [P, P, P, I64, P, P, P]),
         "hga_decode_session_step": (I32, [P, P, I64, P, P, P, P, P, ctypes.POINTER(hga_tier_stats)]),
+        "hga_attend_backward_workspace_bytes": (SZ, [CP, I32, I64, I64]),
+        "hga_attend_backward": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, P, P, P,
+                                      P, SZ, P]),
         "hga_status_string": (ctypes.c_char_p, [I32]),
         "hga_last_hip_error": (ctypes.c_int, []),
     }
@@ -361,6 +365,37 @@ def attend_host_tiered(cfg: Config, q, q_pos0: int, kv_host, kv_cap: int, chunk_
         ctypes.c_void_p(xs.cuda_stream), ctypes.byref(stats))
     _check(st, "hga_attend_host_tiered")
     return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}
+
+
+def attend_backward_workspace_bytes(cfg: Config, batch: int, q_pos0: int, n_q: int) -> int:
+    return int(lib().hga_attend_backward_workspace_bytes(ctypes.byref(cfg.c()), batch, q_pos0, n_q))
+
+
+def attend_backward(cfg: Config, q, q_pos0: int, k_rot, v, granules, granule_count, out, lse, d_out,
+                    dq, dk, dv, workspace, stream=None):
+    """dq, dk, dv (f32) of exact-token attention over fixed granule lists."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    kv_cap = k_rot.shape[2]
+    _dev(q, "q")
+    for t, name in ((out, "out"), (d_out, "d_out")):
+        _dev(t, name, q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, n_q), torch.float32)
+    _dev(k_rot, "k_rot", k_rot.shape, q.dtype)
+    _dev(v, "v", k_rot.shape, q.dtype)
+    _dev(dq, "dq", q.shape, torch.float32)
+    _dev(dk, "dk", k_rot.shape, torch.float32)
+    _dev(dv, "dv", k_rot.shape, torch.float32)
+    _dev(granules, "granules")
+    _dev(granule_count, "granule_count")
+    _dev(workspace, "workspace")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib().hga_attend_backward(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q, k_rot.data_ptr(), v.data_ptr(),
+        kv_cap, granules.data_ptr(), granule_count.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        d_out.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(s.cuda_stream))
+    _check(st, "hga_attend_backward")
 
 
 def decode_session_buffer_bytes(cfg: Config, dtype, batch: int, kv_cap: int, cache_slots: int):

@@ -213,4 +213,39 @@ hga_status hga_dense_causal(const hga_config* cfg, hga_dtype dtype, int32_t batc
                        true, out, lse, workspace, workspace_bytes, stream);
 }
 
+size_t hga_attend_backward_workspace_bytes(const hga_config* cfg, int32_t batch, int64_t q_pos0,
+                                           int64_t n_q) {
+  hga::Geometry g;
+  if (cfg == nullptr || cfg->chunk_size <= 0) return 0;
+  const int64_t capc = ((q_pos0 + n_q + cfg->chunk_size - 1) / cfg->chunk_size) * cfg->chunk_size;
+  if (make_geometry(cfg, HGA_BF16, batch, capc > 0 ? capc : cfg->chunk_size, q_pos0, n_q, g) != HGA_OK)
+    return 0;
+  return hga::backward_workspace(g);
+}
+
+hga_status hga_attend_backward(const hga_config* cfg, hga_dtype dtype, int32_t batch, const void* q_raw,
+                               int64_t q_pos0, int64_t n_q, const void* k_rot, const void* v,
+                               int64_t kv_cap, const int32_t* granules, const int32_t* granule_count,
+                               const void* out, const float* lse, const void* d_out, float* dq,
+                               float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  hga::Geometry g;
+  hga_status st = make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return HGA_OK;
+  if (q_raw == nullptr || k_rot == nullptr || v == nullptr || granules == nullptr ||
+      granule_count == nullptr || out == nullptr || lse == nullptr || d_out == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_raw) || !aligned16(k_rot) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(d_out) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (!hga::backward_supported(g) || !hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
+  const size_t need = hga::backward_workspace(g);
+  if (workspace == nullptr || workspace_bytes < need) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = hga::launch_backward(g, q_raw, k_rot, v, granules, granule_count, out, lse, d_out, dq,
+                                      dk, dv, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HGA_OK : hip_fail(e);
+}
+
 }  // extern "C"

@@ -77,4 +77,14 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
                          void* out, float* lse, void* ws, hipStream_t stream,
                          const AttendExtra* extra = nullptr);
 
+// Backward of routed exact-token attention (bf16): dq (raw queries), dk (raw
+// keys) and dv, all f32; dk and dv are overwritten.  Workspace: one f32 per
+// query row.
+bool backward_supported(const Geometry& g);
+size_t backward_workspace(const Geometry& g);
+hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, const void* v,
+                           const int32_t* granules, const int32_t* granule_count, const void* out,
+                           const float* lse, const void* d_out, float* dq, float* dk, float* dv,
+                           void* ws, hipStream_t stream);
+
 }  // namespace hga

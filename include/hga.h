@@ -263,6 +263,33 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
                                   hga_tier_stats* stats);
 
 /*
+ * hga_attend_backward -- gradients of exact-token attention (the training
+ * path; xllm-io page, section 3, exact-token output, Eq. 1 restricted to the
+ * visible tokens) with the routes of a forward hga_route held fixed: no
+ * gradient flows through summaries or selection.
+ *   q_raw, out, d_out : [B][Hq][n_q][d] (dtype; out and lse from hga_attend
+ *                       on the same inputs, d_out = dL/d out)
+ *   k_rot, v          : [B][Hkv][kv_cap][d] (dtype)
+ *   granules, granule_count : the forward's lists
+ *   dq                : [B][Hq][n_q][d] f32, dL/d q_raw (through R^T)
+ *   dk, dv            : [B][Hkv][kv_cap][d] f32, dL/d k_raw (through R^T) and
+ *                       dL/d v; overwritten (zero where no query looks)
+ * With P = exp(s q~.k~ - lse): dP = dO.v, D = dO.O, dS = P (dP - D),
+ * dq~ = s dS k~, dk~ = s dS^T q~, dv = P^T dO.  bf16 only.  Workspace:
+ * hga_attend_backward_workspace_bytes (one f32 per query row).
+ */
+size_t hga_attend_backward_workspace_bytes(const hga_config* cfg, int32_t batch, int64_t q_pos0,
+                                           int64_t n_q);
+
+hga_status hga_attend_backward(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                               const void* q_raw, int64_t q_pos0, int64_t n_q,
+                               const void* k_rot, const void* v, int64_t kv_cap,
+                               const int32_t* granules, const int32_t* granule_count,
+                               const void* out, const float* lse, const void* d_out,
+                               float* dq, float* dk, float* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Streaming decode from the host tier (xllm-io page, section 3, tiered K/V
  * store, RAM-cached decode): the token K/V history stays in the pinned
  * granule-major host store (layout of hga_attend_host_tiered), summaries and

@@ -86,6 +86,24 @@ def test_decode_session_sizes_and_checks(lib):
     lib.hga_decode_session_destroy(None)
 
 
+def test_backward_checks(lib):
+    """hga_attend_backward: workspace size and host-side argument checks."""
+    cfg = H.Config.from_workload(W.QWEN3_PREFILL)
+    c = ctypes.byref(cfg.c())
+    need = H.attend_backward_workspace_bytes(cfg, 1, 0, 32768)
+    assert need >= 32 * 32768 * 4
+    args = [c, 1, 1, 16, 0, 64, 16, 16, 64, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None]
+    bad = list(args)
+    bad[3] = None  # no queries
+    assert lib.hga_attend_backward(*bad) == 1
+    f32 = list(args)
+    f32[1] = 0  # f32 inputs: not supported by the backward
+    assert lib.hga_attend_backward(*f32) == 2
+    small = list(args)
+    small[17], small[18] = 16, 4  # workspace too small
+    assert lib.hga_attend_backward(*small) == 3
+
+
 def test_status_strings(lib):
     for code, name in H._STATUS.items():
         assert lib.hga_status_string(code).decode() == name

@@ -1,0 +1,109 @@
+"""GPU backward of routed exact-token attention vs the fp64 oracle
+(oracle.hga_ref.attend_backward) on the GPU's own granule lists.
+
+Tolerance: the products take bf16 operands (scaled rotated queries, keys,
+values, dO, P and dS are each rounded once to 8 significant bits, relative
+error <= 2^-9) with f32 accumulation, so each gradient element carries a
+relative error of a few 2^-9 on its largest terms; over whole tensors the
+rel-L2 error must stay <= 1.5e-2 and every element within 3e-2 of the
+tensor's largest magnitude.  Keys no query sees get exactly zero.
+"""
+import numpy as np
+import pytest
+
+import hierarchical_kv_routing_amd as H
+import workloads as W
+from oracle import hga_ref as R
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1.5e-2
+MAX_REL = 3e-2
+
+CASES = {
+    "qwen3_ragged": W.QWEN3_PREFILL.scaled(n_ctx=1011, kv_cap=1024, n_q=1011, planted=8),
+    "qwen3_ragged_start": W.QWEN3_PREFILL.scaled(n_ctx=1011, kv_cap=1024, q_pos0=200, n_q=811, planted=8),
+    "chunk_only": W.HOST_TIERED_CHUNK.scaled(n_ctx=1500, kv_cap=1536, n_q=1500, planted=8),
+    "smalllm_d64": W.SMALLLM_PREFILL.scaled(batch=2, n_q_heads=4, n_kv_heads=4, n_ctx=1000,
+                                            kv_cap=1024, n_q=1000, planted=8),
+    "rope_wrap_p256": W.QWEN3_PREFILL.scaled(n_ctx=900, kv_cap=960, n_q=900, planted=8, rope_period=256),
+    "decode_single_query": W.DECODE_64K.scaled(batch=2, n_ctx=3073, kv_cap=3136, q_pos0=3072, n_q=1),
+}
+
+
+def _compare(name, got, ref, unseen=None):
+    g = got.cpu().numpy().astype(np.float64)
+    err = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    mx = np.abs(g - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err <= REL_L2 and mx <= MAX_REL, (name, err, mx)
+    if unseen is not None:
+        assert np.all(g[unseen] == 0), (name, "nonzero for a key no query sees")
+    return err, mx
+
+
+def _unseen_keys(w, gr, gc):
+    """[B, Hkv, kv_cap, 1] mask of the keys in no unit's granule list."""
+    seen = np.zeros((w.batch, w.n_kv_heads, w.kv_cap), bool)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            for u in range(gr.shape[2]):
+                for gid in gr[b, h, u, : gc[b, h, u]]:
+                    seen[b, h, gid * w.group_size:(gid + 1) * w.group_size] = True
+    seen[:, :, w.q_pos0 + w.n_q:] = False  # past the last query: never attended
+    return ~seen[..., None].repeat(w.head_dim, axis=-1)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_matches_oracle(case):
+    import torch
+    w = CASES[case]
+    q, k, v = P.make_inputs_parallel(w)
+    print(f"[gpu] backward {case}: {w}", flush=True)
+    run = P.GpuRun(w, q, k, v)
+    dev = run.q.device
+    do = W.round_to_bf16(np.random.default_rng(31).standard_normal(q.shape).astype(np.float32))
+    d_out = torch.from_numpy(do).to(dev).to(torch.bfloat16)
+    dq = torch.full(run.q.shape, float("nan"), dtype=torch.float32, device=dev)
+    dk = torch.full(run.k.shape, float("nan"), dtype=torch.float32, device=dev)
+    dv = torch.full(run.k.shape, float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(H.attend_backward_workspace_bytes(run.cfg, w.batch, w.q_pos0, w.n_q), 16),
+                     dtype=torch.uint8, device=dev)
+    ro = run.ro
+    H.attend_backward(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, ro["granules"], ro["granule_count"],
+                      run.out, run.lse, d_out, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    p = R.params_from_workload(w)
+    gr, gc = run.np("granules"), run.np("granule_count")
+    rdq, rdk, rdv = R.attend_backward(q, w.q_pos0, w.n_q, k, v, gr, gc, do.astype(np.float64), p,
+                                      t0=w.q_pos0 // w.chunk_size)
+    unseen = _unseen_keys(w, gr, gc)
+    res = [_compare("dq", dq, rdq), _compare("dk", dk, rdk, unseen), _compare("dv", dv, rdv, unseen)]
+    print(f"[gpu] backward {case}: (rel_l2, max/max) dq {res[0]}, dk {res[1]}, dv {res[2]}", flush=True)
+
+
+def test_backward_deterministic_except_atomics():
+    """dq has no atomics: bitwise repeatable; dk and dv are sums of atomic
+    adds and agree to f32 rounding between two calls."""
+    import torch
+    w = CASES["qwen3_ragged"]
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.GpuRun(w, q, k, v)
+    dev = run.q.device
+    d_out = torch.from_numpy(W.round_to_bf16(np.random.default_rng(32).standard_normal(q.shape).astype(np.float32))
+                             ).to(dev).to(torch.bfloat16)
+    ws = torch.empty(max(H.attend_backward_workspace_bytes(run.cfg, w.batch, w.q_pos0, w.n_q), 16),
+                     dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(2):
+        dq = torch.empty(run.q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(run.k.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(run.k.shape, dtype=torch.float32, device=dev)
+        H.attend_backward(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, run.ro["granules"],
+                          run.ro["granule_count"], run.out, run.lse, d_out, dq, dk, dv, ws)
+        outs.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    for i in (1, 2):
+        a, b = outs[0][i], outs[1][i]
+        assert torch.allclose(a, b, rtol=1e-5, atol=1e-6 * float(a.abs().max()))
