@@ -254,7 +254,7 @@ def bench_backward(args, pipe=None, pairs=None):
     flops = 8.0 * w.head_dim * pairs  # dP, dQ, dK, dV: 2 flops per MAC, 4 products
     return dict(workload=w.name, ms=ms, algorithmic_flops=flops, tflops=flops / (ms * 1e-3) / 1e12,
                 frac_of_peak=flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                timing="HIP events around hga_attend_backward (clear, D, dq, dk/dv, R^T kernels)")
+                timing="HIP events around hga_attend_backward (D and Q', transposes, lists, dq, dk/dv partials, reduce)")
 
 
 def graph_step_ms(torch, fns, steps, warmup=3):

@@ -13,22 +13,30 @@
 // and dq = R_i^T dq~, dk = R_j^T dk~ (transposed RoPE turns).
 //
 // Kernels (bf16 operands on 16x16x32 matrix cores, f32 accumulation):
-//  * delta_kernel: D_i for every row.
+//  * prep_kernel: D_i for every row, and Q'_i = R_i q_i * s * log2(e) as bf16
+//    (the forward's query operand), row-major, into the workspace.
+//  * transpose_kernel: Q' and dO transposed per (sequence, KV head) to
+//    [d][row], each query chunk's (query, head) rows contiguous and padded to
+//    a multiple of 32 (zeros where no query is), and k~ to [d][token], so
+//    that the products contracting over rows or keys find their k slots
+//    (runs of 4 rows or keys of one column) contiguous.
 //  * dq_kernel: one workgroup per (unit, 128 rows), four waves of 32 rows,
-//    loops over the unit's visible keys 32 at a time.  S^T = K Q'^T and
-//    dP^T = V dO^T take K and V rows straight from HBM as A operands (query
-//    rows on N); dS stays in registers and is directly the B operand of
-//    dQ^T += K^T dS^T, whose A operand reads the wave's K rows back from
-//    LDS transposed.  The epilogue applies R^T and writes dq.
-//  * dkv_kernel: one workgroup per (unit, 128 keys), four waves of 32 keys,
-//    loops over the unit's rows 32 at a time: the same S^T and dP^T, then P,
-//    dS, the scaled queries and dO go through LDS and are read back
-//    transposed for dV^T += dO^T P and dK^T += Q'^T dS (contraction over
-//    rows).  The workgroup adds its keys' dk~, dv into f32 outputs with
-//    atomics (a key is visible to several units).
-//  * unrotate_kernel: dk = R^T dk~ in place.
-// Q' = q~ * s * log2(e) rounded to bf16 (the forward's query operand), so
-// P = exp2(S' - lse * log2(e)) and dk~ = ln(2) * sum_i dS_ij Q'_i.
+//    over the unit's keys 32 at a time: the workgroup stages K, V and K^T of
+//    the 32 keys in LDS (double-buffered through registers); each wave forms
+//    S^T = K Q'^T and dP^T = V dO^T (query rows on N, Q' and dO held in
+//    registers), dS^T in registers as the B operand of dQ^T += K^T dS^T.  The
+//    epilogue applies R^T and writes dq.
+//  * dkv_kernel: one workgroup per (unit, 128 keys of its list), four waves
+//    of 32 keys (K and V held in registers), over the unit's rows 32 at a
+//    time: the workgroup stages Q', dO, Q'^T and dO^T of the 32 rows in LDS;
+//    each wave forms S = Q' K^T and dP = dO V^T (keys on N), so P and dS sit
+//    in registers as the A operands of dV += P^T dO and dK~ += dS^T Q'.  A
+//    unit's sums go to a partial buffer, one row per (unit, list key).
+//  * list kernels: for every (sequence, KV head) and granule, the (unit,
+//    list entry) pairs that hold it (counted, scanned and scattered).
+//  * reduce_kernel: per 16 tokens, the sum of their partial rows, turned by
+//    R^T for dk; tokens in no list get zeros.
+// P = exp2(S' - lse * log2(e)) with S' = Q' . k~, and dk~ = ln(2) sum_i dS_ij Q'_i.
 #include "hga_device.h"
 
 namespace hga {
@@ -36,9 +44,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBwdRows = 32;        // rows per wave (two 16-row blocks)
-constexpr int kBwdKeys = 32;        // keys per wave (two 16-key tiles)
-constexpr int kBwdMaxQ = 64;        // queries per unit (C <= 64)
+constexpr int kRowsWave = 32;   // rows per wave in dq_kernel (two 16-row blocks)
+constexpr int kStage = 32;      // keys (dq_kernel) or rows (dkv_kernel) per LDS stage
+constexpr int kKeysWG = 128;    // keys per dkv_kernel workgroup (four waves of 32)
+constexpr int kTT = 64;         // rows (or tokens) per transpose tile
+constexpr int kTPitch = kStage + 8;  // LDS pitch (elements) of a transposed stage
 
 struct BwdParams {
   const void* q;        // [B][Hq][n_q][D] raw queries
@@ -50,17 +60,27 @@ struct BwdParams {
   const int32_t* gran;  // [units][gmax]
   const int32_t* gcnt;  // [units]
   float* dq;            // [B][Hq][n_q][D]
-  float* dk;            // [B][Hkv][kv_cap][D] (accumulated, then turned back)
-  float* dv;            // [B][Hkv][kv_cap][D] (accumulated)
-  float* delta;         // [B][Hq][n_q]
-  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total;
-  int B, Hq, Hkv, G, C, gs, lg_gs, gmax;
+  float* dk;            // [B][Hkv][kv_cap][D]
+  float* dv;            // [B][Hkv][kv_cap][D]
+  // workspace
+  float* delta;         // [rows_total]
+  uint16_t* qr;         // [rows_total][D] Q' (bf16)
+  uint16_t* qt;         // [B*Hkv][D][NR] Q' by chunk row (chunk trel at trel*CGp)
+  uint16_t* gt;         // [B*Hkv][D][NR] dO likewise
+  uint16_t* kt;         // [B*Hkv][D][KR] k~ by token
+  int32_t* cnt;         // [slabs][ngran] entries per granule, then scatter cursors
+  int32_t* off;         // [slabs][ngran + 1] list offsets
+  int32_t* list;        // [slabs][nqc * gmax] entries slot * gmax + i
+  float* pk;            // [units * gmax * gs][D] dk~ per (unit, list key)
+  float* pv;            // [units * gmax * gs][D] dv likewise
+  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total, NR, KR, n_tok;
+  int B, Hq, Hkv, G, C, CGp, gs, lg_gs, gmax, ngran, nkb, nslice;
   float scale, scale_log2;
   RopeFreqs rope;
 };
 
 struct BUnit {
-  int b, kvh;
+  int b, kvh, trel;
   int64_t t, qlo, slot;
   int nq, R, nkeys;
 };
@@ -72,17 +92,12 @@ __device__ __forceinline__ int64_t uni64(int64_t x) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Unit u (units < 2^31): (sequence, KV head) fastest, largest query chunk first.
-__device__ __forceinline__ BUnit make_bunit(const BwdParams& p, int64_t u) {
+// The unit of (sequence, KV head) slab x and relative query chunk trel.
+__device__ __forceinline__ BUnit unit_of(const BwdParams& p, int64_t x, int trel) {
   BUnit w;
-  const uint32_t bh = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.Hkv);
-  const uint32_t u32 = static_cast<uint32_t>(u);
-  const uint32_t q = u32 / bh;
-  const uint32_t rem = u32 - q * bh;
-  const int64_t trel = p.nqc - 1 - static_cast<int64_t>(q);
-  const uint32_t bq = rem / static_cast<uint32_t>(p.Hkv);
-  w.b = __builtin_amdgcn_readfirstlane(static_cast<int>(bq));
-  w.kvh = __builtin_amdgcn_readfirstlane(static_cast<int>(rem - bq * static_cast<uint32_t>(p.Hkv)));
+  w.b = __builtin_amdgcn_readfirstlane(static_cast<int>(x / p.Hkv));
+  w.kvh = __builtin_amdgcn_readfirstlane(static_cast<int>(x - static_cast<int64_t>(w.b) * p.Hkv));
+  w.trel = trel;
   w.t = uni64(p.t0 + trel);
   const int64_t c0 = w.t * p.C;
   w.qlo = uni64(c0 > p.q_pos0 ? c0 : p.q_pos0);
@@ -90,129 +105,40 @@ __device__ __forceinline__ BUnit make_bunit(const BwdParams& p, int64_t u) {
   const int64_t qhi = (c0 + p.C) < qend ? (c0 + p.C) : qend;
   w.nq = __builtin_amdgcn_readfirstlane(static_cast<int>(qhi - w.qlo));
   w.R = w.nq * p.G;
-  w.slot = uni64((static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nqc + trel);
+  w.slot = uni64(x * p.nqc + trel);
   w.nkeys = __builtin_amdgcn_readfirstlane(p.gcnt[w.slot] * p.gs);
   return w;
 }
 
-// Element offset of row r's first element in a [B][Hq][n_q][D] tensor, and
-// its index in [B][Hq][n_q].
+// Workgroup -> (unit, part) with all parts of a unit on one XCD (workgroups
+// are dealt to the eight XCDs in turn), units largest query chunk first and
+// (sequence, KV head) fastest.  Returns false past the last unit.
+__device__ __forceinline__ bool map_block(const BwdParams& p, int parts, BUnit& w, int& part) {
+  const uint32_t i = blockIdx.x, xcd = i & 7, j = i >> 3;
+  const uint32_t v = (j / parts) * 8 + xcd;
+  part = static_cast<int>(j % parts);
+  if (v >= static_cast<uint64_t>(p.units)) return false;
+  const uint32_t bh = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.Hkv);
+  const uint32_t q = v / bh;
+  w = unit_of(p, v - q * bh, static_cast<int>(p.nqc - 1 - q));
+  return true;
+}
+
+// Index of row r (counted from the unit's first query) in [B][Hq][n_q].
 __device__ __forceinline__ int64_t row_index(const BwdParams& p, const BUnit& w, int r) {
   const int qi = r / p.G, hl = r - qi * p.G;
   return (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0);
 }
 
-// cos / sin of the unit's queries for every pair, in LDS.
-template <int H>
-__device__ __forceinline__ void fill_cs(const BwdParams& p, const BUnit& w, float2* cs) {
-  const int64_t q0 = rope_base(p.rope, w.qlo);
-  for (int i = threadIdx.x; i < w.nq * H; i += blockDim.x) {
-    const int qi = i / H, pr = i - qi * H;
-    float c, s;
-    rope_cs(static_cast<double>(q0 + qi), rope_freq(p.rope, pr), c, s);
-    cs[i] = make_float2(c, s);
-  }
-}
-
-// The B operands of a 16-row block for the S and dP products: the rotated
-// queries scaled by s*log2(e) (bf16) and dO (bf16), d slots
-// ks*32 + 8*(lane/16) + i of row (lane % 16); plus the row's lse*log2(e) and
-// D.  Rows past R repeat row R-1 (their products are masked).
+// D_i = dO_i . O_i and Q'_i (bf16), one wave per row; lane owns the pairs
+// (j, j + D/2) for j = lane, lane + 64, ...
 template <int D>
-__device__ __forceinline__ void load_row_block(const BwdParams& p, const BUnit& w, int r0,
-                                               const float2* cs, Pack8 (&qb)[D / 32],
-                                               Pack8 (&gb)[D / 32], float& lse2, float& dl) {
-  constexpr int KS = D / 32, H = D / 2;
-  const int lane = threadIdx.x & 63, n = lane & 15, sub = lane >> 4;
-  int r = r0 + n;
-  if (r >= w.R) r = w.R - 1;
-  const int64_t ri = row_index(p, w, r);
-  float x[KS][8];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    load8<true>(p.q, ri * D + ks * 32 + sub * 8, x[ks]);
-    gb[ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dout) + ri * D + ks * 32 + sub * 8);
-  }
-  lse2 = p.lse[ri] * kLog2e;
-  dl = p.delta[ri];
-  const int qi = r / p.G;
-#pragma unroll
-  for (int ks = 0; ks < KS / 2; ++ks) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float2 t = cs[qi * H + ks * 32 + sub * 8 + i];
-      const float a = x[ks][i], b = x[ks + KS / 2][i];
-      qb[ks].h[i] = f32_to_bf16((a * t.x - b * t.y) * p.scale_log2);
-      qb[ks + KS / 2].h[i] = f32_to_bf16((a * t.y + b * t.x) * p.scale_log2);
-    }
-  }
-}
-
-// Key kb + (lane % 32) of the unit: its token (or -1 past the list) and the
-// A operands (key lane % 16 of tile t, d slots ks*32 + 8*(lane/16) + i) of K
-// and V for the two 16-key tiles.
-template <int D>
-__device__ __forceinline__ int load_key_block(const BwdParams& p, const BUnit& w, int64_t kb,
-                                              Pack8 (&ka)[2][D / 32], Pack8 (&va)[2][D / 32]) {
-  constexpr int KS = D / 32;
-  const int lane = threadIdx.x & 63, n = lane & 15, sub = lane >> 4;
-  const int64_t k = kb + (lane & 31);
-  int tok = -1;
-  if (k < w.nkeys) {
-    const int g = p.gran[w.slot * p.gmax + (k >> p.lg_gs)];
-    tok = g >= 0 ? g * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
-  }
-  const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int kt = __shfl(tok, t * 16 + n);
-    const int64_t e = (slab + (kt >= 0 ? kt : 0)) * D + sub * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      ka[t][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e + ks * 32);
-      va[t][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e + ks * 32);
-    }
-  }
-  return tok;
-}
-
-// P and dS of one 16-row block against the two key tiles: lane holds row
-// r0 + lane%16 and keys 16t + 4*(lane/16) + i.
-template <int D>
-__device__ __forceinline__ void probs(const BwdParams& p, const BUnit& w, int r0, int tok,
-                                      const Pack8 (&ka)[2][D / 32], const Pack8 (&va)[2][D / 32],
-                                      const Pack8 (&qb)[D / 32], const Pack8 (&gb)[D / 32],
-                                      float lse2, float dl, float (&pr)[2][4], float (&ds)[2][4]) {
-  constexpr int KS = D / 32;
-  const int lane = threadIdx.x & 63, n = lane & 15, sub = lane >> 4;
-  const int r = r0 + n;
-  const bool row_ok = r < w.R;
-  const int64_t qpos = w.qlo + (row_ok ? r / p.G : 0);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma16x16x32(ka[t][ks].v, qb[ks].v, s);
-      dp = mfma16x16x32(va[t][ks].v, gb[ks].v, dp);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kt = __shfl(tok, t * 16 + sub * 4 + i);
-      const bool ok = row_ok && kt >= 0 && kt <= qpos;
-      const float e = ok ? exp2f(s[i] - lse2) : 0.f;
-      pr[t][i] = e;
-      ds[t][i] = e * (dp[i] - dl);
-    }
-  }
-}
-
-// D_i = dO_i . O_i, one wave per row.
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void prep_kernel(BwdParams p) {
+  constexpr int H = D / 2;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= p.rows_total) return;
   const int lane = threadIdx.x & 63;
+  const int64_t pos = p.q_pos0 + row % p.n_q;
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
@@ -222,265 +148,688 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) p.delta[row] = acc;
+  for (int j = lane; j < H; j += 64) {
+    float c, s;
+    rope_cs(static_cast<double>(rope_base(p.rope, pos)), rope_freq(p.rope, j), c, s);
+    const float a = load1<true>(p.q, row * D + j), b = load1<true>(p.q, row * D + j + H);
+    p.qr[row * D + j] = f32_to_bf16((a * c - b * s) * p.scale_log2);
+    p.qr[row * D + j + H] = f32_to_bf16((a * s + b * c) * p.scale_log2);
+  }
 }
+
+// Transposes kTT rows of one (sequence, KV head) to [d][row] (through LDS).
+// KEYS = false: row i is chunk trel = i / CGp, chunk row rr = i % CGp, i.e.
+// query (t0 + trel) * C + rr / G and head rr % G of src = Q' or dO
+// ([B][Hq][n_q][D]), zero where that is not a query of the call (or rr is
+// padding); KEYS = true: row i is token i of k~ ([B][Hkv][kv_cap][D]), zero
+// from n_tok on.
+template <int D, bool KEYS>
+__global__ __launch_bounds__(256) void transpose_kernel(BwdParams p, const uint16_t* src, uint16_t* dst,
+                                                        int64_t nrows) {
+  constexpr int TP = D + 8;  // LDS row pitch (elements)
+  __shared__ __align__(16) uint16_t tile[kTT * TP];
+  const int64_t x = blockIdx.y;  // slab
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTT;
+  const int b = static_cast<int>(x / p.Hkv), kvh = static_cast<int>(x - static_cast<int64_t>(b) * p.Hkv);
+  for (int i = threadIdx.x; i < kTT * (D / 8); i += 256) {
+    const int j = i / (D / 8), c = i - j * (D / 8);
+    const int64_t r = r0 + j;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    int64_t srow = -1;
+    if (KEYS) {
+      if (r < p.n_tok) srow = x * p.kv_cap + r;
+    } else {
+      const int64_t trel = r / p.CGp;
+      const int rr = static_cast<int>(r - trel * p.CGp);
+      const int64_t q = (p.t0 + trel) * p.C + rr / p.G;
+      if (rr < p.C * p.G && q >= p.q_pos0 && q < p.q_pos0 + p.n_q)
+        srow = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + rr % p.G) * p.n_q + (q - p.q_pos0);
+    }
+    if (srow >= 0) val = *reinterpret_cast<const uint4*>(src + srow * D + c * 8);
+    *reinterpret_cast<uint2*>(&tile[j * TP + c * 8]) = make_uint2(val.x, val.y);
+    *reinterpret_cast<uint2*>(&tile[j * TP + c * 8 + 4]) = make_uint2(val.z, val.w);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * (kTT / 8); i += 256) {
+    const int d = i / (kTT / 8), c = i - d * (kTT / 8);
+    Pack8 o;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o.h[m] = tile[(c * 8 + m) * TP + d];
+    *reinterpret_cast<uint4*>(dst + (x * D + d) * nrows + r0 + c * 8) = o.q;
+  }
+}
+
+// Token of unit list key k (per lane), or -1 past the list.  With at most
+// 128 granules per list, the list sits in two registers per lane (entries
+// lane and lane + 64) and is read with lane shuffles; longer lists are read
+// from memory.  Every lane must call it (a shuffle reads other lanes'
+// registers, and a lane that is switched off gives no data).
+struct GranList {
+  int lo = -1, hi = -1;
+  bool regs = false;
+};
+
+__device__ __forceinline__ GranList load_glist(const BwdParams& p, const BUnit& w) {
+  GranList gl;
+  gl.regs = p.gmax <= 128;
+  if (gl.regs) {
+    const int lane = threadIdx.x & 63;
+    const int32_t* src = p.gran + w.slot * p.gmax;
+    gl.lo = lane < p.gmax ? src[lane] : -1;
+    gl.hi = lane + 64 < p.gmax ? src[lane + 64] : -1;
+  }
+  return gl;
+}
+
+__device__ __forceinline__ int token_of(const BwdParams& p, const BUnit& w, const GranList& gl, int64_t k) {
+  const bool in = k < w.nkeys;
+  const int gi = in ? static_cast<int>(k >> p.lg_gs) : 0;
+  int g;
+  if (gl.regs) {  // uniform
+    const int a = __shfl(gl.lo, gi & 63), b = __shfl(gl.hi, gi & 63);
+    g = gi < 64 ? a : b;
+  } else {
+    g = in ? p.gran[w.slot * p.gmax + gi] : -1;
+  }
+  return in && g >= 0 ? g * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
+}
+
+__device__ __forceinline__ uint4 ld_lds16(const uint16_t* s) { return *reinterpret_cast<const uint4*>(s); }
+__device__ __forceinline__ uint2 ld_lds8(const uint16_t* s) { return *reinterpret_cast<const uint2*>(s); }
+
+// k slots of a contraction over 32 rows (or keys) held as two 16-blocks:
+// slot 8*(lane/16) + j <-> index 16*(j/4) + 4*(lane/16) + j%4.  Reads them for
+// column `col` of a transposed LDS stage.
+__device__ __forceinline__ Pack8 ld_tslots(const uint16_t* stage, int col, int sub) {
+  const uint16_t* s = stage + col * kTPitch + 4 * sub;
+  const uint2 a = ld_lds8(s), b = ld_lds8(s + 16);
+  Pack8 r;
+  r.u[0] = a.x;
+  r.u[1] = a.y;
+  r.u[2] = b.x;
+  r.u[3] = b.y;
+  return r;
+}
+
+// dq: stage of 32 keys in LDS: K and V rows ([key][D + 8]), K^T ([D][40]),
+// and the keys' tokens.
+template <int D>
+struct DqStage {
+  static constexpr int RP = D + 8;
+  static constexpr int K = 0, V = kStage * RP, KT = 2 * kStage * RP;
+  static constexpr int ELEMS = KT + D * kTPitch;  // uint16 elements
+  static constexpr int NROW = kStage * D / 8 / 256;  // 16-byte pieces of K (and of V) per thread
+  static constexpr int NT = D * kStage / 4 / 256;    // 8-byte pieces of K^T per thread
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
+  using S = DqStage<D>;
   constexpr int KS = D / 32, H = D / 2, NT = D / 16;
-  constexpr int RP = D * 2 + 8;  // K row pitch in LDS (bytes)
-  __shared__ float2 cs[kBwdMaxQ * H];
-  __shared__ __align__(16) char kl[4][kBwdKeys * RP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, sub = lane >> 4;
-  const int per = (p.C * p.G + 4 * kBwdRows - 1) / (4 * kBwdRows);  // row blocks of 128 per unit
-  const int64_t u = blockIdx.x / per;
-  const int blk = static_cast<int>(blockIdx.x - u * per);
-  const BUnit w = make_bunit(p, u);
-  const int rbase = blk * 4 * kBwdRows;
-  if (rbase >= w.R) return;  // uniform
-  fill_cs<H>(p, w, cs);
-  __syncthreads();
-  const int r0 = rbase + wave * kBwdRows;
-  if (r0 >= w.R) return;  // uniform per wave; no barrier follows
+  __shared__ __align__(16) uint16_t lds[2][S::ELEMS];
+  __shared__ int toks[2][kStage];
+  BUnit w;
+  int slice;
+  if (!map_block(p, p.nslice, w, slice)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, sub = lane >> 4;
+  const int r0 = slice * 4 * kRowsWave + wave * kRowsWave;  // this wave's rows
+  if (slice * 4 * kRowsWave >= w.R) return;  // uniform over the workgroup
+  const int64_t x = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + x * p.kv_cap * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + x * p.kv_cap * D;
+  const uint16_t* ktx = p.kt + x * D * p.KR;
+  const GranList gl = load_glist(p, w);
+  // B operands of the wave's two 16-row blocks (rows past the unit repeat
+  // its last row and are dropped at the end): Q' and dO at d slots
+  // ks*32 + 8*(lane/16) + i of row lane % 16, and lse*log2(e), D
   Pack8 qb[2][KS], gb[2][KS];
   float lse2[2], dl[2];
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) load_row_block<D>(p, w, r0 + sb * 16, cs, qb[sb], gb[sb], lse2[sb], dl[sb]);
+  for (int sb = 0; sb < 2; ++sb) {
+    int r = r0 + sb * 16 + n;
+    if (r >= w.R) r = w.R - 1;
+    const int64_t ri = row_index(p, w, r);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qb[sb][ks].q = *reinterpret_cast<const uint4*>(p.qr + ri * D + ks * 32 + sub * 8);
+      gb[sb][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dout) + ri * D + ks * 32 + sub * 8);
+    }
+    lse2[sb] = p.lse[ri] * kLog2e;
+    dl[sb] = p.delta[ri];
+  }
   f32x4 acc[NT][2];
 #pragma unroll
   for (int c = 0; c < NT; ++c)
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) acc[c][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  char* myk = kl[wave];
-  for (int64_t kb = 0; kb < w.nkeys; kb += kBwdKeys) {
-    Pack8 ka[2][KS], va[2][KS];
-    const int tok = load_key_block<D>(p, w, kb, ka, va);
-    // the K rows for the transposed reads (wave-local LDS)
+  // stage loads: thread piece i of K / V is (key i / (D/8), 16 bytes at
+  // 8 * (i % (D/8))); of K^T (d = i / 8, keys 4 * (i % 8) .. + 3)
+  uint4 rk[S::NROW], rv[S::NROW];
+  uint2 rt[S::NT];
+  int my_tok = -1;
+  auto load_stage = [&](int64_t kb) {
+    const int tok = token_of(p, w, gl, kb + (lane & 31));  // token of key kb + lane % 32
+    my_tok = tok;
+#pragma unroll
+    for (int m = 0; m < S::NROW; ++m) {
+      const int i = tid + 256 * m, key = i / (D / 8), c = i - key * (D / 8);
+      const int tk = __shfl(tok, key);
+      const int64_t e = static_cast<int64_t>(tk >= 0 ? tk : 0) * D + c * 8;
+      rk[m] = tk >= 0 ? *reinterpret_cast<const uint4*>(kg + e) : make_uint4(0, 0, 0, 0);
+      rv[m] = tk >= 0 ? *reinterpret_cast<const uint4*>(vg + e) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < S::NT; ++m) {
+      const int i = tid + 256 * m, d = i / (kStage / 4), c = i - d * (kStage / 4);
+      const int tk = __shfl(tok, 4 * c);  // tokens 4c .. 4c+3 are consecutive
+      rt[m] = tk >= 0 ? *reinterpret_cast<const uint2*>(ktx + static_cast<int64_t>(d) * p.KR + tk)
+                      : make_uint2(0, 0);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* st = lds[buf];
+#pragma unroll
+    for (int m = 0; m < S::NROW; ++m) {
+      const int i = tid + 256 * m, key = i / (D / 8), c = i - key * (D / 8);
+      *reinterpret_cast<uint4*>(st + S::K + key * S::RP + c * 8) = rk[m];
+      *reinterpret_cast<uint4*>(st + S::V + key * S::RP + c * 8) = rv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < S::NT; ++m) {
+      const int i = tid + 256 * m, d = i / (kStage / 4), c = i - d * (kStage / 4);
+      *reinterpret_cast<uint2*>(st + S::KT + d * kTPitch + 4 * c) = rt[m];
+    }
+    if (tid < kStage) toks[buf][tid] = my_tok;
+  };
+  const int nst = (w.nkeys + kStage - 1) / kStage;
+  if (nst > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nst) load_stage(static_cast<int64_t>(s + 1) * kStage);
+    const uint16_t* st = lds[buf];
+    // S^T and dP^T: lane holds row lane % 16 of block sb and keys 16t + 4*(lane/16) + i
+    f32x4 sv[2][2], dp[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        sv[t][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[t][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        char* dst = myk + (t * 16 + n) * RP + (ks * 32 + sub * 8) * 2;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(ka[t][ks].u[0], ka[t][ks].u[1]);
-        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(ka[t][ks].u[2], ka[t][ks].u[3]);
+        Pack8 ka, va;
+        ka.q = ld_lds16(st + S::K + (t * 16 + n) * S::RP + ks * 32 + sub * 8);
+        va.q = ld_lds16(st + S::V + (t * 16 + n) * S::RP + ks * 32 + sub * 8);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          sv[t][sb] = mfma16x16x32(ka.v, qb[sb][ks].v, sv[t][sb]);
+          dp[t][sb] = mfma16x16x32(va.v, gb[sb][ks].v, dp[t][sb]);
+        }
       }
     Pack8 dsb[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      float pr[2][4], ds[2][4];
-      probs<D>(p, w, r0 + sb * 16, tok, ka, va, qb[sb], gb[sb], lse2[sb], dl[sb], pr, ds);
-      // k slots: keys 4*sub + i (tile 0), then 16 + 4*sub + i (tile 1)
+      const int r = r0 + sb * 16 + n;
+      const bool row_ok = r < w.R;
+      const int64_t qpos = w.qlo + (row_ok ? r / p.G : 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dsb[sb].h[i] = f32_to_bf16(ds[0][i]);
-        dsb[sb].h[4 + i] = f32_to_bf16(ds[1][i]);
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = toks[buf][t * 16 + sub * 4 + i];
+          const bool ok = row_ok && tk >= 0 && tk <= qpos;
+          const float e = ok ? exp2f(sv[t][sb][i] - lse2[sb]) : 0.f;
+          dsb[sb].h[t * 4 + i] = f32_to_bf16(e * (dp[t][sb][i] - dl[sb]));
+        }
     }
     // dQ^T[d][rows] += K^T[d][keys] dS^T[keys][rows]
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      Pack8 kt;
+      const Pack8 kt_ = ld_tslots(st + S::KT, c * 16 + n, sub);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kt.h[i] = *reinterpret_cast<const uint16_t*>(myk + (sub * 4 + i) * RP + (c * 16 + n) * 2);
-        kt.h[4 + i] = *reinterpret_cast<const uint16_t*>(myk + (16 + sub * 4 + i) * RP + (c * 16 + n) * 2);
-      }
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) acc[c][sb] = mfma16x16x32(kt.v, dsb[sb].v, acc[c][sb]);
+      for (int sb = 0; sb < 2; ++sb) acc[c][sb] = mfma16x16x32(kt_.v, dsb[sb].v, acc[c][sb]);
     }
+    if (s + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
   }
   // dq = R^T (s * dq~): lane holds d = c*16 + 4*(lane/16) + i of row r0 + sb*16 + n
+  const int64_t q0 = rope_base(p.rope, w.qlo);
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int r = r0 + sb * 16 + n;
     if (r >= w.R) continue;
     const int64_t ri = row_index(p, w, r);
-    const int qi = r / p.G;
+    const double pos = static_cast<double>(q0 + r / p.G);
 #pragma unroll
     for (int c = 0; c < NT / 2; ++c) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = c * 16 + sub * 4 + i;
-        const float2 t = cs[qi * H + d];
+        float cs, sn;
+        rope_cs(pos, rope_freq(p.rope, d), cs, sn);
         const float a = acc[c][sb][i] * p.scale, b = acc[c + NT / 2][sb][i] * p.scale;
-        p.dq[ri * D + d] = a * t.x + b * t.y;
-        p.dq[ri * D + d + H] = b * t.x - a * t.y;
+        p.dq[ri * D + d] = a * cs + b * sn;
+        p.dq[ri * D + d + H] = b * cs - a * sn;
       }
     }
   }
 }
+
+// dkv: stage of 32 chunk rows in LDS: Q' and dO rows ([row][D + 8]), their
+// transposes ([D][40]), and lse*log2(e), D of the rows.
+template <int D>
+struct DkvStage {
+  static constexpr int RP = D + 8;
+  static constexpr int QA = 0, GA = kStage * RP, QT = 2 * kStage * RP, GT = QT + D * kTPitch;
+  static constexpr int ELEMS = GT + D * kTPitch;
+  static constexpr int NROW = kStage * D / 8 / 256;  // 16-byte pieces per thread, per tensor
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void dkv_kernel(BwdParams p) {
-  constexpr int KS = D / 32, H = D / 2, NT = D / 16;
-  constexpr int RP = D * 2 + 8;              // q' / dO row pitch in LDS (bytes)
-  constexpr int PP = kBwdKeys * 2 + 8;       // P / dS row pitch in LDS (bytes)
-  __shared__ float2 cs[kBwdMaxQ * H];
-  __shared__ __align__(16) char ql[4][kBwdRows * RP];
-  __shared__ __align__(16) char gl[4][kBwdRows * RP];
-  __shared__ __align__(16) char pl[4][kBwdRows * PP];
-  __shared__ __align__(16) char sl[4][kBwdRows * PP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, sub = lane >> 4;
-  const int per = (p.gmax * p.gs + 4 * kBwdKeys - 1) / (4 * kBwdKeys);  // key blocks of 128 per unit
-  const int64_t u = blockIdx.x / per;
-  const int blk = static_cast<int>(blockIdx.x - u * per);
-  const BUnit w = make_bunit(p, u);
-  const int64_t kbase = static_cast<int64_t>(blk) * 4 * kBwdKeys;
-  if (kbase >= w.nkeys) return;  // uniform
-  fill_cs<H>(p, w, cs);
-  __syncthreads();
-  const int64_t kb = kbase + wave * kBwdKeys;
-  if (kb >= w.nkeys) return;  // uniform per wave; no barrier follows
-  Pack8 ka[2][KS], va[2][KS];
-  const int tok = load_key_block<D>(p, w, kb, ka, va);
-  f32x4 dka[NT][2], dva[NT][2];
-#pragma unroll
-  for (int c = 0; c < NT; ++c)
+  using S = DkvStage<D>;
+  constexpr int KS = D / 32, NT = D / 16;
+  __shared__ __align__(16) uint16_t lds[2][S::ELEMS];
+  __shared__ __align__(16) float rowv[2][2][kStage];  // lse * log2(e), D
+  BUnit w;
+  int kblk;
+  if (!map_block(p, p.nkb, w, kblk)) return;
+  if (kblk * kKeysWG >= w.nkeys || w.R == 0) return;  // uniform over the workgroup
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, sub = lane >> 4;
+  const int64_t x = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
+  const int64_t kw0 = static_cast<int64_t>(kblk) * kKeysWG + wave * 32;  // this wave's first list key
+  const GranList gl = load_glist(p, w);
+  // the wave's 32 keys: K and V operands (key lane % 16 of tile t, d slots
+  // ks*32 + 8*(lane/16) + i) and the token of key 16t + lane % 16
+  Pack8 kb[2][KS], vb[2][KS];
+  int ktok[2];
+  {
+    const int tok = token_of(p, w, gl, kw0 + (lane & 31));
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + x * p.kv_cap * D;
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + x * p.kv_cap * D;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      dka[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dva[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  char* myq = ql[wave];
-  char* myg = gl[wave];
-  char* myp = pl[wave];
-  char* mys = sl[wave];
-  for (int r0 = 0; r0 < w.R; r0 += kBwdRows) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      Pack8 qb[KS], gb[KS];
-      float lse2, dl;
-      load_row_block<D>(p, w, r0 + sb * 16, cs, qb, gb, lse2, dl);
-      float pr[2][4], ds[2][4];
-      probs<D>(p, w, r0 + sb * 16, tok, ka, va, qb, gb, lse2, dl, pr, ds);
-      // rows sb*16 + n of the wave's LDS tiles
-      const int row = sb * 16 + n;
+      ktok[t] = __shfl(tok, t * 16 + n);
+      const int64_t e = static_cast<int64_t>(ktok[t] >= 0 ? ktok[t] : 0) * D + sub * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        char* dq_ = myq + row * RP + (ks * 32 + sub * 8) * 2;
-        char* dg_ = myg + row * RP + (ks * 32 + sub * 8) * 2;
-        *reinterpret_cast<uint2*>(dq_) = make_uint2(qb[ks].u[0], qb[ks].u[1]);
-        *reinterpret_cast<uint2*>(dq_ + 8) = make_uint2(qb[ks].u[2], qb[ks].u[3]);
-        *reinterpret_cast<uint2*>(dg_) = make_uint2(gb[ks].u[0], gb[ks].u[1]);
-        *reinterpret_cast<uint2*>(dg_ + 8) = make_uint2(gb[ks].u[2], gb[ks].u[3]);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        Pack8 pk, sk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pk.h[i] = f32_to_bf16(pr[t][i]);
-          sk.h[i] = f32_to_bf16(ds[t][i]);
-        }
-        *reinterpret_cast<uint2*>(myp + row * PP + (t * 16 + sub * 4) * 2) = make_uint2(pk.u[0], pk.u[1]);
-        *reinterpret_cast<uint2*>(mys + row * PP + (t * 16 + sub * 4) * 2) = make_uint2(sk.u[0], sk.u[1]);
+        kb[t][ks].q = *reinterpret_cast<const uint4*>(kg + e + ks * 32);
+        vb[t][ks].q = *reinterpret_cast<const uint4*>(vg + e + ks * 32);
       }
     }
-    // dV^T[d][keys] += dO^T[d][rows] P[rows][keys]; dK^T likewise with Q', dS
-    // (k slots: rows 8*(lane/16) + i of the 32)
-    Pack8 pb[2], sbk[2];
+  }
+  f32x4 dka[2][NT], dva[2][NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = sub * 8 + i;
-        pb[t].h[i] = *reinterpret_cast<const uint16_t*>(myp + row * PP + (t * 16 + n) * 2);
-        sbk[t].h[i] = *reinterpret_cast<const uint16_t*>(mys + row * PP + (t * 16 + n) * 2);
-      }
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      Pack8 ga, qa;
+      dka[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dva[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  // the unit's rows in its chunk-row space: row rr is query t*C + rr/G,
+  // head rr % G; valid rows [lo, hi); stages of 32 from a multiple of 32
+  const int lo = static_cast<int>(w.qlo - w.t * p.C) * p.G;
+  const int hi = lo + w.R;
+  const int rb0 = lo / kStage * kStage;
+  const int nst = (hi - rb0 + kStage - 1) / kStage;
+  const uint16_t* qtx = p.qt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
+  const uint16_t* gtx = p.gt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
+  uint4 rq[S::NROW], rg[S::NROW], rqt[S::NROW], rgt[S::NROW];
+  float rl = 0.f, rd = 0.f;
+  // piece i of a row-major tensor: (row i / (D/8), 16 bytes at 8 * (i % (D/8)));
+  // of a transposed one: (d = i / 4, rows 8 * (i % 4) .. + 7)
+  auto load_stage = [&](int rb) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = sub * 8 + i;
-        ga.h[i] = *reinterpret_cast<const uint16_t*>(myg + row * RP + (c * 16 + n) * 2);
-        qa.h[i] = *reinterpret_cast<const uint16_t*>(myq + row * RP + (c * 16 + n) * 2);
+    for (int m = 0; m < S::NROW; ++m) {
+      const int i = tid + 256 * m;
+      const int j = i / (D / 8), c = i - j * (D / 8);
+      const int rr = rb + j;
+      if (rr >= lo && rr < hi) {
+        const int64_t ri = row_index(p, w, rr - lo);
+        rq[m] = *reinterpret_cast<const uint4*>(p.qr + ri * D + c * 8);
+        rg[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dout) + ri * D + c * 8);
+      } else {
+        rq[m] = make_uint4(0, 0, 0, 0);
+        rg[m] = make_uint4(0, 0, 0, 0);
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dva[c][t] = mfma16x16x32(ga.v, pb[t].v, dva[c][t]);
-        dka[c][t] = mfma16x16x32(qa.v, sbk[t].v, dka[c][t]);
+      const int d = i / (kStage / 8), pc = i - d * (kStage / 8);
+      const int64_t te = static_cast<int64_t>(d) * p.NR + rb + pc * 8;
+      rqt[m] = *reinterpret_cast<const uint4*>(qtx + te);
+      rgt[m] = *reinterpret_cast<const uint4*>(gtx + te);
+    }
+    if (tid < kStage) {
+      const int rr = rb + tid;
+      if (rr >= lo && rr < hi) {
+        const int64_t ri = row_index(p, w, rr - lo);
+        rl = p.lse[ri] * kLog2e;
+        rd = p.delta[ri];
+      } else {
+        rl = 0.f;
+        rd = 0.f;
       }
     }
-  }
-  // lane holds key kb + 16t + n and d = c*16 + 4*(lane/16) + i
-  const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* st = lds[buf];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int kt = __shfl(tok, t * 16 + n);
-    if (kt < 0) continue;
-    float* dkr = p.dk + (slab + kt) * D;
-    float* dvr = p.dv + (slab + kt) * D;
+    for (int m = 0; m < S::NROW; ++m) {
+      const int i = tid + 256 * m;
+      const int j = i / (D / 8), c = i - j * (D / 8);
+      *reinterpret_cast<uint4*>(st + S::QA + j * S::RP + c * 8) = rq[m];
+      *reinterpret_cast<uint4*>(st + S::GA + j * S::RP + c * 8) = rg[m];
+      const int d = i / (kStage / 8), pc = i - d * (kStage / 8);
+      *reinterpret_cast<uint4*>(st + S::QT + d * kTPitch + pc * 8) = rqt[m];
+      *reinterpret_cast<uint4*>(st + S::GT + d * kTPitch + pc * 8) = rgt[m];
+    }
+    if (tid < kStage) {
+      rowv[buf][0][tid] = rl;
+      rowv[buf][1][tid] = rd;
+    }
+  };
+  load_stage(rb0);
+  store_stage(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1, rb = rb0 + s * kStage;
+    if (s + 1 < nst) load_stage(rb + kStage);
+    const uint16_t* st = lds[buf];
+    // S and dP of the two 16-row blocks: lane holds key lane % 16 of tile t
+    // and rows 16*sb + 4*(lane/16) + i; P and dS into the A-operand slots
+    Pack8 pb[2], sk[2];
 #pragma unroll
-    for (int c = 0; c < NT; ++c)
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x4 sv[2], dp[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Pack8 qa, ga;
+        qa.q = ld_lds16(st + S::QA + (sb * 16 + n) * S::RP + ks * 32 + sub * 8);
+        ga.q = ld_lds16(st + S::GA + (sb * 16 + n) * S::RP + ks * 32 + sub * 8);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sv[t] = mfma16x16x32(qa.v, kb[t][ks].v, sv[t]);
+          dp[t] = mfma16x16x32(ga.v, vb[t][ks].v, dp[t]);
+        }
+      }
+      const float4 l4 = *reinterpret_cast<const float4*>(&rowv[buf][0][sb * 16 + sub * 4]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&rowv[buf][1][sb * 16 + sub * 4]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int d = c * 16 + sub * 4 + i;
-        unsafeAtomicAdd(dkr + d, dka[c][t][i] * kLn2);
-        unsafeAtomicAdd(dvr + d, dva[c][t][i]);
+        const int rr = rb + sb * 16 + sub * 4 + i;
+        const bool row_ok = rr >= lo && rr < hi;
+        const int64_t qpos = w.t * p.C + rr / p.G;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bool ok = row_ok && ktok[t] >= 0 && ktok[t] <= qpos;
+          const float e = ok ? exp2f(sv[t][i] - lv[i]) : 0.f;
+          pb[t].h[sb * 4 + i] = f32_to_bf16(e);
+          sk[t].h[sb * 4 + i] = f32_to_bf16(e * (dp[t][i] - dv4[i]));
+        }
       }
+    }
+    // dV[keys][d] += P^T[keys][rows] dO[rows][d], dK~ likewise with dS and Q'
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const Pack8 g_ = ld_tslots(st + S::GT, c * 16 + n, sub);
+      const Pack8 q_ = ld_tslots(st + S::QT, c * 16 + n, sub);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dva[t][c] = mfma16x16x32(pb[t].v, g_.v, dva[t][c]);
+        dka[t][c] = mfma16x16x32(sk[t].v, q_.v, dka[t][c]);
+      }
+    }
+    if (s + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+  // partial rows: lane holds d = c*16 + lane % 16 of list keys kw0 + 16t + 4*(lane/16) + i
+  const int64_t prow0 = w.slot * p.gmax * p.gs;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t k = kw0 + t * 16 + sub * 4 + i;
+      if (k >= w.nkeys) continue;
+      float* dkr = p.pk + (prow0 + k) * D;
+      float* dvr = p.pv + (prow0 + k) * D;
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        dkr[c * 16 + n] = dka[t][c][i] * kLn2;
+        dvr[c * 16 + n] = dva[t][c][i];
+      }
+    }
+}
+
+// Entries per granule: one count per (unit, list entry).
+__global__ __launch_bounds__(256) void count_kernel(BwdParams p) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // slot * gmax + i
+  if (e >= p.units * p.gmax) return;
+  const int64_t slot = e / p.gmax;
+  const int i = static_cast<int>(e - slot * p.gmax);
+  if (i >= p.gcnt[slot]) return;
+  const int g = p.gran[e];
+  if (g < 0 || g >= p.ngran) return;
+  const int64_t x = slot / p.nqc;
+  atomicAdd(&p.cnt[x * p.ngran + g], 1);
+}
+
+// Block-wide inclusive scan of one int per thread (1024 threads).
+__device__ __forceinline__ int block_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  __syncthreads();  // wsum is free
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < wave; ++i) pre += wsum[i];
+  return v + pre;
+}
+
+// One workgroup per slab: list offsets (exclusive scan of the counts), and
+// the counts cleared again to serve as scatter cursors.
+__global__ __launch_bounds__(1024) void scan_kernel(BwdParams p) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int64_t x = blockIdx.x;
+  int32_t* cnt = p.cnt + x * p.ngran;
+  int32_t* off = p.off + x * (p.ngran + 1);
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < p.ngran; base += 1024) {
+    const int g = base + tid;
+    const int c = g < p.ngran ? cnt[g] : 0;
+    const int c0 = carry;
+    const int ex = block_scan(c, wsum) - c + c0;
+    if (g < p.ngran) {
+      off[g] = ex;
+      cnt[g] = 0;
+    }
+    __syncthreads();  // every thread has read carry
+    if (tid == 1023) carry = ex + c;
+    __syncthreads();
+  }
+  if (tid == 0) off[p.ngran] = carry;
+}
+
+// Scatter: every list entry (slot * gmax + i) into its granule's list (the
+// order within a list is arbitrary).
+__global__ __launch_bounds__(256) void scatter_kernel(BwdParams p) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= p.units * p.gmax) return;
+  const int64_t slot = e / p.gmax;
+  const int i = static_cast<int>(e - slot * p.gmax);
+  if (i >= p.gcnt[slot]) return;
+  const int g = p.gran[e];
+  if (g < 0 || g >= p.ngran) return;
+  const int64_t x = slot / p.nqc;
+  const int pos = atomicAdd(&p.cnt[x * p.ngran + g], 1);
+  p.list[x * p.nqc * p.gmax + p.off[x * (p.ngran + 1) + g] + pos] = static_cast<int32_t>(e);
+}
+
+// dk and dv of 16 tokens of one slab: thread (token tid / 16, pair columns
+// (tid % 16) * PW .. + PW - 1 and their partners + D/2) sums the partial rows
+// of its granule's list entries, then dk = R^T (sum).  Tokens in no list
+// get zeros.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(BwdParams p) {
+  constexpr int H = D / 2, PW = H / 16;
+  const int64_t slabs = static_cast<int64_t>(p.B) * p.Hkv;
+  const int64_t x = blockIdx.x % slabs, tb = blockIdx.x / slabs;
+  const int64_t tok = tb * 16 + (threadIdx.x >> 4);
+  if (tok >= p.kv_cap) return;
+  const int col = (threadIdx.x & 15) * PW;
+  const int64_t g = tok >> p.lg_gs;
+  int l0 = 0, l1 = 0;
+  if (g < p.ngran) {
+    l0 = p.off[x * (p.ngran + 1) + g];
+    l1 = p.off[x * (p.ngran + 1) + g + 1];
+  }
+  const int32_t* lst = p.list + x * p.nqc * p.gmax;
+  const int64_t kin = tok & (p.gs - 1);
+  float ka[PW] = {}, kb_[PW] = {}, va[PW] = {}, vb_[PW] = {};
+  auto add_row = [&](int32_t e) {
+    const int64_t r = (static_cast<int64_t>(e) * p.gs + kin) * D + col;
+#pragma unroll
+    for (int j = 0; j < PW; j += 2) {
+      const float2 a = *reinterpret_cast<const float2*>(p.pk + r + j);
+      const float2 b = *reinterpret_cast<const float2*>(p.pk + r + H + j);
+      const float2 c = *reinterpret_cast<const float2*>(p.pv + r + j);
+      const float2 d = *reinterpret_cast<const float2*>(p.pv + r + H + j);
+      ka[j] += a.x; ka[j + 1] += a.y;
+      kb_[j] += b.x; kb_[j + 1] += b.y;
+      va[j] += c.x; va[j + 1] += c.y;
+      vb_[j] += d.x; vb_[j + 1] += d.y;
+    }
+  };
+  int l = l0;
+  for (; l + 4 <= l1; l += 4) {
+    const int32_t e0 = lst[l], e1 = lst[l + 1], e2 = lst[l + 2], e3 = lst[l + 3];
+    add_row(e0);
+    add_row(e1);
+    add_row(e2);
+    add_row(e3);
+  }
+  for (; l < l1; ++l) add_row(lst[l]);
+  const double pos = static_cast<double>(rope_base(p.rope, tok));
+  float* dkr = p.dk + (x * p.kv_cap + tok) * D;
+  float* dvr = p.dv + (x * p.kv_cap + tok) * D;
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    float c, s;
+    rope_cs(pos, rope_freq(p.rope, col + j), c, s);
+    dkr[col + j] = ka[j] * c + kb_[j] * s;
+    dkr[col + j + H] = kb_[j] * c - ka[j] * s;
+    dvr[col + j] = va[j];
+    dvr[col + j + H] = vb_[j];
   }
 }
 
-// dk = R_j^T dk~ in place for tokens [0, n_tok) of every (sequence, KV head).
-template <int D>
-__global__ __launch_bounds__(256) void unrotate_kernel(BwdParams p, int64_t n_tok) {
-  constexpr int H = D / 2;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // (slab row, pair)
-  const int64_t total = static_cast<int64_t>(p.B) * p.Hkv * n_tok * H;
-  if (i >= total) return;
-  const int pr = static_cast<int>(i % H);
-  const int64_t rowi = i / H;
-  const int64_t j = rowi % n_tok;
-  const int64_t bh = rowi / n_tok;
-  float* x = p.dk + (bh * p.kv_cap + j) * D;
-  float c, s;
-  rope_cs(static_cast<double>(rope_base(p.rope, j)), rope_freq(p.rope, pr), c, s);
-  const float a = x[pr], b = x[pr + H];
-  x[pr] = a * c + b * s;
-  x[pr + H] = b * c - a * s;
+__global__ __launch_bounds__(256) void zero_i32(int32_t* x, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    x[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float4* x, int64_t n4) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+// Workspace carve-up (256-byte aligned pieces).
+struct BwdLayout {
+  size_t delta, qr, qt, gt, kt, cnt, off, list, pk, pv, total;
+  int64_t NR, KR;
+  int CGp, ngran;
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(const Geometry& g) {
+  BwdLayout L;
+  const size_t rows = static_cast<size_t>(g.B) * g.Hq * g.n_q;
+  const size_t slabs = static_cast<size_t>(g.B) * g.Hkv;
+  const size_t units = slabs * g.nqc;
+  L.ngran = static_cast<int>(g.kv_cap / g.gs);
+  L.CGp = (g.C * g.G + kStage - 1) / kStage * kStage;
+  L.NR = (static_cast<int64_t>(g.nqc) * L.CGp + kTT - 1) / kTT * kTT;
+  L.KR = (g.kv_cap + kTT - 1) / kTT * kTT;
+  const size_t prow = units * g.gmax * g.gs;  // partial rows
+  size_t off = 0;
+  L.delta = off; off = al256(off + rows * 4);
+  L.qr = off; off = al256(off + rows * g.d * 2);
+  L.qt = off; off = al256(off + slabs * g.d * L.NR * 2);
+  L.gt = off; off = al256(off + slabs * g.d * L.NR * 2);
+  L.kt = off; off = al256(off + slabs * g.d * L.KR * 2);
+  L.cnt = off; off = al256(off + slabs * L.ngran * 4);
+  L.off = off; off = al256(off + slabs * (L.ngran + 1) * 4);
+  L.list = off; off = al256(off + slabs * g.nqc * g.gmax * 4);
+  L.pk = off; off = al256(off + prow * g.d * 4);
+  L.pv = off; off = al256(off + prow * g.d * 4);
+  L.total = off;
+  return L;
 }
 
 template <int D>
 hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream) {
-  // dk and dv are accumulated (hardware f32 atomics on device memory): clear
-  // them first (a kernel, not a memset)
-  const int64_t n4 = static_cast<int64_t>(g.B) * g.Hkv * g.kv_cap * D / 4;
-  hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dk), n4);
-  hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dv), n4);
-  hipLaunchKernelGGL((delta_kernel<D>), dim3(static_cast<unsigned>((p.rows_total + 3) / 4)), dim3(256), 0,
+  const int64_t slabs = static_cast<int64_t>(g.B) * g.Hkv;
+  hipLaunchKernelGGL(zero_i32, dim3(256), dim3(256), 0, stream, p.cnt, slabs * p.ngran);
+  hipLaunchKernelGGL((prep_kernel<D>), dim3(static_cast<unsigned>((p.rows_total + 3) / 4)), dim3(256), 0,
                      stream, p);
-  const int per_q = (g.C * g.G + 4 * kBwdRows - 1) / (4 * kBwdRows);
-  hipLaunchKernelGGL((dq_kernel<D>), dim3(static_cast<unsigned>(p.units * per_q)), dim3(256), 0, stream, p);
-  const int per_k = (g.gmax * g.gs + 4 * kBwdKeys - 1) / (4 * kBwdKeys);
-  hipLaunchKernelGGL((dkv_kernel<D>), dim3(static_cast<unsigned>(p.units * per_k)), dim3(256), 0, stream, p);
-  const int64_t n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
-  const int64_t total = static_cast<int64_t>(g.B) * g.Hkv * n_tok * (D / 2);
-  hipLaunchKernelGGL((unrotate_kernel<D>), dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-                     stream, p, n_tok);
+  const dim3 trg(static_cast<unsigned>(p.NR / kTT), static_cast<unsigned>(slabs));
+  hipLaunchKernelGGL((transpose_kernel<D, false>), trg, dim3(256), 0, stream, p, p.qr, p.qt, p.NR);
+  hipLaunchKernelGGL((transpose_kernel<D, false>), trg, dim3(256), 0, stream, p,
+                     static_cast<const uint16_t*>(p.dout), p.gt, p.NR);
+  const dim3 tkg(static_cast<unsigned>(p.KR / kTT), static_cast<unsigned>(slabs));
+  hipLaunchKernelGGL((transpose_kernel<D, true>), tkg, dim3(256), 0, stream, p,
+                     static_cast<const uint16_t*>(p.k), p.kt, p.KR);
+  const int64_t entries = p.units * p.gmax;
+  const unsigned eg = static_cast<unsigned>((entries + 255) / 256);
+  hipLaunchKernelGGL(count_kernel, dim3(eg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>(slabs)), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(scatter_kernel, dim3(eg), dim3(256), 0, stream, p);
+  const int64_t units8 = (p.units + 7) / 8 * 8;
+  hipLaunchKernelGGL((dq_kernel<D>), dim3(static_cast<unsigned>(units8 * p.nslice)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((dkv_kernel<D>), dim3(static_cast<unsigned>(units8 * p.nkb)), dim3(256), 0, stream, p);
+  const int64_t tblocks = (p.kv_cap + 15) / 16;
+  hipLaunchKernelGGL((reduce_kernel<D>), dim3(static_cast<unsigned>(slabs * tblocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool backward_supported(const Geometry& g) {
-  return g.bf16 && (g.d == 64 || g.d == 128) && g.C <= kBwdMaxQ && (g.gs & (g.gs - 1)) == 0 &&
-         g.gs >= 1;
+  // granules of at least 4 tokens (runs of 4 consecutive tokens per key
+  // group of a 32-key stage); list entries (slot * gmax + i) and grid sizes
+  // fit 32 bits
+  const int64_t units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
+  const int64_t units8 = (units + 7) / 8 * 8;
+  const int64_t nkb = (static_cast<int64_t>(g.gmax) * g.gs + kKeysWG - 1) / kKeysWG;
+  const int64_t nslice = (static_cast<int64_t>(g.C) * g.G + 4 * kRowsWave - 1) / (4 * kRowsWave);
+  const int64_t tblocks = static_cast<int64_t>(g.B) * g.Hkv * ((g.kv_cap + 15) / 16);
+  const bool gs_ok = (g.gs & (g.gs - 1)) == 0 && g.gs >= 4;
+  return g.bf16 && (g.d == 64 || g.d == 128) && gs_ok && units * g.gmax < (int64_t{1} << 31) &&
+         units8 * nkb < (int64_t{1} << 31) && units8 * nslice < (int64_t{1} << 31) &&
+         tblocks < (int64_t{1} << 31);
 }
 
-size_t backward_workspace(const Geometry& g) {
-  return static_cast<size_t>(g.B) * g.Hq * g.n_q * sizeof(float);
-}
+size_t backward_workspace(const Geometry& g) { return bwd_layout(g).total; }
 
 hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, const void* v,
                            const int32_t* granules, const int32_t* granule_count, const void* out,
                            const float* lse, const void* d_out, float* dq, float* dk, float* dv,
                            void* ws, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(g);
+  char* w = static_cast<char*>(ws);
   BwdParams p;
   p.q = q;
   p.k = k_rot;
@@ -493,7 +842,16 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.delta = static_cast<float*>(ws);
+  p.delta = reinterpret_cast<float*>(w + L.delta);
+  p.qr = reinterpret_cast<uint16_t*>(w + L.qr);
+  p.qt = reinterpret_cast<uint16_t*>(w + L.qt);
+  p.gt = reinterpret_cast<uint16_t*>(w + L.gt);
+  p.kt = reinterpret_cast<uint16_t*>(w + L.kt);
+  p.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
+  p.off = reinterpret_cast<int32_t*>(w + L.off);
+  p.list = reinterpret_cast<int32_t*>(w + L.list);
+  p.pk = reinterpret_cast<float*>(w + L.pk);
+  p.pv = reinterpret_cast<float*>(w + L.pv);
   p.q_pos0 = g.q_pos0;
   p.n_q = g.n_q;
   p.kv_cap = g.kv_cap;
@@ -501,15 +859,22 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.nqc = g.nqc;
   p.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   p.rows_total = static_cast<int64_t>(g.B) * g.Hq * g.n_q;
+  p.NR = L.NR;
+  p.KR = L.KR;
+  p.n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
   p.B = g.B;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
   p.G = g.G;
   p.C = g.C;
+  p.CGp = L.CGp;
   p.gs = g.gs;
   p.lg_gs = 0;
   while ((1 << p.lg_gs) < g.gs) ++p.lg_gs;
   p.gmax = g.gmax;
+  p.ngran = L.ngran;
+  p.nkb = static_cast<int>((static_cast<int64_t>(g.gmax) * g.gs + kKeysWG - 1) / kKeysWG);
+  p.nslice = (g.C * g.G + 4 * kRowsWave - 1) / (4 * kRowsWave);
   p.scale = g.scale;
   p.scale_log2 = g.scale * kLog2e;
   p.rope = g.rope;

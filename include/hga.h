@@ -275,8 +275,16 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
  *   dk, dv            : [B][Hkv][kv_cap][d] f32, dL/d k_raw (through R^T) and
  *                       dL/d v; overwritten (zero where no query looks)
  * With P = exp(s q~.k~ - lse): dP = dO.v, D = dO.O, dS = P (dP - D),
- * dq~ = s dS k~, dk~ = s dS^T q~, dv = P^T dO.  bf16 only.  Workspace:
- * hga_attend_backward_workspace_bytes (one f32 per query row).
+ * dq~ = s dS k~, dk~ = s dS^T q~, dv = P^T dO.  bf16 only; granules of at
+ * least 4 tokens.  dq is bitwise repeatable; dk and dv sum per-(unit, key)
+ * partials in an order that can change between calls (f32 rounding only).
+ * Workspace: hga_attend_backward_workspace_bytes -- per query row D (f32)
+ * and Q' (bf16); transposed Q', dO and k~ (bf16); granule lists; and two
+ * f32 partial rows of d per (unit, list key), units * gmax * g_s * d * 8
+ * bytes, the largest piece (2.5 GB for 32768 queries, 32 query and 4 KV
+ * heads, d = 128, 76 granules per list).  Errors: HGA_ERR_UNSUPPORTED for
+ * other dtypes or shapes, HGA_ERR_WORKSPACE when workspace_bytes is short;
+ * nothing is launched then.
  */
 size_t hga_attend_backward_workspace_bytes(const hga_config* cfg, int32_t batch, int64_t q_pos0,
                                            int64_t n_q);
