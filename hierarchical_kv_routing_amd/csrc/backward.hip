@@ -17,9 +17,9 @@
 //    (the forward's query operand), row-major, into the workspace.
 //  * transpose_kernel: Q' and dO transposed per (sequence, KV head) to
 //    [d][row], each query chunk's (query, head) rows contiguous and padded to
-//    a multiple of 32 (zeros where no query is), and k~ to [d][token], so
-//    that the products contracting over rows or keys find their k slots
-//    (runs of 4 rows or keys of one column) contiguous.
+//    a multiple of 32 (zeros where no query is; within 32-row blocks the rows
+//    permuted so that one lane's 8 k slots are one 16-byte piece), and k~ to
+//    [d][token] (runs of 4 tokens contiguous).
 //  * dq_kernel: one workgroup per (unit, 128 rows), four waves of 32 rows,
 //    over the unit's keys 32 at a time: the workgroup stages K, V and K^T of
 //    the 32 keys in LDS (double-buffered through registers); each wave forms
@@ -49,6 +49,10 @@ constexpr int kStage = 32;      // keys (dq_kernel) or rows (dkv_kernel) per LDS
 constexpr int kKeysWG = 128;    // keys per dkv_kernel workgroup (four waves of 32)
 constexpr int kTT = 64;         // rows (or tokens) per transpose tile
 constexpr int kTPitch = kStage + 8;  // LDS pitch (elements) of a transposed stage
+#ifndef HGA_DKV_KT
+#define HGA_DKV_KT 1
+#endif
+constexpr int kNoRow = -0x7fffffff - 1;  // query offset of a stage row that is not the unit's
 
 struct BwdParams {
   const void* q;        // [B][Hq][n_q][D] raw queries
@@ -65,7 +69,7 @@ struct BwdParams {
   // workspace
   float* delta;         // [rows_total]
   uint16_t* qr;         // [rows_total][D] Q' (bf16)
-  uint16_t* qt;         // [B*Hkv][D][NR] Q' by chunk row (chunk trel at trel*CGp)
+  uint16_t* qt;         // [B*Hkv][D][NR] Q' by chunk row (chunk trel at trel*CGp; permuted in 32-row blocks)
   uint16_t* gt;         // [B*Hkv][D][NR] dO likewise
   uint16_t* kt;         // [B*Hkv][D][KR] k~ by token
   int32_t* cnt;         // [slabs][ngran] entries per granule, then scatter cursors
@@ -194,7 +198,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(BwdParams p, const uint1
     const int d = i / (kTT / 8), c = i - d * (kTT / 8);
     Pack8 o;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) o.h[m] = tile[(c * 8 + m) * TP + d];
+    for (int m = 0; m < 8; ++m) {
+      // query rows: position 8q + 4h + j of a 32-row block holds row
+      // 16h + 4q + j, so that the 8 k slots one lane takes in a contraction
+      // over the block's rows form one 16-byte piece
+      const int pos = c * 8 + m;
+      const int row = KEYS ? pos : (pos & ~31) + 16 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 3) + (pos & 3);
+      o.h[m] = tile[row * TP + d];
+    }
     *reinterpret_cast<uint4*>(dst + (x * D + d) * nrows + r0 + c * 8) = o.q;
   }
 }
@@ -263,7 +274,7 @@ struct DqStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   using S = DqStage<D>;
   constexpr int KS = D / 32, H = D / 2, NT = D / 16;
   __shared__ __align__(16) uint16_t lds[2][S::ELEMS];
@@ -422,42 +433,99 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
   }
 }
 
-// dkv: stage of 32 chunk rows in LDS: Q' and dO rows ([row][D + 8]), their
-// transposes ([D][40]), and lse*log2(e), D of the rows.
+// dkv: stage of 64 chunk rows in LDS, filled by direct global -> LDS loads
+// (a wave's lane l lands at 16*l, or 4*l, of the wave's block), so the
+// tiles are unpadded and their 16-byte chunks XOR-swizzled against bank
+// conflicts: Q' and dO rows (row j: 2*D bytes, chunk c at c ^ rswz(j)),
+// their transposes (column d: 128 bytes, chunk c at c ^ tswz(d)); then the
+// rows' lse, D and query offsets (RV).
+constexpr int kDkvRows = 64;
 template <int D>
 struct DkvStage {
-  static constexpr int RP = D + 8;
-  static constexpr int QA = 0, GA = kStage * RP, QT = 2 * kStage * RP, GT = QT + D * kTPitch;
-  static constexpr int ELEMS = GT + D * kTPitch;
-  static constexpr int NROW = kStage * D / 8 / 256;  // 16-byte pieces per thread, per tensor
+  static constexpr int TILE = kDkvRows * D * 2;  // bytes of one tensor's tile
+  static constexpr int NBLK = TILE / 1024;       // 1 KB blocks per tile
+  static constexpr int QA = 0, GA = TILE, QT = 2 * TILE, GT = 3 * TILE, RV = 4 * TILE;
+  static constexpr int BYTES = RV + 3 * 4 * kDkvRows;
 };
 
+// Row-major tile: the 16-row read of an A operand (16 lanes, one chunk each)
+// and the fill are spread over all banks.
 template <int D>
-__global__ __launch_bounds__(256) void dkv_kernel(BwdParams p) {
+__device__ __forceinline__ int rswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int tswz(int d) { return (d >> 1) & 7; }
+
+// Direct global -> LDS loads of 16 or 4 bytes per lane: lane l's bytes land
+// at lds_wave + 16*l (4*l); lds_wave is the same in every lane.  The host
+// pass only needs the declaration.
+__device__ __forceinline__ void load_lds16(const void* g, char* lds_wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds_wave, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void load_lds4(const void* g, char* lds_wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds_wave, 4, 0, 0);
+#endif
+}
+
+// Waits until at most k vector-memory operations of this wave are
+// outstanding (k a multiple of the per-stage count, <= 63) and for its LDS
+// operations, then meets the workgroup at a barrier.  The empty asm
+// statements keep the compiler from moving memory accesses across.
+template <int K>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(K >= 0 && K < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4));  // vmcnt(K) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// k slots of a contraction over 32 rows of the stage (half h; slot
+// 8*(lane/16) + j <-> row 32h + 16*(j/4) + 4*(lane/16) + j%4) for column col
+// of a swizzled transposed tile: one 16-byte piece, as the rows are stored
+// permuted.
+__device__ __forceinline__ Pack8 ld_tslots_swz(const char* tile, int col, int h, int sub) {
+  Pack8 r;
+  r.q = *reinterpret_cast<const uint4*>(tile + col * 128 + 16 * ((4 * h + sub) ^ tswz(col)));
+  return r;
+}
+
+// KT key tiles of 16 per wave, 128 / (16 KT) waves per workgroup; two stage
+// buffers.
+constexpr int kDkvThreads = kKeysWG / (16 * HGA_DKV_KT) * 64;
+template <int D, int KT>
+__global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
   using S = DkvStage<D>;
-  constexpr int KS = D / 32, NT = D / 16;
-  __shared__ __align__(16) uint16_t lds[2][S::ELEMS];
-  __shared__ __align__(16) float rowv[2][2][kStage];  // lse * log2(e), D
+  constexpr int KS = D / 32, NT = D / 16, NW = kKeysWG / (16 * KT);
+  static_assert(S::NBLK % NW == 0, "tile blocks spread evenly over the waves");
+  __shared__ __align__(1024) char b0[S::BYTES];
+  __shared__ __align__(1024) char b1[S::BYTES];
   BUnit w;
   int kblk;
   if (!map_block(p, p.nkb, w, kblk)) return;
   if (kblk * kKeysWG >= w.nkeys || w.R == 0) return;  // uniform over the workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, sub = lane >> 4;
   const int64_t x = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
-  const int64_t kw0 = static_cast<int64_t>(kblk) * kKeysWG + wave * 32;  // this wave's first list key
+  const int64_t kw0 = static_cast<int64_t>(kblk) * kKeysWG + wave * 16 * KT;  // this wave's first list key
   const GranList gl = load_glist(p, w);
-  // the wave's 32 keys: K and V operands (key lane % 16 of tile t, d slots
-  // ks*32 + 8*(lane/16) + i) and the token of key 16t + lane % 16
-  Pack8 kb[2][KS], vb[2][KS];
-  int ktok[2];
+  // the wave's 16 KT keys: K and V operands (key lane % 16 of tile t, d
+  // slots ks*32 + 8*(lane/16) + i) and the token of key 16t + lane % 16
+  Pack8 kb[KT][KS], vb[KT][KS];
+  int krel[KT];
   {
-    const int tok = token_of(p, w, gl, kw0 + (lane & 31));
+    const int tok = token_of(p, w, gl, kw0 + (lane & (16 * KT - 1)));
     const uint16_t* kg = static_cast<const uint16_t*>(p.k) + x * p.kv_cap * D;
     const uint16_t* vg = static_cast<const uint16_t*>(p.v) + x * p.kv_cap * D;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      ktok[t] = __shfl(tok, t * 16 + n);
-      const int64_t e = static_cast<int64_t>(ktok[t] >= 0 ? ktok[t] : 0) * D + sub * 8;
+    for (int t = 0; t < KT; ++t) {
+      const int kt_ = __shfl(tok, t * 16 + n);
+      // token relative to the chunk start (absent keys: a large value), so
+      // a key is seen iff krel <= the row's query offset
+      krel[t] = kt_ >= 0 ? static_cast<int>(kt_ - w.t * p.C) : (1 << 30);
+      const int64_t e = static_cast<int64_t>(kt_ >= 0 ? kt_ : 0) * D + sub * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         kb[t][ks].q = *reinterpret_cast<const uint4*>(kg + e + ks * 32);
@@ -465,138 +533,146 @@ __global__ __launch_bounds__(256) void dkv_kernel(BwdParams p) {
       }
     }
   }
-  f32x4 dka[2][NT], dva[2][NT];
+  f32x4 dka[KT][NT], dva[KT][NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < KT; ++t)
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       dka[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
       dva[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   // the unit's rows in its chunk-row space: row rr is query t*C + rr/G,
-  // head rr % G; valid rows [lo, hi); stages of 32 from a multiple of 32
+  // head rr % G; valid rows [lo, hi); stages of 64 from a multiple of 64
   const int lo = static_cast<int>(w.qlo - w.t * p.C) * p.G;
   const int hi = lo + w.R;
-  const int rb0 = lo / kStage * kStage;
-  const int nst = (hi - rb0 + kStage - 1) / kStage;
+  const int rb0 = lo / kDkvRows * kDkvRows;
+  const int nst = (hi - rb0 + kDkvRows - 1) / kDkvRows;
   const uint16_t* qtx = p.qt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
   const uint16_t* gtx = p.gt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
-  uint4 rq[S::NROW], rg[S::NROW], rqt[S::NROW], rgt[S::NROW];
-  float rl = 0.f, rd = 0.f;
-  // piece i of a row-major tensor: (row i / (D/8), 16 bytes at 8 * (i % (D/8)));
-  // of a transposed one: (d = i / 4, rows 8 * (i % 4) .. + 7)
-  auto load_stage = [&](int rb) {
+  const uint16_t* dog = static_cast<const uint16_t*>(p.dout);
+  // Stage rb into st: every wave issues NBLK/NW loads per tile (blocks
+  // wave + k*NW; rows that are not the unit's read row lo instead, their P
+  // and dS being zero) and the loads of the rows' lse and D (all waves
+  // write the same values); wave 0 writes the query offsets.
+  auto issue_stage = [&](int rb, char* st) {
+    // the lane index made opaque here, so that the address arithmetic is
+    // redone per stage rather than hoisted out of the loop and held in
+    // registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int m = 0; m < S::NROW; ++m) {
-      const int i = tid + 256 * m;
-      const int j = i / (D / 8), c = i - j * (D / 8);
-      const int rr = rb + j;
-      if (rr >= lo && rr < hi) {
-        const int64_t ri = row_index(p, w, rr - lo);
-        rq[m] = *reinterpret_cast<const uint4*>(p.qr + ri * D + c * 8);
-        rg[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dout) + ri * D + c * 8);
-      } else {
-        rq[m] = make_uint4(0, 0, 0, 0);
-        rg[m] = make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < S::NBLK / NW; ++k) {
+      const int blk = (wave + k * NW) * 1024;
+      const int o = blk + 16 * ln;
+      {
+        const int r = o / (2 * D), c = ((o % (2 * D)) / 16) ^ rswz<D>(r);
+        int rr = rb + r;
+        if (rr < lo || rr >= hi) rr = lo;
+        const int64_t e = row_index(p, w, rr - lo) * D + 8 * c;
+        load_lds16(p.qr + e, st + S::QA + blk);
+        load_lds16(dog + e, st + S::GA + blk);
       }
-      const int d = i / (kStage / 8), pc = i - d * (kStage / 8);
-      const int64_t te = static_cast<int64_t>(d) * p.NR + rb + pc * 8;
-      rqt[m] = *reinterpret_cast<const uint4*>(qtx + te);
-      rgt[m] = *reinterpret_cast<const uint4*>(gtx + te);
+      {
+        const int d = o / 128, tc = ((o % 128) / 16) ^ tswz(d);
+        const int64_t e = static_cast<int64_t>(d) * p.NR + rb + 8 * tc;
+        load_lds16(qtx + e, st + S::QT + blk);
+        load_lds16(gtx + e, st + S::GT + blk);
+      }
     }
-    if (tid < kStage) {
+    {
+      int rr = rb + ln;
+      if (rr < lo || rr >= hi) rr = lo;
+      const int64_t ri = row_index(p, w, rr - lo);
+      load_lds4(p.lse + ri, st + S::RV);
+      load_lds4(p.delta + ri, st + S::RV + 4 * kDkvRows);
+    }
+    if (tid < kDkvRows) {
       const int rr = rb + tid;
-      if (rr >= lo && rr < hi) {
-        const int64_t ri = row_index(p, w, rr - lo);
-        rl = p.lse[ri] * kLog2e;
-        rd = p.delta[ri];
-      } else {
-        rl = 0.f;
-        rd = 0.f;
-      }
+      reinterpret_cast<int*>(st + S::RV + 8 * kDkvRows)[tid] = rr >= lo && rr < hi ? rr / p.G : kNoRow;
     }
   };
-  auto store_stage = [&](int buf) {
-    uint16_t* st = lds[buf];
-#pragma unroll
-    for (int m = 0; m < S::NROW; ++m) {
-      const int i = tid + 256 * m;
-      const int j = i / (D / 8), c = i - j * (D / 8);
-      *reinterpret_cast<uint4*>(st + S::QA + j * S::RP + c * 8) = rq[m];
-      *reinterpret_cast<uint4*>(st + S::GA + j * S::RP + c * 8) = rg[m];
-      const int d = i / (kStage / 8), pc = i - d * (kStage / 8);
-      *reinterpret_cast<uint4*>(st + S::QT + d * kTPitch + pc * 8) = rqt[m];
-      *reinterpret_cast<uint4*>(st + S::GT + d * kTPitch + pc * 8) = rgt[m];
-    }
-    if (tid < kStage) {
-      rowv[buf][0][tid] = rl;
-      rowv[buf][1][tid] = rd;
-    }
-  };
-  load_stage(rb0);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1, rb = rb0 + s * kStage;
-    if (s + 1 < nst) load_stage(rb + kStage);
-    const uint16_t* st = lds[buf];
+  // 32 rows (half h of the stage)
+  auto compute = [&](const char* st, int h) {
     // S and dP of the two 16-row blocks: lane holds key lane % 16 of tile t
-    // and rows 16*sb + 4*(lane/16) + i; P and dS into the A-operand slots
-    Pack8 pb[2], sk[2];
+    // and rows 32h + 16*sb + 4*(lane/16) + i; P and dS into the A-operand
+    // slots.  The lane's row and column indices are made opaque so that the
+    // LDS addresses are formed here, not hoisted (one set per buffer).
+    int n = lane & 15, sub = lane >> 4;
+    asm volatile("" : "+v"(n), "+v"(sub));
+    Pack8 pb[KT], sk[KT];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      f32x4 sv[2], dp[2];
+      f32x4 sv[KT], dp[KT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < KT; ++t) {
         sv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      const int row = 32 * h + sb * 16 + n;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        const int off = row * (2 * D) + 16 * ((ks * 4 + sub) ^ rswz<D>(row));
         Pack8 qa, ga;
-        qa.q = ld_lds16(st + S::QA + (sb * 16 + n) * S::RP + ks * 32 + sub * 8);
-        ga.q = ld_lds16(st + S::GA + (sb * 16 + n) * S::RP + ks * 32 + sub * 8);
+        qa.q = *reinterpret_cast<const uint4*>(st + S::QA + off);
+        ga.q = *reinterpret_cast<const uint4*>(st + S::GA + off);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < KT; ++t) {
           sv[t] = mfma16x16x32(qa.v, kb[t][ks].v, sv[t]);
           dp[t] = mfma16x16x32(ga.v, vb[t][ks].v, dp[t]);
         }
       }
-      const float4 l4 = *reinterpret_cast<const float4*>(&rowv[buf][0][sb * 16 + sub * 4]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&rowv[buf][1][sb * 16 + sub * 4]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int r4 = 32 * h + sb * 16 + sub * 4;
+      const float4 l4 = *reinterpret_cast<const float4*>(st + S::RV + 4 * r4);
+      const float4 d4 = *reinterpret_cast<const float4*>(st + S::RV + 4 * (kDkvRows + r4));
+      const int4 q4 = *reinterpret_cast<const int4*>(st + S::RV + 4 * (2 * kDkvRows + r4));
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = rb + sb * 16 + sub * 4 + i;
-        const bool row_ok = rr >= lo && rr < hi;
-        const int64_t qpos = w.t * p.C + rr / p.G;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bool ok = row_ok && ktok[t] >= 0 && ktok[t] <= qpos;
+        for (int t = 0; t < KT; ++t) {
+          const bool ok = krel[t] <= qv[i];  // rows that are not the unit's have kNoRow, below all
           const float e = ok ? exp2f(sv[t][i] - lv[i]) : 0.f;
           pb[t].h[sb * 4 + i] = f32_to_bf16(e);
           sk[t].h[sb * 4 + i] = f32_to_bf16(e * (dp[t][i] - dv4[i]));
         }
-      }
     }
     // dV[keys][d] += P^T[keys][rows] dO[rows][d], dK~ likewise with dS and Q'
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      const Pack8 g_ = ld_tslots(st + S::GT, c * 16 + n, sub);
-      const Pack8 q_ = ld_tslots(st + S::QT, c * 16 + n, sub);
+      const Pack8 g_ = ld_tslots_swz(st + S::GT, c * 16 + n, h, sub);
+      const Pack8 q_ = ld_tslots_swz(st + S::QT, c * 16 + n, h, sub);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < KT; ++t) {
         dva[t][c] = mfma16x16x32(pb[t].v, g_.v, dva[t][c]);
         dka[t][c] = mfma16x16x32(sk[t].v, q_.v, dka[t][c]);
       }
     }
-    if (s + 1 < nst) store_stage(buf ^ 1);
-    __syncthreads();
+  };
+  // One stage: issue stage s + 1 into the other buffer, compute stage s,
+  // wait for stage s + 1 and meet at the barrier.  The two buffers are
+  // separate arrays, so the compiler sees that the reads of one do not wait
+  // for the loads into the other.
+  auto step = [&](int s, const char* cur, char* next) {
+    __builtin_amdgcn_sched_barrier(0);  // no interleaving of one stage's work with the next
+    if (s + 1 < nst) issue_stage(rb0 + (s + 1) * kDkvRows, next);
+    compute(cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, 1);
+    wait_vm_barrier<0>();
+  };
+  issue_stage(rb0, b0);
+  wait_vm_barrier<0>();
+  for (int s = 0; s < nst; s += 2) {
+    step(s, b0, b1);
+    if (s + 1 >= nst) break;
+    step(s + 1, b1, b0);
   }
   // partial rows: lane holds d = c*16 + lane % 16 of list keys kw0 + 16t + 4*(lane/16) + i
   const int64_t prow0 = w.slot * p.gmax * p.gs;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < KT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t k = kw0 + t * 16 + sub * 4 + i;
@@ -760,7 +836,7 @@ BwdLayout bwd_layout(const Geometry& g) {
   const size_t slabs = static_cast<size_t>(g.B) * g.Hkv;
   const size_t units = slabs * g.nqc;
   L.ngran = static_cast<int>(g.kv_cap / g.gs);
-  L.CGp = (g.C * g.G + kStage - 1) / kStage * kStage;
+  L.CGp = (g.C * g.G + kDkvRows - 1) / kDkvRows * kDkvRows;
   L.NR = (static_cast<int64_t>(g.nqc) * L.CGp + kTT - 1) / kTT * kTT;
   L.KR = (g.kv_cap + kTT - 1) / kTT * kTT;
   const size_t prow = units * g.gmax * g.gs;  // partial rows
@@ -799,7 +875,8 @@ hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream
   hipLaunchKernelGGL(scatter_kernel, dim3(eg), dim3(256), 0, stream, p);
   const int64_t units8 = (p.units + 7) / 8 * 8;
   hipLaunchKernelGGL((dq_kernel<D>), dim3(static_cast<unsigned>(units8 * p.nslice)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((dkv_kernel<D>), dim3(static_cast<unsigned>(units8 * p.nkb)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((dkv_kernel<D, HGA_DKV_KT>), dim3(static_cast<unsigned>(units8 * p.nkb)),
+                     dim3(kDkvThreads), 0, stream, p);
   const int64_t tblocks = (p.kv_cap + 15) / 16;
   hipLaunchKernelGGL((reduce_kernel<D>), dim3(static_cast<unsigned>(slabs * tblocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
