@@ -225,7 +225,7 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 template <int D, int NW>
 __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffer_rsrc_t kr,
                                            __amdgpu_buffer_rsrc_t vr, const int2* gtab, int gfirst,
-                                           int kb, int kend, int cur0, StageRegs<D, NW>& r) {
+                                           int kb, int kend, int cur0, int qend, StageRegs<D, NW>& r) {
   constexpr int SL = StageRegs<D, NW>::SL;
   const int lg = p.lg_gs, gm = (1 << lg) - 1;
   const int gbase = (kb >> lg) - gfirst;
@@ -236,12 +236,16 @@ __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffe
     gi = gi < kTab - 1 ? gi : kTab - 1;  // keys past kend may point past the table
     return *reinterpret_cast<const unsigned long long*>(gtab + gi);
   };
+  // A key is absent (zeros, token -1) past the list, in an empty entry, or
+  // at or past qend (after the unit's last query: no row sees it, and its
+  // memory need not have been written).
   auto key = [&](int s, unsigned long long ev, int sl, uint32_t& off, int& tok) {
     const int ex = static_cast<int>(static_cast<uint32_t>(ev));
     const int ey = static_cast<int>(static_cast<uint32_t>(ev >> 32));
-    const bool ok = (s < rem) & (ex >= 0);
+    const int t = ey + (s & gm);
+    const bool ok = (s < rem) & (ex >= 0) & (t < qend);
     off = ok ? static_cast<uint32_t>(ex + (s & gm)) * (D * 2) + sl * 16 : kNoRow;
-    tok = ok ? ey + (s & gm) : -1;
+    tok = ok ? t : -1;
   };
 #pragma unroll
   for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
@@ -412,6 +416,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   // in flight while the granule and RoPE tables are built.
   const int n = lane & 31, hsub = lane >> 5;
   const int cur0 = static_cast<int>(w.t * p.C);
+  const int qend = static_cast<int>(w.qlo + w.nq);  // past the unit's last query
   const int q_first = r0 / p.G;
   Pack8 qraw[RB][KS];
   int qpos[RB], hl[RB], row[RB];
@@ -486,7 +491,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   // The first stage's loads go out before the query rows are rotated.
   const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
   StageRegs<D, NW> sr;
-  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, sr);
+  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, qend, sr);
 
   // Rotate, scale by softmax_scale * log2(e) and round the query rows to
   // bf16 MFMA operands.
@@ -542,7 +547,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
     const bool masked = sr.masked;
     __syncthreads();
     if (!rb_on[0]) {  // wave-uniform: this wave has no rows, only loads
-      load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
+      load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, qend, sr);
       return;
     }
     // S^T for the two 32-key halves; each K operand serves every row block.
@@ -567,7 +572,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
     }
     // The next stage's loads go out behind the S products (past the last
     // stage every key is absent: zeros, no memory traffic).
-    load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, sr);
+    load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, qend, sr);
     // Per half: softmax (VALU) then O^T += V^T P^T; the second half's
     // softmax is independent of the first half's PV products.
 #pragma unroll
@@ -704,7 +709,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
       const int s = idx / (D / 4), c4 = idx - s * (D / 4);
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       const int tok = kb + s < kend ? slot_token(p, w, kb + s) : -1;
-      if (tok >= 0) {
+      if (tok >= 0 && tok < w.qlo + w.nq) {  // past the last query: unread (may be unwritten)
         int64_t ko, vo;
         kv_offsets<D>(p, w, kb + s, tok, slab, ko, vo);
         kk = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + ko)[c4];
@@ -902,13 +907,21 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
     for (int ks = 0; ks < KS; ++ks)
       ka[t][ks].q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e + ks * 32);
   }
+  // Keys past the list or past the unit's last query read V as zeros: their
+  // P is zero, but the row they would read (row 0, a pool slot the step did
+  // not fill, or a token not yet written) may hold a non-finite value, and
+  // 0 * NaN is NaN.
   uint32_t vv[kDecWaveKeys];
 #pragma unroll
   for (int j = 0; j < kDecWaveKeys; ++j) {
     const int vr = __builtin_amdgcn_readlane(row, j);
+    const int vt = __builtin_amdgcn_readlane(tok, j);
+    const bool present = vt >= 0 && vt < qhi;
     const int64_t e = (kbase + vshift + vr) * D + lane * DP;
-    if constexpr (DP == 2) vv[j] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v) + e);
-    else vv[j] = static_cast<const uint16_t*>(p.v)[e];
+    if constexpr (DP == 2)
+      vv[j] = present ? *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v) + e) : 0u;
+    else
+      vv[j] = present ? static_cast<const uint16_t*>(p.v)[e] : 0u;
   }
   // RoPE table of the unit's queries, then the rotated, scaled query
   // operand (bf16).

@@ -396,8 +396,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int tk = toks[buf][t * 16 + sub * 4 + i];
           const bool ok = row_ok && tk >= 0 && tk <= qpos;
+          // selects, not products with a zero P: a masked key's V may be
+          // unwritten memory (a NaN there would survive 0 * NaN)
           const float e = ok ? exp2f(sv[t][sb][i] - lse2[sb]) : 0.f;
-          dsb[sb].h[t * 4 + i] = f32_to_bf16(e * (dp[t][sb][i] - dl[sb]));
+          dsb[sb].h[t * 4 + i] = f32_to_bf16(ok ? e * (dp[t][sb][i] - dl[sb]) : 0.f);
         }
     }
     // dQ^T[d][rows] += K^T[d][keys] dS^T[keys][rows]
@@ -633,9 +635,11 @@ __global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
           const bool ok = krel[t] <= qv[i];  // rows that are not the unit's have kNoRow, below all
+          // selects, not products with a zero P: a masked key's V may be
+          // unwritten memory (a NaN there would survive 0 * NaN)
           const float e = ok ? exp2f(sv[t][i] - lv[i]) : 0.f;
           pb[t].h[sb * 4 + i] = f32_to_bf16(e);
-          sk[t].h[sb * 4 + i] = f32_to_bf16(e * (dp[t][i] - dv4[i]));
+          sk[t].h[sb * 4 + i] = f32_to_bf16(ok ? e * (dp[t][i] - dv4[i]) : 0.f);
         }
     }
     // dV[keys][d] += P^T[keys][rows] dO[rows][d], dK~ likewise with dS and Q'
@@ -835,10 +839,14 @@ BwdLayout bwd_layout(const Geometry& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.Hq * g.n_q;
   const size_t slabs = static_cast<size_t>(g.B) * g.Hkv;
   const size_t units = slabs * g.nqc;
-  L.ngran = static_cast<int>(g.kv_cap / g.gs);
+  // only tokens before the last query's end are in any list (granules
+  // holding a visible token), so the per-token pieces cover those: the
+  // workspace depends on q_pos0 + n_q, not on kv_cap
+  const int64_t n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
+  L.ngran = static_cast<int>((n_tok + g.gs - 1) / g.gs);
   L.CGp = (g.C * g.G + kDkvRows - 1) / kDkvRows * kDkvRows;
   L.NR = (static_cast<int64_t>(g.nqc) * L.CGp + kTT - 1) / kTT * kTT;
-  L.KR = (g.kv_cap + kTT - 1) / kTT * kTT;
+  L.KR = (n_tok + kTT - 1) / kTT * kTT;
   const size_t prow = units * g.gmax * g.gs;  // partial rows
   size_t off = 0;
   L.delta = off; off = al256(off + rows * 4);

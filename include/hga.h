@@ -175,8 +175,11 @@ size_t hga_attend_workspace_bytes(const hga_config* cfg, int32_t batch,
  * granules / granule_count are those written by hga_route (or any ascending
  * list of granules inside [0, kv_cap/g_s) with count <= G_max; lists must
  * not repeat a granule).  k_rot holds RoPE-rotated keys (hga_build_summaries).
- * bf16 runs QK^T and PV on bf16 matrix cores (P rounded to bf16) with f32
- * online softmax; f32 runs on f32 vector ALUs.  lse may be NULL.
+ * Rows of k_rot and v at or after the call's last query (q_pos0 + n_q) are
+ * never read into a result and may hold anything (a cache filled up to the
+ * current token).  bf16 runs QK^T and PV on bf16 matrix cores (P rounded
+ * to bf16) with f32 online softmax; f32 runs on f32 vector ALUs.  lse may
+ * be NULL.
  */
 hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                       const void* q_raw, int64_t q_pos0, int64_t n_q,
@@ -278,11 +281,13 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
  * dq~ = s dS k~, dk~ = s dS^T q~, dv = P^T dO.  bf16 only; granules of at
  * least 4 tokens.  dq is bitwise repeatable; dk and dv sum per-(unit, key)
  * partials in an order that can change between calls (f32 rounding only).
- * Workspace: hga_attend_backward_workspace_bytes -- per query row D (f32)
- * and Q' (bf16); transposed Q', dO and k~ (bf16); granule lists; and two
- * f32 partial rows of d per (unit, list key), units * gmax * g_s * d * 8
- * bytes, the largest piece (2.5 GB for 32768 queries, 32 query and 4 KV
- * heads, d = 128, 76 granules per list).  Errors: HGA_ERR_UNSUPPORTED for
+ * As in hga_attend, rows of k_rot and v from q_pos0 + n_q on may hold
+ * anything; dk and dv are zero there.  Workspace:
+ * hga_attend_backward_workspace_bytes (it depends on q_pos0 + n_q, not on
+ * kv_cap) -- per query row D (f32) and Q' (bf16); transposed Q', dO and k~
+ * (bf16); granule lists; and two f32 partial rows of d per (unit, list key),
+ * units * gmax * g_s * d * 8 bytes, the largest piece (2.5 GB for 32768
+ * queries, 32 query and 4 KV heads, d = 128, 76 granules per list).  Errors: HGA_ERR_UNSUPPORTED for
  * other dtypes or shapes, HGA_ERR_WORKSPACE when workspace_bytes is short;
  * nothing is launched then.
  */

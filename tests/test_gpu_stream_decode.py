@@ -45,7 +45,7 @@ def _reference(run, w, dev):
     return outs, lses
 
 
-def _session_run(run, w, cache_slots, dev):
+def _session_run(run, w, cache_slots, dev, poison=False):
     import torch
     cfg = run.cfg
     # store and summary tables hold only the prefix; the session appends the rest
@@ -59,6 +59,10 @@ def _session_run(run, w, cache_slots, dev):
     csum[:, :, PREFIX // cfg.chunk_size:] = 0
     gsum[:, :, PREFIX // cfg.group_size:] = 0
     sess = H.DecodeSession(cfg, w.batch, CAP, PREFIX, cache_slots, store, device=dev)
+    if poison:
+        # the session may not rely on its device buffer's contents: all bits
+        # set reads as NaN in every float format
+        sess.dev.fill_(255)
     outs, lses, stats = [], [], []
     for s in range(w.n_q):
         pos = w.q_pos0 + s
@@ -75,7 +79,7 @@ def _session_run(run, w, cache_slots, dev):
     return outs, lses, stats, csum, gsum, store
 
 
-@pytest.mark.parametrize("cache", ["roomy", "smallest"])
+@pytest.mark.parametrize("cache", ["roomy", "smallest", "smallest_poisoned"])
 def test_stream_decode_equals_device_path(cache):
     import torch
     w = _workload()
@@ -85,11 +89,19 @@ def test_stream_decode_equals_device_path(cache):
     run = P.GpuRun(w, q, k, v, route=False, attend=False)
     ref_out, ref_lse = _reference(run, w, dev)
     need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
-    slots = need if cache == "smallest" else 4 * need
-    outs, lses, stats, csum, gsum, store = _session_run(run, w, slots, dev)
+    slots = 4 * need if cache == "roomy" else need
+    outs, lses, stats, csum, gsum, store = _session_run(run, w, slots, dev, poison=cache.endswith("poisoned"))
     bad = [s for s in range(w.n_q)
            if not (torch.equal(outs[s], ref_out[s]) and torch.equal(lses[s], ref_lse[s]))]
-    assert not bad, f"steps differing from the device path: {bad[:10]}"
+    detail = []
+    for s in bad[:3]:
+        do = (outs[s].float() - ref_out[s].float()).abs()
+        dl = (lses[s] - ref_lse[s]).abs()
+        rows = torch.nonzero(do.amax(dim=-1) > 0).tolist()
+        detail.append(f"step {s}: max|dO| {do.max().item():.3g} max|dlse| {dl.max().item():.3g} "
+                      f"nan {int(torch.isnan(outs[s]).sum())} rows {rows[:8]} "
+                      f"copied {stats[s]['granules_copied']} hits {stats[s]['granules_hit']}")
+    assert not bad, f"steps differing from the device path: {bad[:10]}; " + "; ".join(detail)
     n_closed = (PREFIX + STEPS) // run.cfg.chunk_size
     assert torch.equal(csum[:, :, :n_closed], run.csum[:, :, :n_closed])
     ng_closed = (PREFIX + STEPS) // run.cfg.group_size
