@@ -15,23 +15,22 @@
 // Kernels (bf16 operands on 16x16x32 matrix cores, f32 accumulation):
 //  * prep_kernel: D_i for every row, and Q'_i = R_i q_i * s * log2(e) as bf16
 //    (the forward's query operand), row-major, into the workspace.
-//  * transpose_kernel: Q' and dO transposed per (sequence, KV head) to
-//    [d][row], each query chunk's (query, head) rows contiguous and padded to
-//    a multiple of 32 (zeros where no query is; within 32-row blocks the rows
-//    permuted so that one lane's 8 k slots are one 16-byte piece), and k~ to
-//    [d][token] (runs of 4 tokens contiguous).
+//  * transpose_keys: k~ transposed per (sequence, KV head) to [d][token]
+//    (runs of 4 tokens contiguous) for the dQ product.
 //  * dq_kernel: one workgroup per (unit, 128 rows), four waves of 32 rows,
 //    over the unit's keys 32 at a time: the workgroup stages K, V and K^T of
 //    the 32 keys in LDS (double-buffered through registers); each wave forms
 //    S^T = K Q'^T and dP^T = V dO^T (query rows on N, Q' and dO held in
 //    registers), dS^T in registers as the B operand of dQ^T += K^T dS^T.  The
 //    epilogue applies R^T and writes dq.
-//  * dkv_kernel: one workgroup per (unit, 128 keys of its list), four waves
-//    of 32 keys (K and V held in registers), over the unit's rows 32 at a
-//    time: the workgroup stages Q', dO, Q'^T and dO^T of the 32 rows in LDS;
-//    each wave forms S = Q' K^T and dP = dO V^T (keys on N), so P and dS sit
-//    in registers as the A operands of dV += P^T dO and dK~ += dS^T Q'.  A
-//    unit's sums go to a partial buffer, one row per (unit, list key).
+//  * dkv_kernel: one workgroup per (unit, 128 keys of its list), eight waves
+//    of 16 keys (K and V held in registers), over the unit's rows 64 at a
+//    time: the workgroup stages Q' and dO of the rows in LDS by direct
+//    global -> LDS loads; each wave forms S = Q' K^T and dP = dO V^T (keys on
+//    N), so P and dS sit in registers as the A operands of dV += P^T dO and
+//    dK~ += dS^T Q', whose B operands come from the same tiles through the
+//    transposing LDS read.  A unit's sums go to a partial buffer, one row per
+//    (unit, list key).
 //  * list kernels: for every (sequence, KV head) and granule, the (unit,
 //    list entry) pairs that hold it (counted, scanned and scattered).
 //  * reduce_kernel: per 16 tokens, the sum of their partial rows, turned by
@@ -69,16 +68,14 @@ struct BwdParams {
   // workspace
   float* delta;         // [rows_total]
   uint16_t* qr;         // [rows_total][D] Q' (bf16)
-  uint16_t* qt;         // [B*Hkv][D][NR] Q' by chunk row (chunk trel at trel*CGp; permuted in 32-row blocks)
-  uint16_t* gt;         // [B*Hkv][D][NR] dO likewise
   uint16_t* kt;         // [B*Hkv][D][KR] k~ by token
   int32_t* cnt;         // [slabs][ngran] entries per granule, then scatter cursors
   int32_t* off;         // [slabs][ngran + 1] list offsets
   int32_t* list;        // [slabs][nqc * gmax] entries slot * gmax + i
   float* pk;            // [units * gmax * gs][D] dk~ per (unit, list key)
   float* pv;            // [units * gmax * gs][D] dv likewise
-  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total, NR, KR, n_tok;
-  int B, Hq, Hkv, G, C, CGp, gs, lg_gs, gmax, ngran, nkb, nslice;
+  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total, KR, n_tok;
+  int B, Hq, Hkv, G, C, gs, lg_gs, gmax, ngran, nkb, nslice;
   float scale, scale_log2;
   RopeFreqs rope;
 };
@@ -161,35 +158,20 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdParams p) {
   }
 }
 
-// Transposes kTT rows of one (sequence, KV head) to [d][row] (through LDS).
-// KEYS = false: row i is chunk trel = i / CGp, chunk row rr = i % CGp, i.e.
-// query (t0 + trel) * C + rr / G and head rr % G of src = Q' or dO
-// ([B][Hq][n_q][D]), zero where that is not a query of the call (or rr is
-// padding); KEYS = true: row i is token i of k~ ([B][Hkv][kv_cap][D]), zero
-// from n_tok on.
-template <int D, bool KEYS>
-__global__ __launch_bounds__(256) void transpose_kernel(BwdParams p, const uint16_t* src, uint16_t* dst,
-                                                        int64_t nrows) {
+// Transposes kTT tokens of k~ of one (sequence, KV head) to [d][token]
+// (through LDS), zero from n_tok on.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_keys(BwdParams p) {
   constexpr int TP = D + 8;  // LDS row pitch (elements)
   __shared__ __align__(16) uint16_t tile[kTT * TP];
   const int64_t x = blockIdx.y;  // slab
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTT;
-  const int b = static_cast<int>(x / p.Hkv), kvh = static_cast<int>(x - static_cast<int64_t>(b) * p.Hkv);
+  const uint16_t* src = static_cast<const uint16_t*>(p.k);
   for (int i = threadIdx.x; i < kTT * (D / 8); i += 256) {
     const int j = i / (D / 8), c = i - j * (D / 8);
     const int64_t r = r0 + j;
     uint4 val = make_uint4(0, 0, 0, 0);
-    int64_t srow = -1;
-    if (KEYS) {
-      if (r < p.n_tok) srow = x * p.kv_cap + r;
-    } else {
-      const int64_t trel = r / p.CGp;
-      const int rr = static_cast<int>(r - trel * p.CGp);
-      const int64_t q = (p.t0 + trel) * p.C + rr / p.G;
-      if (rr < p.C * p.G && q >= p.q_pos0 && q < p.q_pos0 + p.n_q)
-        srow = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + rr % p.G) * p.n_q + (q - p.q_pos0);
-    }
-    if (srow >= 0) val = *reinterpret_cast<const uint4*>(src + srow * D + c * 8);
+    if (r < p.n_tok) val = *reinterpret_cast<const uint4*>(src + (x * p.kv_cap + r) * D + c * 8);
     *reinterpret_cast<uint2*>(&tile[j * TP + c * 8]) = make_uint2(val.x, val.y);
     *reinterpret_cast<uint2*>(&tile[j * TP + c * 8 + 4]) = make_uint2(val.z, val.w);
   }
@@ -198,15 +180,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(BwdParams p, const uint1
     const int d = i / (kTT / 8), c = i - d * (kTT / 8);
     Pack8 o;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      // query rows: position 8q + 4h + j of a 32-row block holds row
-      // 16h + 4q + j, so that the 8 k slots one lane takes in a contraction
-      // over the block's rows form one 16-byte piece
-      const int pos = c * 8 + m;
-      const int row = KEYS ? pos : (pos & ~31) + 16 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 3) + (pos & 3);
-      o.h[m] = tile[row * TP + d];
-    }
-    *reinterpret_cast<uint4*>(dst + (x * D + d) * nrows + r0 + c * 8) = o.q;
+    for (int m = 0; m < 8; ++m) o.h[m] = tile[(c * 8 + m) * TP + d];
+    *reinterpret_cast<uint4*>(p.kt + (x * D + d) * p.KR + r0 + c * 8) = o.q;
   }
 }
 
@@ -438,15 +413,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 // dkv: stage of 64 chunk rows in LDS, filled by direct global -> LDS loads
 // (a wave's lane l lands at 16*l, or 4*l, of the wave's block), so the
 // tiles are unpadded and their 16-byte chunks XOR-swizzled against bank
-// conflicts: Q' and dO rows (row j: 2*D bytes, chunk c at c ^ rswz(j)),
-// their transposes (column d: 128 bytes, chunk c at c ^ tswz(d)); then the
-// rows' lse, D and query offsets (RV).
+// conflicts: Q' and dO rows (row j: 2*D bytes, chunk c at c ^ rswz(j));
+// then the rows' lse, D and query offsets (RV).  The products that
+// contract over rows read them with the transposing LDS read.
 constexpr int kDkvRows = 64;
 template <int D>
 struct DkvStage {
   static constexpr int TILE = kDkvRows * D * 2;  // bytes of one tensor's tile
   static constexpr int NBLK = TILE / 1024;       // 1 KB blocks per tile
-  static constexpr int QA = 0, GA = TILE, QT = 2 * TILE, GT = 3 * TILE, RV = 4 * TILE;
+  static constexpr int QA = 0, GA = TILE, RV = 2 * TILE;
   static constexpr int BYTES = RV + 3 * 4 * kDkvRows;
 };
 
@@ -456,7 +431,6 @@ template <int D>
 __device__ __forceinline__ int rswz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-__device__ __forceinline__ int tswz(int d) { return (d >> 1) & 7; }
 
 // Direct global -> LDS loads of 16 or 4 bytes per lane: lane l's bytes land
 // at lds_wave + 16*l (4*l); lds_wave is the same in every lane.  The host
@@ -486,12 +460,29 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // k slots of a contraction over 32 rows of the stage (half h; slot
-// 8*(lane/16) + j <-> row 32h + 16*(j/4) + 4*(lane/16) + j%4) for column col
-// of a swizzled transposed tile: one 16-byte piece, as the rows are stored
-// permuted.
-__device__ __forceinline__ Pack8 ld_tslots_swz(const char* tile, int col, int h, int sub) {
+// 8*(lane/16) + j <-> row 32h + 16*(j/4) + 4*(lane/16) + j%4) for column
+// 16c + lane%16 of a swizzled row-major tile, by two transposing LDS reads
+// (ds_read_b64_tr_b16): in each group of 16 lanes, lane j reads 8 bytes of
+// row base + j/4 at columns 4*(j%4) .. +3 of the 16, and lane i receives
+// column i of the 4 rows.
+template <int D>
+__device__ __forceinline__ Pack8 ld_rowslots(const char* tile, int c, int h, int n, int sub) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
   Pack8 r;
-  r.q = *reinterpret_cast<const uint4*>(tile + col * 128 + 16 * ((4 * h + sub) ^ tswz(col)));
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 32 * h + 16 * half + 4 * sub + (n >> 2);
+    const int col = 16 * c + 4 * (n & 3);           // element column of this lane's 8 bytes
+    const int off = row * (2 * D) + 16 * ((col >> 3) ^ rswz<D>(row)) + 2 * (col & 7);
+#if defined(__HIP_DEVICE_COMPILE__)
+    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
+#else
+    const v4s v = {0, 0, 0, 0};
+#endif
+    r.u[2 * half] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
+    r.u[2 * half + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
+  }
   return r;
 }
 
@@ -549,8 +540,6 @@ __global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
   const int hi = lo + w.R;
   const int rb0 = lo / kDkvRows * kDkvRows;
   const int nst = (hi - rb0 + kDkvRows - 1) / kDkvRows;
-  const uint16_t* qtx = p.qt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
-  const uint16_t* gtx = p.gt + x * D * p.NR + static_cast<int64_t>(w.trel) * p.CGp;
   const uint16_t* dog = static_cast<const uint16_t*>(p.dout);
   // Stage rb into st: every wave issues NBLK/NW loads per tile (blocks
   // wave + k*NW; rows that are not the unit's read row lo instead, their P
@@ -573,12 +562,6 @@ __global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
         const int64_t e = row_index(p, w, rr - lo) * D + 8 * c;
         load_lds16(p.qr + e, st + S::QA + blk);
         load_lds16(dog + e, st + S::GA + blk);
-      }
-      {
-        const int d = o / 128, tc = ((o % 128) / 16) ^ tswz(d);
-        const int64_t e = static_cast<int64_t>(d) * p.NR + rb + 8 * tc;
-        load_lds16(qtx + e, st + S::QT + blk);
-        load_lds16(gtx + e, st + S::GT + blk);
       }
     }
     {
@@ -645,8 +628,8 @@ __global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
     // dV[keys][d] += P^T[keys][rows] dO[rows][d], dK~ likewise with dS and Q'
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      const Pack8 g_ = ld_tslots_swz(st + S::GT, c * 16 + n, h, sub);
-      const Pack8 q_ = ld_tslots_swz(st + S::QT, c * 16 + n, h, sub);
+      const Pack8 g_ = ld_rowslots<D>(st + S::GA, c, h, n, sub);
+      const Pack8 q_ = ld_rowslots<D>(st + S::QA, c, h, n, sub);
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         dva[t][c] = mfma16x16x32(pb[t].v, g_.v, dva[t][c]);
@@ -827,9 +810,9 @@ __global__ __launch_bounds__(256) void zero_i32(int32_t* x, int64_t n) {
 
 // Workspace carve-up (256-byte aligned pieces).
 struct BwdLayout {
-  size_t delta, qr, qt, gt, kt, cnt, off, list, pk, pv, total;
-  int64_t NR, KR;
-  int CGp, ngran;
+  size_t delta, qr, kt, cnt, off, list, pk, pv, total;
+  int64_t KR;
+  int ngran;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -844,15 +827,11 @@ BwdLayout bwd_layout(const Geometry& g) {
   // workspace depends on q_pos0 + n_q, not on kv_cap
   const int64_t n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
   L.ngran = static_cast<int>((n_tok + g.gs - 1) / g.gs);
-  L.CGp = (g.C * g.G + kDkvRows - 1) / kDkvRows * kDkvRows;
-  L.NR = (static_cast<int64_t>(g.nqc) * L.CGp + kTT - 1) / kTT * kTT;
   L.KR = (n_tok + kTT - 1) / kTT * kTT;
   const size_t prow = units * g.gmax * g.gs;  // partial rows
   size_t off = 0;
   L.delta = off; off = al256(off + rows * 4);
   L.qr = off; off = al256(off + rows * g.d * 2);
-  L.qt = off; off = al256(off + slabs * g.d * L.NR * 2);
-  L.gt = off; off = al256(off + slabs * g.d * L.NR * 2);
   L.kt = off; off = al256(off + slabs * g.d * L.KR * 2);
   L.cnt = off; off = al256(off + slabs * L.ngran * 4);
   L.off = off; off = al256(off + slabs * (L.ngran + 1) * 4);
@@ -869,13 +848,8 @@ hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream
   hipLaunchKernelGGL(zero_i32, dim3(256), dim3(256), 0, stream, p.cnt, slabs * p.ngran);
   hipLaunchKernelGGL((prep_kernel<D>), dim3(static_cast<unsigned>((p.rows_total + 3) / 4)), dim3(256), 0,
                      stream, p);
-  const dim3 trg(static_cast<unsigned>(p.NR / kTT), static_cast<unsigned>(slabs));
-  hipLaunchKernelGGL((transpose_kernel<D, false>), trg, dim3(256), 0, stream, p, p.qr, p.qt, p.NR);
-  hipLaunchKernelGGL((transpose_kernel<D, false>), trg, dim3(256), 0, stream, p,
-                     static_cast<const uint16_t*>(p.dout), p.gt, p.NR);
   const dim3 tkg(static_cast<unsigned>(p.KR / kTT), static_cast<unsigned>(slabs));
-  hipLaunchKernelGGL((transpose_kernel<D, true>), tkg, dim3(256), 0, stream, p,
-                     static_cast<const uint16_t*>(p.k), p.kt, p.KR);
+  hipLaunchKernelGGL((transpose_keys<D>), tkg, dim3(256), 0, stream, p);
   const int64_t entries = p.units * p.gmax;
   const unsigned eg = static_cast<unsigned>((entries + 255) / 256);
   hipLaunchKernelGGL(count_kernel, dim3(eg), dim3(256), 0, stream, p);
@@ -929,8 +903,6 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.dv = dv;
   p.delta = reinterpret_cast<float*>(w + L.delta);
   p.qr = reinterpret_cast<uint16_t*>(w + L.qr);
-  p.qt = reinterpret_cast<uint16_t*>(w + L.qt);
-  p.gt = reinterpret_cast<uint16_t*>(w + L.gt);
   p.kt = reinterpret_cast<uint16_t*>(w + L.kt);
   p.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
   p.off = reinterpret_cast<int32_t*>(w + L.off);
@@ -944,7 +916,6 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.nqc = g.nqc;
   p.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   p.rows_total = static_cast<int64_t>(g.B) * g.Hq * g.n_q;
-  p.NR = L.NR;
   p.KR = L.KR;
   p.n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
   p.B = g.B;
@@ -952,7 +923,6 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.Hkv = g.Hkv;
   p.G = g.G;
   p.C = g.C;
-  p.CGp = L.CGp;
   p.gs = g.gs;
   p.lg_gs = 0;
   while ((1 << p.lg_gs) < g.gs) ++p.lg_gs;
