@@ -15,14 +15,13 @@
 // Kernels (bf16 operands on 16x16x32 matrix cores, f32 accumulation):
 //  * prep_kernel: D_i for every row, and Q'_i = R_i q_i * s * log2(e) as bf16
 //    (the forward's query operand), row-major, into the workspace.
-//  * transpose_keys: k~ transposed per (sequence, KV head) to [d][token]
-//    (runs of 4 tokens contiguous) for the dQ product.
 //  * dq_kernel: one workgroup per (unit, 128 rows), four waves of 32 rows,
-//    over the unit's keys 32 at a time: the workgroup stages K, V and K^T of
-//    the 32 keys in LDS (double-buffered through registers); each wave forms
+//    over the unit's keys 32 at a time: the workgroup stages K and V of the
+//    32 keys in LDS by direct global -> LDS loads; each wave forms
 //    S^T = K Q'^T and dP^T = V dO^T (query rows on N, Q' and dO held in
-//    registers), dS^T in registers as the B operand of dQ^T += K^T dS^T.  The
-//    epilogue applies R^T and writes dq.
+//    registers), dS^T in registers as the B operand of dQ^T += K^T dS^T,
+//    whose K^T operand comes from the K rows through the transposing LDS
+//    read.  The epilogue applies R^T and writes dq.
 //  * dkv_kernel: one workgroup per (unit, 128 keys of its list), eight waves
 //    of 16 keys (K and V held in registers), over the unit's rows 64 at a
 //    time: the workgroup stages Q' and dO of the rows in LDS by direct
@@ -46,8 +45,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRowsWave = 32;   // rows per wave in dq_kernel (two 16-row blocks)
 constexpr int kStage = 32;      // keys (dq_kernel) or rows (dkv_kernel) per LDS stage
 constexpr int kKeysWG = 128;    // keys per dkv_kernel workgroup (four waves of 32)
-constexpr int kTT = 64;         // rows (or tokens) per transpose tile
-constexpr int kTPitch = kStage + 8;  // LDS pitch (elements) of a transposed stage
 #ifndef HGA_DKV_KT
 #define HGA_DKV_KT 1
 #endif
@@ -68,13 +65,12 @@ struct BwdParams {
   // workspace
   float* delta;         // [rows_total]
   uint16_t* qr;         // [rows_total][D] Q' (bf16)
-  uint16_t* kt;         // [B*Hkv][D][KR] k~ by token
   int32_t* cnt;         // [slabs][ngran] entries per granule, then scatter cursors
   int32_t* off;         // [slabs][ngran + 1] list offsets
   int32_t* list;        // [slabs][nqc * gmax] entries slot * gmax + i
   float* pk;            // [units * gmax * gs][D] dk~ per (unit, list key)
   float* pv;            // [units * gmax * gs][D] dv likewise
-  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total, KR, n_tok;
+  int64_t q_pos0, n_q, kv_cap, t0, nqc, units, rows_total, n_tok;
   int B, Hq, Hkv, G, C, gs, lg_gs, gmax, ngran, nkb, nslice;
   float scale, scale_log2;
   RopeFreqs rope;
@@ -158,33 +154,6 @@ __global__ __launch_bounds__(256) void prep_kernel(BwdParams p) {
   }
 }
 
-// Transposes kTT tokens of k~ of one (sequence, KV head) to [d][token]
-// (through LDS), zero from n_tok on.
-template <int D>
-__global__ __launch_bounds__(256) void transpose_keys(BwdParams p) {
-  constexpr int TP = D + 8;  // LDS row pitch (elements)
-  __shared__ __align__(16) uint16_t tile[kTT * TP];
-  const int64_t x = blockIdx.y;  // slab
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTT;
-  const uint16_t* src = static_cast<const uint16_t*>(p.k);
-  for (int i = threadIdx.x; i < kTT * (D / 8); i += 256) {
-    const int j = i / (D / 8), c = i - j * (D / 8);
-    const int64_t r = r0 + j;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < p.n_tok) val = *reinterpret_cast<const uint4*>(src + (x * p.kv_cap + r) * D + c * 8);
-    *reinterpret_cast<uint2*>(&tile[j * TP + c * 8]) = make_uint2(val.x, val.y);
-    *reinterpret_cast<uint2*>(&tile[j * TP + c * 8 + 4]) = make_uint2(val.z, val.w);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < D * (kTT / 8); i += 256) {
-    const int d = i / (kTT / 8), c = i - d * (kTT / 8);
-    Pack8 o;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) o.h[m] = tile[(c * 8 + m) * TP + d];
-    *reinterpret_cast<uint4*>(p.kt + (x * D + d) * p.KR + r0 + c * 8) = o.q;
-  }
-}
-
 // Token of unit list key k (per lane), or -1 past the list.  With at most
 // 128 granules per list, the list sits in two registers per lane (entries
 // lane and lane + 64) and is read with lane shuffles; longer lists are read
@@ -220,40 +189,51 @@ __device__ __forceinline__ int token_of(const BwdParams& p, const BUnit& w, cons
   return in && g >= 0 ? g * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
 }
 
-__device__ __forceinline__ uint4 ld_lds16(const uint16_t* s) { return *reinterpret_cast<const uint4*>(s); }
-__device__ __forceinline__ uint2 ld_lds8(const uint16_t* s) { return *reinterpret_cast<const uint2*>(s); }
-
-// k slots of a contraction over 32 rows (or keys) held as two 16-blocks:
-// slot 8*(lane/16) + j <-> index 16*(j/4) + 4*(lane/16) + j%4.  Reads them for
-// column `col` of a transposed LDS stage.
-__device__ __forceinline__ Pack8 ld_tslots(const uint16_t* stage, int col, int sub) {
-  const uint16_t* s = stage + col * kTPitch + 4 * sub;
-  const uint2 a = ld_lds8(s), b = ld_lds8(s + 16);
+// k slots of a contraction over 32 rows of the stage (half h; slot
+// 8*(lane/16) + j <-> row 32h + 16*(j/4) + 4*(lane/16) + j%4) for column
+// 16c + lane%16 of a swizzled row-major tile, by two transposing LDS reads
+// (ds_read_b64_tr_b16): in each group of 16 lanes, lane j reads 8 bytes of
+// row base + j/4 at columns 4*(j%4) .. +3 of the 16, and lane i receives
+// column i of the 4 rows.
+template <int D>
+__device__ __forceinline__ Pack8 ld_rowslots(const char* tile, int c, int h, int n, int sub) {
   Pack8 r;
-  r.u[0] = a.x;
-  r.u[1] = a.y;
-  r.u[2] = b.x;
-  r.u[3] = b.y;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 32 * h + 16 * half + 4 * sub + (n >> 2);
+    const int col = 16 * c + 4 * (n & 3);           // element column of this lane's 8 bytes
+    const int off = row * (2 * D) + 16 * ((col >> 3) ^ rswz<D>(row)) + 2 * (col & 7);
+    const uint2 v = lds_read_tr16(tile + off);
+    r.u[2 * half] = v.x;
+    r.u[2 * half + 1] = v.y;
+  }
   return r;
 }
 
-// dq: stage of 32 keys in LDS: K and V rows ([key][D + 8]), K^T ([D][40]),
-// and the keys' tokens.
+// dq: stage of 32 keys in LDS, filled by direct global -> LDS loads: K and
+// V rows (unswizzled order, XOR-swizzled chunks as rswz); the keys' tokens
+// in a separate array.  The dQ product's K^T operand (keys in the k slots)
+// comes from the K rows through the transposing LDS read.
 template <int D>
 struct DqStage {
-  static constexpr int RP = D + 8;
-  static constexpr int K = 0, V = kStage * RP, KT = 2 * kStage * RP;
-  static constexpr int ELEMS = KT + D * kTPitch;  // uint16 elements
-  static constexpr int NROW = kStage * D / 8 / 256;  // 16-byte pieces of K (and of V) per thread
-  static constexpr int NT = D * kStage / 4 / 256;    // 8-byte pieces of K^T per thread
+  static constexpr int ROW = 2 * D;
+  static constexpr int TILE = kStage * ROW;
+  static constexpr int K = 0, V = TILE, BYTES = 2 * TILE;
+  static constexpr int NBLK = TILE / 1024;
 };
+
+// Source of absent keys' K and V rows (their products are selected out or
+// multiplied by zero, so the row must hold finite values: zeros).
+__device__ __align__(16) uint4 g_zero_row[16];
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   using S = DqStage<D>;
-  constexpr int KS = D / 32, H = D / 2, NT = D / 16;
-  __shared__ __align__(16) uint16_t lds[2][S::ELEMS];
-  __shared__ int toks[2][kStage];
+  constexpr int KS = D / 32, H = D / 2, NT = D / 16, NW = 4;
+  static_assert(S::NBLK % NW == 0, "tile blocks spread evenly over the waves");
+  __shared__ __align__(1024) char b0[S::BYTES];
+  __shared__ __align__(1024) char b1[S::BYTES];
+  __shared__ int tok0[kStage], tok1[kStage];
   BUnit w;
   int slice;
   if (!map_block(p, p.nslice, w, slice)) return;
@@ -261,9 +241,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int r0 = slice * 4 * kRowsWave + wave * kRowsWave;  // this wave's rows
   if (slice * 4 * kRowsWave >= w.R) return;  // uniform over the workgroup
   const int64_t x = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + x * p.kv_cap * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + x * p.kv_cap * D;
-  const uint16_t* ktx = p.kt + x * D * p.KR;
+  const char* kg = static_cast<const char*>(p.k) + x * p.kv_cap * S::ROW;
+  const char* vg = static_cast<const char*>(p.v) + x * p.kv_cap * S::ROW;
+  const char* zrow = reinterpret_cast<const char*>(g_zero_row);
   const GranList gl = load_glist(p, w);
   // B operands of the wave's two 16-row blocks (rows past the unit repeat
   // its last row and are dropped at the end): Q' and dO at d slots
@@ -288,55 +268,34 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   for (int c = 0; c < NT; ++c)
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) acc[c][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // stage loads: thread piece i of K / V is (key i / (D/8), 16 bytes at
-  // 8 * (i % (D/8))); of K^T (d = i / 8, keys 4 * (i % 8) .. + 3)
-  uint4 rk[S::NROW], rv[S::NROW];
-  uint2 rt[S::NT];
-  int my_tok = -1;
-  auto load_stage = [&](int64_t kb) {
-    const int tok = token_of(p, w, gl, kb + (lane & 31));  // token of key kb + lane % 32
-    my_tok = tok;
+  // Stage of list keys kb .. kb+31 into st: each wave issues its 1 KB blocks
+  // of the K and V tiles (block row m = key m); a key past the list, or at
+  // or after n_tok (no query sees it, and its memory may be unwritten),
+  // reads the zero row and gets token -1.
+  auto issue_stage = [&](int64_t kb, char* st, int* tok) {
+    const int tk = token_of(p, w, gl, kb + (lane & 31));  // token of key kb + lane % 32
+    const int tkv = tk < p.n_tok ? tk : -1;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // addresses formed here, not hoisted out of the loop
 #pragma unroll
-    for (int m = 0; m < S::NROW; ++m) {
-      const int i = tid + 256 * m, key = i / (D / 8), c = i - key * (D / 8);
-      const int tk = __shfl(tok, key);
-      const int64_t e = static_cast<int64_t>(tk >= 0 ? tk : 0) * D + c * 8;
-      rk[m] = tk >= 0 ? *reinterpret_cast<const uint4*>(kg + e) : make_uint4(0, 0, 0, 0);
-      rv[m] = tk >= 0 ? *reinterpret_cast<const uint4*>(vg + e) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < S::NBLK / NW; ++j) {
+      const int blk = (wave + j * NW) * 1024;
+      const int o = blk + 16 * ln;
+      const int m = o / S::ROW;
+      const int c = ((o % S::ROW) / 16) ^ rswz<D>(m);
+      const int t = __shfl(tkv, m);
+      const int64_t e = static_cast<int64_t>(t) * S::ROW + 16 * c;
+      load_lds16(t >= 0 ? kg + e : zrow + 16 * c, st + S::K + blk);
+      load_lds16(t >= 0 ? vg + e : zrow + 16 * c, st + S::V + blk);
     }
-#pragma unroll
-    for (int m = 0; m < S::NT; ++m) {
-      const int i = tid + 256 * m, d = i / (kStage / 4), c = i - d * (kStage / 4);
-      const int tk = __shfl(tok, 4 * c);  // tokens 4c .. 4c+3 are consecutive
-      rt[m] = tk >= 0 ? *reinterpret_cast<const uint2*>(ktx + static_cast<int64_t>(d) * p.KR + tk)
-                      : make_uint2(0, 0);
-    }
+    if (tid < kStage) tok[tid] = tkv;
   };
-  auto store_stage = [&](int buf) {
-    uint16_t* st = lds[buf];
-#pragma unroll
-    for (int m = 0; m < S::NROW; ++m) {
-      const int i = tid + 256 * m, key = i / (D / 8), c = i - key * (D / 8);
-      *reinterpret_cast<uint4*>(st + S::K + key * S::RP + c * 8) = rk[m];
-      *reinterpret_cast<uint4*>(st + S::V + key * S::RP + c * 8) = rv[m];
-    }
-#pragma unroll
-    for (int m = 0; m < S::NT; ++m) {
-      const int i = tid + 256 * m, d = i / (kStage / 4), c = i - d * (kStage / 4);
-      *reinterpret_cast<uint2*>(st + S::KT + d * kTPitch + 4 * c) = rt[m];
-    }
-    if (tid < kStage) toks[buf][tid] = my_tok;
-  };
+  // One stage: the next stage's loads into nxt, then S^T, dP^T, dS^T and
+  // dQ^T from cur, then wait for the next stage and meet at the barrier.
   const int nst = (w.nkeys + kStage - 1) / kStage;
-  if (nst > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nst) load_stage(static_cast<int64_t>(s + 1) * kStage);
-    const uint16_t* st = lds[buf];
+  auto step = [&](int s, const char* cur, const int* toks, char* nxt, int* ntok) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nst) issue_stage(static_cast<int64_t>(s + 1) * kStage, nxt, ntok);
     // S^T and dP^T: lane holds row lane % 16 of block sb and keys 16t + 4*(lane/16) + i
     f32x4 sv[2][2], dp[2][2];
 #pragma unroll
@@ -347,18 +306,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         dp[t][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const int m = t * 16 + n;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        const int off = m * S::ROW + 16 * ((ks * 4 + sub) ^ rswz<D>(m));
         Pack8 ka, va;
-        ka.q = ld_lds16(st + S::K + (t * 16 + n) * S::RP + ks * 32 + sub * 8);
-        va.q = ld_lds16(st + S::V + (t * 16 + n) * S::RP + ks * 32 + sub * 8);
+        ka.q = *reinterpret_cast<const uint4*>(cur + S::K + off);
+        va.q = *reinterpret_cast<const uint4*>(cur + S::V + off);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           sv[t][sb] = mfma16x16x32(ka.v, qb[sb][ks].v, sv[t][sb]);
           dp[t][sb] = mfma16x16x32(va.v, gb[sb][ks].v, dp[t][sb]);
         }
       }
+    }
     Pack8 dsb[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -369,23 +331,29 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tk = toks[buf][t * 16 + sub * 4 + i];
+          const int tk = toks[t * 16 + sub * 4 + i];
           const bool ok = row_ok && tk >= 0 && tk <= qpos;
-          // selects, not products with a zero P: a masked key's V may be
-          // unwritten memory (a NaN there would survive 0 * NaN)
+          // selects, not products with a zero P (0 * NaN is NaN)
           const float e = ok ? exp2f(sv[t][sb][i] - lse2[sb]) : 0.f;
           dsb[sb].h[t * 4 + i] = f32_to_bf16(ok ? e * (dp[t][sb][i] - dl[sb]) : 0.f);
         }
     }
-    // dQ^T[d][rows] += K^T[d][keys] dS^T[keys][rows]
+    // dQ^T[d][rows] += K^T[d][keys] dS^T[keys][rows]: A = K^T through the
+    // transposing read (k slots: keys 4*(lane/16) + i, then 16 + 4*(lane/16) + i)
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      const Pack8 kt_ = ld_tslots(st + S::KT, c * 16 + n, sub);
+      const Pack8 kt_ = ld_rowslots<D>(cur + S::K, c, 0, n, sub);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) acc[c][sb] = mfma16x16x32(kt_.v, dsb[sb].v, acc[c][sb]);
     }
-    if (s + 1 < nst) store_stage(buf ^ 1);
-    __syncthreads();
+    wait_vm_barrier<0>();
+  };
+  if (nst > 0) issue_stage(0, b0, tok0);
+  wait_vm_barrier<0>();
+  for (int s = 0; s < nst; s += 2) {
+    step(s, b0, tok0, b1, tok1);
+    if (s + 1 >= nst) break;
+    step(s + 1, b1, tok1, b0, tok0);
   }
   // dq = R^T (s * dq~): lane holds d = c*16 + 4*(lane/16) + i of row r0 + sb*16 + n
   const int64_t q0 = rope_base(p.rope, w.qlo);
@@ -424,67 +392,6 @@ struct DkvStage {
   static constexpr int QA = 0, GA = TILE, RV = 2 * TILE;
   static constexpr int BYTES = RV + 3 * 4 * kDkvRows;
 };
-
-// Row-major tile: the 16-row read of an A operand (16 lanes, one chunk each)
-// and the fill are spread over all banks.
-template <int D>
-__device__ __forceinline__ int rswz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-
-// Direct global -> LDS loads of 16 or 4 bytes per lane: lane l's bytes land
-// at lds_wave + 16*l (4*l); lds_wave is the same in every lane.  The host
-// pass only needs the declaration.
-__device__ __forceinline__ void load_lds16(const void* g, char* lds_wave) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds_wave, 16, 0, 0);
-#endif
-}
-__device__ __forceinline__ void load_lds4(const void* g, char* lds_wave) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds_wave, 4, 0, 0);
-#endif
-}
-
-// Waits until at most k vector-memory operations of this wave are
-// outstanding (k a multiple of the per-stage count, <= 63) and for its LDS
-// operations, then meets the workgroup at a barrier.  The empty asm
-// statements keep the compiler from moving memory accesses across.
-template <int K>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(K >= 0 && K < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4));  // vmcnt(K) lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// k slots of a contraction over 32 rows of the stage (half h; slot
-// 8*(lane/16) + j <-> row 32h + 16*(j/4) + 4*(lane/16) + j%4) for column
-// 16c + lane%16 of a swizzled row-major tile, by two transposing LDS reads
-// (ds_read_b64_tr_b16): in each group of 16 lanes, lane j reads 8 bytes of
-// row base + j/4 at columns 4*(j%4) .. +3 of the 16, and lane i receives
-// column i of the 4 rows.
-template <int D>
-__device__ __forceinline__ Pack8 ld_rowslots(const char* tile, int c, int h, int n, int sub) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s lds_v4s;
-  Pack8 r;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = 32 * h + 16 * half + 4 * sub + (n >> 2);
-    const int col = 16 * c + 4 * (n & 3);           // element column of this lane's 8 bytes
-    const int off = row * (2 * D) + 16 * ((col >> 3) ^ rswz<D>(row)) + 2 * (col & 7);
-#if defined(__HIP_DEVICE_COMPILE__)
-    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
-#else
-    const v4s v = {0, 0, 0, 0};
-#endif
-    r.u[2 * half] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
-    r.u[2 * half + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
-  }
-  return r;
-}
 
 // KT key tiles of 16 per wave, 128 / (16 KT) waves per workgroup; two stage
 // buffers.
@@ -810,8 +717,7 @@ __global__ __launch_bounds__(256) void zero_i32(int32_t* x, int64_t n) {
 
 // Workspace carve-up (256-byte aligned pieces).
 struct BwdLayout {
-  size_t delta, qr, kt, cnt, off, list, pk, pv, total;
-  int64_t KR;
+  size_t delta, qr, cnt, off, list, pk, pv, total;
   int ngran;
 };
 
@@ -827,12 +733,10 @@ BwdLayout bwd_layout(const Geometry& g) {
   // workspace depends on q_pos0 + n_q, not on kv_cap
   const int64_t n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
   L.ngran = static_cast<int>((n_tok + g.gs - 1) / g.gs);
-  L.KR = (n_tok + kTT - 1) / kTT * kTT;
   const size_t prow = units * g.gmax * g.gs;  // partial rows
   size_t off = 0;
   L.delta = off; off = al256(off + rows * 4);
   L.qr = off; off = al256(off + rows * g.d * 2);
-  L.kt = off; off = al256(off + slabs * g.d * L.KR * 2);
   L.cnt = off; off = al256(off + slabs * L.ngran * 4);
   L.off = off; off = al256(off + slabs * (L.ngran + 1) * 4);
   L.list = off; off = al256(off + slabs * g.nqc * g.gmax * 4);
@@ -848,8 +752,6 @@ hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream
   hipLaunchKernelGGL(zero_i32, dim3(256), dim3(256), 0, stream, p.cnt, slabs * p.ngran);
   hipLaunchKernelGGL((prep_kernel<D>), dim3(static_cast<unsigned>((p.rows_total + 3) / 4)), dim3(256), 0,
                      stream, p);
-  const dim3 tkg(static_cast<unsigned>(p.KR / kTT), static_cast<unsigned>(slabs));
-  hipLaunchKernelGGL((transpose_keys<D>), tkg, dim3(256), 0, stream, p);
   const int64_t entries = p.units * p.gmax;
   const unsigned eg = static_cast<unsigned>((entries + 255) / 256);
   hipLaunchKernelGGL(count_kernel, dim3(eg), dim3(256), 0, stream, p);
@@ -903,7 +805,6 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.dv = dv;
   p.delta = reinterpret_cast<float*>(w + L.delta);
   p.qr = reinterpret_cast<uint16_t*>(w + L.qr);
-  p.kt = reinterpret_cast<uint16_t*>(w + L.kt);
   p.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
   p.off = reinterpret_cast<int32_t*>(w + L.off);
   p.list = reinterpret_cast<int32_t*>(w + L.list);
@@ -916,7 +817,6 @@ hipError_t launch_backward(const Geometry& g, const void* q, const void* k_rot, 
   p.nqc = g.nqc;
   p.units = static_cast<int64_t>(g.B) * g.Hkv * g.nqc;
   p.rows_total = static_cast<int64_t>(g.B) * g.Hq * g.n_q;
-  p.KR = L.KR;
   p.n_tok = std::min<int64_t>(g.kv_cap, g.q_pos0 + g.n_q);
   p.B = g.B;
   p.Hq = g.Hq;

@@ -122,4 +122,59 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Stage tiles filled by direct global -> LDS loads are unpadded rows of
+// 2*D bytes whose 16-byte chunks are XOR-swizzled: chunk c of row r sits at
+// position c ^ rswz<D>(r), which spreads both a 16-row operand read (one
+// chunk per lane) and the fill over all banks.
+template <int D>
+__device__ __forceinline__ int rswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Direct global -> LDS loads of 16 or 4 bytes per lane: lane l's bytes land
+// at lds_wave + 16*l (4*l); lds_wave is the same in every lane of the wave.
+// The host pass only needs the declaration.
+__device__ __forceinline__ void load_lds16(const void* g, char* lds_wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds_wave, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void load_lds4(const void* g, char* lds_wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds_wave, 4, 0, 0);
+#endif
+}
+
+// Waits until at most K vector-memory operations of this wave are
+// outstanding and for its LDS operations, then meets the workgroup at a
+// barrier.  Unlike __syncthreads, whose fence waits for every load in
+// flight (direct LDS loads included), the loads of a later stage may stay
+// in flight.  The empty asm statements keep the compiler from moving memory
+// accesses across.
+template <int K>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(K >= 0 && K < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4));  // vmcnt(K) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Transposing LDS read of 16-bit elements (ds_read_b64_tr_b16): in each
+// group of 16 lanes, lane j passes the address of 4 consecutive elements
+// (8 bytes) of row j/4 at columns 4*(j%4) .. +3 of a 4 x 16 block, and lane
+// i receives column i of the block's 4 rows (row 0 in the low half of .x).
+__device__ __forceinline__ uint2 lds_read_tr16(const char* lds_addr) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_addr));
+#else
+  const v4s v = {0, 0, 0, 0};
+  (void)lds_addr;
+#endif
+  return make_uint2(static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16),
+                    static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16));
+}
+
 }  // namespace hga

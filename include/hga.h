@@ -284,8 +284,8 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
  * As in hga_attend, rows of k_rot and v from q_pos0 + n_q on may hold
  * anything; dk and dv are zero there.  Workspace:
  * hga_attend_backward_workspace_bytes (it depends on q_pos0 + n_q, not on
- * kv_cap) -- per query row D (f32) and Q' (bf16); transposed k~ (bf16);
- * granule lists; and two f32 partial rows of d per (unit, list key),
+ * kv_cap) -- per query row D (f32) and Q' (bf16); granule lists; and two
+ * f32 partial rows of d per (unit, list key),
  * units * gmax * g_s * d * 8 bytes, the largest piece (2.5 GB for 32768
  * queries, 32 query and 4 KV heads, d = 128, 76 granules per list).  Errors: HGA_ERR_UNSUPPORTED for
  * other dtypes or shapes, HGA_ERR_WORKSPACE when workspace_bytes is short;
