@@ -14,7 +14,9 @@
 //
 // Kernels (bf16 operands on 16x16x32 matrix cores, f32 accumulation):
 //  * prep_kernel: D_i for every row, and Q'_i = R_i q_i * s * log2(e) as bf16
-//    (the forward's query operand), row-major, into the workspace.
+//    (the forward's query operand), row-major, into the workspace; one
+//    workgroup per (sequence, query position), its RoPE table shared by the
+//    query heads.
 //  * dq_kernel: one workgroup per (unit, 128 rows), four waves of 32 rows,
 //    over the unit's keys 32 at a time: the workgroup stages K and V of the
 //    32 keys in LDS by direct global -> LDS loads; each wave forms
@@ -127,30 +129,41 @@ __device__ __forceinline__ int64_t row_index(const BwdParams& p, const BUnit& w,
   return (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0);
 }
 
-// D_i = dO_i . O_i and Q'_i (bf16), one wave per row; lane owns the pairs
+// D_i = dO_i . O_i and Q'_i (bf16) for every query head of one (sequence,
+// query position): the position's cos/sin table is formed once in LDS, then
+// each wave takes heads wave, wave + 4, ...; lane owns the pairs
 // (j, j + D/2) for j = lane, lane + 64, ...
 template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(BwdParams p) {
   constexpr int H = D / 2;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows_total) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t pos = p.q_pos0 + row % p.n_q;
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int64_t e = row * D + lane + 64 * i;
-    acc += load1<true>(p.dout, e) * load1<true>(p.out, e);
+  __shared__ float2 cs[H];
+  const int64_t bq = blockIdx.x;  // b * n_q + query index
+  const int64_t b = bq / p.n_q, qi = bq - b * p.n_q;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const double pos = static_cast<double>(rope_base(p.rope, p.q_pos0 + qi));
+  for (int j = threadIdx.x; j < H; j += 256) {
+    float c, sn;
+    rope_cs(pos, rope_freq(p.rope, j), c, sn);
+    cs[j] = make_float2(c, sn);
   }
+  __syncthreads();
+  for (int h = wave; h < p.Hq; h += 4) {
+    const int64_t row = (b * p.Hq + h) * p.n_q + qi;
+    float acc = 0.f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) p.delta[row] = acc;
-  for (int j = lane; j < H; j += 64) {
-    float c, s;
-    rope_cs(static_cast<double>(rope_base(p.rope, pos)), rope_freq(p.rope, j), c, s);
-    const float a = load1<true>(p.q, row * D + j), b = load1<true>(p.q, row * D + j + H);
-    p.qr[row * D + j] = f32_to_bf16((a * c - b * s) * p.scale_log2);
-    p.qr[row * D + j + H] = f32_to_bf16((a * s + b * c) * p.scale_log2);
+    for (int i = 0; i < D / 64; ++i) {
+      const int64_t e = row * D + lane + 64 * i;
+      acc += load1<true>(p.dout, e) * load1<true>(p.out, e);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) p.delta[row] = acc;
+    for (int j = lane; j < H; j += 64) {
+      const float2 t = cs[j];
+      const float a = load1<true>(p.q, row * D + j), c2 = load1<true>(p.q, row * D + j + H);
+      p.qr[row * D + j] = f32_to_bf16((a * t.x - c2 * t.y) * p.scale_log2);
+      p.qr[row * D + j + H] = f32_to_bf16((a * t.y + c2 * t.x) * p.scale_log2);
+    }
   }
 }
 
@@ -750,7 +763,7 @@ template <int D>
 hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream) {
   const int64_t slabs = static_cast<int64_t>(g.B) * g.Hkv;
   hipLaunchKernelGGL(zero_i32, dim3(256), dim3(256), 0, stream, p.cnt, slabs * p.ngran);
-  hipLaunchKernelGGL((prep_kernel<D>), dim3(static_cast<unsigned>((p.rows_total + 3) / 4)), dim3(256), 0,
+  hipLaunchKernelGGL((prep_kernel<D>), dim3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.n_q)), dim3(256), 0,
                      stream, p);
   const int64_t entries = p.units * p.gmax;
   const unsigned eg = static_cast<unsigned>((entries + 255) / 256);
@@ -780,7 +793,7 @@ bool backward_supported(const Geometry& g) {
   const bool gs_ok = (g.gs & (g.gs - 1)) == 0 && g.gs >= 4;
   return g.bf16 && (g.d == 64 || g.d == 128) && gs_ok && units * g.gmax < (int64_t{1} << 31) &&
          units8 * nkb < (int64_t{1} << 31) && units8 * nslice < (int64_t{1} << 31) &&
-         tblocks < (int64_t{1} << 31);
+         tblocks < (int64_t{1} << 31) && static_cast<int64_t>(g.B) * g.n_q < (int64_t{1} << 31);
 }
 
 size_t backward_workspace(const Geometry& g) { return bwd_layout(g).total; }
