@@ -34,8 +34,9 @@
 //    (unit, list key).
 //  * list kernels: for every (sequence, KV head) and granule, the (unit,
 //    list entry) pairs that hold it (counted, scanned and scattered).
-//  * reduce_kernel: per 16 tokens, the sum of their partial rows, turned by
-//    R^T for dk; tokens in no list get zeros.
+//  * reduce_kernel: per 16 tokens, the sum of their partial rows (each list
+//    split four ways inside the workgroup), turned by R^T for dk; tokens in
+//    no list get zeros.
 // P = exp2(S' - lse * log2(e)) with S' = Q' . k~, and dk~ = ln(2) sum_i dS_ij Q'_i.
 #include "hga_device.h"
 
@@ -664,21 +665,24 @@ __global__ __launch_bounds__(256) void scatter_kernel(BwdParams p) {
   p.list[x * p.nqc * p.gmax + p.off[x * (p.ngran + 1) + g] + pos] = static_cast<int32_t>(e);
 }
 
-// dk and dv of 16 tokens of one slab: thread (token tid / 16, pair columns
-// (tid % 16) * PW .. + PW - 1 and their partners + D/2) sums the partial rows
-// of its granule's list entries, then dk = R^T (sum).  Tokens in no list
-// get zeros.
+// dk and dv of 16 tokens of one slab, four quarters of 256 threads: thread
+// (quarter, token, pair columns ((tid % 256) % 16) * PW .. + PW - 1 and their
+// partners + D/2) sums every fourth partial row of its granule's list (a
+// sink granule's list holds every unit of the slab); the quarters meet in
+// LDS, then dk = R^T (sum).  Tokens in no list get zeros.
 template <int D>
-__global__ __launch_bounds__(256) void reduce_kernel(BwdParams p) {
+__global__ __launch_bounds__(1024) void reduce_kernel(BwdParams p) {
   constexpr int H = D / 2, PW = H / 16;
+  __shared__ float4 part[3][256][PW];  // quarters 1..3: (dk lo, dk hi, dv lo, dv hi) per column
   const int64_t slabs = static_cast<int64_t>(p.B) * p.Hkv;
   const int64_t x = blockIdx.x % slabs, tb = blockIdx.x / slabs;
-  const int64_t tok = tb * 16 + (threadIdx.x >> 4);
-  if (tok >= p.kv_cap) return;
-  const int col = (threadIdx.x & 15) * PW;
+  const int quarter = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int64_t tok = tb * 16 + (t >> 4);
+  const bool tok_ok = tok < p.kv_cap;
+  const int col = (t & 15) * PW;
   const int64_t g = tok >> p.lg_gs;
   int l0 = 0, l1 = 0;
-  if (g < p.ngran) {
+  if (tok_ok && g < p.ngran) {
     l0 = p.off[x * (p.ngran + 1) + g];
     l1 = p.off[x * (p.ngran + 1) + g + 1];
   }
@@ -699,15 +703,31 @@ __global__ __launch_bounds__(256) void reduce_kernel(BwdParams p) {
       vb_[j] += d.x; vb_[j + 1] += d.y;
     }
   };
-  int l = l0;
-  for (; l + 4 <= l1; l += 4) {
-    const int32_t e0 = lst[l], e1 = lst[l + 1], e2 = lst[l + 2], e3 = lst[l + 3];
+  int l = l0 + quarter;
+  for (; l + 12 < l1; l += 16) {
+    const int32_t e0 = lst[l], e1 = lst[l + 4], e2 = lst[l + 8], e3 = lst[l + 12];
     add_row(e0);
     add_row(e1);
     add_row(e2);
     add_row(e3);
   }
-  for (; l < l1; ++l) add_row(lst[l]);
+  for (; l < l1; l += 4) add_row(lst[l]);
+  if (quarter > 0) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) part[quarter - 1][t][j] = make_float4(ka[j], kb_[j], va[j], vb_[j]);
+  }
+  __syncthreads();
+  if (quarter > 0 || !tok_ok) return;
+#pragma unroll
+  for (int qq = 0; qq < 3; ++qq)
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const float4 v = part[qq][t][j];
+      ka[j] += v.x;
+      kb_[j] += v.y;
+      va[j] += v.z;
+      vb_[j] += v.w;
+    }
   const double pos = static_cast<double>(rope_base(p.rope, tok));
   float* dkr = p.dk + (x * p.kv_cap + tok) * D;
   float* dvr = p.dv + (x * p.kv_cap + tok) * D;
@@ -775,7 +795,7 @@ hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream
   hipLaunchKernelGGL((dkv_kernel<D, HGA_DKV_KT>), dim3(static_cast<unsigned>(units8 * p.nkb)),
                      dim3(kDkvThreads), 0, stream, p);
   const int64_t tblocks = (p.kv_cap + 15) / 16;
-  hipLaunchKernelGGL((reduce_kernel<D>), dim3(static_cast<unsigned>(slabs * tblocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((reduce_kernel<D>), dim3(static_cast<unsigned>(slabs * tblocks)), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 
