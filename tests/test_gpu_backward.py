@@ -107,3 +107,66 @@ def test_backward_deterministic_except_atomics():
     for i in (1, 2):
         a, b = outs[0][i], outs[1][i]
         assert torch.allclose(a, b, rtol=1e-5, atol=1e-6 * float(a.abs().max()))
+
+
+def test_backward_qwen3_32k_sampled():
+    """The full Qwen3-shaped prefill (n = 32768, the configuration bench.py
+    times): dq of sampled units, and dk, dv of the tokens of sampled granules
+    together with every unit that lists them (so their sums are complete),
+    against the oracle on the GPU's own granule lists.  Sink granules (listed
+    by every unit of the slab) are left out for the oracle's time."""
+    import torch
+    w = W.QWEN3_PREFILL
+    q, k, v = P.make_inputs_parallel(w)
+    print("[gpu] backward qwen3 32k: inputs ready", flush=True)
+    run = P.GpuRun(w, q, k, v)
+    dev = run.q.device
+    do = W.round_to_bf16(np.random.default_rng(41).standard_normal(q.shape).astype(np.float32))
+    d_out = torch.from_numpy(do).to(dev).to(torch.bfloat16)
+    dq = torch.empty(run.q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(run.k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(run.k.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(H.attend_backward_workspace_bytes(run.cfg, w.batch, w.q_pos0, w.n_q), 16),
+                     dtype=torch.uint8, device=dev)
+    H.attend_backward(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, run.ro["granules"], run.ro["granule_count"],
+                      run.out, run.lse, d_out, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    print("[gpu] backward qwen3 32k: gpu done", flush=True)
+    gr, gc = run.np("granules"), run.np("granule_count")
+    nqc = gr.shape[2]
+    sink = w.n_sink_chunks * (w.chunk_size // w.group_size)
+    rng = np.random.default_rng(42)
+    units, picks = set(), []
+    for (b, h) in [(0, 0), (0, 3)]:
+        holders = {}
+        for t in range(nqc):
+            for g in gr[b, h, t, : gc[b, h, t]].tolist():
+                holders.setdefault(g, []).append(t)
+        cand = sorted(g for g, ts in holders.items() if g >= sink and 2 <= len(ts) <= 16)
+        for g in rng.choice(cand, 3, replace=False).tolist():
+            picks.append((b, h, g))
+            units.update((b, h, t) for t in holders[g])
+    units.update([(0, 1, 7), (0, 2, 300)])
+    units = sorted(units)
+    p = R.params_from_workload(w)
+    rdq, rdk, rdv = R.attend_backward(q, w.q_pos0, w.n_q, k, v, gr, gc, do.astype(np.float64), p,
+                                      t0=0, units=units)
+    G = w.n_q_heads // w.n_kv_heads
+    C = w.chunk_size
+    gs = w.group_size
+    qsel = [(b, h * G + hl, t * C + i) for (b, h, t) in units for hl in range(G) for i in range(C)]
+    bi, hi, qi = (torch.tensor([s[j] for s in qsel], device=dev) for j in range(3))
+    got_q = dq[bi, hi, qi].cpu().numpy().astype(np.float64)
+    want_q = rdq[np.array([s[0] for s in qsel]), np.array([s[1] for s in qsel]), np.array([s[2] for s in qsel])]
+    tsel = [(b, h, g * gs + j) for (b, h, g) in picks for j in range(gs)]
+    tb, th, tt = (torch.tensor([s[j] for s in tsel], device=dev) for j in range(3))
+    ib, ih, it = (np.array([s[j] for s in tsel]) for j in range(3))
+    res = []
+    for name, got, want in (("dq", got_q, want_q),
+                            ("dk", dk[tb, th, tt].cpu().numpy().astype(np.float64), rdk[ib, ih, it]),
+                            ("dv", dv[tb, th, tt].cpu().numpy().astype(np.float64), rdv[ib, ih, it])):
+        err = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+        mx = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
+        res.append((name, round(float(err), 5), round(float(mx), 5)))
+        assert err <= REL_L2 and mx <= MAX_REL, (name, err, mx)
+    print(f"[gpu] backward qwen3 32k: {len(units)} units, {len(picks)} granules: {res}", flush=True)
