@@ -53,6 +53,11 @@ struct RouteParams {
   // offsets, and (group routing) nseg*Kc*r group keys, all 32-bit words
   uint32_t* ws;
   int64_t ws_stride;
+  // unsegmented calls with several row groups per unit: the summary tables
+  // split into bf16 hi / lo rows (split_kernel), [slab][row][hi d, lo d]
+  const uint16_t* csplit;
+  const uint16_t* gsplit;
+  int64_t csplit_rows, gsplit_rows;  // rows per (sequence, KV head) table
   int64_t q_pos0, n_q, t0, nqc, nchunk_cap, ngroup_cap;
   int B, Hq, Hkv, G, d, C, gs, r, F, L, Kc, Kg, gmax;
   int seg_chunks, nseg;
@@ -169,40 +174,30 @@ __device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, i
 
 // Summary rows staged in LDS, split into bf16 hi and lo halves, so that the
 // waves of a block that score the same rows for different query rows share
-// one load and one split.  Rows are padded by 16 bytes, which puts the 16
-// rows read by a quarter wave in distinct banks.
+// one load.  The split is made once per call into the workspace (split_kernel:
+// row = d hi values then d lo values), so a stage is a plain copy: direct
+// global -> LDS loads (a wave's lane l lands at 16*l of the wave's 1 KB
+// block) into unpadded rows of 2*d bytes with XOR-swizzled 16-byte chunks
+// (rswz), two stages in separate buffers so that the next stage's loads
+// overlap the current stage's products.
 constexpr int kStageRows = 64;
-constexpr int kStageStride = 4 * kMaxHalfDim + 16;  // bytes per staged row
 
-// Stages rows 0..kStageRows-1 given by row(i) (rows at or past n repeat row
-// n-1).  Block-wide.
-template <typename RowPtr>
-__device__ __forceinline__ void stage_rows(int n, int d, RowPtr row, char* shi, char* slo) {
-  const int segs = d / 8;
-  for (int i = threadIdx.x; i < kStageRows * segs; i += blockDim.x) {
-    const int r = i / segs, sg = i - r * segs;
-    float x[8];
-    load8<false>(row(r < n ? r : n - 1), sg * 8, x);
-    Pack8 h, l;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) split_bf16(x[k], h.h[k], l.h[k]);
-    *reinterpret_cast<uint4*>(shi + r * kStageStride + sg * 16) = h.q;
-    *reinterpret_cast<uint4*>(slo + r * kStageStride + sg * 16) = l.q;
-  }
-}
-
-// score16 for the 16 staged rows of tile `tile`.
+// Score tiles of one staged 64-row block: tile `tile` (16 rows), the max
+// over the wave's row blocks of q . row (split products hi.hi + hi.lo +
+// lo.hi).
 template <int KS, int NB>
 __device__ __forceinline__ float score16_staged(const char* shi, const char* slo, int tile,
                                                 const Pack8 (&ahi)[NB][KS],
                                                 const Pack8 (&alo)[NB][KS]) {
+  constexpr int D = 32 * KS;
   const int lane = threadIdx.x & 63;
-  const int off = (tile * 16 + (lane & 15)) * kStageStride + (lane >> 4) * 16;
+  const int row = tile * 16 + (lane & 15), sub = lane >> 4;
   Pack8 bhi[KS], blo[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    bhi[ks].q = *reinterpret_cast<const uint4*>(shi + off + ks * 64);
-    blo[ks].q = *reinterpret_cast<const uint4*>(slo + off + ks * 64);
+    const int off = row * (2 * D) + 16 * ((4 * ks + sub) ^ rswz<D>(row));
+    bhi[ks].q = *reinterpret_cast<const uint4*>(shi + off);
+    blo[ks].q = *reinterpret_cast<const uint4*>(slo + off);
   }
   float best = -INFINITY;
 #pragma unroll
@@ -221,27 +216,76 @@ __device__ __forceinline__ float score16_staged(const char* shi, const char* slo
   return best;
 }
 
-// Max-scores of n candidates (row(i) -> summary row) into keys[0..n), one
-// staged block of rows at a time; used when several row groups share tiles.
+// Max-scores of n candidates into keys[0..n) (atomic max: several row
+// groups share the tiles); row(i) is the split row of candidate i.  Stages
+// of 64 rows alternate between buffers (h0, l0) and (h1, l1); rows at or
+// past n repeat row n-1.  Block-wide.
 template <int KS, int NB, typename RowPtr>
-__device__ __forceinline__ void score_staged(int n, int d, RowPtr row, bool has_rows, int tg,
-                                             int TG, const Pack8 (&ahi)[NB][KS],
-                                             const Pack8 (&alo)[NB][KS], char* shi, char* slo,
-                                             uint32_t* keys) {
-  const int lane = threadIdx.x & 63;
-  for (int b0 = 0; b0 < n; b0 += kStageRows) {
-    const int nb = n - b0 < kStageRows ? n - b0 : kStageRows;
-    stage_rows(nb, d, [&](int i) { return row(b0 + i); }, shi, slo);
-    __syncthreads();
+__device__ __forceinline__ void score_staged(int n, RowPtr row, bool has_rows, int tg, int TG,
+                                             const Pack8 (&ahi)[NB][KS],
+                                             const Pack8 (&alo)[NB][KS], char* h0, char* l0,
+                                             char* h1, char* l1, uint32_t* keys) {
+  constexpr int D = 32 * KS;
+  constexpr int ROW = 2 * D;
+  constexpr int NBLK = kStageRows * ROW / 1024;  // 1 KB blocks per tile
+  static_assert(NBLK % kRouteWaves == 0, "stage blocks spread evenly over the waves");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nst = (n + kStageRows - 1) / kStageRows;
+  auto issue = [&](int s, char* hs, char* ls) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // addresses formed here, not hoisted into registers
+#pragma unroll
+    for (int j = 0; j < NBLK / kRouteWaves; ++j) {
+      const int blk = (wave + j * kRouteWaves) * 1024;
+      const int o = blk + 16 * ln;
+      const int m = o / ROW;
+      const int c = ((o % ROW) / 16) ^ rswz<D>(m);
+      int i = s * kStageRows + m;
+      i = i < n ? i : n - 1;
+      const char* src = reinterpret_cast<const char*>(row(i)) + 16 * c;
+      load_lds16(src, hs + blk);
+      load_lds16(src + ROW, ls + blk);
+    }
+  };
+  auto step = [&](int s, const char* hs, const char* ls, char* hn, char* ln_) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nst) issue(s + 1, hn, ln_);
     if (has_rows) {
+      const int nb = n - s * kStageRows < kStageRows ? n - s * kStageRows : kStageRows;
       for (int tile = tg; tile * 16 < nb; tile += TG) {
-        const float v = score16_staged<KS, NB>(shi, slo, tile, ahi, alo);
-        const int c = b0 + tile * 16 + (lane & 15);
+        const float v = score16_staged<KS, NB>(hs, ls, tile, ahi, alo);
+        const int c = s * kStageRows + tile * 16 + (lane & 15);
         if (lane < 16 && c < n) atomicMax(&keys[c], order_key(v));
       }
     }
-    __syncthreads();
+    wait_vm_barrier<0>();
+  };
+  if (nst > 0) issue(0, h0, l0);
+  wait_vm_barrier<0>();
+  for (int s = 0; s < nst; s += 2) {
+    step(s, h0, l0, h1, l1);
+    if (s + 1 >= nst) break;
+    step(s + 1, h1, l1, h0, l0);
   }
+}
+
+// Summary rows (f32) -> split rows (d bf16 hi values, then d lo values), for
+// the first `rows` rows of every (sequence, KV head) table of cap rows, into
+// tables of `rows` rows; one thread per 8 values.
+__global__ __launch_bounds__(256) void split_kernel(const float* src, uint16_t* dst, int64_t cap, int64_t rows,
+                                                    int64_t slabs, int d) {
+  const int64_t segs = d / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= slabs * rows * segs) return;
+  const int64_t sg = i % segs, r = (i / segs) % rows, x = i / (segs * rows);
+  float v[8];
+  load8<false>(src + (x * cap + r) * d, sg * 8, v);
+  Pack8 h, l;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) split_bf16(v[k], h.h[k], l.h[k]);
+  uint16_t* o = dst + (x * rows + r) * 2 * d;
+  *reinterpret_cast<uint4*>(o + sg * 8) = h.q;
+  *reinterpret_cast<uint4*>(o + d + sg * 8) = l.q;
 }
 
 constexpr int kRankMax = 512;  // rank_select: at most one candidate per thread
@@ -752,8 +796,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
-  __shared__ __align__(16) char shi[kStageRows * kStageStride];
-  __shared__ __align__(16) char slo[kStageRows * kStageStride];
+  // staged split rows, two stages (the stage buffers are separate arrays so
+  // that the compiler sees that reading one need not wait for loads into
+  // the other)
+  __shared__ __align__(1024) char sh0[kStageRows * 4 * kMaxHalfDim];
+  __shared__ __align__(1024) char sl0[kStageRows * 4 * kMaxHalfDim];
+  __shared__ __align__(1024) char sh1[kStageRows * 4 * kMaxHalfDim];
+  __shared__ __align__(1024) char sl1[kStageRows * 4 * kMaxHalfDim];
 
   const Unit w = make_unit(p, blockIdx.x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -780,9 +829,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
       __syncthreads();
       const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
       if (RG > 1) {
-        const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
-        score_staged<KS, NB>(n_mid, p.d, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
-                             has_rows, tg, TG, ahi, alo, shi, slo, keys);
+        const int64_t slab = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
+        const uint16_t* c0 = p.csplit + (slab * p.csplit_rows + w.mid_lo) * 2 * p.d;
+        score_staged<KS, NB>(n_mid, [&](int c) { return c0 + static_cast<int64_t>(c) * 2 * p.d; },
+                             has_rows, tg, TG, ahi, alo, sh0, sl0, sh1, sl1, keys);
       } else if (has_rows) {
         const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
         score_stream<KS, NB>(n_mid, tg, TG, [&](int c) { return c0 + static_cast<int64_t>(c) * p.d; },
@@ -810,7 +860,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
       return g0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * p.d;
     };
     if (RG > 1) {
-      score_staged<KS, NB>(nc, p.d, grow, has_rows, tg, TG, ahi, alo, shi, slo, keys);
+      const uint16_t* gs0 = p.gsplit + (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.gsplit_rows * 2 * p.d;
+      score_staged<KS, NB>(nc, [&](int c) {
+                             const int cr = c / p.r;
+                             return gs0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * 2 * p.d;
+                           },
+                           has_rows, tg, TG, ahi, alo, sh0, sl0, sh1, sl1, keys);
     } else if (has_rows) {
       score_stream<KS, NB>(nc, tg, TG, grow, ahi, alo, [&](int tile, float v) {
         const int c = tile * 16 + (lane & 15);
@@ -898,6 +953,25 @@ SegPlan seg_plan(const Geometry& g) {
   return sp;
 }
 
+// Unsegmented calls whose units have more rows than one wave holds score
+// staged split rows (split_kernel); the split tables live in the workspace:
+// [slab][chunk][2d] then [slab][group][2d] bf16.
+bool use_split(const Geometry& g) {
+  const int64_t rows = (g.C < g.n_q ? g.C : g.n_q) * static_cast<int64_t>(g.G);
+  return !use_segmented(g) && g.Kc > 0 && rows > kRowsPerWave;
+}
+// Rows split: chunks [0, t_last] (a unit reads middle chunks before its own)
+// and their groups; independent of kv_cap (the sizing call has none).
+int64_t split_chunks(const Geometry& g) { return g.t0 + g.nqc; }
+size_t split_bytes(const Geometry& g, size_t& gsplit_off) {
+  const size_t slabs = static_cast<size_t>(g.B) * g.Hkv;
+  const size_t row = static_cast<size_t>(g.d) * 2 * 2;
+  const size_t rc = static_cast<size_t>(split_chunks(g));
+  const size_t c = slabs * rc * row;
+  gsplit_off = (c + 255) / 256 * 256;
+  return gsplit_off + (g.Kg > 0 ? slabs * rc * static_cast<size_t>(g.r) * row : 0);
+}
+
 }  // namespace
 
 bool route_supported(const Geometry& g) {
@@ -906,7 +980,12 @@ bool route_supported(const Geometry& g) {
          static_cast<int64_t>(g.Kc) * g.r <= kMaxCand;
 }
 
+
 size_t route_workspace(const Geometry& g) {
+  if (use_split(g)) {
+    size_t goff = 0;
+    return split_bytes(g, goff);
+  }
   if (!use_segmented(g) || g.Kc <= 0) return 0;
   const SegPlan sp = seg_plan(g);
   return static_cast<size_t>(g.B) * g.Hkv * g.nqc * static_cast<size_t>(sp.nseg) * g.Kc *
@@ -952,6 +1031,33 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   p.seg_chunks = sp.seg_chunks;
   p.nseg = sp.nseg;
   p.ws_stride = static_cast<int64_t>(sp.nseg) * g.Kc * (2 + (g.Kg > 0 ? g.r : 0));
+  p.csplit = nullptr;
+  p.gsplit = nullptr;
+  p.csplit_rows = p.gsplit_rows = 0;
+  if (use_split(g)) {
+    // split the summary rows the call can read: chunks before the last
+    // query chunk and their groups
+    size_t goff = 0;
+    split_bytes(g, goff);
+    uint16_t* cs = static_cast<uint16_t*>(ws);
+    uint16_t* gsp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + goff);
+    const int64_t slabs = static_cast<int64_t>(g.B) * g.Hkv;
+    const int64_t rc = split_chunks(g);  // <= nchunk_cap (q_pos0 + n_q <= kv_cap)
+    const int64_t n8 = slabs * rc * (g.d / 8);
+    hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, stream,
+                       chunk_sum, cs, p.nchunk_cap, rc, slabs, g.d);
+    p.csplit_rows = rc;
+    p.gsplit_rows = rc * g.r;
+    if (g.Kg > 0) {
+      const int64_t g8 = slabs * rc * g.r * (g.d / 8);
+      hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>((g8 + 255) / 256)), dim3(256), 0, stream,
+                         group_sum, gsp, p.ngroup_cap, rc * g.r, slabs, g.d);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.csplit = cs;
+    p.gsplit = gsp;
+  }
   if (g.bf16) {
     return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)
                       : launch_route_t<true, 2>(p, units, seg, stream);

@@ -125,7 +125,11 @@ hga_status hga_build_summaries(const hga_config* cfg, hga_dtype dtype, int32_t b
  * (C/g_s)(1 + F + max(L,1)) + (K_g if K_g > 0 else K_c C/g_s).  -1 on a bad config. */
 int32_t hga_max_granules(const hga_config* cfg);
 
-/* Workspace bytes hga_route needs for this call shape (may be 0). */
+/* Workspace bytes hga_route needs for this call shape (may be 0): the
+ * segment winners of decode-shaped calls, or, for calls whose units have
+ * more than 64 (query, head) rows, the summary rows the call can read split
+ * into bf16 hi / lo halves (chunks up to the last query chunk and their
+ * groups, 4 * d bytes per row). */
 size_t hga_route_workspace_bytes(const hga_config* cfg, int32_t batch,
                                  int64_t q_pos0, int64_t n_q);
 

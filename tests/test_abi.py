@@ -191,7 +191,8 @@ def test_workspace_checks(lib):
     assert H.route_workspace_bytes(H.Config.from_workload(W.DECODE_64K, top_chunks=0), 16, 65536, 1) == 0
     # many query chunks: one routing workgroup per unit
     big = H.Config.from_workload(W.QWEN3_PREFILL)
-    assert H.route_workspace_bytes(big, 1, 0, 32768) == 0
+    # prefill: the summary tables split into bf16 hi / lo rows for the staged scoring
+    assert H.route_workspace_bytes(big, 1, 0, 32768) == 4 * (512 + 512 * 4) * 128 * 2 * 2
 
 
 def test_host_tier_sizes_and_checks(lib):
