@@ -466,12 +466,8 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   const int nqt = (rend - 1) / p.G - q_first + 1;
   float2* cs = reinterpret_cast<float2*>(smem);
   const int64_t q0 = rope_base(p.rope, w.qlo) + q_first;  // the unit's queries share one chunk
-  for (int i = threadIdx.x; i < nqt * H; i += NW * 64) {
-    const int qi = i / H, pr = i - qi * H;
-    float c, s;
-    rope_cs(static_cast<double>(q0 + qi), rope_freq(p.rope, pr), c, s);
-    cs[i] = make_float2(c, s);
-  }
+  static_assert(80 * H * 8 <= kMain, "RoPE table and its scratch fit the stage space");
+  rope_table(p.rope, q0, nqt, H, cs, reinterpret_cast<float2*>(smem + 64 * H * 8));
   __syncthreads();
 
   // K and V buffer resources: the (sequence, KV head) slab, or the staging

@@ -96,6 +96,32 @@ __device__ __forceinline__ double rope_freq(const RopeFreqs& r, int i) {
   return f;
 }
 
+// cos/sin of (p0 + i) * theta_j into cs[i * h + j] for i < n, j < h.  Block-
+// wide (every thread of the block calls it); the caller waits on a barrier
+// before reading cs.  The angles at the coarse positions p0 + 8a and at the
+// offsets b < 8 are evaluated as rope_cs does, and each entry is their
+// product (angle addition in f32, about 2 ulp beyond rope_cs): a quarter of
+// the evaluations of one rope_cs per entry.  scratch holds
+// (ceil(n / 8) + 8) * h float2 and is free for the call.
+__device__ __forceinline__ void rope_table(const RopeFreqs& r, int64_t p0, int n, int h, float2* cs,
+                                           float2* scratch) {
+  const int na = (n + 7) >> 3;
+  for (int i = threadIdx.x; i < (na + 8) * h; i += blockDim.x) {
+    const int a = i / h, j = i - a * h;
+    const int64_t pos = a < na ? p0 + 8 * a : a - na;
+    float c, s;
+    rope_cs(static_cast<double>(pos), rope_freq(r, j), c, s);
+    scratch[i] = make_float2(c, s);
+  }
+  __syncthreads();
+  const float2* fine = scratch + na * h;
+  for (int i = threadIdx.x; i < n * h; i += blockDim.x) {
+    const int q = i / h, j = i - q * h;
+    const float2 x = scratch[(q >> 3) * h + j], y = fine[(q & 7) * h + j];
+    cs[i] = make_float2(x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x);
+  }
+}
+
 // Rotation position of the token at absolute position p: p mod period when
 // positions wrap.  Periods are multiples of C, so a caller wraps the first
 // position of a chunk or group once and adds in-block offsets to it.

@@ -100,16 +100,12 @@ __device__ __forceinline__ Unit make_unit(const RouteParams& p, int64_t u) {
   return w;
 }
 
-// cos/sin of every (query of the unit, pair) into LDS.
-__device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit& w, float2* cs) {
-  const int h = p.d >> 1;
-  const int64_t q0 = rope_base(p.rope, w.qlo);  // a unit's queries share one chunk
-  for (int i = threadIdx.x; i < w.nq * h; i += blockDim.x) {
-    const int qi = i / h, pr = i - qi * h;
-    float c, s;
-    rope_cs(static_cast<double>(q0 + qi), rope_freq(p.rope, pr), c, s);
-    cs[i] = make_float2(c, s);
-  }
+// cos/sin of every (query of the unit, pair) into LDS (block-wide; scratch:
+// 16 * d/2 float2, free for the call).
+__device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit& w, float2* cs,
+                                                float2* scratch) {
+  // a unit's queries share one chunk, so one wrap of its first position
+  rope_table(p.rope, rope_base(p.rope, w.qlo), w.nq, p.d >> 1, cs, scratch);
 }
 
 // The wave's NB row blocks of 16 rotated query rows as split-bf16 A operands
@@ -631,7 +627,7 @@ __device__ __forceinline__ void score_stream(int n, int tile0, int step, RowPtr 
 template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
-  __shared__ uint32_t keys[kMaxCand];
+  __shared__ __align__(16) uint32_t keys[kMaxCand];  // also the RoPE table scratch
   __shared__ int sel[kMaxSel];
   __shared__ SelScratch scr;
   if (p.Kc <= 0) return;  // uniform: the merge does not route either
@@ -664,14 +660,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) load_row_raw<BF16, KS>(p, w, row_of_lane(w, 0, blk), xq[blk]);
       score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit, [&] {
-        fill_rope_table(p, w, cs);
+        fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
         __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
           rotate_split<KS>(p, row_of_lane(w, 0, blk), cs, xq[blk], ahi[blk], alo[blk]);
       });
     } else {
-      fill_rope_table(p, w, cs);
+      fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
       __syncthreads();
       load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
       score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit);
@@ -792,7 +788,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(RouteParams p) {
 template <bool BF16, int KS, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ float2 cs[kMaxTableQ * kMaxHalfDim];
-  __shared__ uint32_t keys[kMaxCand];
+  __shared__ __align__(16) uint32_t keys[kMaxCand];  // also the RoPE table scratch
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
@@ -822,7 +818,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   int nselc = 0;
   if (route) {
     {
-      fill_rope_table(p, w, cs);
+      fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
       __syncthreads();
       if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
       for (int i = threadIdx.x; i < n_mid; i += blockDim.x) keys[i] = 0u;
