@@ -1,0 +1,40 @@
+"""Seeded random shapes for parity sweeps: chunk and group sizes, sink and
+recent windows, chunk and group budgets, GQA ratio, head size, dtype,
+ragged query starts and RoPE wraps drawn inside the documented limits
+(g_s | C <= 64, C * G <= 512 query rows per unit, d in {64, 128}), at sizes
+the oracle handles in seconds.  Shared by the CPU check that every drawn
+shape is accepted by the library's sizing calls and by the GPU parity sweep.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import workloads as W
+
+N_CONFIGS = 40
+
+
+def random_workload(i: int) -> W.Workload:
+    rng = np.random.default_rng(7100 + i)
+    d = int(rng.choice([64, 128]))
+    C = int(rng.choice([16, 32, 64]))
+    gs = int(rng.choice([g for g in (2, 4, 8, 16, 32) if g <= C]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8) if C * g <= 512]))
+    hkv = int(rng.choice([1, 2]))
+    r = C // gs
+    kc = int(rng.integers(0, 7))
+    # K_g: whole chunks (0), fewer groups than the chosen chunks hold, or more
+    kg = int(rng.choice([0, max(1, kc * r // 2), kc * r + 3])) if kc > 0 else 0
+    n_ctx = int(rng.integers(150, 1200))
+    extra = int(rng.choice([0, C]))
+    kv_cap = (n_ctx + C - 1) // C * C + extra
+    q_pos0 = int(rng.choice([0, int(rng.integers(1, n_ctx - 1))]))
+    period = int(rng.choice([0, C * int(rng.integers(2, 9))]))
+    return W.Workload(
+        name=f"random_{i}", batch=int(rng.integers(1, 3)), n_q_heads=hkv * G, n_kv_heads=hkv,
+        head_dim=d, n_ctx=n_ctx, kv_cap=kv_cap, q_pos0=q_pos0, n_q=n_ctx - q_pos0,
+        dtype=str(rng.choice(["bf16", "bf16", "f32"])), rope_theta=float(rng.choice([1e4, 1e6])),
+        chunk_size=C, group_size=gs, n_sink_chunks=int(rng.integers(0, 4)),
+        n_recent_chunks=int(rng.integers(0, 4)), top_chunks=kc, top_groups=kg,
+        n_hf_pairs=int(rng.integers(0, d // 2 + 1)), planted=0, seed_offset=40 + i,
+        rope_period=period)
