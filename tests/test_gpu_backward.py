@@ -15,6 +15,7 @@ import hierarchical_kv_routing_amd as H
 import workloads as W
 from oracle import hga_ref as R
 from tests import parity as P
+from tests.random_configs import N_CONFIGS, random_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -54,11 +55,10 @@ def _unseen_keys(w, gr, gc):
     return ~seen[..., None].repeat(w.head_dim, axis=-1)
 
 
-@pytest.mark.parametrize("case", sorted(CASES))
-def test_backward_matches_oracle(case):
+def _check_backward(case, w, seed=0):
+    """GPU backward on the GPU's own routes vs the oracle, whole tensors."""
     import torch
-    w = CASES[case]
-    q, k, v = P.make_inputs_parallel(w)
+    q, k, v = P.make_inputs_parallel(w, seed)
     print(f"[gpu] backward {case}: {w}", flush=True)
     run = P.GpuRun(w, q, k, v)
     dev = run.q.device
@@ -80,6 +80,23 @@ def test_backward_matches_oracle(case):
     unseen = _unseen_keys(w, gr, gc)
     res = [_compare("dq", dq, rdq), _compare("dk", dk, rdk, unseen), _compare("dv", dv, rdv, unseen)]
     print(f"[gpu] backward {case}: (rel_l2, max/max) dq {res[0]}, dk {res[1]}, dv {res[2]}", flush=True)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_matches_oracle(case):
+    _check_backward(case, CASES[case])
+
+
+# The random parity shapes the backward supports (bf16, g_s a power of two
+# of at least 4): chunk / group sizes, windows, budgets, GQA ratio, d,
+# ragged starts and RoPE wraps beyond the named cases.
+RANDOM = [i for i in range(N_CONFIGS)
+          if random_workload(i).dtype == "bf16" and random_workload(i).group_size >= 4]
+
+
+@pytest.mark.parametrize("i", RANDOM)
+def test_backward_random_shapes(i):
+    _check_backward(f"random {i}", random_workload(i), seed=i)
 
 
 def test_backward_deterministic_except_atomics():
