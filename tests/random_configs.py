@@ -38,3 +38,31 @@ def random_workload(i: int) -> W.Workload:
         n_recent_chunks=int(rng.integers(0, 4)), top_chunks=kc, top_groups=kg,
         n_hf_pairs=int(rng.integers(0, d // 2 + 1)), planted=0, seed_offset=40 + i,
         rope_period=period)
+
+
+N_DECODE = 12
+
+
+def random_decode_workload(i: int) -> W.Workload:
+    """One query per sequence at the end of a long context (up to a few
+    hundred middle chunks, so that some draws take the segmented scoring and
+    all of them the split-key decode attention)."""
+    rng = np.random.default_rng(9300 + i)
+    d = int(rng.choice([64, 128]))
+    C = int(rng.choice([16, 32, 64]))
+    gs = int(rng.choice([g for g in (2, 4, 8, 16, 32) if g <= C]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    r = C // gs
+    kc = int(rng.integers(1, 9))
+    kg = int(rng.choice([0, max(1, kc * r // 2), kc * r + 2]))
+    n_ctx = int(rng.integers(100, 420)) * C + int(rng.integers(1, C + 1))
+    kv_cap = (n_ctx + C - 1) // C * C + int(rng.choice([0, C]))
+    period = int(rng.choice([0, C * int(rng.integers(8, 64))]))
+    return W.Workload(
+        name=f"random_decode_{i}", batch=int(rng.integers(1, 5)), n_q_heads=hkv * G,
+        n_kv_heads=hkv, head_dim=d, n_ctx=n_ctx, kv_cap=kv_cap, q_pos0=n_ctx - 1, n_q=1,
+        dtype="bf16", rope_theta=float(rng.choice([1e4, 1e7])), chunk_size=C, group_size=gs,
+        n_sink_chunks=int(rng.integers(0, 4)), n_recent_chunks=int(rng.integers(0, 9)),
+        top_chunks=kc, top_groups=kg, n_hf_pairs=int(rng.integers(0, d // 2 + 1)), planted=0,
+        seed_offset=90 + i, rope_period=period)

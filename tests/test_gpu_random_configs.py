@@ -7,13 +7,13 @@ import pytest
 
 import hierarchical_kv_routing_amd as H
 from tests import parity as P
-from tests.random_configs import N_CONFIGS, random_workload
+from tests.random_configs import N_CONFIGS, N_DECODE, random_decode_workload, random_workload
 
 
-@pytest.mark.parametrize("i", range(N_CONFIGS))
+@pytest.mark.parametrize("i", range(N_CONFIGS + N_DECODE))
 def test_random_shape_accepted(i):
     """Every drawn shape is inside the library's limits (CPU: sizing calls only)."""
-    w = random_workload(i)
+    w = random_workload(i) if i < N_CONFIGS else random_decode_workload(i - N_CONFIGS)
     cfg = H.Config.from_workload(w)
     assert 0 < H.max_granules(cfg) <= 2048
     assert H.route_workspace_bytes(cfg, w.batch, w.q_pos0, w.n_q) >= 0
@@ -33,4 +33,20 @@ def test_random_shape_parity(i):
     exact, near = P.compare_routes(run, orc, units)
     assert exact + near == len(units)
     assert near <= max(2, len(units) // 50)
+    P.check_attention(run, q, k, v, units)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_DECODE))
+def test_random_decode_parity(i):
+    w = random_decode_workload(i)
+    print(f"[gpu] random decode {i}: {w}", flush=True)
+    q, k, v = P.make_inputs_parallel(w, seed=i)
+    run = P.GpuRun(w, q, k, v)
+    P.check_summaries(run, k, slabs=[(w.batch - 1, w.n_kv_heads - 1)])
+    units = P.all_units(w)
+    orc = P.oracle_route(run, q, k, units)
+    exact, near = P.compare_routes(run, orc, units)
+    assert exact + near == len(units)
+    assert near <= max(1, len(units) // 20)
     P.check_attention(run, q, k, v, units)
