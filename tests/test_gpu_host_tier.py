@@ -7,6 +7,7 @@ import pytest
 import hierarchical_kv_routing_amd as H
 import workloads as W
 from tests import parity as P
+from tests.random_configs import N_CONFIGS, random_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +107,31 @@ def test_host_tier_rejects_pageable_memory():
     # the failed pointer query left no error behind for the next launch
     run.attend()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("i", range(0, N_CONFIGS, 2))
+def test_host_tier_random_shapes(i):
+    """The random parity shapes through the host tier: cold, with random
+    window sizes and slot counts, against the oracle; with a warm tier and
+    other window and slot sizes, equal to the cold run bit for bit (each
+    unit's attention does not depend on its window or on where its granules
+    sit in the pool).  The device path is not the reference here: for
+    few-unit calls it splits each unit's keys over workgroups, or takes the
+    decode kernel for units of at most 16 rows, which the host tier does not,
+    so the two agree only to rounding on such shapes."""
+    import torch
+    w = random_workload(i)
+    rng = np.random.default_rng(500 + i)
+    q, k, v = P.make_inputs_parallel(w, seed=i)
+    run = P.GpuRun(w, q, k, v)
+    need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
+    draws = [(need + int(rng.integers(0, 2 * need + 1)), int(rng.integers(1, 9))) for _ in range(2)]
+    cache = need + int(rng.integers(0, need + 1))
+    print(f"[gpu] host tier random {i}: {w} (slots, window) {draws} cache {cache}", flush=True)
+    out, lse, cold = run_host_tier(run, max_window_chunks=draws[0][1], slots=draws[0][0],
+                                   threads=int(rng.integers(0, 4)))
+    P.check_attention(run, q, k, v, P.all_units(w), out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+    out2, lse2, warm = run_host_tier(run, max_window_chunks=draws[1][1], slots=draws[1][0],
+                                     cache_slots=cache, threads=int(rng.integers(0, 4)))
+    same = (bool(torch.equal(out2, out)), bool(torch.equal(lse2, lse)))
+    assert all(same), (same, cold, warm)
