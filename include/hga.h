@@ -213,8 +213,13 @@ hga_status hga_dense_causal(const hga_config* cfg, hga_dtype dtype, int32_t batc
  * call dtype, K block then V block of each granule (g_s * d elements each).
  *
  * hga_attend_host_tiered computes the same outputs as hga_route followed by
- * hga_attend on device-resident K/V (bitwise: the same granules in the same
- * order), for queries [q_pos0, q_pos0 + n_q):
+ * hga_attend on device-resident K/V, for queries [q_pos0, q_pos0 + n_q):
+ * the same granules in the same order, and bitwise the same values whenever
+ * hga_attend plans one work item per unit row slice with units of more than
+ * 16 rows; for few-unit calls hga_attend instead splits each unit's keys
+ * over workgroups or takes its decode kernel (units of at most 16 rows),
+ * which sum in another order and agree to rounding.  The outputs do not
+ * depend on max_window_chunks, slots_per_window or cache_slots (bitwise).
  *   1. routes every unit on compute_stream (chunk_sum / group_sum in HBM);
  *   2. copies the granule lists to the host (the call blocks for this);
  *   3. walks windows of at most max_window_chunks query chunks whose union
