@@ -110,6 +110,11 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise HGAError(f"{LIB_PATH} is not built; run: python -m hierarchical_kv_routing_amd.build")
+    # torch first: its HIP runtime carries the soname the library links
+    # against, so the library binds to it.  Loaded the other way round, the
+    # process would hold two HIP runtimes, and the library's would find no
+    # device once torch's owns it.
+    import torch  # noqa: F401
     try:
         l = ctypes.CDLL(LIB_PATH)
     except OSError as e:

@@ -66,3 +66,36 @@ def random_decode_workload(i: int) -> W.Workload:
         n_sink_chunks=int(rng.integers(0, 4)), n_recent_chunks=int(rng.integers(0, 9)),
         top_chunks=kc, top_groups=kg, n_hf_pairs=int(rng.integers(0, d // 2 + 1)), planted=0,
         seed_offset=90 + i, rope_period=period)
+
+
+N_STREAM = 8
+
+
+def random_stream_workload(i: int):
+    """(workload, cache_slots) of a streaming decode session: one query per
+    step for n_q steps after a prefix of q_pos0 tokens (bf16, at most 16
+    rows per unit); the cache is the smallest allowed or a roomy one."""
+    import hierarchical_kv_routing_amd as H
+    rng = np.random.default_rng(11500 + i)
+    d = int(rng.choice([64, 128]))
+    C = int(rng.choice([16, 32, 64]))
+    gs = int(rng.choice([g for g in (2, 4, 8, 16, 32) if g <= C]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2]))
+    r = C // gs
+    kc = int(rng.integers(1, 7))
+    kg = int(rng.choice([0, max(1, kc * r // 2), kc * r + 2]))
+    prefix = int(rng.integers(20, 120)) * C  # sessions start at a chunk boundary
+    steps = int(rng.integers(C // 2, 2 * C + 8))
+    kv_cap = (prefix + steps + C - 1) // C * C + int(rng.choice([0, C]))
+    period = int(rng.choice([0, C * int(rng.integers(4, 32))]))
+    w = W.Workload(
+        name=f"random_stream_{i}", batch=int(rng.integers(1, 3)), n_q_heads=hkv * G,
+        n_kv_heads=hkv, head_dim=d, n_ctx=prefix + steps, kv_cap=kv_cap, q_pos0=prefix, n_q=steps,
+        dtype="bf16", rope_theta=float(rng.choice([1e4, 1e7])), chunk_size=C, group_size=gs,
+        n_sink_chunks=int(rng.integers(0, 3)), n_recent_chunks=int(rng.integers(0, 4)),
+        top_chunks=kc, top_groups=kg, n_hf_pairs=int(rng.integers(0, d // 2 + 1)), planted=0,
+        seed_offset=130 + i, rope_period=period)
+    need = w.batch * w.n_kv_heads * H.max_granules(H.Config.from_workload(w))
+    cache = need if rng.integers(0, 2) == 0 else 3 * need
+    return w, cache

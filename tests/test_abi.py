@@ -225,3 +225,21 @@ def test_host_tier_sizes_and_checks(lib):
                                       256, 0, 64, 16384, 0, 4, None, None, ctypes.byref(stats)) == 1
     assert lib.hga_attend_host_tiered(c, 1, 1, 16, 0, 131072, 16, 131072, 16, 16, 16, None, 256, 0,
                                       256, 0, 64, 16384, 0, -1, None, None, ctypes.byref(stats)) == 1
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before torch must not leave two HIP runtimes in the
+    process (the library's would then find no device): the binding imports
+    torch first, so the library binds to the runtime torch carries."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import hierarchical_kv_routing_amd as H\n"
+        "H.lib()\n"
+        "import torch\n"
+        "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n"
+    ) % (ROOT,)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

@@ -8,6 +8,7 @@ import pytest
 import hierarchical_kv_routing_amd as H
 import workloads as W
 from tests import parity as P
+from tests.random_configs import N_STREAM, random_stream_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +33,7 @@ def _reference(run, w, dev):
         pos = w.q_pos0 + s
         q = run.q[:, :, s:s + 1].contiguous()
         ro = H.route_outputs(cfg, w.batch, pos, 1, dev)
-        H.route(cfg, q, pos, run.csum, run.gsum, CAP, ro["chunk_idx"], ro["group_idx"],
+        H.route(cfg, q, pos, run.csum, run.gsum, w.kv_cap, ro["chunk_idx"], ro["group_idx"],
                 ro["granules"], ro["granule_count"], ro["workspace"])
         aw = H.attend_workspace_bytes(cfg, w.batch, pos, 1)
         ws = torch.empty(max(aw, 16), dtype=torch.uint8, device=dev)
@@ -49,16 +50,17 @@ def _session_run(run, w, cache_slots, dev, poison=False):
     import torch
     cfg = run.cfg
     # store and summary tables hold only the prefix; the session appends the rest
+    prefix = w.q_pos0
     k_rot = run.k_rot.clone()
     v = run.v.clone()
-    k_rot[:, :, PREFIX:] = 0
-    v[:, :, PREFIX:] = 0
+    k_rot[:, :, prefix:] = 0
+    v[:, :, prefix:] = 0
     store = H.host_store(cfg, k_rot, v)
     csum = run.csum.clone()
     gsum = run.gsum.clone()
-    csum[:, :, PREFIX // cfg.chunk_size:] = 0
-    gsum[:, :, PREFIX // cfg.group_size:] = 0
-    sess = H.DecodeSession(cfg, w.batch, CAP, PREFIX, cache_slots, store, device=dev)
+    csum[:, :, prefix // cfg.chunk_size:] = 0
+    gsum[:, :, prefix // cfg.group_size:] = 0
+    sess = H.DecodeSession(cfg, w.batch, w.kv_cap, prefix, cache_slots, store, device=dev)
     if poison:
         # the session may not rely on its device buffer's contents: all bits
         # set reads as NaN in every float format
@@ -79,18 +81,15 @@ def _session_run(run, w, cache_slots, dev, poison=False):
     return outs, lses, stats, csum, gsum, store
 
 
-@pytest.mark.parametrize("cache", ["roomy", "smallest", "smallest_poisoned"])
-def test_stream_decode_equals_device_path(cache):
+def _check_session(w, cache_slots, poison=False, seed=0):
+    """Session outputs vs the device path at every step, then its summaries
+    and host store vs a prefill build; returns the per-step stats."""
     import torch
-    w = _workload()
     dev = torch.device("cuda:0")
-    q, k, v = P.make_inputs_parallel(w)
-    print(f"[gpu] stream decode ({cache}): {w}", flush=True)
+    q, k, v = P.make_inputs_parallel(w, seed)
     run = P.GpuRun(w, q, k, v, route=False, attend=False)
     ref_out, ref_lse = _reference(run, w, dev)
-    need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
-    slots = 4 * need if cache == "roomy" else need
-    outs, lses, stats, csum, gsum, store = _session_run(run, w, slots, dev, poison=cache.endswith("poisoned"))
+    outs, lses, stats, csum, gsum, store = _session_run(run, w, cache_slots, dev, poison=poison)
     bad = [s for s in range(w.n_q)
            if not (torch.equal(outs[s], ref_out[s]) and torch.equal(lses[s], ref_lse[s]))]
     detail = []
@@ -102,20 +101,31 @@ def test_stream_decode_equals_device_path(cache):
                       f"nan {int(torch.isnan(outs[s]).sum())} rows {rows[:8]} "
                       f"copied {stats[s]['granules_copied']} hits {stats[s]['granules_hit']}")
     assert not bad, f"steps differing from the device path: {bad[:10]}; " + "; ".join(detail)
-    n_closed = (PREFIX + STEPS) // run.cfg.chunk_size
+    end = w.q_pos0 + w.n_q
+    n_closed = end // run.cfg.chunk_size
     assert torch.equal(csum[:, :, :n_closed], run.csum[:, :, :n_closed])
-    ng_closed = (PREFIX + STEPS) // run.cfg.group_size
+    ng_closed = end // run.cfg.group_size
     assert torch.equal(gsum[:, :, :ng_closed], run.gsum[:, :, :ng_closed])
     ref_store = H.host_store(run.cfg, run.k_rot, run.v)
-    ng = (PREFIX + STEPS + run.cfg.group_size - 1) // run.cfg.group_size
+    ng = (end + run.cfg.group_size - 1) // run.cfg.group_size
     got = store[:, :, :ng].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
     want = ref_store[:, :, :ng].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
-    # token rows [0, PREFIX + STEPS) of both halves (K, V)
+    # token rows [0, end) of both halves (K, V)
     g = run.cfg.group_size
     sel = np.arange(ng * 2 * g).reshape(ng, 2, g)
     tok = (np.arange(ng)[:, None, None] * g + np.arange(g)[None, None, :]).repeat(2, axis=1)
-    rows = sel[tok < PREFIX + STEPS]
+    rows = sel[tok < end]
     assert torch.equal(got[:, :, rows], want[:, :, rows])
+    return stats
+
+
+@pytest.mark.parametrize("cache", ["roomy", "smallest", "smallest_poisoned"])
+def test_stream_decode_equals_device_path(cache):
+    w = _workload()
+    print(f"[gpu] stream decode ({cache}): {w}", flush=True)
+    need = w.batch * w.n_kv_heads * H.max_granules(H.Config.from_workload(w))
+    slots = 4 * need if cache == "roomy" else need
+    stats = _check_session(w, slots, poison=cache.endswith("poisoned"))
     copied = [st["granules_copied"] for st in stats]
     hits = [st["granules_hit"] for st in stats]
     print(f"[gpu] stream decode ({cache}): copied first {copied[0]} then mean "
@@ -127,3 +137,14 @@ def test_stream_decode_equals_device_path(cache):
         # (the synthetic queries are independent, so routes change a lot)
         assert np.mean(copied[1:]) < 0.5 * copied[0]
         assert min(hits[1:]) > 0
+
+
+@pytest.mark.parametrize("i", range(N_STREAM))
+def test_stream_decode_random_shapes(i):
+    """Random streaming shapes (chunk / group sizes, windows, budgets, GQA
+    ratio, d, prefix length, steps crossing chunk boundaries, RoPE wrap,
+    the smallest or a roomy cache): every step bit for bit equal to the
+    device path."""
+    w, cache = random_stream_workload(i)
+    print(f"[gpu] stream decode random {i}: {w} cache {cache}", flush=True)
+    _check_session(w, cache, seed=i)
