@@ -6,6 +6,7 @@ start and RoPE wrap."""
 import pytest
 
 import hierarchical_kv_routing_amd as H
+from oracle import hga_ref as R
 from tests import parity as P
 from tests.random_configs import N_CONFIGS, N_DECODE, random_decode_workload, random_workload
 
@@ -50,3 +51,25 @@ def test_random_decode_parity(i):
     assert exact + near == len(units)
     assert near <= max(1, len(units) // 20)
     P.check_attention(run, q, k, v, units)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(1, N_CONFIGS, 4))
+def test_random_shape_dense_and_full_coverage(i):
+    """Eq. 1 on random shapes: hga_dense_causal, and routing whose chunk
+    budget covers every middle chunk (K_g = 0), both against the oracle's
+    dense causal attention over every query row."""
+    import torch
+    w0 = random_workload(i)
+    w = w0.scaled(top_chunks=w0.kv_cap // w0.chunk_size, top_groups=0)
+    print(f"[gpu] random dense {i}: {w}", flush=True)
+    q, k, v = P.make_inputs_parallel(w, seed=i)
+    run = P.GpuRun(w, q, k, v)
+    dense = torch.full_like(run.out, float("nan"))
+    dlse = torch.full_like(run.lse, float("nan"))
+    H.dense_causal(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, dense, dlse, run.aws)
+    torch.cuda.synchronize()
+    p = R.params_from_workload(w)
+    o_ref, l_ref = R.dense_causal(q, w.q_pos0, w.n_q, k, v, p)
+    P.compare_out(w, dense.float().cpu().numpy(), dlse.cpu().numpy(), o_ref, l_ref, q=q, k=k)
+    P.compare_out(w, run.np("out"), run.np("lse"), o_ref, l_ref, q=q, k=k)
