@@ -45,7 +45,7 @@ def make_inputs_parallel(w, seed=0, threads=16):
     return W.make_inputs(w, seed, threads=threads)
 
 
-class GpuRun:
+class DeviceRun:
     """Device tensors and outputs of one pass of the whole path."""
 
     def __init__(self, w, q, k, v, cfg=None, build=True, route=True, attend=True):
@@ -94,7 +94,7 @@ class GpuRun:
         return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
 
 
-def check_summaries(run: GpuRun, k, slabs=None):
+def check_summaries(run: DeviceRun, k, slabs=None):
     """GPU summaries and rotated keys vs the oracle on the listed (b, kvh) slabs."""
     w = run.w
     p = R.params_from_workload(w)
@@ -119,7 +119,7 @@ def check_summaries(run: GpuRun, k, slabs=None):
     return worst
 
 
-def oracle_route(run: GpuRun, q, k, units):
+def oracle_route(run: DeviceRun, q, k, units):
     """Oracle routing (own f64 summaries) of the given units."""
     w = run.w
     p = R.params_from_workload(w)
@@ -138,7 +138,7 @@ def oracle_route(run: GpuRun, q, k, units):
     return R.route(q, w.q_pos0, w.n_q, cs, gs, p, units=units)
 
 
-def compare_routes(run: GpuRun, orc: dict, units):
+def compare_routes(run: DeviceRun, orc: dict, units):
     """Returns (exact, near_tie) counts; asserts every other unit matches."""
     w = run.w
     p = R.params_from_workload(w)
@@ -175,7 +175,7 @@ def compare_routes(run: GpuRun, orc: dict, units):
     return exact, near
 
 
-def check_attention(run: GpuRun, q, k, v, units, out=None, lse=None):
+def check_attention(run: DeviceRun, q, k, v, units, out=None, lse=None):
     """Oracle attention on the GPU's granule lists for ``units``."""
     w = run.w
     p = R.params_from_workload(w)

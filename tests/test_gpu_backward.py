@@ -60,7 +60,7 @@ def _check_backward(case, w, seed=0):
     import torch
     q, k, v = P.make_inputs_parallel(w, seed)
     print(f"[gpu] backward {case}: {w}", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     dev = run.q.device
     do = W.round_to_bf16(np.random.default_rng(31).standard_normal(q.shape).astype(np.float32))
     d_out = torch.from_numpy(do).to(dev).to(torch.bfloat16)
@@ -105,7 +105,7 @@ def test_backward_deterministic_except_atomics():
     import torch
     w = CASES["qwen3_ragged"]
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     dev = run.q.device
     d_out = torch.from_numpy(W.round_to_bf16(np.random.default_rng(32).standard_normal(q.shape).astype(np.float32))
                              ).to(dev).to(torch.bfloat16)
@@ -136,7 +136,7 @@ def test_backward_qwen3_32k_sampled():
     w = W.QWEN3_PREFILL
     q, k, v = P.make_inputs_parallel(w)
     print("[gpu] backward qwen3 32k: inputs ready", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     dev = run.q.device
     do = W.round_to_bf16(np.random.default_rng(41).standard_normal(q.shape).astype(np.float32))
     d_out = torch.from_numpy(do).to(dev).to(torch.bfloat16)

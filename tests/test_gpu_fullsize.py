@@ -17,7 +17,7 @@ def test_qwen3_prefill_32k_full():
     w = W.QWEN3_PREFILL
     q, k, v = P.make_inputs_parallel(w)
     print("[gpu] qwen3 prefill 32k: inputs ready", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     P.check_summaries(run, k, slabs=[(0, 0), (0, 3)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
@@ -32,7 +32,7 @@ def test_decode_64k_full():
     w = W.DECODE_64K
     q, k, v = P.make_inputs_parallel(w)
     print("[gpu] decode 64k: inputs ready", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     units = [(0, 0, 1024), (5, 2, 1024), (11, 1, 1024), (15, 3, 1024)]
     P.check_summaries(run, k, slabs=[(b, h) for b, h, _ in units])
     orc = P.oracle_route(run, q, k, units)
@@ -53,7 +53,7 @@ def test_host_tiered_128k_full(base):
     cache = 8192 if w.rope_period else 0
     q, k, v = P.make_inputs_parallel(w)
     print(f"[gpu] host tier 128k {base}: inputs ready", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     slots = 16384
     if w.rope_period:
         P.check_summaries(run, k, slabs=[(0, 2)])

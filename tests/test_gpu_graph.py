@@ -15,7 +15,7 @@ def test_decode_step_graph_replays_match_eager(batch):
     import torch
     w = W.DECODE_64K.scaled(batch=batch, n_ctx=20481, kv_cap=20544, q_pos0=20480)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     ro, cfg = run.ro, run.cfg
     out = torch.empty_like(run.out)
     lse = torch.empty_like(run.lse)
@@ -67,7 +67,7 @@ def test_prefill_and_backward_graph_replays_match_eager(shape):
     else:
         w = W.SMALLLM_PREFILL.scaled(batch=2, n_ctx=1500, kv_cap=1536, n_q=1500, planted=8)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v, build=False, route=False, attend=False)
+    run = P.DeviceRun(w, q, k, v, build=False, route=False, attend=False)
     ro, cfg, dev = run.ro, run.cfg, run.q.device
     do = torch.from_numpy(W.round_to_bf16(np.random.default_rng(3).standard_normal(q.shape).astype(np.float32)))
     d_out = do.to(dev).to(run.q.dtype)

@@ -37,7 +37,7 @@ def test_host_tier_equals_device_path(base):
     w0 = W.HOST_TIERED_CHUNK if base == "chunk_only" else W.HOST_TIERED_GROUP
     w = w0.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=16)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     gmax = H.max_granules(run.cfg)
     slots = w.batch * w.n_kv_heads * gmax + 64    # windows split on slot capacity
     out, lse, stats = run_host_tier(run, max_window_chunks=16, slots=slots)
@@ -59,7 +59,7 @@ def test_warm_tier_equals_device_path(base):
     w0 = W.HOST_TIERED_CHUNK if base == "chunk_only" else W.HOST_TIERED_GROUP
     w = w0.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=16)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
     cache = need + 64  # below the 1024 granules of the 4 (sequence, KV head) slabs
     _, _, cold = run_host_tier(run, max_window_chunks=4, slots=need + 64)
@@ -78,7 +78,7 @@ def test_host_tier_same_stream_and_no_threads():
     import torch
     w = W.HOST_TIERED_GROUP.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=8)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     slots = 2 * w.batch * w.n_kv_heads * H.max_granules(run.cfg)
     out, lse, stats = run_host_tier(run, 8, slots, threads=0, copy_stream=False)
     same = bool(torch.equal(out, run.out))
@@ -89,7 +89,7 @@ def test_host_tier_rejects_pageable_memory():
     import torch
     w = W.HOST_TIERED_GROUP.scaled(n_ctx=1024, kv_cap=1024, n_q=1024, planted=0)
     q, k, v = P.make_inputs_parallel(w)
-    run = P.GpuRun(w, q, k, v, attend=False)
+    run = P.DeviceRun(w, q, k, v, attend=False)
     cfg = run.cfg
     B, Hkv, cap, d = run.k.shape
     pageable = torch.zeros((B, Hkv, cap // w.group_size, 2, w.group_size, d), dtype=torch.bfloat16)
@@ -123,7 +123,7 @@ def test_host_tier_random_shapes(i):
     w = random_workload(i)
     rng = np.random.default_rng(500 + i)
     q, k, v = P.make_inputs_parallel(w, seed=i)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     need = w.batch * w.n_kv_heads * H.max_granules(run.cfg)
     draws = [(need + int(rng.integers(0, 2 * need + 1)), int(rng.integers(1, 9))) for _ in range(2)]
     cache = need + int(rng.integers(0, need + 1))

@@ -40,7 +40,7 @@ def case(request):
     w = CASES[request.param]
     q, k, v = _inputs(w)
     print(f"[gpu] case {request.param}: {w}", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     return request.param, w, q, k, v, run
 
 
@@ -84,7 +84,7 @@ def test_full_coverage_equals_dense(dtype, d):
                n_ctx=1280, kv_cap=1280, n_q=1280, top_chunks=64, top_groups=0,
                n_hf_pairs=R.high_freq_pair_count(d, 1e7, 64), planted=4)
     q, k, v = _inputs(w, seed=1)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     import torch
     dense = torch.zeros_like(run.out)
     dlse = torch.zeros_like(run.lse)
@@ -106,7 +106,7 @@ def test_dense_causal_partial_queries():
     w = _small(W.SMALLLM_PREFILL, batch=1, n_q_heads=2, n_kv_heads=1, n_ctx=700, kv_cap=704,
                q_pos0=133, n_q=567, planted=0)
     q, k, v = _inputs(w, seed=2)
-    run = P.GpuRun(w, q, k, v, route=False, attend=False)
+    run = P.DeviceRun(w, q, k, v, route=False, attend=False)
     import torch
     H.dense_causal(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, run.out, run.lse, run.aws)
     torch.cuda.synchronize()
@@ -133,7 +133,7 @@ def test_edge_cases(name):
     over.update(EDGE[name])
     w = _small(W.QWEN3_PREFILL, **over)
     q, k, v = _inputs(w, seed=3)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
     P.compare_routes(run, orc, units)
@@ -160,7 +160,7 @@ def test_rope_wrap(name):
     w = WRAP[name]
     q, k, v = _inputs(w, seed=5)
     print(f"[gpu] rope wrap {name}: {w}", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     P.check_summaries(run, k, slabs=[(0, 0), (w.batch - 1, w.n_kv_heads - 1)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
@@ -168,7 +168,7 @@ def test_rope_wrap(name):
     assert near <= max(2, len(units) // 50)
     P.check_attention(run, q, k, v, units)
     # the period reaches the kernels: absolute positions give other outputs
-    flat = P.GpuRun(w.scaled(rope_period=0), q, k, v)
+    flat = P.DeviceRun(w.scaled(rope_period=0), q, k, v)
     assert not np.array_equal(flat.np("out"), run.np("out"))
 
 
@@ -176,7 +176,7 @@ def test_empty_call_is_noop():
     w = _small(W.SMALLLM_PREFILL, batch=1, n_q_heads=1, n_kv_heads=1, n_ctx=128, kv_cap=128,
                n_q=128, planted=0)
     q, k, v = _inputs(w)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     import torch
     before = run.out.clone()
     H.attend(run.cfg, run.q[:, :, :0], 0, run.k_rot, run.v, run.ro["granules"][:, :, :0],
@@ -192,7 +192,7 @@ def test_summary_single_token_blocks():
     w = _small(W.TINY_F32, chunk_size=1, group_size=1, n_ctx=256, kv_cap=256, n_q=256,
                n_hf_pairs=5, planted=0)
     q, k, v = _inputs(w)
-    run = P.GpuRun(w, q, k, v, route=False, attend=False)
+    run = P.DeviceRun(w, q, k, v, route=False, attend=False)
     P.check_summaries(run, k)
     np.testing.assert_allclose(run.np("csum")[0, 0], run.np("k_rot")[0, 0], atol=1e-6)
     np.testing.assert_allclose(run.np("gsum")[0, 0], run.np("k_rot")[0, 0], atol=1e-6)
@@ -204,8 +204,8 @@ def test_append_matches_prefill_build():
     cache vs no-cache check)."""
     w = _small(W.QWEN3_PREFILL, n_ctx=700, kv_cap=704, n_q=700, planted=0)
     q, k, v = _inputs(w)
-    full = P.GpuRun(w, q, k, v, route=False, attend=False)
-    inc = P.GpuRun(w, q, k, v, build=False, route=False, attend=False)
+    full = P.DeviceRun(w, q, k, v, route=False, attend=False)
+    inc = P.DeviceRun(w, q, k, v, build=False, route=False, attend=False)
     import torch
     H.build_summaries(inc.cfg, inc.k, 0, 500, inc.k_rot, inc.csum, inc.gsum)
     for p in range(500, 700):
@@ -223,7 +223,7 @@ def test_decode_segmented_and_split():
     cfg = H.Config.from_workload(w)
     assert H.route_workspace_bytes(cfg, w.batch, w.q_pos0, 1) > 0
     assert H.attend_workspace_bytes(cfg, w.batch, w.q_pos0, 1) > 0
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     units = P.all_units(w)
     P.check_summaries(run, k, slabs=[(0, 0), (2, 3)])
     orc = P.oracle_route(run, q, k, units)

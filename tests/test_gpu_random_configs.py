@@ -27,7 +27,7 @@ def test_random_shape_parity(i):
     w = random_workload(i)
     print(f"[gpu] random shape {i}: {w}", flush=True)
     q, k, v = P.make_inputs_parallel(w, seed=i)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     P.check_summaries(run, k, slabs=[(w.batch - 1, w.n_kv_heads - 1)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
@@ -43,7 +43,7 @@ def test_random_decode_parity(i):
     w = random_decode_workload(i)
     print(f"[gpu] random decode {i}: {w}", flush=True)
     q, k, v = P.make_inputs_parallel(w, seed=i)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     P.check_summaries(run, k, slabs=[(w.batch - 1, w.n_kv_heads - 1)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
@@ -64,7 +64,7 @@ def test_random_shape_dense_and_full_coverage(i):
     w = w0.scaled(top_chunks=w0.kv_cap // w0.chunk_size, top_groups=0)
     print(f"[gpu] random dense {i}: {w}", flush=True)
     q, k, v = P.make_inputs_parallel(w, seed=i)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     dense = torch.full_like(run.out, float("nan"))
     dlse = torch.full_like(run.lse, float("nan"))
     H.dense_causal(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, dense, dlse, run.aws)

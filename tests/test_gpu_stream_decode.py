@@ -87,7 +87,7 @@ def _check_session(w, cache_slots, poison=False, seed=0):
     import torch
     dev = torch.device("cuda:0")
     q, k, v = P.make_inputs_parallel(w, seed)
-    run = P.GpuRun(w, q, k, v, route=False, attend=False)
+    run = P.DeviceRun(w, q, k, v, route=False, attend=False)
     ref_out, ref_lse = _reference(run, w, dev)
     outs, lses, stats, csum, gsum, store = _session_run(run, w, cache_slots, dev, poison=poison)
     bad = [s for s in range(w.n_q)

@@ -37,7 +37,7 @@ def test_attend_ignores_memory_after_last_query(case):
     w = CASES[case]
     q, k, v = P.make_inputs_parallel(w)
     print(f"[gpu] unwritten tail, attend {case}: {w}", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     k_rot, vv = _poisoned(run, w)
     out = torch.full_like(run.out, float("nan"))
     lse = torch.full_like(run.lse, float("nan"))
@@ -52,7 +52,7 @@ def test_backward_ignores_memory_after_last_query():
     w = CASES["bf16_prefill"]
     q, k, v = P.make_inputs_parallel(w)
     print(f"[gpu] unwritten tail, backward: {w}", flush=True)
-    run = P.GpuRun(w, q, k, v)
+    run = P.DeviceRun(w, q, k, v)
     dev = run.q.device
     do = W.round_to_bf16(np.random.default_rng(33).standard_normal(q.shape).astype(np.float32))
     d_out = torch.from_numpy(do).to(dev).to(torch.bfloat16)
