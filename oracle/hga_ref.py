@@ -2,7 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Every array is
 float64; inputs are widened exactly from the float32 / bfloat16 values the
-generators produce.
+generators produce.  The one rounding modelled is the rotated-key cache
+the attention reads: keys rotated in float64 are held in the workload's
+dtype (``round_to_cache``, ``Params.key_cache``), as a model of that dtype
+caches its post-RoPE keys; ``key_cache="f64"`` gives exact keys.
 
 Layouts: q [B][Hq][n_q][d] (query qi sits at position q_pos0 + qi);
 k, v [B][Hkv][kv_cap][d] (slot j holds position j); chunk summaries
@@ -32,6 +35,7 @@ class Params:
     d: int
     scale: float = 0.0  # 0 -> 1/sqrt(d)
     period: int = 0     # RoPE positions wrap modulo period; 0 = absolute
+    key_cache: str = "f64"  # dtype the rotated-key cache holds: "bf16", "f32" or "f64"
 
     @property
     def softmax_scale(self) -> float:
@@ -46,7 +50,24 @@ def params_from_workload(w) -> Params:
     return Params(C=w.chunk_size, gs=w.group_size, F=w.n_sink_chunks,
                   L=w.n_recent_chunks, Kc=w.top_chunks, Kg=w.top_groups,
                   n_hf=w.n_hf_pairs, theta=w.rope_theta, Hq=w.n_q_heads,
-                  Hkv=w.n_kv_heads, d=w.head_dim, period=w.rope_period)
+                  Hkv=w.n_kv_heads, d=w.head_dim, period=w.rope_period, key_cache=w.dtype)
+
+
+def round_to_cache(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The value a rotated-key cache of ``dtype`` holds for float64 x: an
+    attention that reads a cache of rotated keys sees them in the model's
+    dtype (a bf16 model keeps its keys, rotated, in bf16).  bf16: x rounded
+    to 8 significant bits, ties to even; f32: numpy's round-to-nearest;
+    f64: x itself."""
+    x = np.asarray(x, np.float64)
+    if dtype == "f64":
+        return x
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    m, e = np.frexp(x)                 # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)  # np.round: half to even
 
 
 # --------------------------------------------------------------------------
@@ -328,7 +349,8 @@ def attend_given(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, p: Par
     for (b, kvh, t) in units:
         gl = np.asarray(granules[b, kvh, t - t0, : int(count[b, kvh, t - t0])], np.int64)
         tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
-        kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period)
+        kk = round_to_cache(rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period),
+                            p.key_cache)
         vv = np.asarray(v[b, kvh][tok], np.float64)
         qpos = unit_queries(t, q_pos0, n_q, p.C)
         mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
@@ -382,7 +404,8 @@ def attend_backward(q_raw, q_pos0: int, n_q: int, k_raw, v, granules, count, d_o
     for (b, kvh, t) in units:
         gl = np.asarray(granules[b, kvh, t - t0, : int(count[b, kvh, t - t0])], np.int64)
         tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
-        kk = rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period)
+        kk = round_to_cache(rope(np.asarray(k_raw[b, kvh][tok], np.float64), tok, p.theta, p.period),
+                            p.key_cache)
         vv = np.asarray(v[b, kvh][tok], np.float64)
         qpos = unit_queries(t, q_pos0, n_q, p.C)
         mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
@@ -419,7 +442,8 @@ def dense_causal(q_raw, q_pos0: int, n_q: int, k_raw, v, p: Params, heads=None, 
     for b in range(B):
         qrot = rope(q[b][:, qi, :], q_pos0 + qi, p.theta, p.period)
         for kvh in range(p.Hkv):
-            kk = rope(np.asarray(k_raw[b, kvh][:nk], np.float64), np.arange(nk), p.theta, p.period)
+            kk = round_to_cache(rope(np.asarray(k_raw[b, kvh][:nk], np.float64), np.arange(nk), p.theta,
+                                     p.period), p.key_cache)
             vv = np.asarray(v[b, kvh][:nk], np.float64)
             mask = np.arange(nk)[None, :] <= (q_pos0 + qi)[:, None]
             for hl in range(G):

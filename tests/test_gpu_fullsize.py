@@ -28,6 +28,23 @@ def test_qwen3_prefill_32k_full():
     print(f"[gpu] qwen3 32k attention: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
 
+def test_smalllm_prefill_4k_full():
+    """The SmallLM-shaped prefill bench.py also times (4 sequences, 8 / 8
+    heads, d = 64, 4096 tokens): every unit's routes, the attention of
+    every row of sampled units."""
+    w = W.SMALLLM_PREFILL
+    q, k, v = P.make_inputs_parallel(w)
+    run = P.DeviceRun(w, q, k, v)
+    P.check_summaries(run, k, slabs=[(0, 0), (3, 7)])
+    units = P.all_units(w)
+    orc = P.oracle_route(run, q, k, units)
+    exact, near = P.compare_routes(run, orc, units)
+    print(f"[gpu] smalllm 4k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
+    assert near <= len(units) // 50
+    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 24))
+    print(f"[gpu] smalllm 4k attention: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
+
+
 def test_decode_64k_full():
     w = W.DECODE_64K
     q, k, v = P.make_inputs_parallel(w)

@@ -6,6 +6,7 @@ compares the oracle with itself: the checks are closed forms, values printed
 on the pages or derived by hand from their rules (tests/golden/), a library
 routine (torch SDPA), textbook identities, or the independent brute force.
 """
+import dataclasses
 import json
 import math
 import os
@@ -202,7 +203,8 @@ def _brute_pipeline(w, q, k, v, b):
 
 
 def _oracle_pipeline(w, q, k, v):
-    p = R.params_from_workload(w)
+    # exact keys: the brute force it is checked against rotates in float64
+    p = dataclasses.replace(R.params_from_workload(w), key_cache="f64")
     cs, gsum = R.summaries(k, w.q_pos0 + w.n_q, p)
     rt = R.route(q, w.q_pos0, w.n_q, cs, gsum, p)
     out, lse = R.attend_given(q, w.q_pos0, w.n_q, k, v, rt["granules"], rt["count"], p, t0=rt["t0"])
@@ -549,3 +551,20 @@ def test_max_granules_bound():
         r = p.groups_per_chunk
         routed = min(p.Kg, r * min(p.Kc, nmid)) if p.Kg else r * min(p.Kc, nmid)
         assert len(R.fixed_chunks(t, p.F, p.L)) * r + r + routed <= R.max_granules(p)
+
+
+def test_cache_rounding_is_round_to_nearest_even():
+    """round_to_cache("bf16") against torch's float32 -> bfloat16 conversion
+    (round to nearest, ties to even) on float32-exact values, including exact
+    halfway cases; "f32" against numpy's float64 -> float32 conversion."""
+    import torch
+    rng = np.random.default_rng(5)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    bits = x32.view(np.uint32)
+    half = ((bits & ~np.uint32(0xFFFF)) | np.uint32(0x8000)).view(np.float32)  # exact ties
+    x = np.concatenate([x32, half, -half, np.float32([0.0, 1.0, -2.5, 3.0e38])]).astype(np.float64)
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(R.round_to_cache(x, "bf16"), want)
+    y = rng.standard_normal(1000) * 1e3
+    np.testing.assert_array_equal(R.round_to_cache(y, "f32"), y.astype(np.float32).astype(np.float64))
+    np.testing.assert_array_equal(R.round_to_cache(y, "f64"), y)
