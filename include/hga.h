@@ -155,7 +155,9 @@ size_t hga_route_workspace_bytes(const hga_config* cfg, int32_t batch,
  *
  * chunk_sum must hold every chunk < the last query chunk; group_sum every
  * group of those chunks (group_sum / group_idx may be NULL iff K_g == 0).
- * Requires kv_cap % C == 0 and q_pos0 + n_q <= kv_cap.
+ * Requires kv_cap % C == 0 and q_pos0 + n_q <= kv_cap.  HGA_ERR_UNSUPPORTED
+ * when K_c or K_g exceeds 256, a unit has more than 512 (query, head) rows
+ * (C * G), more than 4096 middle chunks, or K_c * C/g_s exceeds 4096.
  */
 hga_status hga_route(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                      const void* q_raw, int64_t q_pos0, int64_t n_q,

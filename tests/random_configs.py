@@ -55,7 +55,7 @@ def random_decode_workload(i: int) -> W.Workload:
     hkv = int(rng.choice([1, 2, 4]))
     r = C // gs
     kc = int(rng.integers(1, 9))
-    kg = int(rng.choice([0, max(1, kc * r // 2), kc * r + 2]))
+    kg = min(256, int(rng.choice([0, max(1, kc * r // 2), kc * r + 2])))  # routing selects <= 256
     n_ctx = int(rng.integers(100, 420)) * C + int(rng.integers(1, C + 1))
     kv_cap = (n_ctx + C - 1) // C * C + int(rng.choice([0, C]))
     period = int(rng.choice([0, C * int(rng.integers(8, 64))]))
@@ -84,7 +84,7 @@ def random_stream_workload(i: int):
     hkv = int(rng.choice([1, 2]))
     r = C // gs
     kc = int(rng.integers(1, 7))
-    kg = int(rng.choice([0, max(1, kc * r // 2), kc * r + 2]))
+    kg = min(256, int(rng.choice([0, max(1, kc * r // 2), kc * r + 2])))  # routing selects <= 256
     prefix = int(rng.integers(20, 120)) * C  # sessions start at a chunk boundary
     steps = int(rng.integers(C // 2, 2 * C + 8))
     kv_cap = (prefix + steps + C - 1) // C * C + int(rng.choice([0, C]))
