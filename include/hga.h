@@ -81,7 +81,7 @@ typedef enum {
 typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
 
 typedef struct hga_config {
-  int32_t chunk_size;      /* C: tokens per chunk (framework paragraph)           */
+  int32_t chunk_size;      /* C: tokens per chunk (framework paragraph), <= 64    */
   int32_t group_size;      /* g_s: tokens per group; C % g_s == 0                 */
   int32_t n_sink_chunks;   /* F: first chunks always visible (routing policy)    */
   int32_t n_recent_chunks; /* L: last closed chunks always visible               */
@@ -185,7 +185,8 @@ size_t hga_attend_workspace_bytes(const hga_config* cfg, int32_t batch,
  * never read into a result and may hold anything (a cache filled up to the
  * current token).  bf16 runs QK^T and PV on bf16 matrix cores (P rounded
  * to bf16) with f32 online softmax; f32 runs on f32 vector ALUs.  lse may
- * be NULL.
+ * be NULL.  HGA_ERR_UNSUPPORTED when g_s is not a power of two, or (bf16)
+ * when one (sequence, KV head) slab of k_rot or v reaches 2^31 bytes.
  */
 hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                       const void* q_raw, int64_t q_pos0, int64_t n_q,
