@@ -176,7 +176,9 @@ def compare_routes(run: DeviceRun, orc: dict, units):
 
 
 def check_attention(run: DeviceRun, q, k, v, units, out=None, lse=None):
-    """Oracle attention on the GPU's granule lists for ``units``."""
+    """Oracle attention on the GPU's granule lists for ``units``: within the
+    tolerances against the keys as the workload's dtype caches them, and
+    (bf16) within the rel-L2 bar against exact float64 keys too."""
     w = run.w
     p = R.params_from_workload(w)
     gr, gc = run.np("granules"), run.np("granule_count")
@@ -184,7 +186,16 @@ def check_attention(run: DeviceRun, q, k, v, units, out=None, lse=None):
                                   t0=w.q_pos0 // w.chunk_size, units=units)
     out = run.np("out") if out is None else out
     lse = run.np("lse") if lse is None else lse
-    return compare_out(w, out, lse, o_ref, l_ref, q=q, k=k)
+    res = compare_out(w, out, lse, o_ref, l_ref, q=q, k=k)
+    if w.dtype == "bf16":
+        import dataclasses
+        o_x, _ = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc,
+                                dataclasses.replace(p, key_cache="f64"),
+                                t0=w.q_pos0 // w.chunk_size, units=units)
+        sel = ~np.isnan(o_x)
+        rel = float(np.linalg.norm(out[sel] - o_x[sel]) / max(np.linalg.norm(o_x[sel]), 1e-30))
+        assert rel <= TOL["bf16"][1], ("rel-L2 against exact keys", rel)
+    return res
 
 
 def lse_tolerance(w, q, k):
