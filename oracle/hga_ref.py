@@ -2,10 +2,12 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Every array is
 float64; inputs are widened exactly from the float32 / bfloat16 values the
-generators produce.  The one rounding modelled is the rotated-key cache
-the attention reads: keys rotated in float64 are held in the workload's
-dtype (``round_to_cache``, ``Params.key_cache``), as a model of that dtype
-caches its post-RoPE keys; ``key_cache="f64"`` gives exact keys.
+generators produce, and every step is exact float64 arithmetic by default.
+One rounding can be modelled on request, as a stated reading of a point the
+pages leave open: ``Params.key_cache`` = "bf16" / "f32" holds the rotated
+keys the attention reads in that dtype (``round_to_cache``), as a model of
+that dtype caches its post-RoPE keys.  The default, "f64", is the plain
+definition (exact rotated keys).
 
 Layouts: q [B][Hq][n_q][d] (query qi sits at position q_pos0 + qi);
 k, v [B][Hkv][kv_cap][d] (slot j holds position j); chunk summaries
@@ -35,7 +37,7 @@ class Params:
     d: int
     scale: float = 0.0  # 0 -> 1/sqrt(d)
     period: int = 0     # RoPE positions wrap modulo period; 0 = absolute
-    key_cache: str = "f64"  # dtype the rotated-key cache holds: "bf16", "f32" or "f64"
+    key_cache: str = "f64"  # rotated keys as attention reads them: exact ("f64"), or held in "bf16" / "f32"
 
     @property
     def softmax_scale(self) -> float:
@@ -50,7 +52,7 @@ def params_from_workload(w) -> Params:
     return Params(C=w.chunk_size, gs=w.group_size, F=w.n_sink_chunks,
                   L=w.n_recent_chunks, Kc=w.top_chunks, Kg=w.top_groups,
                   n_hf=w.n_hf_pairs, theta=w.rope_theta, Hq=w.n_q_heads,
-                  Hkv=w.n_kv_heads, d=w.head_dim, period=w.rope_period, key_cache=w.dtype)
+                  Hkv=w.n_kv_heads, d=w.head_dim, period=w.rope_period)
 
 
 def round_to_cache(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -8,16 +8,26 @@ Tolerances (written here, used by every parity test):
   rotated element of magnitude <= 15; f32 sums of 64 such terms add <= 1e-6.
 * bf16 rotated key cache: one bf16 rounding, <= 2^-8 |x| + 2e-5.
 * Routing: chunk / group index lists bit-exact, except units whose oracle
-  top-K margin s_(K) - s_(K+1) is below 1e-3 |s_(K)| (near-ties, counted and
-  reported); there every GPU-selected id must still score within that band of
-  the oracle's K-th score.  Granule lists bit-exact given the selections.
-* Attention, computed by the oracle on the GPU's own granule lists:
-  bf16 max-abs <= 2e-2 and rel-L2 <= 1e-2; f32 max-abs <= 1e-5 and rel-L2 <= 1e-5.
-* Log-sum-exp: the bf16 path rounds the scaled rotated query and the rotated
-  keys to bf16, so each product q_i k_i carries a relative error below 2^-8
-  and every logit moves by at most 2^-8 * scale * sum_i |q_i k_i| <=
-  2^-8 * scale * |q| * |k|; the LSE moves by at most the largest logit move:
-  tol(row) = 2^-8 * scale * |q_row| * max_j |k_j| + 1e-5.  f32: 1e-5.
+  top-K margin s_(K) - s_(K+1) is positive and below 1e-3 |s_(K)| (near-ties,
+  counted and reported); there every GPU-selected id must still score within
+  that band of the oracle's K-th score.  An exact tie (margin 0) is no
+  exception: the lowest index wins.  Granule lists bit-exact given the
+  selections.
+* Attention, computed by the oracle on the GPU's own granule lists.
+  f32: max-abs <= 1e-5 and rel-L2 <= 1e-5 against exact keys; LSE <= 1e-5.
+  bf16, three checks on every compared row:
+  (a) against exact float64 rotated keys (the plain definition): rel-L2 <=
+      1e-2, and every output element and every LSE within the rounding
+      bound derived from the bf16 arithmetic (``_rounding_bound``: bf16
+      rounding of the scaled rotated query and of the rotated keys moves a
+      logit by at most 2u scale sum_d |q~_d k~_d|, u = 2^-8; P and the output
+      are rounded to bf16 once more);
+  (b) against the rotated keys as a bf16 key cache holds them (each rotated
+      key rounded to bf16, the reading a bf16 model's post-RoPE key cache
+      gives): max-abs <= 2e-2 and rel-L2 <= 1e-2;
+  (c) recorded, not asserted: max-abs against exact keys and the number of
+      rows whose max-abs against exact keys exceeds 2e-2 (a row whose two
+      largest logits compete loses up to ~3e-2 to the key rounding alone).
 """
 from __future__ import annotations
 
@@ -124,10 +134,10 @@ def oracle_route(run: DeviceRun, q, k, units):
     w = run.w
     p = R.params_from_workload(w)
     n_sum = w.n_ctx
-    sums = {}
-    for (b, h, _) in units:
-        if (b, h) not in sums:
-            sums[(b, h)] = R.summaries(k[b, h].astype(np.float64), n_sum, p)
+    slabs = sorted({(b, h) for (b, h, _) in units})
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        done = ex.map(lambda bh: R.summaries(k[bh[0], bh[1]].astype(np.float64), n_sum, p), slabs)
+        sums = dict(zip(slabs, done))
     B, Hkv = w.batch, w.n_kv_heads
     nc = sums[next(iter(sums))][0].shape[0]
     ng = sums[next(iter(sums))][1].shape[0]
@@ -138,7 +148,7 @@ def oracle_route(run: DeviceRun, q, k, units):
     return R.route(q, w.q_pos0, w.n_q, cs, gs, p, units=units)
 
 
-def compare_routes(run: DeviceRun, orc: dict, units):
+def compare_routes(run: DeviceRun, orc: dict, units, name=None):
     """Returns (exact, near_tie) counts; asserts every other unit matches."""
     w = run.w
     p = R.params_from_workload(w)
@@ -159,72 +169,191 @@ def compare_routes(run: DeviceRun, orc: dict, units):
         assert all(x == -1 for x in gr[b, h, u, gc[b, h, u]:])
         if g_ch != info["sel_chunks"]:
             band = TIE_REL * abs(info["s_kc"])
-            assert info["margin_c"] < band, ((b, h, t), g_ch, info["sel_chunks"], info["margin_c"])
+            # an exact tie (margin 0) has one answer: the lowest index
+            assert 0 < info["margin_c"] < band, ((b, h, t), g_ch, info["sel_chunks"], info["margin_c"])
             sc = dict(zip(info["mid"], info["chunk_scores"]))
             assert all(sc[m] >= info["s_kc"] - band for m in g_ch), (b, h, t)
             near += 1
             continue
         if p.Kg > 0 and g_gr != info["sel_groups"]:
             band = TIE_REL * abs(info["s_kg"])
-            assert info["margin_g"] < band, ((b, h, t), g_gr, info["sel_groups"], info["margin_g"])
+            assert 0 < info["margin_g"] < band, ((b, h, t), g_gr, info["sel_groups"], info["margin_g"])
             sg = dict(zip(info["group_cands"], info["group_scores"]))
             assert all(sg[x] >= info["s_kg"] - band for x in g_gr), (b, h, t)
             near += 1
             continue
         exact += 1
+    ties = sum(1 for u in units if orc["info"][u]["margin_c"] == 0 or orc["info"][u]["margin_g"] == 0)
+    record("routes", name or w.name, units=len(units), exact=exact, near_tie=near, exact_ties=ties)
     return exact, near
 
 
-def check_attention(run: DeviceRun, q, k, v, units, out=None, lse=None):
-    """Oracle attention on the GPU's granule lists for ``units``: within the
-    tolerances against the keys as the workload's dtype caches them, and
-    (bf16) within the rel-L2 bar against exact float64 keys too."""
+class AttnStats(tuple):
+    """(max_abs, rel_l2, lse_err) against exact float64 keys, plus the
+    detail of the comparison as attributes."""
+
+    def __new__(cls, **kw):
+        obj = super().__new__(cls, (kw["max_abs"], kw["rel_l2"], kw["lse_err"]))
+        obj.__dict__.update(kw)
+        return obj
+
+    def as_dict(self):
+        return dict(self.__dict__)
+
+
+# Results of every attention comparison made in this process (reported by
+# conftest.py at the end of a run and written to gpurun_out/ when present).
+RECORDS = []
+
+
+def record(kind, name, **kw):
+    RECORDS.append(dict(kind=kind, name=name, **kw))
+
+
+def _rounding_bound(w, p, rows, kk, vv, mask, o, lse):
+    """Per-element bound on |gpu - exact| for bf16 attention of query rows
+    ``rows`` [R,d] (rotated, float64) over keys kk [nk,d] (rotated, exact),
+    values vv, with the exact output o [R,d] and log-sum-exp lse [R].
+
+    The bf16 path rounds scale*q~ and k~ to bf16 (relative error <= u = 2^-8
+    each) and accumulates in f32, so logit j of a row moves by at most
+      E_j = scale * sum_d |q~_d k~_jd| * (2u + u^2 + 2^-16)
+    (the last term covers the f32 sums over d <= 128 and the f32 RoPE).  With
+    E-bar = log sum_j p_j e^{E_j}, softmax weights move to p'_j with
+    |p'_j - p_j| <= p_j (e^{E_j + E-bar} - 1), and since sum_j (p'_j - p_j) = 0,
+      |o'_d - o_d| <= sum_j p_j (e^{E_j+E-bar} - 1) |v_jd - o_d|
+                   <= sum_j p_j (e^{E_j+E-bar} - 1) (|v_jd| + |o_d|).
+    P is rounded to bf16 for the PV product (<= u sum_j p'_j |v_jd|) and the
+    output to bf16 (<= u |o'_d|).  The LSE moves by at most E-bar, plus f32
+    rounding of its sum over nk terms (nk 2^-24) and of the log.
+    Returns (bound_out [R,d], bound_lse [R])."""
+    u = 2.0 ** -8
+    scale = p.softmax_scale
+    E = scale * (np.abs(rows) @ np.abs(kk).T) * (2 * u + u * u + 2.0 ** -16)
+    E = np.where(mask, E, 0.0)
+    logits = scale * (rows @ kk.T)
+    pr = np.where(mask, np.exp(np.where(mask, logits, -np.inf) - lse[:, None]), 0.0)
+    ebar = np.log(np.sum(pr * np.exp(E), axis=1))
+    grow = np.exp(E + ebar[:, None])
+    av = np.abs(vv)
+    ao = np.abs(o)
+    w1 = pr * (grow - 1.0)
+    t1 = w1 @ av + w1.sum(axis=1)[:, None] * ao
+    t2 = u * ((pr * grow) @ av)
+    t3 = u * (ao + t1 + t2)
+    b_out = 1.02 * (t1 + t2 + t3) + 2e-5
+    nk = mask.sum(axis=1)
+    b_lse = 1.02 * ebar + (nk + 8) * 2.0 ** -24 + 2.0 ** -22 * np.abs(lse) + 2e-6
+    return b_out, b_lse
+
+
+def _unit_bounds(w, p, q, k, v, tok, qpos, mask, b, kvh, o_ref, l_ref, bo, bl):
+    """Fill bo / bl (like o_ref / l_ref) for the rows of one unit."""
+    G = p.Hq // p.Hkv
+    kk = R.rope(np.asarray(k[b, kvh][tok], np.float64), tok, p.theta, p.period)
+    vv = np.asarray(v[b, kvh][tok], np.float64)
+    qi = qpos - w.q_pos0
+    for hl in range(G):
+        h = kvh * G + hl
+        rows = R.rope(np.asarray(q[b, h, qi, :], np.float64), qpos, p.theta, p.period)
+        o_b, l_b = _rounding_bound(w, p, rows, kk, vv, mask, o_ref[b, h, qi], l_ref[b, h, qi])
+        bo[b, h, qi] = o_b
+        bl[b, h, qi] = l_b
+
+
+def _compare(w, name, out, lse, o_ref, l_ref, o_cached=None, l_cached=None, bo=None, bl=None):
+    """The acceptance rule for attention outputs (see the module docstring)."""
+    sel = ~np.isnan(o_ref)
+    assert sel.any()
+    diff = np.abs(out - o_ref)
+    max_abs = float(diff[sel].max())
+    rel_l2 = float(np.linalg.norm((out - o_ref)[sel]) / max(np.linalg.norm(o_ref[sel]), 1e-30))
+    lsel = ~np.isnan(l_ref)
+    lerr = np.abs(lse - l_ref)
+    lse_err = float(lerr[lsel].max())
+    tol_abs, tol_rel = TOL[w.dtype]
+    rowmax = np.where(sel, diff, 0.0).max(axis=-1)
+    rows = int(np.count_nonzero(lsel))
+    rows_over = int(np.count_nonzero(rowmax[lsel] > tol_abs))
+    kw = dict(dtype=w.dtype, rows=rows, max_abs=max_abs, rel_l2=rel_l2, lse_err=lse_err,
+              rows_over_abs_tol=rows_over)
+    if w.dtype != "bf16":
+        record("attention", name, **kw)
+        assert max_abs <= tol_abs and rel_l2 <= tol_rel, (name, max_abs, rel_l2)
+        assert lse_err <= tol_abs, (name, lse_err)
+        return AttnStats(**kw)
+    # against the rotated keys held in bf16 (the stated cache reading): the full bar
+    dc = np.abs(out - o_cached)[sel]
+    kw["max_abs_cached_keys"] = float(dc.max())
+    kw["rel_l2_cached_keys"] = float(np.linalg.norm((out - o_cached)[sel])
+                                     / max(np.linalg.norm(o_cached[sel]), 1e-30))
+    # against exact keys: every element and every LSE within its rounding bound
+    ratio = float((diff[sel] / bo[sel]).max())
+    lratio = float((lerr[lsel] / bl[lsel]).max())
+    kw.update(bound_ratio_max=ratio, lse_bound_ratio_max=lratio)
+    record("attention", name, **kw)
+    assert kw["max_abs_cached_keys"] <= tol_abs and kw["rel_l2_cached_keys"] <= tol_rel, (name, kw)
+    assert rel_l2 <= tol_rel, (name, "rel-L2 against exact keys", kw)
+    assert ratio <= 1.0, (name, "output beyond its rounding bound", kw)
+    assert lratio <= 1.0, (name, "LSE beyond its rounding bound", kw)
+    return AttnStats(**kw)
+
+
+def check_attention(run: DeviceRun, q, k, v, units, out=None, lse=None, name=None):
+    """GPU attention of ``units`` against the oracle on the GPU's own granule
+    lists (the acceptance rule is in the module docstring)."""
+    import dataclasses
     w = run.w
     p = R.params_from_workload(w)
     gr, gc = run.np("granules"), run.np("granule_count")
-    o_ref, l_ref = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc, p,
-                                  t0=w.q_pos0 // w.chunk_size, units=units)
+    t0 = w.q_pos0 // w.chunk_size
+    o_ref, l_ref = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc, p, t0=t0, units=units)
     out = run.np("out") if out is None else out
     lse = run.np("lse") if lse is None else lse
-    res = compare_out(w, out, lse, o_ref, l_ref, q=q, k=k)
+    o_c = l_c = bo = bl = None
     if w.dtype == "bf16":
-        import dataclasses
-        o_x, _ = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc,
-                                dataclasses.replace(p, key_cache="f64"),
-                                t0=w.q_pos0 // w.chunk_size, units=units)
-        sel = ~np.isnan(o_x)
-        rel = float(np.linalg.norm(out[sel] - o_x[sel]) / max(np.linalg.norm(o_x[sel]), 1e-30))
-        assert rel <= TOL["bf16"][1], ("rel-L2 against exact keys", rel)
-    return res
+        o_c, l_c = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc,
+                                  dataclasses.replace(p, key_cache="bf16"), t0=t0, units=units)
+        bo = np.full(o_ref.shape, np.nan)
+        bl = np.full(l_ref.shape, np.nan)
+        for (b, kvh, t) in units:
+            gl = np.asarray(gr[b, kvh, t - t0, : int(gc[b, kvh, t - t0])], np.int64)
+            tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
+            qpos = R.unit_queries(t, w.q_pos0, w.n_q, p.C)
+            mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
+            _unit_bounds(w, p, q, k, v, tok, qpos, mask, b, kvh, o_ref, l_ref, bo, bl)
+    return _compare(w, name or w.name, out, lse, o_ref, l_ref, o_c, l_c, bo, bl)
 
 
-def lse_tolerance(w, q, k):
-    """Per-row LSE bound [B,Hq,n_q] (see the module docstring)."""
-    if w.dtype != "bf16":
-        return np.full(q.shape[:3], 1e-5)
-    scale = 1.0 / math.sqrt(w.head_dim)
-    qn = np.linalg.norm(q.astype(np.float64), axis=-1)                    # [B,Hq,n_q]
-    kmax = np.linalg.norm(k[:, :, : w.n_ctx].astype(np.float64), axis=-1).max(axis=-1)  # [B,Hkv]
-    kmax = np.repeat(kmax, w.group_ratio, axis=1)[:, :, None]
-    return 2.0 ** -8 * scale * qn * kmax + 1e-5
-
-
-def compare_out(w, out, lse, o_ref, l_ref, q=None, k=None):
-    sel = ~np.isnan(o_ref)
-    assert sel.any()
-    diff = np.abs(out[sel] - o_ref[sel])
-    max_abs = float(diff.max())
-    rel_l2 = float(np.linalg.norm(out[sel] - o_ref[sel]) / max(np.linalg.norm(o_ref[sel]), 1e-30))
-    lsel = ~np.isnan(l_ref)
-    lerr = np.abs(lse[lsel] - l_ref[lsel])
-    tol_abs, tol_rel = TOL[w.dtype]
-    assert max_abs <= tol_abs and rel_l2 <= tol_rel, (max_abs, rel_l2)
-    if q is not None:
-        ltol = lse_tolerance(w, q, k)[lsel]
-        assert np.all(lerr <= ltol), float((lerr / ltol).max())
-    else:
-        assert lerr.max() <= tol_abs, float(lerr.max())
-    return max_abs, rel_l2, float(lerr.max())
+def check_dense(w, out, lse, q, k, v, heads=None, q_index=None, name=None):
+    """GPU dense causal attention (Eq. 1) against the oracle's, on the rows
+    of ``heads`` x ``q_index`` (all when None); same acceptance rule."""
+    import dataclasses
+    p = R.params_from_workload(w)
+    o_ref, l_ref = R.dense_causal(q, w.q_pos0, w.n_q, k, v, p, heads=heads, q_index=q_index)
+    o_c = l_c = bo = bl = None
+    if w.dtype == "bf16":
+        o_c, l_c = R.dense_causal(q, w.q_pos0, w.n_q, k, v, dataclasses.replace(p, key_cache="bf16"),
+                                  heads=heads, q_index=q_index)
+        bo = np.full(o_ref.shape, np.nan)
+        bl = np.full(l_ref.shape, np.nan)
+        qi = np.arange(w.n_q) if q_index is None else np.asarray(q_index)
+        qpos = w.q_pos0 + qi
+        nk = int(qpos.max()) + 1
+        tok = np.arange(nk)
+        mask = tok[None, :] <= qpos[:, None]
+        G = p.Hq // p.Hkv
+        for b in range(w.batch):
+            for kvh in range(p.Hkv):
+                if heads is not None and not any(h // G == kvh for h in heads):
+                    continue
+                _unit_bounds(w, p, q, k, v, tok, qpos, mask, b, kvh, o_ref, l_ref, bo, bl)
+        if heads is not None:
+            keep = np.zeros(p.Hq, bool)
+            keep[list(heads)] = True
+            bo[:, ~keep] = np.nan
+            bl[:, ~keep] = np.nan
+    return _compare(w, name or (w.name + ":dense"), out, lse, o_ref, l_ref, o_c, l_c, bo, bl)
 
 
 def all_units(w):

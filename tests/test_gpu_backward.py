@@ -3,10 +3,18 @@
 
 Tolerance: the products take bf16 operands (scaled rotated queries, keys,
 values, dO, P and dS are each rounded once to 8 significant bits, relative
-error <= 2^-9) with f32 accumulation, so each gradient element carries a
-relative error of a few 2^-9 on its largest terms; over whole tensors the
-rel-L2 error must stay <= 1.5e-2 and every element within 3e-2 of the
-tensor's largest magnitude.  Keys no query sees get exactly zero.
+error <= u = 2^-8) with f32 accumulation, so each gradient element carries
+an error of a few u of the magnitude of its terms.  Two bars:
+* rel-L2 <= 1e-2 per tensor;
+* elementwise, |gpu - oracle| <= 16 u M + 1e-6 max|M|, where M is the
+  magnitude of the element's exact formula (``_magnitudes``):
+  M(dv_j) = sum_i P_ij |dO_i|, M(dk~_j) = s sum_i P_ij (|dP_ij| + |D_i|) |q~_i|,
+  M(dq~_i) = s sum_j P_ij (|dP_ij| + |D_i|) |k~_j|, carried through R^T as
+  |cos| M_a + |sin| M_b per pair.  A CPU emulation of the kernel's roundings
+  (bf16 logits' operands, P, dS and the forward output that D reads) reaches
+  8.8 u on dq and 2.5 u on dk and dv (rel-L2 3e-3), so 16 u leaves a
+  factor of about 2.
+Keys no query sees get exactly zero.
 """
 import numpy as np
 import pytest
@@ -19,8 +27,8 @@ from tests.random_configs import N_CONFIGS, random_workload
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 1.5e-2
-MAX_REL = 3e-2
+REL_L2 = 1e-2
+ELEM = 16 * 2.0 ** -8
 
 CASES = {
     "qwen3_ragged": W.QWEN3_PREFILL.scaled(n_ctx=1011, kv_cap=1024, n_q=1011, planted=8),
@@ -33,14 +41,58 @@ CASES = {
 }
 
 
-def _compare(name, got, ref, unseen=None):
-    g = got.cpu().numpy().astype(np.float64)
+def _magnitudes(w, q, k, v, gr, gc, do, units, t0):
+    """M of the module docstring for dq [B,Hq,n_q,d], dk, dv [B,Hkv,kv_cap,d]
+    (summed over ``units``; rows outside them stay 0)."""
+    p = R.params_from_workload(w)
+    G = p.Hq // p.Hkv
+    sc = p.softmax_scale
+    h2 = p.d // 2
+    inv = R.rope_inv_freq(p.d, p.theta)
+
+    def through_rt(m, pos):
+        ang = np.multiply.outer(R.rope_position(pos, p.period), inv)
+        c, s = np.abs(np.cos(ang)), np.abs(np.sin(ang))
+        return np.concatenate([c * m[:, :h2] + s * m[:, h2:], s * m[:, :h2] + c * m[:, h2:]], axis=1)
+
+    mq = np.zeros(q.shape)
+    mk = np.zeros(k.shape)
+    mv = np.zeros(k.shape)
+    for (b, kvh, t) in units:
+        gl = np.asarray(gr[b, kvh, t - t0, : int(gc[b, kvh, t - t0])], np.int64)
+        tok = (gl[:, None] * p.gs + np.arange(p.gs)[None, :]).reshape(-1)
+        qpos = R.unit_queries(t, w.q_pos0, w.n_q, p.C)
+        qi = qpos - w.q_pos0
+        mask = (tok[None, :] < t * p.C) | (tok[None, :] <= qpos[:, None])
+        kk = R.rope(np.asarray(k[b, kvh][tok], np.float64), tok, p.theta, p.period)
+        vv = np.asarray(v[b, kvh][tok], np.float64)
+        mkk = np.zeros(kk.shape)
+        for hl in range(G):
+            h = kvh * G + hl
+            rows = R.rope(np.asarray(q[b, h, qi], np.float64), qpos, p.theta, p.period)
+            s = np.where(mask, sc * (rows @ kk.T), -np.inf)
+            pr = np.exp(s - s.max(axis=1, keepdims=True))
+            pr /= pr.sum(axis=1, keepdims=True)
+            g = do[b, h, qi]
+            dp = g @ vv.T
+            dd = (g * (pr @ vv)).sum(axis=1, keepdims=True)
+            a = pr * (np.abs(dp) + np.abs(dd))
+            mv[b, kvh][tok] += pr.T @ np.abs(g)
+            mq[b, h, qi] = through_rt(sc * (a @ np.abs(kk)), qpos)
+            mkk += sc * (a.T @ np.abs(rows))
+        mk[b, kvh][tok] += through_rt(mkk, tok)
+    return mq, mk, mv
+
+
+def _compare(name, got, ref, mag, unseen=None):
+    g = got.cpu().numpy().astype(np.float64) if hasattr(got, "cpu") else np.asarray(got, np.float64)
     err = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    mx = np.abs(g - ref).max() / max(np.abs(ref).max(), 1e-30)
-    assert err <= REL_L2 and mx <= MAX_REL, (name, err, mx)
+    bound = ELEM * mag + 1e-6 * np.abs(mag).max()
+    ratio = float((np.abs(g - ref) / bound).max())
+    assert err <= REL_L2 and ratio <= 1.0, (name, err, ratio)
     if unseen is not None:
         assert np.all(g[unseen] == 0), (name, "nonzero for a key no query sees")
-    return err, mx
+    return round(float(err), 5), round(ratio, 4)
 
 
 def _unseen_keys(w, gr, gc):
@@ -78,8 +130,11 @@ def _check_backward(case, w, seed=0):
     rdq, rdk, rdv = R.attend_backward(q, w.q_pos0, w.n_q, k, v, gr, gc, do.astype(np.float64), p,
                                       t0=w.q_pos0 // w.chunk_size)
     unseen = _unseen_keys(w, gr, gc)
-    res = [_compare("dq", dq, rdq), _compare("dk", dk, rdk, unseen), _compare("dv", dv, rdv, unseen)]
-    print(f"[gpu] backward {case}: (rel_l2, max/max) dq {res[0]}, dk {res[1]}, dv {res[2]}", flush=True)
+    mq, mk, mv = _magnitudes(w, q, k, v, gr, gc, do.astype(np.float64), P.all_units(w), w.q_pos0 // w.chunk_size)
+    res = [_compare("dq", dq, rdq, mq), _compare("dk", dk, rdk, mk, unseen),
+           _compare("dv", dv, rdv, mv, unseen)]
+    print(f"[gpu] backward {case}: (rel_l2, max |err| / bound) dq {res[0]}, dk {res[1]}, dv {res[2]}",
+          flush=True)
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
@@ -168,6 +223,7 @@ def test_backward_qwen3_32k_sampled():
     p = R.params_from_workload(w)
     rdq, rdk, rdv = R.attend_backward(q, w.q_pos0, w.n_q, k, v, gr, gc, do.astype(np.float64), p,
                                       t0=0, units=units)
+    mq, mk, mv = _magnitudes(w, q, k, v, gr, gc, do.astype(np.float64), units, 0)
     G = w.n_q_heads // w.n_kv_heads
     C = w.chunk_size
     gs = w.group_size
@@ -178,12 +234,12 @@ def test_backward_qwen3_32k_sampled():
     tsel = [(b, h, g * gs + j) for (b, h, g) in picks for j in range(gs)]
     tb, th, tt = (torch.tensor([s[j] for s in tsel], device=dev) for j in range(3))
     ib, ih, it = (np.array([s[j] for s in tsel]) for j in range(3))
+    qb, qh, qq = (np.array([s[j] for s in qsel]) for j in range(3))
     res = []
-    for name, got, want in (("dq", got_q, want_q),
-                            ("dk", dk[tb, th, tt].cpu().numpy().astype(np.float64), rdk[ib, ih, it]),
-                            ("dv", dv[tb, th, tt].cpu().numpy().astype(np.float64), rdv[ib, ih, it])):
-        err = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
-        mx = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
-        res.append((name, round(float(err), 5), round(float(mx), 5)))
-        assert err <= REL_L2 and mx <= MAX_REL, (name, err, mx)
+    for name, got, want, mag in (("dq", got_q, want_q, mq[qb, qh, qq]),
+                                 ("dk", dk[tb, th, tt].cpu().numpy().astype(np.float64), rdk[ib, ih, it],
+                                  mk[ib, ih, it]),
+                                 ("dv", dv[tb, th, tt].cpu().numpy().astype(np.float64), rdv[ib, ih, it],
+                                  mv[ib, ih, it])):
+        res.append((name,) + _compare(name, got, want, mag))
     print(f"[gpu] backward qwen3 32k: {len(units)} units, {len(picks)} granules: {res}", flush=True)

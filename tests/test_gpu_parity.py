@@ -94,11 +94,9 @@ def test_full_coverage_equals_dense(dtype, d):
     assert same_out, "routed full coverage differs from dense"
     same_lse = bool(torch.equal(dlse, run.lse))
     assert same_lse, "routed full coverage LSE differs from dense"
-    p = R.params_from_workload(w)
     heads = [0, 5]
     qi = np.r_[0:70, 600:640, 1200:1280]
-    o_ref, l_ref = R.dense_causal(q, 0, w.n_q, k, v, p, heads=heads, q_index=qi)
-    P.compare_out(w, run.np("out"), run.np("lse"), o_ref, l_ref, q=q, k=k)
+    P.check_dense(w, run.np("out"), run.np("lse"), q, k, v, heads=heads, q_index=qi)
 
 
 def test_dense_causal_partial_queries():
@@ -110,9 +108,7 @@ def test_dense_causal_partial_queries():
     import torch
     H.dense_causal(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, run.out, run.lse, run.aws)
     torch.cuda.synchronize()
-    p = R.params_from_workload(w)
-    o_ref, l_ref = R.dense_causal(q, w.q_pos0, w.n_q, k, v, p)
-    P.compare_out(w, run.np("out"), run.np("lse"), o_ref, l_ref, q=q, k=k)
+    P.check_dense(w, run.np("out"), run.np("lse"), q, k, v)
 
 
 EDGE = {

@@ -69,7 +69,5 @@ def test_random_shape_dense_and_full_coverage(i):
     dlse = torch.full_like(run.lse, float("nan"))
     H.dense_causal(run.cfg, run.q, w.q_pos0, run.k_rot, run.v, dense, dlse, run.aws)
     torch.cuda.synchronize()
-    p = R.params_from_workload(w)
-    o_ref, l_ref = R.dense_causal(q, w.q_pos0, w.n_q, k, v, p)
-    P.compare_out(w, dense.float().cpu().numpy(), dlse.cpu().numpy(), o_ref, l_ref, q=q, k=k)
-    P.compare_out(w, run.np("out"), run.np("lse"), o_ref, l_ref, q=q, k=k)
+    P.check_dense(w, dense.float().cpu().numpy(), dlse.cpu().numpy(), q, k, v, name=f"random{i}:dense")
+    P.check_dense(w, run.np("out"), run.np("lse"), q, k, v, name=f"random{i}:full_coverage")
