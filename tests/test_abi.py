@@ -149,6 +149,36 @@ def test_bad_config_rejected(lib, over, status):
                           None, 0, None) == status
 
 
+@pytest.mark.parametrize("over,call", [
+    (dict(top_chunks=257), {}),                       # K_c <= 256
+    (dict(top_groups=257), {}),                       # K_g <= 256
+    (dict(n_q_heads=64, n_kv_heads=4), {}),           # C * G = 1024 rows > 512 per unit
+    (dict(top_chunks=256, group_size=2), {}),         # K_c * C / g_s = 8192 candidate groups > 4096
+    ({}, dict(q_pos0=4200 * 64, n_q=64, cap=4201 * 64)),  # 4189 middle chunks > 4096
+])
+def test_route_limits_rejected(lib, over, call):
+    """The shape limits hga_route documents in include/hga.h return
+    HGA_ERR_UNSUPPORTED before anything is read or launched."""
+    cfg = H.Config.from_workload(W.QWEN3_PREFILL, **over)
+    assert _route(lib, cfg, **call) == 2
+
+
+@pytest.mark.parametrize("over,cap,dtype,status", [
+    (dict(chunk_size=48, group_size=12), 4800, 1, 2),   # g_s not a power of two
+    ({}, 1 << 23, 1, 2),                               # bf16 slab kv_cap * d * 2 = 2^31 bytes
+    ({}, (1 << 23) - 64, 1, "ok"),                     # just below: accepted by the size rule
+    ({}, 1 << 23, 0, "ok"),                            # f32 slabs are not buffer-addressed
+])
+def test_attend_limits_rejected(lib, over, cap, dtype, status):
+    """hga_attend's documented limits: g_s a power of two, bf16 (sequence, KV
+    head) slabs below 2^31 bytes.  Accepted shapes fail later, on the null
+    output pointer (HGA_ERR_INVALID_ARGUMENT); nothing is ever launched."""
+    cfg = H.Config.from_workload(W.QWEN3_PREFILL, **over)
+    rc = lib.hga_attend(ctypes.byref(cfg.c()), dtype, 1, 16, 0, 64, 16, 16, cap, 16, 16, None, None,
+                        None, 0, None)
+    assert rc == (1 if status == "ok" else status)
+
+
 def test_bad_arguments_rejected(lib):
     cfg = H.Config.from_workload(W.QWEN3_PREFILL)
     assert _route(lib, cfg, dtype=7) == 1

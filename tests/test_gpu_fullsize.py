@@ -21,11 +21,13 @@ def test_qwen3_prefill_32k_full():
     P.check_summaries(run, k, slabs=[(0, 0), (0, 3)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
-    exact, near = P.compare_routes(run, orc, units)
+    exact, near = P.compare_routes(run, orc, units, name="fullsize:" + w.name)
     print(f"[gpu] qwen3 32k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
     assert near <= len(units) // 50
-    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 12))
-    print(f"[gpu] qwen3 32k attention: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
+    last = w.n_q // w.chunk_size - 1
+    att = sorted(set(P.sample_units(w, 64)) | {(0, h, last) for h in range(w.n_kv_heads)})
+    m, r, l = P.check_attention(run, q, k, v, att, name="fullsize:" + w.name)
+    print(f"[gpu] qwen3 32k attention on {len(att)} units: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
 
 def test_smalllm_prefill_4k_full():
@@ -38,10 +40,10 @@ def test_smalllm_prefill_4k_full():
     P.check_summaries(run, k, slabs=[(0, 0), (3, 7)])
     units = P.all_units(w)
     orc = P.oracle_route(run, q, k, units)
-    exact, near = P.compare_routes(run, orc, units)
+    exact, near = P.compare_routes(run, orc, units, name="fullsize:" + w.name)
     print(f"[gpu] smalllm 4k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
     assert near <= len(units) // 50
-    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 24))
+    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 64), name="fullsize:" + w.name)
     print(f"[gpu] smalllm 4k attention: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
 
@@ -50,12 +52,14 @@ def test_decode_64k_full():
     q, k, v = P.make_inputs_parallel(w)
     print("[gpu] decode 64k: inputs ready", flush=True)
     run = P.DeviceRun(w, q, k, v)
-    units = [(0, 0, 1024), (5, 2, 1024), (11, 1, 1024), (15, 3, 1024)]
-    P.check_summaries(run, k, slabs=[(b, h) for b, h, _ in units])
+    units = P.all_units(w)          # all 64 (sequence, KV head) units
+    P.check_summaries(run, k, slabs=[(0, 0), (5, 2), (11, 1), (15, 3)])
     orc = P.oracle_route(run, q, k, units)
-    exact, near = P.compare_routes(run, orc, units)
+    exact, near = P.compare_routes(run, orc, units, name="fullsize:" + w.name)
+    print(f"[gpu] decode 64k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
     assert exact + near == len(units)
-    P.check_attention(run, q, k, v, units)
+    m, r, l = P.check_attention(run, q, k, v, units, name="fullsize:" + w.name)
+    print(f"[gpu] decode 64k attention on {len(units)} units: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
 
 # "group_wrap64k": RoPE positions wrapped modulo 65536 (xllm-io page,
@@ -79,7 +83,12 @@ def test_host_tiered_128k_full(base):
     print(f"[gpu] host tier 128k {base}: {stats}", flush=True)
     same = bool(torch.equal(out, run.out))
     assert same, "host tier differs from the device-resident path"
-    units = [(0, 0, 2047), (0, 3, 1500), (0, 1, 700)]
+    # 32 units spread over the query chunks and KV heads, with the last chunk
+    nqc = w.n_q // w.chunk_size
+    units = sorted({(0, i % w.n_kv_heads, int(t)) for i, t in enumerate(np.linspace(11, nqc - 1, 32))}
+                   | {(0, 3, nqc - 1)})
     orc = P.oracle_route(run, q, k, units)
-    P.compare_routes(run, orc, units)
-    P.check_attention(run, q, k, v, units, out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+    exact, near = P.compare_routes(run, orc, units, name=f"fullsize:{base}")
+    print(f"[gpu] host tier 128k {base}: routes exact={exact} near_tie={near} of {len(units)}", flush=True)
+    P.check_attention(run, q, k, v, units, out=out.float().cpu().numpy(), lse=lse.cpu().numpy(),
+                      name=f"fullsize:{base}")

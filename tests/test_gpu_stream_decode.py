@@ -1,7 +1,9 @@
 """Streaming decode from the host tier (DecodeSession) against the
 device-resident path: every step's output and LSE bit for bit, the session's
 summaries and host store after the appends, with a roomy cache and with the
-smallest allowed one (evictions on every step)."""
+smallest allowed one (evictions on every step); and the routes and outputs
+of sampled steps against the oracle (the pages' "cache vs no cache" and
+"decode vs recompute" checks, xllm-io page, Tab. 7)."""
 import numpy as np
 import pytest
 
@@ -25,10 +27,10 @@ def _workload(**kw):
 
 
 def _reference(run, w, dev):
-    """Device-resident route + attend of every step's query."""
+    """Device-resident route + attend of every step's query (and its routes)."""
     import torch
     cfg = run.cfg
-    outs, lses = [], []
+    outs, lses, routes = [], [], []
     for s in range(w.n_q):
         pos = w.q_pos0 + s
         q = run.q[:, :, s:s + 1].contiguous()
@@ -42,8 +44,39 @@ def _reference(run, w, dev):
         H.attend(cfg, q, pos, run.k_rot, run.v, ro["granules"], ro["granule_count"], out, lse, ws)
         outs.append(out)
         lses.append(lse)
+        routes.append(ro)
     torch.cuda.synchronize()
-    return outs, lses
+    return outs, lses, routes
+
+
+class _StepRun:
+    """The arrays parity.compare_routes / check_attention read, for one
+    decode step (one query per sequence at position pos)."""
+
+    def __init__(self, w, pos, ro, out, lse):
+        self.w = w.scaled(q_pos0=pos, n_q=1, n_ctx=pos + 1)
+        self.arrays = {n: ro[n].cpu().numpy() for n in ("chunk_idx", "group_idx", "granules",
+                                                        "granule_count")}
+        self.arrays["out"] = out.float().cpu().numpy()
+        self.arrays["lse"] = lse.float().cpu().numpy()
+
+    def np(self, name):
+        return self.arrays[name]
+
+
+def _oracle_steps(w, q, k, v, routes, outs, lses, steps):
+    """The session's routes and outputs at the given steps against the
+    oracle (own summaries of the tokens up to each step's position, routes
+    of that one query, attention on the step's granule lists)."""
+    for s in steps:
+        pos = w.q_pos0 + s
+        run = _StepRun(w, pos, routes[s], outs[s], lses[s])
+        qs = np.ascontiguousarray(q[:, :, s:s + 1])
+        units = P.all_units(run.w)
+        orc = P.oracle_route(run, qs, k, units)
+        exact, near = P.compare_routes(run, orc, units, name=f"stream:{w.name}:step{s}")
+        assert exact + near == len(units)
+        P.check_attention(run, qs, k, v, units, name=f"stream:{w.name}:step{s}")
 
 
 def _session_run(run, w, cache_slots, dev, poison=False):
@@ -88,7 +121,7 @@ def _check_session(w, cache_slots, poison=False, seed=0):
     dev = torch.device("cuda:0")
     q, k, v = P.make_inputs_parallel(w, seed)
     run = P.DeviceRun(w, q, k, v, route=False, attend=False)
-    ref_out, ref_lse = _reference(run, w, dev)
+    ref_out, ref_lse, ref_routes = _reference(run, w, dev)
     outs, lses, stats, csum, gsum, store = _session_run(run, w, cache_slots, dev, poison=poison)
     bad = [s for s in range(w.n_q)
            if not (torch.equal(outs[s], ref_out[s]) and torch.equal(lses[s], ref_lse[s]))]
@@ -116,6 +149,13 @@ def _check_session(w, cache_slots, poison=False, seed=0):
     tok = (np.arange(ng)[:, None, None] * g + np.arange(g)[None, None, :]).repeat(2, axis=1)
     rows = sel[tok < end]
     assert torch.equal(got[:, :, rows], want[:, :, rows])
+    # the session's steps (bitwise the device path's) against the oracle:
+    # the first step, the step that closes the first chunk and the one after
+    # it, a middle one and the last
+    C = run.cfg.chunk_size
+    close = (C - 1 - w.q_pos0 % C) % C
+    steps = sorted({0, min(close, w.n_q - 1), min(close + 1, w.n_q - 1), w.n_q // 2, w.n_q - 1})
+    _oracle_steps(w, q, k, v, ref_routes, outs, lses, steps)
     return stats
 
 

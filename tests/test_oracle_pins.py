@@ -568,3 +568,58 @@ def test_cache_rounding_is_round_to_nearest_even():
     y = rng.standard_normal(1000) * 1e3
     np.testing.assert_array_equal(R.round_to_cache(y, "f32"), y.astype(np.float32).astype(np.float64))
     np.testing.assert_array_equal(R.round_to_cache(y, "f64"), y)
+
+
+def _eq2_by_arithmetic(n, C, gs, F, L, Kc, Kg):
+    """Eq. (2)'s count for a full prefill of n tokens, from the per-chunk
+    min() expressions of tests/golden/eq2_counts.json (no sets, no oracle)."""
+    total = 0
+    for t in range(n // C):
+        fixed = min(t, F + L)
+        mid = max(0, t - F - L)
+        routed = gs * min(Kg, (C // gs) * min(Kc, mid)) if Kg else C * min(Kc, mid)
+        total += C * (C * fixed + routed) + C * (C + 1) // 2
+    return total
+
+
+@pytest.mark.parametrize("case", _load("eq2_counts.json")["cases"], ids=lambda c: c["name"])
+def test_eq2_counts_at_the_workloads(case):
+    """Eq. (2) at the five benchmark workloads: the hand-derived counts of
+    tests/golden/eq2_counts.json equal (a) the per-chunk arithmetic,
+    (b) the count over the oracle's own visible sets (fixed windows, a
+    full-size routed selection, causal current chunk) at the full length, and
+    (c) the oracle's closed form; each stays below n (C + (F+L)C + B_route)."""
+    w = {x.name: x for x in W.ALL}[case["name"]]
+    p = R.params_from_workload(w)
+    assert (p.F, p.L, p.Kc, p.Kg, w.n_q, p.C, p.gs) == (case["F"], case["L"], case["Kc"], case["Kg"],
+                                                        case["n"], 64, 16)
+    assert _eq2_by_arithmetic(case["n"], 64, 16, case["F"], case["L"], case["Kc"], case["Kg"]) == case["count"]
+    r = p.groups_per_chunk
+    lists = {}
+    for t in range(case["n"] // p.C):
+        mids = R.middle_chunks(t, p.F, p.L)
+        # any selection of the right size gives the same count: take the
+        # highest-index middle chunks and the last groups of the candidates
+        sel = mids[len(mids) - min(p.Kc, len(mids)):]
+        cands = [m * r + g for m in sel for g in range(r)]
+        groups = cands[len(cands) - min(p.Kg, len(cands)):] if p.Kg else []
+        lists[t] = R.visible_granules(t, (t + 1) * p.C - 1, sel, groups, p)
+    assert R.visible_token_count(lists, 0, case["n"], p) == case["count"]
+    assert R.visible_token_count_closed_form(0, case["n"], p) == case["count"]
+    assert case["count"] <= R.eq2_bound(case["n"], p) == case["bound"]
+
+
+def test_eq2_decode_step_count():
+    """The decode step (one query at position 65536, the current chunk holding
+    only that token) sees 1 + (F+L)C + K_g g_s = 897 tokens (Eq. 2 for one
+    query)."""
+    fx = _load("eq2_counts.json")["decode"]
+    w = W.DECODE_64K
+    p = R.params_from_workload(w)
+    t = fx["pos"] // p.C
+    mids = R.middle_chunks(t, p.F, p.L)
+    sel = mids[: p.Kc]
+    groups = [m * p.groups_per_chunk + g for m in sel for g in range(p.groups_per_chunk)][: p.Kg]
+    gl = R.visible_granules(t, fx["pos"], sel, groups, p)
+    assert R.visible_token_count({t: gl}, fx["pos"], 1, p) == fx["count"]
+    assert R.visible_token_count_closed_form(fx["pos"], 1, p) == fx["count"]
