@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -32,26 +33,44 @@ def build(verbose: bool = False) -> str:
     return _build_lib(LIB, SOURCES, verbose)
 
 
-def _build_lib(lib: str, sources, verbose: bool) -> str:
-    tmp = lib + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
-           # packed f32 VALU forms stay off (hipcc forms them by itself otherwise)
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(HERE, "..", "include"),
-           "-o", tmp] + [os.path.join(CSRC, s) for s in sources]
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Wall", "-Wno-unused-function",
+            # packed f32 VALU forms stay off (hipcc forms them by itself otherwise)
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(HERE, "..", "include")]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
     if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, lib)
+
+
+def _build_lib(lib: str, sources, verbose: bool) -> str:
+    """Compile each source to an object (in parallel), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmpdir = tempfile.mkdtemp(prefix="hga_build_")
+    tmp = lib + f".tmp{os.getpid()}"
+    try:
+        objs = [os.path.join(tmpdir, s + ".o") for s in sources]
+        jobs = [[hipcc()] + _flags() + ["-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(sources, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, lib)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return lib
 
 

@@ -144,13 +144,13 @@ hga_status hga_route(const hga_config* cfg, hga_dtype dtype, int32_t batch, cons
   hga_status st = make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
   if (st != HGA_OK) return st;
   if (n_q == 0) return HGA_OK;  // nothing to route
+  if (!hga::route_supported(g)) return HGA_ERR_UNSUPPORTED;
   if (q_raw == nullptr || granules == nullptr || granule_count == nullptr)
     return HGA_ERR_INVALID_ARGUMENT;
   if (g.Kc > 0 && (chunk_sum == nullptr || chunk_idx == nullptr)) return HGA_ERR_INVALID_ARGUMENT;
   if (g.Kg > 0 && (group_sum == nullptr || group_idx == nullptr)) return HGA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q_raw) || !aligned16(chunk_sum) || !aligned16(group_sum) || !aligned16(workspace))
     return HGA_ERR_INVALID_ARGUMENT;
-  if (!hga::route_supported(g)) return HGA_ERR_UNSUPPORTED;
   const size_t need = hga::route_workspace(g);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   hipError_t e = hga::launch_route(g, q_raw, chunk_sum, group_sum, chunk_idx, group_idx, granules,
@@ -183,13 +183,13 @@ static hga_status attend_common(const hga_config* cfg, hga_dtype dtype, int32_t 
   hga_status st = make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
   if (st != HGA_OK) return st;
   if (n_q == 0) return HGA_OK;  // no queries
+  if (!hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
   if (q_raw == nullptr || k_rot == nullptr || v == nullptr || out == nullptr)
     return HGA_ERR_INVALID_ARGUMENT;
   if (!dense && (granules == nullptr || granule_count == nullptr)) return HGA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q_raw) || !aligned16(k_rot) || !aligned16(v) || !aligned16(out) ||
       !aligned16(workspace))
     return HGA_ERR_INVALID_ARGUMENT;
-  if (!hga::attend_supported(g)) return HGA_ERR_UNSUPPORTED;
   const size_t need = hga::attend_workspace(g, dense);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   hipError_t e = hga::launch_attend(g, q_raw, k_rot, v, granules, granule_count, dense, out, lse,
