@@ -7,7 +7,7 @@
 // chunks, with no summary tokens) and Eq. (1) (dense causal attention).
 //
 // bf16 path (attend_mfma_kernel): a workgroup holds NW waves, each with RB
-// blocks of 32 query rows of one unit (sequence, KV head, query chunk); a
+// (= 1) blocks of 32 query rows of one unit (sequence, KV head, query chunk); a
 // row is (query, head) with the G query heads of the KV head interleaved, so
 // all GQA heads share every K/V stage.  Stages of 64 gathered tokens are
 // staged in LDS (K row-major, V transposed, written as packed key pairs) and
@@ -33,12 +33,12 @@
 // f32 path (attend_f32_kernel): one wave per 64 rows, one lane per row,
 // K/V tiles in LDS, f32 vector ALU; exact to f32 rounding.
 #include <algorithm>
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "hga_device.h"
-
-#ifndef HGA_ATTEND_RB
-#define HGA_ATTEND_RB 1
-#endif
 
 namespace hga {
 namespace {
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
 }
 
 struct Plan {
-  int nw, rb, slices, splits, kps, rcap;
+  int nw, slices, splits, kps, rcap;
   bool decode;
   int64_t units;
 };
@@ -1060,17 +1060,31 @@ int64_t max_keys(const Geometry& g, bool dense) {
   return std::min<int64_t>(static_cast<int64_t>(g.gmax) * g.gs, causal);
 }
 
-// Compute units of the current device (queried once per device).
-int64_t device_cus() {
-  static int cus[16] = {};
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (cus[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  return dev;
+}
+
+// Compute units of the current device (queried once per device; the cache
+// entries are atomics, so concurrent first calls agree).
+constexpr int kMaxDevices = 64;
+int64_t device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  const int dev = current_device();
+  if (dev >= kMaxDevices) {
     int n = 0;
     (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    cus[dev] = n > 0 ? n : 256;
+    return n > 0 ? n : 256;
   }
-  return cus[dev];
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    v = n > 0 ? n : 256;
+    cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
@@ -1079,7 +1093,6 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
   // Rows of the largest unit: a query chunk holds at most min(C, n_q) queries.
   const int64_t rows = std::min<int64_t>(g.C, g.n_q) * static_cast<int64_t>(g.G);
   pl.rcap = static_cast<int>(rows);
-  pl.rb = 1;
   pl.decode = false;
   if (g.bf16 && allow_split && rows <= kDecRows) {
     // decode kernel: kDecKeys keys per item
@@ -1093,13 +1106,10 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
     return pl;
   }
   if (g.bf16) {
-    const int64_t blocks = (rows + 31) / 32;
-    pl.rb = blocks >= 2 * HGA_ATTEND_RB ? HGA_ATTEND_RB : 1;
-    const int64_t wblocks = (blocks + pl.rb - 1) / pl.rb;  // waves needed
+    const int64_t wblocks = (rows + 31) / 32;  // waves needed
     // Always 8 waves: the LDS stages hold one workgroup per CU, and waves
     // without rows (few-row units such as decode) still share the loads.
-    const int maxw = pl.rb == 2 ? 4 : 8;
-    pl.nw = maxw;
+    pl.nw = 8;
     pl.slices = static_cast<int>((wblocks + pl.nw - 1) / pl.nw);
   } else {
     pl.nw = 1;
@@ -1138,20 +1148,30 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
 
 // Workgroups that fit on the device at once for kernel k (a multiple of 8,
 // so that blockIdx.x and every bx it takes sit on the same XCD), at most n.
+// Cached per (device, kernel, block size) under a lock.
 template <typename Kernel>
 unsigned resident_grid(Kernel k, int threads, int64_t n) {
-  static int slots[16] = {};  // per device, computed once
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (slots[dev] == 0) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int>, int> slots;
+  const int dev = current_device();
+  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(k), threads);
+  int v = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = slots.find(key);
+    if (it != slots.end()) v = it->second;
+  }
+  if (v == 0) {
     int cus = 0, occ = 0;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), threads, 0);
-    int v = (cus > 0 ? cus : 8) * (occ > 0 ? occ : 1);
+    v = (cus > 0 ? cus : 8) * (occ > 0 ? occ : 1);
     v -= v % 8;
-    slots[dev] = v >= 8 ? v : 8;
+    if (v < 8) v = 8;
+    std::lock_guard<std::mutex> lock(mu);
+    slots[key] = v;
   }
-  return static_cast<unsigned>(n < slots[dev] ? n : slots[dev]);
+  return static_cast<unsigned>(n < v ? n : v);
 }
 
 template <int D, int RB, bool POOL>
@@ -1189,15 +1209,7 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
   p.nblocks = groups * 8 * p.per_unit;
   const unsigned grid = static_cast<unsigned>(p.nblocks);
   if (g.bf16) {
-    if constexpr (HGA_ATTEND_RB == 2) {
-      if (pl.rb == 2) {
-        launch_mfma_pool<D, 2>(pl.nw, p.nblocks, stream, p);
-      } else {
-        launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
-      }
-    } else {
-      launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
-    }
+    launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
   } else {
     hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(64), 0, stream, p);
   }

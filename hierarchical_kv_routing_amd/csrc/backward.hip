@@ -48,9 +48,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRowsWave = 32;   // rows per wave in dq_kernel (two 16-row blocks)
 constexpr int kStage = 32;      // keys (dq_kernel) or rows (dkv_kernel) per LDS stage
 constexpr int kKeysWG = 128;    // keys per dkv_kernel workgroup (four waves of 32)
-#ifndef HGA_DKV_KT
-#define HGA_DKV_KT 1
-#endif
+constexpr int kDkvKT = 1;        // 16-key tiles per dkv_kernel wave
 constexpr int kNoRow = -0x7fffffff - 1;  // query offset of a stage row that is not the unit's
 
 struct BwdParams {
@@ -409,7 +407,7 @@ struct DkvStage {
 
 // KT key tiles of 16 per wave, 128 / (16 KT) waves per workgroup; two stage
 // buffers.
-constexpr int kDkvThreads = kKeysWG / (16 * HGA_DKV_KT) * 64;
+constexpr int kDkvThreads = kKeysWG / (16 * kDkvKT) * 64;
 template <int D, int KT>
 __global__ __launch_bounds__(kDkvThreads) void dkv_kernel(BwdParams p) {
   using S = DkvStage<D>;
@@ -792,7 +790,7 @@ hipError_t launch_backward_d(const Geometry& g, BwdParams& p, hipStream_t stream
   hipLaunchKernelGGL(scatter_kernel, dim3(eg), dim3(256), 0, stream, p);
   const int64_t units8 = (p.units + 7) / 8 * 8;
   hipLaunchKernelGGL((dq_kernel<D>), dim3(static_cast<unsigned>(units8 * p.nslice)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((dkv_kernel<D, HGA_DKV_KT>), dim3(static_cast<unsigned>(units8 * p.nkb)),
+  hipLaunchKernelGGL((dkv_kernel<D, kDkvKT>), dim3(static_cast<unsigned>(units8 * p.nkb)),
                      dim3(kDkvThreads), 0, stream, p);
   const int64_t tblocks = (p.kv_cap + 15) / 16;
   hipLaunchKernelGGL((reduce_kernel<D>), dim3(static_cast<unsigned>(slabs * tblocks)), dim3(1024), 0, stream, p);
