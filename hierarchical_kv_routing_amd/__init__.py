@@ -35,7 +35,8 @@ ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_b
                "hga_decode_session_buffer_bytes", "hga_decode_session_create",
                "hga_decode_session_destroy", "hga_decode_session_append",
                "hga_decode_session_step", "hga_attend_backward_workspace_bytes",
-               "hga_attend_backward", "hga_status_string", "hga_last_hip_error")
+               "hga_attend_backward", "hga_attend_noalloc", "hga_attend_noalloc_max_scratch_bytes",
+               "hga_status_string", "hga_last_hip_error")
 
 
 class HGAError(RuntimeError):
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
         "hga_attend_workspace_bytes": (SZ, [CP, I32, I64, I64]),
         "hga_attend": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P, SZ, P]),
         "hga_dense_causal": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, SZ, P]),
+        "hga_attend_noalloc": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P]),
+        "hga_attend_noalloc_max_scratch_bytes": (SZ, []),
         "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64, I64,
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
@@ -289,6 +292,32 @@ def attend(cfg: Config, q, q_pos0: int, k_rot, v, granules, granule_count, out, 
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(q, stream))
     _check(st, "hga_attend")
+
+
+def attend_noalloc(cfg: Config, q, q_pos0: int, k_rot, v, granules, granule_count, out, lse=None,
+                   stream=None):
+    """hga_attend with the library's static device scratch instead of a
+    workspace (allocates nothing; calls on one device must not overlap)."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    kv_cap = k_rot.shape[2]
+    nqc = cfg.n_query_chunks(q_pos0, n_q)
+    _dev(q, "q")
+    _dev(k_rot, "k_rot", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(v, "v", (B, cfg.n_kv_heads, kv_cap, d), q.dtype)
+    _dev(granules, "granules", (B, cfg.n_kv_heads, nqc, max_granules(cfg)), torch.int32)
+    _dev(granule_count, "granule_count", (B, cfg.n_kv_heads, nqc), torch.int32)
+    _dev(out, "out", q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, n_q), torch.float32)
+    st = lib().hga_attend_noalloc(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), q_pos0, n_q, k_rot.data_ptr(),
+        v.data_ptr(), kv_cap, granules.data_ptr(), granule_count.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q, stream))
+    _check(st, "hga_attend_noalloc")
+
+
+def attend_noalloc_max_scratch_bytes() -> int:
+    return int(lib().hga_attend_noalloc_max_scratch_bytes())
 
 
 def dense_causal(cfg: Config, q, q_pos0: int, k_rot, v, out, lse=None, workspace=None, stream=None):

@@ -178,7 +178,8 @@ static hga_status attend_common(const hga_config* cfg, hga_dtype dtype, int32_t 
                                 const void* q_raw, int64_t q_pos0, int64_t n_q, const void* k_rot,
                                 const void* v, int64_t kv_cap, const int32_t* granules,
                                 const int32_t* granule_count, bool dense, void* out, float* lse,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                bool static_scratch = false) {
   hga::Geometry g;
   hga_status st = make_geometry(cfg, dtype, batch, kv_cap, q_pos0, n_q, g);
   if (st != HGA_OK) return st;
@@ -191,11 +192,31 @@ static hga_status attend_common(const hga_config* cfg, hga_dtype dtype, int32_t 
       !aligned16(workspace))
     return HGA_ERR_INVALID_ARGUMENT;
   const size_t need = hga::attend_workspace(g, dense);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (static_scratch) {
+    // the library's static scratch replaces the caller's workspace
+    if (need > hga::kNoAllocScratchBytes) return HGA_ERR_WORKSPACE_TOO_SMALL;
+    workspace = nullptr;
+    if (need > 0) {
+      const hipError_t e = hga::attend_noalloc_scratch(&workspace);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return HGA_ERR_WORKSPACE_TOO_SMALL;
+  }
   hipError_t e = hga::launch_attend(g, q_raw, k_rot, v, granules, granule_count, dense, out, lse,
                                     workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? HGA_OK : hip_fail(e);
 }
+
+hga_status hga_attend_noalloc(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                              const void* q_raw, int64_t q_pos0, int64_t n_q, const void* k_rot,
+                              const void* v, int64_t kv_cap, const int32_t* granules,
+                              const int32_t* granule_count, void* out, float* lse, void* stream) {
+  return attend_common(cfg, dtype, batch, q_raw, q_pos0, n_q, k_rot, v, kv_cap, granules,
+                       granule_count, false, out, lse, nullptr, 0, stream, true);
+}
+
+size_t hga_attend_noalloc_max_scratch_bytes(void) { return hga::kNoAllocScratchBytes; }
 
 hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch, const void* q_raw,
                       int64_t q_pos0, int64_t n_q, const void* k_rot, const void* v, int64_t kv_cap,

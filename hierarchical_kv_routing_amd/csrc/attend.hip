@@ -40,6 +40,13 @@
 
 #include "hga_device.h"
 
+// Scratch of hga_attend_noalloc (the split-key partials of few-unit calls),
+// for callers that cannot allocate device memory.  Each device the library
+// runs on holds its own copy until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress returns for the current
+// device (attend_noalloc_scratch), never through the name.
+static __device__ __align__(256) char scratch[hga::kNoAllocScratchBytes];
+
 namespace hga {
 namespace {
 
@@ -1286,6 +1293,26 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
   p.scale_log2 = g.scale * kLog2e;
   p.rope = g.rope;
   return g.d == 128 ? launch_attend_d<128>(g, p, pl, stream) : launch_attend_d<64>(g, p, pl, stream);
+}
+
+hipError_t attend_noalloc_scratch(void** ptr) {
+  // Resolved once per device, with that device current; the array's own
+  // name is a host-side stand-in, not its device address.
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  addr[dev] = p;
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace hga

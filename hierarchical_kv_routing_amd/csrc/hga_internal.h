@@ -71,6 +71,10 @@ struct AttendExtra {
 constexpr int kAttendTable = 2048;
 
 bool attend_supported(const Geometry& g);
+// Bytes of the static device scratch of hga_attend_noalloc, and its address
+// on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+hipError_t attend_noalloc_scratch(void** ptr);
 size_t attend_workspace(const Geometry& g, bool dense, bool allow_split = true);
 hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, const void* v,
                          const int32_t* granules, const int32_t* granule_count, bool dense,

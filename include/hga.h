@@ -44,9 +44,11 @@
  * routing keep absolute positions.
  *
  * Ownership: the caller owns every buffer and allocates it; the library never
- * allocates device memory and keeps no mutable global state apart from a
- * per-thread last-HIP-error code.  All device pointers must be 16-byte
- * aligned device (or managed) memory.
+ * allocates device memory.  Its global state is a per-thread last-HIP-error
+ * code, device properties cached once per device, and the static device
+ * scratch of hga_attend_noalloc (allocated with the code object, one copy
+ * per device).  All device pointers must be 16-byte aligned device (or
+ * managed) memory.
  *
  * Asynchrony: every entry point enqueues work on `stream` (a hipStream_t,
  * NULL = the default stream) and returns without synchronising, except
@@ -194,6 +196,30 @@ hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                       const int32_t* granules, const int32_t* granule_count,
                       void* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hga_attend_noalloc -- hga_attend without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments (minus
+ * the workspace), checks, kernels and outputs (bitwise) as hga_attend.
+ * The scratch hga_attend would take from its workspace (the split-key
+ * partials of calls with few units, e.g. decode) lives instead in a static
+ * device array of hga_attend_noalloc_max_scratch_bytes() bytes (16 MiB) that
+ * the library holds on each device it runs on until the process ends.  A
+ * call that needs more (hga_attend_workspace_bytes above that) returns
+ * HGA_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.  The call allocates
+ * nothing.  Every call on a device shares that device's array: calls that
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller; nothing in the array needs clearing between
+ * calls.
+ */
+hga_status hga_attend_noalloc(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                              const void* q_raw, int64_t q_pos0, int64_t n_q,
+                              const void* k_rot, const void* v, int64_t kv_cap,
+                              const int32_t* granules, const int32_t* granule_count,
+                              void* out, float* lse, void* stream);
+
+size_t hga_attend_noalloc_max_scratch_bytes(void);
 
 /*
  * hga_dense_causal -- Eq. (1): every query i attends to all keys j <= i.

@@ -273,3 +273,18 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_attend_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """hga_attend_noalloc: a call whose split partials exceed the static
+    scratch (16 MiB) returns HGA_ERR_WORKSPACE_TOO_SMALL before any HIP call;
+    the usual argument checks come first."""
+    assert H.attend_noalloc_max_scratch_bytes() == 16 << 20
+    # 256 sequences x 4 KV heads of decode with 256 routed whole chunks:
+    # 1068 granules, 134 key splits per unit
+    cfg = H.Config.from_workload(W.DECODE_64K, n_q_heads=16, top_chunks=256, top_groups=0)
+    assert H.attend_workspace_bytes(cfg, 256, 20000, 1) > 16 << 20
+    c = ctypes.byref(cfg.c())
+    assert lib.hga_attend_noalloc(c, 1, 256, 16, 20000, 1, 16, 16, 20032, 16, 16, 16, None, None) == 3
+    assert lib.hga_attend_noalloc(c, 1, 256, None, 20000, 1, 16, 16, 20032, 16, 16, 16, None, None) == 1
+    assert lib.hga_attend_noalloc(c, 1, 256, 16, 20000, 0, 16, 16, 20032, 16, 16, 16, None, None) == 0
