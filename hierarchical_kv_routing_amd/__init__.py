@@ -36,6 +36,7 @@ ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_b
                "hga_decode_session_destroy", "hga_decode_session_append",
                "hga_decode_session_step", "hga_attend_backward_workspace_bytes",
                "hga_attend_backward", "hga_attend_noalloc", "hga_attend_noalloc_max_scratch_bytes",
+               "hga_decode_step_workspace_bytes", "hga_decode_step",
                "hga_status_string", "hga_last_hip_error")
 
 
@@ -132,6 +133,8 @@ def lib() -> ctypes.CDLL:
         "hga_dense_causal": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, SZ, P]),
         "hga_attend_noalloc": (I32, [CP, I32, I32, P, I64, I64, P, P, I64, P, P, P, P, P]),
         "hga_attend_noalloc_max_scratch_bytes": (SZ, []),
+        "hga_decode_step_workspace_bytes": (SZ, [CP, I32, I64]),
+        "hga_decode_step": (I32, [CP, I32, I32, P, I64, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64, I64,
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
@@ -318,6 +321,56 @@ def attend_noalloc(cfg: Config, q, q_pos0: int, k_rot, v, granules, granule_coun
 
 def attend_noalloc_max_scratch_bytes() -> int:
     return int(lib().hga_attend_noalloc_max_scratch_bytes())
+
+
+def decode_step_workspace_bytes(cfg: Config, batch: int, pos: int) -> int:
+    return int(lib().hga_decode_step_workspace_bytes(ctypes.byref(cfg.c()), batch, pos))
+
+
+def decode_step_workspace(cfg: Config, batch: int, pos: int, device):
+    """A workspace for hga_decode_step (no initial contents needed)."""
+    torch = _torch()
+    n = decode_step_workspace_bytes(cfg, batch, pos)
+    if n == 0:
+        raise HGAError("hga_decode_step does not support this shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_step(cfg: Config, q, pos: int, k_rot, v, chunk_sum, group_sum, out, lse=None,
+                lists=None, workspace=None, stream=None):
+    """One decode step (query of every sequence at position pos) in two
+    launches: routing, gather and attention.  ``lists`` (optional): dict with
+    chunk_idx, group_idx, granules, granule_count as route_outputs(cfg, B,
+    pos, 1) allocates them."""
+    torch = _torch()
+    B, Hq, n_q, d = q.shape
+    if n_q != 1:
+        raise HGAError("decode_step takes one query per sequence")
+    kv_cap = k_rot.shape[2]
+    Hkv = cfg.n_kv_heads
+    _dev(q, "q")
+    _dev(k_rot, "k_rot", (B, Hkv, kv_cap, d), q.dtype)
+    _dev(v, "v", (B, Hkv, kv_cap, d), q.dtype)
+    _dev(chunk_sum, "chunk_sum", (B, Hkv, kv_cap // cfg.chunk_size, d), torch.float32)
+    _dev(group_sum, "group_sum", (B, Hkv, kv_cap // cfg.group_size, d), torch.float32)
+    _dev(out, "out", q.shape, q.dtype)
+    _dev(lse, "lse", (B, Hq, 1), torch.float32)
+    _dev(workspace, "workspace")
+    ptr = lambda name: lists[name].data_ptr() if lists is not None else None  # noqa: E731
+    if lists is not None:
+        _dev(lists["chunk_idx"], "chunk_idx", (B, Hkv, 1, max(cfg.top_chunks, 1)), torch.int32)
+        _dev(lists["group_idx"], "group_idx", (B, Hkv, 1, max(cfg.top_groups, 1)), torch.int32)
+        _dev(lists["granules"], "granules", (B, Hkv, 1, max_granules(cfg)), torch.int32)
+        _dev(lists["granule_count"], "granule_count", (B, Hkv, 1), torch.int32)
+    st = lib().hga_decode_step(
+        ctypes.byref(cfg.c()), _dtype_code(q), B, q.data_ptr(), pos, k_rot.data_ptr(), v.data_ptr(),
+        kv_cap, chunk_sum.data_ptr(), group_sum.data_ptr() if group_sum is not None else None,
+        ptr("chunk_idx"), ptr("group_idx"), ptr("granules"), ptr("granule_count"),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(q, stream))
+    _check(st, "hga_decode_step")
 
 
 def dense_causal(cfg: Config, q, q_pos0: int, k_rot, v, out, lse=None, workspace=None, stream=None):

@@ -13,7 +13,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhga.so")
-SOURCES = ["summarize.hip", "route.hip", "attend.hip", "backward.hip", "api.cpp", "host_tier.cpp"]
+SOURCES = ["summarize.hip", "route.hip", "attend.hip", "decode.hip", "backward.hip", "api.cpp",
+           "host_tier.cpp"]
 PEAK_LIB = os.path.join(HERE, "libhga_peak.so")   # roofline microbenchmarks (bench.py)
 PEAK_SOURCES = ["peak.hip"]
 ARCH = "gfx950"

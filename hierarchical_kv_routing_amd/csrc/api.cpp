@@ -1,6 +1,7 @@
 // C ABI of the routed exact-token attention library: argument validation,
 // call geometry, workspace sizing and kernel dispatch.  Every check runs on
 // the host before anything is enqueued; on an error nothing is enqueued.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -11,6 +12,33 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 }  // namespace
+
+int hga::current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  return dev;
+}
+
+// Compute units of the current device, queried once per device (the cache
+// entries are atomics, so concurrent first calls agree).
+int64_t hga::device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  const int dev = current_device();
+  if (dev >= kMaxDevices) {
+    int n = 0;
+    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    return n > 0 ? n : 256;
+  }
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    v = n > 0 ? n : 256;
+    cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 hga_status hga::hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -217,6 +245,44 @@ hga_status hga_attend_noalloc(const hga_config* cfg, hga_dtype dtype, int32_t ba
 }
 
 size_t hga_attend_noalloc_max_scratch_bytes(void) { return hga::kNoAllocScratchBytes; }
+
+size_t hga_decode_step_workspace_bytes(const hga_config* cfg, int32_t batch, int64_t pos) {
+  hga::Geometry g;
+  if (cfg == nullptr || cfg->chunk_size <= 0 || pos < 0) return 0;
+  const int64_t cap = (pos / cfg->chunk_size + 1) * cfg->chunk_size;
+  if (make_geometry(cfg, HGA_BF16, batch, cap, pos, 1, g) != HGA_OK) return 0;
+  return hga::decode_step_workspace(g);
+}
+
+hga_status hga_decode_step(const hga_config* cfg, hga_dtype dtype, int32_t batch, const void* q_raw,
+                           int64_t pos, const void* k_rot, const void* v, int64_t kv_cap,
+                           const float* chunk_sum, const float* group_sum, int32_t* chunk_idx,
+                           int32_t* group_idx, int32_t* granules, int32_t* granule_count,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  hga::Geometry g;
+  hga_status st = make_geometry(cfg, dtype, batch, kv_cap, pos, 1, g);
+  if (st != HGA_OK) return st;
+  if (!hga::decode_step_supported(g)) return HGA_ERR_UNSUPPORTED;
+  if (q_raw == nullptr || k_rot == nullptr || v == nullptr || out == nullptr || workspace == nullptr)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (g.Kc > 0 && chunk_sum == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  if (g.Kg > 0 && group_sum == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  // the lists: all or none (group_idx only with group routing)
+  const bool lists = granules != nullptr;
+  if (lists != (granule_count != nullptr) || (lists && g.Kc > 0 && chunk_idx == nullptr) ||
+      (lists && g.Kg > 0 && group_idx == nullptr))
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_raw) || !aligned16(k_rot) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(chunk_sum) || !aligned16(group_sum) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < hga::decode_step_workspace(g)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = hga::launch_decode_step(g, q_raw, k_rot, v, chunk_sum, group_sum,
+                                         lists ? chunk_idx : nullptr, lists ? group_idx : nullptr,
+                                         granules, granule_count, out, lse, workspace,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HGA_OK : hip_fail(e);
+}
 
 hga_status hga_attend(const hga_config* cfg, hga_dtype dtype, int32_t batch, const void* q_raw,
                       int64_t q_pos0, int64_t n_q, const void* k_rot, const void* v, int64_t kv_cap,

@@ -33,7 +33,6 @@
 // f32 path (attend_f32_kernel): one wave per 64 rows, one lane per row,
 // K/V tiles in LDS, f32 vector ALU; exact to f32 rounding.
 #include <algorithm>
-#include <atomic>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -1065,33 +1064,6 @@ int64_t max_keys(const Geometry& g, bool dense) {
   const int64_t causal = (qlast / g.gs + 1) * g.gs;
   if (dense) return causal;
   return std::min<int64_t>(static_cast<int64_t>(g.gmax) * g.gs, causal);
-}
-
-int current_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  return dev;
-}
-
-// Compute units of the current device (queried once per device; the cache
-// entries are atomics, so concurrent first calls agree).
-constexpr int kMaxDevices = 64;
-int64_t device_cus() {
-  static std::atomic<int> cus[kMaxDevices];
-  const int dev = current_device();
-  if (dev >= kMaxDevices) {
-    int n = 0;
-    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    return n > 0 ? n : 256;
-  }
-  int v = cus[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int n = 0;
-    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    v = n > 0 ? n : 256;
-    cus[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
 }
 
 Plan make_plan(const Geometry& g, bool dense, bool allow_split) {

@@ -38,6 +38,9 @@ hga_status make_geometry(const hga_config* cfg, hga_dtype dtype, int32_t batch, 
                          int64_t q_pos0, int64_t n_q, Geometry& g);
 // Records a failed HIP call as this thread's last error; returns HGA_ERR_HIP.
 hga_status hip_fail(hipError_t e);
+// The current HIP device, and its compute units (cached per device).
+int current_device();
+int64_t device_cus();
 
 // k_raw / k_rot hold tokens [k_first, k_first + k_rows) per (sequence, KV
 // head) (k_rows <= 0: the whole cache); every token the call reads or writes
@@ -80,6 +83,14 @@ hipError_t launch_attend(const Geometry& g, const void* q, const void* k_rot, co
                          const int32_t* granules, const int32_t* granule_count, bool dense,
                          void* out, float* lse, void* ws, hipStream_t stream,
                          const AttendExtra* extra = nullptr);
+
+// One decode step (n_q = 1 at position q_pos0) in two launches (decode.hip).
+bool decode_step_supported(const Geometry& g);
+size_t decode_step_workspace(const Geometry& g);
+hipError_t launch_decode_step(const Geometry& g, const void* q, const void* k_rot, const void* v,
+                              const float* chunk_sum, const float* group_sum, int32_t* chunk_idx,
+                              int32_t* group_idx, int32_t* granules, int32_t* granule_count, void* out,
+                              float* lse, void* ws, hipStream_t stream);
 
 // Backward of routed exact-token attention (bf16): dq (raw queries), dk (raw
 // keys) and dv, all f32; dk and dv are overwritten.  Workspace: one f32 per

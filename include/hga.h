@@ -12,6 +12,7 @@
  *   append               -> hga_build_summaries
  *   read + fetch (route) -> hga_route
  *   gather + attend      -> hga_attend, hga_attend_host_tiered
+ *   one decode step      -> hga_decode_step (route + gather + attend, two launches)
  *   Eq. (1) reference    -> hga_dense_causal
  *
  * Conventions shared by every entry point
@@ -220,6 +221,49 @@ hga_status hga_attend_noalloc(const hga_config* cfg, hga_dtype dtype, int32_t ba
                               void* out, float* lse, void* stream);
 
 size_t hga_attend_noalloc_max_scratch_bytes(void);
+
+/*
+ * hga_decode_step -- one decode step (one new query per sequence at
+ * position pos, n_q = 1) of hga_route + hga_attend in two launches.
+ *
+ * Routing policy, selection equation and exact-token output (xllm-io page,
+ * section 3) for the query of every (sequence, KV head) unit: the same
+ * selections, lists and attention as hga_route followed by hga_attend with
+ * q_pos0 = pos, n_q = 1, except that chunk and group scores are evaluated
+ * with f32 matrix-core products (about 1e-7 relative to an f64 evaluation;
+ * ties still go to the lowest index) and the attention sums its keys in
+ * another order (outputs agree to rounding, not bitwise).  The first launch
+ * scans the middle chunks and, at the same time, attends the fixed windows
+ * (sink and recent chunks, the current chunk up to pos), which routing does
+ * not change; the second selects, writes the lists, attends the routed
+ * tokens and merges.
+ *   q_raw [B][Hq][1][d], out [B][Hq][1][d], lse [B][Hq][1] (may be NULL);
+ *   k_rot, v, chunk_sum, group_sum as for hga_route / hga_attend (every chunk
+ *   and group before pos's chunk summarised; rows after pos may hold
+ *   anything);
+ *   chunk_idx [B][Hkv][K_c], group_idx [B][Hkv][K_g], granules
+ *   [B][Hkv][G_max], granule_count [B][Hkv]: the lists hga_route would write;
+ *   pass NULL for all four to skip them (group_idx may be NULL iff K_g == 0).
+ * workspace: device memory of hga_decode_step_workspace_bytes, 256-byte
+ * aligned, no initial contents needed; calls sharing one workspace must not
+ * overlap.
+ * bf16 only; d in {64, 128}; at most 16 query heads per KV head; K_c, K_g
+ * <= 256; at most 1024 routed granules per unit; g_s a power of two; the
+ * fixed windows and current chunk in W = ceil(keys / 128) blocks with
+ * W * R * (d + 2) <= 16384 floats (d = 128) or 8448 (d = 64), R the query
+ * heads per KV head rounded up to 4, 8 or 16 (896 keys at 16 heads and
+ * d = 128).  Other shapes return HGA_ERR_UNSUPPORTED (hga_route +
+ * hga_attend cover them).
+ */
+size_t hga_decode_step_workspace_bytes(const hga_config* cfg, int32_t batch, int64_t pos);
+hga_status hga_decode_step(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                           const void* q_raw, int64_t pos,
+                           const void* k_rot, const void* v, int64_t kv_cap,
+                           const float* chunk_sum, const float* group_sum,
+                           int32_t* chunk_idx, int32_t* group_idx,
+                           int32_t* granules, int32_t* granule_count,
+                           void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * hga_dense_causal -- Eq. (1): every query i attends to all keys j <= i.
