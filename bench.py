@@ -10,14 +10,21 @@ Inputs are resident in HBM before the timed region.
 
 Also measured in the same run (extra fields of the one JSON line):
   decode  -- one decode step for 16 sequences x 65536 cached tokens
-             (route + attend at position 65536, summaries precomputed);
+             (hga_decode_step, and hga_route + hga_attend, at position 65536,
+             summaries precomputed), with the oracle on a few of its units;
   smalllm -- the SmallLM-shaped prefill (batch 4, 8/8 heads, d=64, 4096 tokens);
+  tiny    -- the tiny f32 workload (1024 tokens, one head): us per step;
+  cpu_baseline_small -- the oracle on the tiny and SmallLM workloads, on all
+             BLAS threads and on one;
   host_tiered -- prefill over 131072 tokens with K/V in pinned host RAM
              (with and without the device cache of granules);
   decode_host_tier_stream -- the decode shape streamed token by token with
              its K/V history in pinned host RAM (DecodeSession);
   backward -- hga_attend_backward (dq, dk, dv) on the prefill's routes;
-  cpu_baseline -- the CPU oracle on a bounded sample of the prefill step.
+  cpu_baseline -- the CPU oracle on a bounded sample of the prefill step,
+             and the GPU's routes and outputs checked on that sample.
+Every timed region is preceded by half a second of dense matrix products, so
+that the GPU runs at its steady clock whatever --warmup is.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--only prefill|decode|smalllm|host|stream|backward|copy|peaks]
@@ -119,6 +126,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+CLOCK_WARMUP_S = 0.5
+
+
+def warm_clock(torch, seconds=CLOCK_WARMUP_S):
+    """Dense bf16 matrix products for ``seconds`` of wall time: the GPU leaves
+    its idle clock (the first tens of ms of load otherwise run 10-20 %
+    slower), so the timed steps see the steady clock whatever --warmup is."""
+    a = torch.randn(8192, 8192, device="cuda:0", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b = a @ a
+        torch.cuda.synchronize()
+    del a, b
+
+
 class Pipeline:
     """Device buffers and the three calls of one step."""
 
@@ -164,8 +187,10 @@ class Pipeline:
 
 
 def timed_steps(torch, stages, steps, warmup):
-    """Run ``warmup`` then ``steps`` steps of the stage list; events bracket the
-    whole timed region and every stage (same stream as the launches)."""
+    """Run ``warmup`` then ``steps`` steps of the stage list (after the clock
+    warmup); events bracket the whole timed region and every stage (same
+    stream as the launches)."""
+    warm_clock(torch)
     for _ in range(warmup):
         for _, fn in stages:
             fn()
@@ -259,7 +284,8 @@ def bench_backward(args, pipe=None, pairs=None):
 
 def graph_step_ms(torch, fns, steps, warmup=3):
     """Average time of one replay of a HIP graph that holds the calls fns
-    (captured on a side stream after a few eager warmup runs there)."""
+    (captured on a side stream after a few eager warmup runs there; the clock
+    warmed before the replays)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -272,6 +298,7 @@ def graph_step_ms(torch, fns, steps, warmup=3):
     with torch.cuda.graph(g):
         for fn in fns:
             fn()
+    warm_clock(torch)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -284,44 +311,83 @@ def graph_step_ms(torch, fns, steps, warmup=3):
     return e0.elapsed_time(e1) / steps
 
 
+def decode_bytes(w, counts):
+    """Algorithmic bytes of one decode step: scanned chunk summaries, the
+    group summaries of the chosen chunks, gathered K and V of the visible
+    tokens, q in and o out."""
+    B, Hkv, d = w.batch, w.n_kv_heads, w.head_dim
+    t = w.q_pos0 // w.chunk_size
+    n_mid = t - w.n_sink_chunks - max(w.n_recent_chunks, 1)
+    keys = (counts - 1) * w.group_size + 1  # the current chunk holds one token
+    return (B * Hkv * n_mid * d * 4 + B * Hkv * w.top_chunks * (w.chunk_size // w.group_size) * d * 4
+            + int(keys.sum()) * d * 2 * 2 + 2 * B * w.n_q_heads * d * 2)
+
+
 def bench_decode(args):
+    """One decode step of 16 sequences at position 65536 (summaries of the
+    65536 cached tokens precomputed, untimed): hga_decode_step (two launches)
+    and hga_route + hga_attend, each replayed as a HIP graph (a serving
+    loop's form) and eagerly."""
     import torch
     w = W.DECODE_64K
     pipe = Pipeline(w)
     pipe.build()  # cache + summaries of the 65536 cached tokens and the new token (untimed)
     torch.cuda.synchronize()
-    # a decode step is short: 10x the steps, and warmup long enough (tens of
-    # ms) for the GPU to reach its steady clock
-    eager_ms, stage = timed_steps(torch, [("route", pipe.route), ("attend", pipe.attend)],
-                                  max(args.steps * 10, 50), max(args.warmup * 10, 50))
-    # the step as a serving loop runs it: route + attend replayed as one HIP graph
-    ms = graph_step_ms(torch, [pipe.route, pipe.attend], max(args.steps * 10, 50),
-                       max(args.warmup * 10, 50))
+    H = pipe.H
+    n = max(args.steps * 10, 50)
+    nw = max(args.warmup * 10, 50)
+    eager_ms, stage = timed_steps(torch, [("route", pipe.route), ("attend", pipe.attend)], n, nw)
+    ms_ra = graph_step_ms(torch, [pipe.route, pipe.attend], n, nw)
+    ws = H.decode_step_workspace(pipe.cfg, w.batch, w.q_pos0, pipe.q.device)
+    lists = H.route_outputs(pipe.cfg, w.batch, w.q_pos0, 1, pipe.q.device)
+    out = torch.empty_like(pipe.out)
+
+    def step():
+        H.decode_step(pipe.cfg, pipe.q, w.q_pos0, pipe.k_rot, pipe.v, pipe.csum, pipe.gsum, out,
+                      None, lists=lists, workspace=ws)
+    eager_step_ms, _ = timed_steps(torch, [("decode_step", step)], n, nw)
+    ms_step = graph_step_ms(torch, [step], n, nw)
     counts = pipe.ro["granule_count"].cpu().numpy().astype(np.int64)
-    B, Hkv, d = w.batch, w.n_kv_heads, w.head_dim
-    t = w.q_pos0 // w.chunk_size
-    n_mid = t - w.n_sink_chunks - max(w.n_recent_chunks, 1)
-    n_groups = min(w.top_groups, w.top_chunks * (w.chunk_size // w.group_size))
-    # algorithmic bytes: scanned chunk summaries, fetched group summaries,
-    # gathered K and V of the visible tokens, q in and o out
-    keys = (counts - 1) * w.group_size + 1  # the current chunk holds one token
-    bytes_step = (B * Hkv * n_mid * d * 4 + B * Hkv * w.top_chunks * (w.chunk_size // w.group_size) * d * 4
-                  + int(keys.sum()) * d * 2 * 2 + 2 * B * w.n_q_heads * d * 2)
-    del n_groups
-    us = ms * 1e3
-    return pipe, dict(us_per_step=us, us_per_step_eager=eager_ms * 1e3,
+    bytes_step = decode_bytes(w, counts)
+    best = min(ms_step, ms_ra)
+    return pipe, dict(us_per_step=best * 1e3,
+                      timing="HIP graph replay of one step, the faster of the two paths",
+                      decode_step_us=ms_step * 1e3, decode_step_us_eager=eager_step_ms * 1e3,
+                      route_attend_us=ms_ra * 1e3, route_attend_us_eager=eager_ms * 1e3,
                       stage_us_eager={k: v * 1e3 for k, v in stage.items()},
-                      bytes_per_step=bytes_step,
-                      achieved_gbs=bytes_step / (ms * 1e-3) / 1e9)
+                      bytes_per_step=bytes_step, achieved_gbs=bytes_step / (best * 1e-3) / 1e9)
 
 
 def bench_smalllm(args):
+    """The SmallLM-shaped prefill: Mtok/s, and the attention launch against
+    the bf16 matrix peak (4 d flops per visible (row, key) pair) and against
+    HBM (gathered K and V of the visible tokens plus q and o, 2 bytes each)."""
     import torch
     w = W.SMALLLM_PREFILL
     pipe = Pipeline(w)
     ms, stage = timed_steps(torch, [("build_summaries", pipe.build), ("route", pipe.route),
                                     ("attend", pipe.attend)], args.steps, args.warmup)
-    return pipe, dict(ms=ms, stage_ms=stage, mtok_s=w.batch * w.n_q / (ms * 1e-3) / 1e6)
+    counts = pipe.ro["granule_count"].cpu().numpy()
+    pairs = visible_pairs(w, counts)
+    flops = 4.0 * w.head_dim * pairs
+    keys = int(counts.astype(np.int64).sum()) * w.group_size  # gathered per unit (rows share them)
+    gbytes = keys * w.head_dim * 2 * 2 + 2 * w.batch * w.n_q_heads * w.n_q * w.head_dim * 2
+    t = stage["attend"] * 1e-3
+    return pipe, dict(ms=ms, stage_ms=stage, mtok_s=w.batch * w.n_q / (ms * 1e-3) / 1e6,
+                      attend_tflops=flops / t / 1e12, attend_frac_mfma=flops / t / 1e12 / PEAK_BF16_TFLOPS,
+                      attend_gathered_bytes=gbytes, attend_gbs=gbytes / t / 1e9,
+                      attend_frac_hbm=gbytes / t / 1e9 / PEAK_HBM_GBS)
+
+
+def bench_tiny(args):
+    """The tiny f32 workload (1024 tokens, one head): the whole step's time
+    (a launch-latency-bound case)."""
+    import torch
+    w = W.TINY_F32
+    pipe = Pipeline(w)
+    ms, stage = timed_steps(torch, [("build_summaries", pipe.build), ("route", pipe.route),
+                                    ("attend", pipe.attend)], max(args.steps, 50), max(args.warmup, 20))
+    return dict(workload=w.name, us_per_step=ms * 1e3, stage_us={k: v * 1e3 for k, v in stage.items()})
 
 
 def pinned_copy_gbs(torch, nbytes=256 << 20, reps=5):
@@ -448,18 +514,38 @@ def bench_stream_decode(args):
                 timing="wall clock of append + step, synchronised every step")
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _unit_parity(R, p, w, info, gpu_ci, gpu_gi, u):
+    """'exact', 'near_tie' or 'mismatch' for one unit's GPU chunk / group
+    lists against the oracle's route_unit result (a near-tie: the oracle's
+    top-K margin is positive and below 1e-3 |s_(K)|)."""
+    g_ch = [int(x) for x in gpu_ci if x >= 0] if p.Kc > 0 else []
+    g_gr = [int(x) for x in gpu_gi if x >= 0] if p.Kg > 0 else []
+    if g_ch != info["sel_chunks"]:
+        return "near_tie" if 0 < info["margin_c"] < 1e-3 * abs(info["s_kc"]) else "mismatch"
+    if p.Kg > 0 and g_gr != info["sel_groups"]:
+        return "near_tie" if 0 < info["margin_g"] < 1e-3 * abs(info["s_kg"]) else "mismatch"
+    return "exact"
+
+
 def cpu_baseline(pipe, budget_s=12.0):
     """Time the CPU oracle on a bounded, unbiased sample of the prefill step
     and scale to the whole step: summaries of one (sequence, KV head) slab
-    and the route + attention of randomly ordered units of that slab."""
+    and, for randomly ordered units of that slab, routing from those
+    summaries and attention over the GPU's own granule lists.  The same
+    sample checks the GPU: its routes against the oracle's (exact or
+    near-tie) and its outputs against the oracle's attention (exact keys)."""
     from oracle import hga_ref as R
     w = pipe.w
     p = R.params_from_workload(w)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = _blas_threads()
     q, k, v = pipe.q_np, pipe.k_np, pipe.v_np
     t0 = time.time()
     cs, gs = R.summaries(k[0, 0].astype(np.float64), w.n_ctx, p)
@@ -467,14 +553,28 @@ def cpu_baseline(pipe, budget_s=12.0):
     csum = np.zeros((1, w.n_kv_heads) + cs.shape)
     gsum = np.zeros((1, w.n_kv_heads) + gs.shape)
     csum[0, 0], gsum[0, 0] = cs, gs
+    gr = pipe.ro["granules"].cpu().numpy()
+    gc = pipe.ro["granule_count"].cpu().numpy()
+    ci = pipe.ro["chunk_idx"].cpu().numpy()
+    gi = pipe.ro["group_idx"].cpu().numpy()
+    out = pipe.out.float().cpu().numpy()
     nqc = w.n_q // w.chunk_size
     order = np.random.default_rng(0).permutation(nqc)
     done = 0
+    tally = dict(exact=0, near_tie=0, mismatch=0)
+    diff2 = ref2 = 0.0
+    max_abs = 0.0
     t1 = time.time()
     for t in order:
         unit = [(0, 0, int(t))]
         rt = R.route(q, w.q_pos0, w.n_q, csum, gsum, p, units=unit)
-        R.attend_given(q, w.q_pos0, w.n_q, k, v, rt["granules"], rt["count"], p, t0=0, units=unit)
+        o, _ = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc, p, t0=0, units=unit)
+        tally[_unit_parity(R, p, w, rt["info"][unit[0]], ci[0, 0, t], gi[0, 0, t], unit[0])] += 1
+        rows = np.s_[0, 0:w.group_ratio, t * w.chunk_size:(t + 1) * w.chunk_size]  # the unit's rows
+        dd = out[rows] - o[rows]
+        diff2 += float(np.sum(dd * dd))
+        ref2 += float(np.sum(o[rows] * o[rows]))
+        max_abs = max(max_abs, float(np.abs(dd).max()))
         done += 1
         if time.time() - t1 > budget_s:
             break
@@ -485,7 +585,96 @@ def cpu_baseline(pipe, budget_s=12.0):
                 sample=(f"{w.name}: summaries of 1 of {w.batch * w.n_kv_heads} (sequence, kv head) "
                         f"slabs ({t_sum:.2f}s) + route and attention of {done} of {units_total} units "
                         f"in random query-chunk order ({t_units:.2f}s); scaled to the whole step "
-                        f"= {est_s:.1f}s per step"))
+                        f"= {est_s:.1f}s per step"),
+                parity_on_sample=dict(units=done, routes=tally, attention_max_abs=max_abs,
+                                      attention_rel_l2=math.sqrt(diff2 / max(ref2, 1e-300)),
+                                      against="the oracle's routes from its own summaries; its "
+                                              "attention (exact float64 keys) on the GPU's granule lists"))
+
+
+def cpu_baseline_decode(pipe, units=4):
+    """The oracle on the decode step (one query per (sequence, KV head) unit
+    at position 65536): routing from precomputed summaries (untimed, as on
+    the GPU) and attention, for a few units, scaled to all 64; parity of
+    the GPU's lists and outputs on those units."""
+    from oracle import hga_ref as R
+    w = pipe.w
+    p = R.params_from_workload(w)
+    q, k, v = pipe.q_np, pipe.k_np, pipe.v_np
+    pick = [(b, h) for b, h in [(0, 0), (5, 2), (11, 1), (15, 3)]][:units]
+    t_pos = w.q_pos0 // w.chunk_size
+    csum = np.zeros((w.batch, w.n_kv_heads, t_pos + 1, w.head_dim))
+    gsum = np.zeros((w.batch, w.n_kv_heads, (t_pos + 1) * (w.chunk_size // w.group_size), w.head_dim))
+    for b, h in pick:
+        c, g = R.summaries(k[b, h].astype(np.float64), w.n_ctx, p)
+        csum[b, h, : c.shape[0]], gsum[b, h, : g.shape[0]] = c, g
+    gr = pipe.ro["granules"].cpu().numpy()
+    gc = pipe.ro["granule_count"].cpu().numpy()
+    ci = pipe.ro["chunk_idx"].cpu().numpy()
+    gi = pipe.ro["group_idx"].cpu().numpy()
+    out = pipe.out.float().cpu().numpy()
+    tally = dict(exact=0, near_tie=0, mismatch=0)
+    max_abs = 0.0
+    t0 = time.time()
+    for b, h in pick:
+        unit = [(b, h, t_pos)]
+        rt = R.route(q, w.q_pos0, w.n_q, csum, gsum, p, units=unit)
+        o, _ = R.attend_given(q, w.q_pos0, w.n_q, k, v, gr, gc, p, t0=t_pos, units=unit)
+        tally[_unit_parity(R, p, w, rt["info"][unit[0]], ci[b, h, 0], gi[b, h, 0], unit[0])] += 1
+        rows = np.s_[b, h * w.group_ratio:(h + 1) * w.group_ratio, 0]
+        max_abs = max(max_abs, float(np.abs(out[rows] - o[rows]).max()))
+    t = time.time() - t0
+    per_step = t * (w.batch * w.n_kv_heads) / len(pick)
+    return dict(value=per_step * 1e6, unit="us/step", cores=_blas_threads(), kind="oracle",
+                sample=f"{w.name}: route + attention of {len(pick)} of {w.batch * w.n_kv_heads} units "
+                       f"({t:.2f}s), summaries precomputed; scaled to all units",
+                parity_on_sample=dict(units=len(pick), routes=tally, attention_max_abs=max_abs))
+
+
+def cpu_baseline_small(budget_s=4.0):
+    """The oracle on the tiny workload (whole step) and the SmallLM-shaped
+    prefill (sample, scaled), on all BLAS threads and on one."""
+    from oracle import hga_ref as R
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    res = {}
+    for w in (W.TINY_F32, W.SMALLLM_PREFILL):
+        q, k, v = W.make_inputs(w, 0, threads=16)
+        p = R.params_from_workload(w)
+        nqc = w.n_q // w.chunk_size
+        for label, limit in (("all_cores", None), ("one_core", 1)):
+            ctx = threadpool_limits(limits=limit) if (limit and threadpool_limits) else None
+            if ctx is not None:
+                ctx.__enter__()
+            try:
+                cores = _blas_threads()
+                t0 = time.time()
+                cs, gs = R.summaries(k[0, 0].astype(np.float64), w.n_ctx, p)
+                t_sum = time.time() - t0
+                csum = np.zeros((1, 1) + cs.shape)
+                gsum = np.zeros((1, 1) + gs.shape)
+                csum[0, 0], gsum[0, 0] = cs, gs
+                done = 0
+                t1 = time.time()
+                for t in np.random.default_rng(0).permutation(nqc):
+                    unit = [(0, 0, int(t))]
+                    rt = R.route(q, w.q_pos0, w.n_q, csum, gsum, p, units=unit)
+                    R.attend_given(q, w.q_pos0, w.n_q, k, v, rt["granules"], rt["count"], p, t0=0, units=unit)
+                    done += 1
+                    if time.time() - t1 > budget_s:
+                        break
+                t_units = time.time() - t1
+            finally:
+                if ctx is not None:
+                    ctx.__exit__(None, None, None)
+            slabs = w.batch * w.n_kv_heads
+            est = t_sum * slabs + t_units * slabs * nqc / done
+            res[f"{w.name}:{label}"] = dict(value=w.batch * w.n_q / est / 1e6, unit="Mtok/s", cores=cores,
+                                            kind="oracle", seconds_per_step=est,
+                                            sample=f"{done} of {slabs * nqc} units timed, scaled")
+    return res
 
 
 def copy_calibration(args):
@@ -506,8 +695,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "host", "stream", "backward", "copy",
-                                       "peaks"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "smalllm", "tiny", "host", "stream", "backward",
+                                       "copy", "peaks"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -529,6 +718,9 @@ def main():
     if args.only == "decode":
         _, dec = bench_decode(args)
         print(json.dumps(dict(decode=dec)), flush=True)
+        return
+    if args.only == "tiny":
+        print(json.dumps(dict(tiny=bench_tiny(args))), flush=True)
         return
     if args.only == "host":
         gbs = pinned_copy_gbs(torch)
@@ -573,22 +765,28 @@ def main():
         line["roofline"]["frac_of_measured_peak"] = pre["attend_tflops"] / peaks["mfma_bf16_tflops"]
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(pipe)
+            log(f"[bench] cpu baseline: {line['cpu_baseline']}")
         line["backward"] = bench_backward(args, pipe, pre["pairs"])
         log(f"[bench] backward: {line['backward']}")
         del pipe
         torch.cuda.empty_cache()
-        _, dec = bench_decode(args)
-        line["decode"] = dict(workload=W.DECODE_64K.name, us_per_step=dec["us_per_step"],
-                              timing="HIP graph replay of route + attend",
-                              us_per_step_eager=dec["us_per_step_eager"],
-                              stage_us_eager=dec["stage_us_eager"],
+        dpipe, dec = bench_decode(args)
+        line["decode"] = dict(workload=W.DECODE_64K.name, **{k: v for k, v in dec.items()
+                                                             if k not in ("bytes_per_step", "achieved_gbs")},
                               roofline=dict(bound="hbm", achieved=dec["achieved_gbs"], peak=PEAK_HBM_GBS,
                                             unit="GB/s", frac=dec["achieved_gbs"] / PEAK_HBM_GBS,
                                             frac_of_measured_peak=dec["achieved_gbs"] / peaks["hbm_copy_gbs"],
                                             bytes_per_step=dec["bytes_per_step"]))
+        if not args.no_cpu_baseline:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(dpipe)
+        log(f"[bench] decode: {line['decode']}")
+        del dpipe
+        torch.cuda.empty_cache()
         _, sm = bench_smalllm(args)
-        line["smalllm"] = dict(workload=W.SMALLLM_PREFILL.name, mtok_s=sm["mtok_s"], ms=sm["ms"],
-                               stage_ms=sm["stage_ms"])
+        line["smalllm"] = dict(workload=W.SMALLLM_PREFILL.name, **sm)
+        line["tiny"] = bench_tiny(args)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline_small"] = cpu_baseline_small()
         torch.cuda.empty_cache()
         gbs = pinned_copy_gbs(torch)
         line["host_tiered"] = {}
