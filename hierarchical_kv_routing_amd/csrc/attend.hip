@@ -49,8 +49,6 @@ static __device__ __align__(256) char scratch[hga::kNoAllocScratchBytes];
 namespace hga {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kTK = 64;                // keys per LDS stage (bf16 path)
 constexpr int kTab = kAttendTable;     // granule-table entries per work item (bf16 path)

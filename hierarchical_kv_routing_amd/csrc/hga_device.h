@@ -12,6 +12,8 @@ namespace hga {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 union Pack8 {
   bf16x8 v;
@@ -41,6 +43,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+// split_bf16 of two values with the hardware conversion (round to nearest
+// even, the same values): packed hi pair and packed lo pair.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const f32x2 f = {x0, x1};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  const f32x2 r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
 // Eight consecutive elements as f32 (16-byte aligned source).
@@ -134,6 +145,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Inverse of order_key.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// -0 -> +0, so that equal values get equal order keys.
+__device__ __forceinline__ float plus_zero(float f) { return f == 0.f ? 0.f : f; }
 
 // Matrix-core wrappers (gfx950 double-rate bf16 forms).
 //   16x16x32: A[m][k] m = lane%16; B[k][n] n = lane%16; each lane brings 8

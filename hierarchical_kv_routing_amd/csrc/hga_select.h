@@ -34,10 +34,13 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+__device__ __forceinline__ uint32_t shfl_xor_key(uint32_t v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int m) { return shfl_xor64(v, m); }
+
 // Bitonic sort of the wave's 64*M keys (element s*64 + lane in v[s]) into
 // descending order, entirely in registers.
-template <int M>
-__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[M]) {
+template <int M, typename T>
+__device__ __forceinline__ void wave_sort_desc(T (&v)[M]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int size = 2; size <= 64 * M; size <<= 1) {
@@ -49,15 +52,15 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[M]) {
         if (stride >= 64) {
           const int ps = s ^ (stride >> 6);
           if (ps > s) {
-            const uint64_t a = v[s], b = v[ps];
+            const T a = v[s], b = v[ps];
             const bool sw = up ? (a < b) : (a > b);
             v[s] = sw ? b : a;
             v[ps] = sw ? a : b;
           }
         } else {
-          const uint64_t o = shfl_xor64(v[s], stride);
+          const T o = shfl_xor_key(v[s], stride);
           const bool lower = (lane & stride) == 0;
-          const uint64_t mx = v[s] > o ? v[s] : o, mn = v[s] > o ? o : v[s];
+          const T mx = v[s] > o ? v[s] : o, mn = v[s] > o ? o : v[s];
           v[s] = (lower == up) ? mx : mn;
         }
       }
@@ -177,21 +180,14 @@ __device__ __forceinline__ int block_excl_scan(int v, SelScratch& s, int& total)
   return pre + inc - v;
 }
 
-// Indices of the k largest keys[0..n) (ties to the lower index), ascending,
-// into out[].  Exact radix select over the 32-bit keys, then a stable
-// compaction in index order.  Block-wide; every thread must call it.
-__device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
+// The k-th largest of keys[0..n) (0 < k < n) by an exact radix select over
+// the 32-bit keys (four 8-bit digits, most significant first); need is set
+// to how many keys equal to it rank among the k largest.  Block-wide; every
+// thread must call it.
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, SelScratch& s, int& need) {
   const int tid = threadIdx.x, nt = blockDim.x;
-  if (k <= 0 || n <= 0) return 0;
-  if (n <= k) {
-    for (int i = tid; i < n; i += nt) out[i] = i;
-    __syncthreads();
-    return n;
-  }
-  if (n <= static_cast<int>(blockDim.x) && n <= kRankMax) return rank_select(keys, n, k, out, s);
-  if (small_select_ok(n, k)) return small_select(keys, n, k, out, s);
   uint32_t prefix = 0, pmask = 0;
-  int need = k;
+  need = k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256; i += nt) s.hist[i] = 0;
@@ -234,6 +230,91 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
     pmask |= 255u << shift;
     __syncthreads();
   }
+  return prefix;
+}
+
+// The k-th largest of keys[0..n) (0 < k < n).  For n <= 64 * waves and
+// k <= 16: every wave sorts its 64 keys in registers and keeps its k
+// largest, and one wave sorts the 16 * waves survivors (the k largest of
+// the whole set are among them); otherwise radix_kth.  Block-wide; every
+// thread must call it.
+__device__ __forceinline__ uint32_t block_kth(const uint32_t* keys, int n, int k, SelScratch& s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (n > 64 * nw || k > 16 || nw > 8) {
+    int need;
+    return radix_kth(keys, n, k, s, need);
+  }
+  uint32_t* cand = reinterpret_cast<uint32_t*>(s.cand);  // 128 entries
+  {
+    const int i = wave * 64 + lane;
+    uint32_t v[1] = {i < n ? keys[i] : 0u};  // 0 ranks below every real key
+    wave_sort_desc<1>(v);
+    if (lane < 16) cand[wave * 16 + lane] = lane < k ? v[0] : 0u;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = j * 64 + lane;
+      v[j] = i < nw * 16 ? cand[i] : 0u;
+    }
+    wave_sort_desc<2>(v);
+    if (lane == k - 1) s.bcast[2] = static_cast<int>(v[0]);
+  }
+  __syncthreads();
+  return static_cast<uint32_t>(s.bcast[2]);
+}
+
+// Indices i < n with keys[i] >= thr into out[], ascending; returns their
+// count.  Block-wide; every thread must call it.
+__device__ __forceinline__ int block_compact_ge(const uint32_t* keys, int n, uint32_t thr, int* out,
+                                                SelScratch& s) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (n <= nt) {  // one key per thread: wave ballots
+    const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    const bool take = tid < n && keys[tid] >= thr;
+    const uint64_t m = __ballot(take);
+    if (lane == 0) s.wsum[wave] = __popcll(m);
+    __syncthreads();
+    int pos = __popcll(m & ((1ull << lane) - 1ull)), total = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int c = s.wsum[w];
+      pos += w < wave ? c : 0;
+      total += c;
+    }
+    if (take) out[pos] = tid;
+    __syncthreads();
+    return total;
+  }
+  const int per = (n + nt - 1) / nt;
+  const int lo = tid * per;
+  const int hi = lo + per < n ? lo + per : n;
+  int c = 0;
+  for (int i = lo; i < hi; ++i) c += keys[i] >= thr;
+  int total;
+  int pos = block_excl_scan(c, s, total);
+  for (int i = lo; i < hi; ++i)
+    if (keys[i] >= thr) out[pos++] = i;
+  __syncthreads();
+  return total;
+}
+
+// Indices of the k largest keys[0..n) (ties to the lower index), ascending,
+// into out[].  Exact radix select over the 32-bit keys, then a stable
+// compaction in index order.  Block-wide; every thread must call it.
+__device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int* out, SelScratch& s) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (k <= 0 || n <= 0) return 0;
+  if (n <= k) {
+    for (int i = tid; i < n; i += nt) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  if (n <= static_cast<int>(blockDim.x) && n <= kRankMax) return rank_select(keys, n, k, out, s);
+  if (small_select_ok(n, k)) return small_select(keys, n, k, out, s);
+  int need;
+  const uint32_t prefix = radix_kth(keys, n, k, s, need);
   const uint32_t thr = prefix;
   const int per = (n + nt - 1) / nt;
   const int lo = tid * per;

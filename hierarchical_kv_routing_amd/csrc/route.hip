@@ -41,6 +41,19 @@ constexpr int kMaxRows = kRowsPerWave * kRouteWaves;
 constexpr int kMaxCand = 4096;          // middle chunks per unit held in LDS
 constexpr int kMaxSel = 256;            // K_c, K_g upper bound
 constexpr int kMaxTableQ = 64;          // queries per unit (C <= 64)
+constexpr int kScreenMin = 64;          // middle chunks above which chunk scoring is screened
+
+// Screening bound.  With x = hi + lo + e (hi = bf16(x), lo = bf16(x - hi),
+// u = 2^-8: |hi| <= (1+u)|x|, |lo| <= u(1+u)|x|), the split score
+// hi.hi + hi.lo + lo.hi of a query row q and a chunk summary c differs from
+// hi.hi alone by at most 2u(1+u)^2 sum_d |q_d c_d| <= 2u(1+u)^2 |q| |c|
+// (Cauchy-Schwarz), plus the f32 accumulation of both (at most 384 terms,
+// 2^-24 each, of a sum of magnitudes <= (1+u)^2 |q| |c|): in all below
+// 1.014 * 2^-7 |q| |c|.  The max over a unit's rows moves by at most the
+// same with |q| -> Q, the largest row norm.  kScreenEps adds headroom for
+// the f32 rounding of the norms and of s -/+ E; kScreenAbs keeps E > 0.
+constexpr float kScreenEps = 1.03f / 128.f;
+constexpr float kScreenAbs = 1e-30f;
 
 struct RouteParams {
   const void* q;
@@ -58,6 +71,7 @@ struct RouteParams {
   // split into bf16 hi / lo rows (split_kernel), [slab][row][hi d, lo d]
   const uint16_t* csplit;
   const uint16_t* gsplit;
+  const float* cnorm;                // |c_m| of every split chunk row, [slab][row]
   int64_t csplit_rows, gsplit_rows;  // rows per (sequence, KV head) table
   int64_t q_pos0, n_q, t0, nqc, nchunk_cap, ngroup_cap;
   int B, Hq, Hkv, G, d, C, gs, r, F, L, Kc, Kg, gmax;
@@ -103,10 +117,12 @@ __device__ __forceinline__ Unit make_unit(const RouteParams& p, int64_t u) {
 
 // cos/sin of every (query of the unit, pair) into LDS (block-wide; scratch:
 // 16 * d/2 float2, free for the call).
+template <int KS>
 __device__ __forceinline__ void fill_rope_table(const RouteParams& p, const Unit& w, float2* cs,
                                                 float2* scratch) {
-  // a unit's queries share one chunk, so one wrap of its first position
-  rope_table(p.rope, rope_base(p.rope, w.qlo), w.nq, p.d >> 1, cs, scratch);
+  // a unit's queries share one chunk, so one wrap of its first position;
+  // d/2 = 16 KS is a constant here, so the table's index arithmetic is shifts
+  rope_table(p.rope, rope_base(p.rope, w.qlo), w.nq, 16 * KS, cs, scratch);
 }
 
 // The wave's NB row blocks of 16 rotated query rows as split-bf16 A operands
@@ -132,10 +148,12 @@ __device__ __forceinline__ void load_row_raw(const RouteParams& p, const Unit& w
 }
 
 // Rotates one row block's raw elements with the unit's RoPE table and splits
-// them into the bf16 hi / lo A operands.
+// them into the bf16 hi / lo A operands; ss receives the sum of squares of
+// the lane's rotated elements (a quarter of its row).
 template <int KS>
 __device__ __forceinline__ void rotate_split(const RouteParams& p, int r, const float2* cs,
-                                             float (&x)[KS][8], Pack8 (&ahi)[KS], Pack8 (&alo)[KS]) {
+                                             float (&x)[KS][8], Pack8 (&ahi)[KS], Pack8 (&alo)[KS],
+                                             float& ss) {
   const int sub = (threadIdx.x & 63) >> 4;
   const int h = p.d >> 1;
   const int qi = r / p.G;
@@ -149,24 +167,87 @@ __device__ __forceinline__ void rotate_split(const RouteParams& p, int r, const 
       x[ks + KS / 2][i] = a * t.y + b * t.x;
     }
   }
+  ss = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) split_bf16(x[ks][i], ahi[ks].h[i], alo[ks].h[i]);
+    for (int i = 0; i < 4; ++i) {
+      split_bf16x2(x[ks][2 * i], x[ks][2 * i + 1], ahi[ks].u[i], alo[ks].u[i]);
+      ss += x[ks][2 * i] * x[ks][2 * i] + x[ks][2 * i + 1] * x[ks][2 * i + 1];
+    }
   }
 }
 
+// bf16 queries: the raw 16-byte slices of the wave's NB row blocks, issued
+// together (before the RoPE table is built) and held as packed bf16.
+template <int KS, int NB>
+__device__ __forceinline__ void issue_rows16(const RouteParams& p, const Unit& w, int rbase,
+                                             uint4 (&raw)[NB][KS]) {
+  const int sub = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int r = row_of_lane(w, rbase, blk);
+    const int qi = r / p.G;
+    const int hl = r - qi * p.G;
+    const int64_t base =
+        ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.n_q + (w.qlo + qi - p.q_pos0)) * p.d;
+    const uint16_t* src = static_cast<const uint16_t*>(p.q) + base + sub * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[blk][ks] = *reinterpret_cast<const uint4*>(src + ks * 32);
+  }
+}
+
+// Rotates and splits the rows issue_rows16 loaded; returns the largest
+// squared norm of the wave's rotated rows (the same value in every lane).
+template <int KS, int NB>
+__device__ __forceinline__ float rotate_rows16(const RouteParams& p, const Unit& w, int rbase,
+                                               const float2* cs, const uint4 (&raw)[NB][KS],
+                                               Pack8 (&ahi)[NB][KS], Pack8 (&alo)[NB][KS]) {
+  float n2 = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    float x[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t u[4] = {raw[blk][ks].x, raw[blk][ks].y, raw[blk][ks].z, raw[blk][ks].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[ks][2 * i] = __uint_as_float(u[i] << 16);
+        x[ks][2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    }
+    float ss;
+    rotate_split<KS>(p, row_of_lane(w, rbase, blk), cs, x, ahi[blk], alo[blk], ss);
+    ss += __shfl_xor(ss, 16);  // the four lanes of a row
+    ss += __shfl_xor(ss, 32);
+    n2 = fmaxf(n2, ss);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+  return n2;
+}
+
+// The wave's rows as split operands; returns the largest squared norm of
+// the wave's rotated rows (the same value in every lane).
 template <bool BF16, int KS, int NB>
-__device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, int rbase,
-                                          const float2* cs, Pack8 (&ahi)[NB][KS],
-                                          Pack8 (&alo)[NB][KS]) {
+__device__ __forceinline__ float load_rows(const RouteParams& p, const Unit& w, int rbase,
+                                           const float2* cs, Pack8 (&ahi)[NB][KS],
+                                           Pack8 (&alo)[NB][KS]) {
+  float n2 = 0.f;
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int r = row_of_lane(w, rbase, blk);
     float x[KS][8];
     load_row_raw<BF16, KS>(p, w, r, x);
-    rotate_split<KS>(p, r, cs, x, ahi[blk], alo[blk]);
+    float ss;
+    rotate_split<KS>(p, r, cs, x, ahi[blk], alo[blk], ss);
+    ss += __shfl_xor(ss, 16);  // the four lanes of a row
+    ss += __shfl_xor(ss, 32);
+    n2 = fmaxf(n2, ss);
   }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+  return n2;
 }
 
 // Summary rows staged in LDS, split into bf16 hi and lo halves, so that the
@@ -180,9 +261,12 @@ __device__ __forceinline__ void load_rows(const RouteParams& p, const Unit& w, i
 constexpr int kStageRows = 64;
 
 // Score tiles of one staged 64-row block: tile `tile` (16 rows), the max
-// over the wave's row blocks of q . row (split products hi.hi + hi.lo +
-// lo.hi).
-template <int KS, int NB>
+// over the wave's row blocks of q . row: the split products hi.hi + hi.lo +
+// lo.hi (FULL), or hi.hi alone (the screening pass, no lo rows staged).
+// Returns the lane's part of the max: candidate lane%16 over the rows
+// 4*(lane/16) + j of each row block (the caller combines the four lanes of
+// a candidate with an LDS atomic max).
+template <int KS, int NB, bool FULL>
 __device__ __forceinline__ float score16_staged(const char* shi, const char* slo, int tile,
                                                 const Pack8 (&ahi)[NB][KS],
                                                 const Pack8 (&alo)[NB][KS]) {
@@ -194,7 +278,7 @@ __device__ __forceinline__ float score16_staged(const char* shi, const char* slo
   for (int ks = 0; ks < KS; ++ks) {
     const int off = row * (2 * D) + 16 * ((4 * ks + sub) ^ rswz<D>(row));
     bhi[ks].q = *reinterpret_cast<const uint4*>(shi + off);
-    blo[ks].q = *reinterpret_cast<const uint4*>(slo + off);
+    if constexpr (FULL) blo[ks].q = *reinterpret_cast<const uint4*>(slo + off);
   }
   float best = -INFINITY;
 #pragma unroll
@@ -203,21 +287,53 @@ __device__ __forceinline__ float score16_staged(const char* shi, const char* slo
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       acc = mfma16x16x32(ahi[blk][ks].v, bhi[ks].v, acc);
-      acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
-      acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
+      if constexpr (FULL) {
+        acc = mfma16x16x32(ahi[blk][ks].v, blo[ks].v, acc);
+        acc = mfma16x16x32(alo[blk][ks].v, bhi[ks].v, acc);
+      }
     }
     best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
   }
-  best = fmaxf(best, __shfl_xor(best, 16));
-  best = fmaxf(best, __shfl_xor(best, 32));
   return best;
+}
+
+// hi.hi scores of two staged tiles (t0, t1) at once: both tiles' operands
+// are read before the products, so the LDS reads of the second overlap the
+// products of the first.  Lane parts of the max, as score16_staged.
+template <int KS, int NB>
+__device__ __forceinline__ void score16x2_hh(const char* shi, int t0, int t1, const Pack8 (&ahi)[NB][KS],
+                                             float& v0, float& v1) {
+  constexpr int D = 32 * KS;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4;
+  Pack8 b0[KS], b1[KS];
+  const int r0 = t0 * 16 + (lane & 15), r1 = t1 * 16 + (lane & 15);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    b0[ks].q = *reinterpret_cast<const uint4*>(shi + r0 * (2 * D) + 16 * ((4 * ks + sub) ^ rswz<D>(r0)));
+    b1[ks].q = *reinterpret_cast<const uint4*>(shi + r1 * (2 * D) + 16 * ((4 * ks + sub) ^ rswz<D>(r1)));
+  }
+  v0 = -INFINITY;
+  v1 = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      a0 = mfma16x16x32(ahi[blk][ks].v, b0[ks].v, a0);
+      a1 = mfma16x16x32(ahi[blk][ks].v, b1[ks].v, a1);
+    }
+    v0 = fmaxf(v0, fmaxf(fmaxf(a0[0], a0[1]), fmaxf(a0[2], a0[3])));
+    v1 = fmaxf(v1, fmaxf(fmaxf(a1[0], a1[1]), fmaxf(a1[2], a1[3])));
+  }
 }
 
 // Max-scores of n candidates into keys[0..n) (atomic max: several row
 // groups share the tiles); row(i) is the split row of candidate i.  Stages
 // of 64 rows alternate between buffers (h0, l0) and (h1, l1); rows at or
-// past n repeat row n-1.  Block-wide.
-template <int KS, int NB, typename RowPtr>
+// past n repeat row n-1.  FULL = false: hi.hi products only, and only the hi
+// halves are staged.  Block-wide.
+template <int KS, int NB, bool FULL, typename RowPtr>
 __device__ __forceinline__ void score_staged(int n, RowPtr row, bool has_rows, int tg, int TG,
                                              const Pack8 (&ahi)[NB][KS],
                                              const Pack8 (&alo)[NB][KS], char* h0, char* l0,
@@ -241,7 +357,7 @@ __device__ __forceinline__ void score_staged(int n, RowPtr row, bool has_rows, i
       i = i < n ? i : n - 1;
       const char* src = reinterpret_cast<const char*>(row(i)) + 16 * c;
       load_lds16(src, hs + blk);
-      load_lds16(src + ROW, ls + blk);
+      if constexpr (FULL) load_lds16(src + ROW, ls + blk);
     }
   };
   auto step = [&](int s, const char* hs, const char* ls, char* hn, char* ln_) {
@@ -250,9 +366,9 @@ __device__ __forceinline__ void score_staged(int n, RowPtr row, bool has_rows, i
     if (has_rows) {
       const int nb = n - s * kStageRows < kStageRows ? n - s * kStageRows : kStageRows;
       for (int tile = tg; tile * 16 < nb; tile += TG) {
-        const float v = score16_staged<KS, NB>(hs, ls, tile, ahi, alo);
+        const float v = score16_staged<KS, NB, FULL>(hs, ls, tile, ahi, alo);
         const int c = s * kStageRows + tile * 16 + (lane & 15);
-        if (lane < 16 && c < n) atomicMax(&keys[c], order_key(v));
+        if (c < n) atomicMax(&keys[c], order_key(v));
       }
     }
     wait_vm_barrier<0>();
@@ -266,23 +382,104 @@ __device__ __forceinline__ void score_staged(int n, RowPtr row, bool has_rows, i
   }
 }
 
+// hi.hi max-scores of n candidates into keys[0..n) (atomic max), the
+// screening pass: only the hi halves of the split rows are staged, through
+// a ring of four 64-row buffers with three stages in flight (the loop is
+// unrolled by four so that every stage names its buffers statically, and
+// the LDS reads of one buffer need not wait for the loads into the others).
+// Rows at or past n repeat row n-1.  Block-wide.
+template <int KS, int NB, typename RowPtr>
+__device__ __forceinline__ void screen_staged(int n, RowPtr row, bool has_rows, int tg, int TG,
+                                              const Pack8 (&ahi)[NB][KS], const Pack8 (&alo)[NB][KS],
+                                              char* b0, char* b1, char* b2, char* b3, uint32_t* keys) {
+  constexpr int D = 32 * KS;
+  constexpr int ROW = 2 * D;
+  constexpr int NBLK = kStageRows * ROW / 1024;  // 1 KB blocks per stage
+  constexpr int LPS = NBLK / kRouteWaves;        // loads per wave per stage
+  static_assert(NBLK % kRouteWaves == 0, "stage blocks spread evenly over the waves");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nst = (n + kStageRows - 1) / kStageRows;
+  auto issue = [&](int s, char* hs) {
+    if (s >= nst) return;  // uniform
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int j = 0; j < LPS; ++j) {
+      const int blk = (wave + j * kRouteWaves) * 1024;
+      const int o = blk + 16 * ln;
+      const int m = o / ROW;
+      const int c = ((o % ROW) / 16) ^ rswz<D>(m);
+      int i = s * kStageRows + m;
+      i = i < n ? i : n - 1;
+      load_lds16(reinterpret_cast<const char*>(row(i)) + 16 * c, hs + blk);
+    }
+  };
+  auto step = [&](int s, const char* hs, char* nxt) {
+    // stage s landed (later stages may stay in flight), in every wave
+    if (s + 2 < nst) wait_vm_barrier<2 * LPS>();
+    else if (s + 1 < nst) wait_vm_barrier<LPS>();
+    else wait_vm_barrier<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + 3, nxt);  // into the buffer stage s-1 used
+    if (has_rows) {
+      const int nb = n - s * kStageRows < kStageRows ? n - s * kStageRows : kStageRows;
+      for (int tile = tg; tile * 16 < nb; tile += 2 * TG) {
+        const int t1 = (tile + TG) * 16 < nb ? tile + TG : tile;  // a lone last tile is scored twice
+        float v0, v1;
+        score16x2_hh<KS, NB>(hs, tile, t1, ahi, v0, v1);
+        const int c0 = s * kStageRows + tile * 16 + (lane & 15);
+        const int c1 = s * kStageRows + t1 * 16 + (lane & 15);
+        if (c0 < n) atomicMax(&keys[c0], order_key(v0));
+        if (c1 < n) atomicMax(&keys[c1], order_key(v1));
+      }
+    }
+  };
+  issue(0, b0);
+  issue(1, b1);
+  issue(2, b2);
+  for (int s = 0; s < nst; s += 4) {
+    step(s, b0, b3);
+    if (s + 1 >= nst) break;
+    step(s + 1, b1, b0);
+    if (s + 2 >= nst) break;
+    step(s + 2, b2, b1);
+    if (s + 3 >= nst) break;
+    step(s + 3, b3, b2);
+  }
+  __syncthreads();  // every wave's reads of the ring are done
+}
+
 // Summary rows (f32) -> split rows (d bf16 hi values, then d lo values), for
 // the first `rows` rows of every (sequence, KV head) table of cap rows, into
-// tables of `rows` rows; one thread per 8 values.
-__global__ __launch_bounds__(256) void split_kernel(const float* src, uint16_t* dst, int64_t cap, int64_t rows,
-                                                    int64_t slabs, int d) {
+// tables of `rows` rows; one thread per 8 values.  norms (may be null):
+// the f32 norm of every row, [slab][row].  The d/8 threads of a row are
+// consecutive lanes of one wave (d/8 divides 64), and a row is either
+// wholly inside the grid's range or wholly outside.
+__global__ __launch_bounds__(256) void split_kernel(const float* src, uint16_t* dst, float* norms, int64_t cap,
+                                                    int64_t rows, int64_t slabs, int d) {
   const int64_t segs = d / 8;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= slabs * rows * segs) return;
-  const int64_t sg = i % segs, r = (i / segs) % rows, x = i / (segs * rows);
+  const bool in = i < slabs * rows * segs;
+  const int64_t ii = in ? i : 0;
+  const int64_t sg = ii % segs, r = (ii / segs) % rows, x = ii / (segs * rows);
   float v[8];
   load8<false>(src + (x * cap + r) * d, sg * 8, v);
   Pack8 h, l;
+  float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) split_bf16(v[k], h.h[k], l.h[k]);
-  uint16_t* o = dst + (x * rows + r) * 2 * d;
-  *reinterpret_cast<uint4*>(o + sg * 8) = h.q;
-  *reinterpret_cast<uint4*>(o + d + sg * 8) = l.q;
+  for (int k = 0; k < 8; ++k) {
+    split_bf16(v[k], h.h[k], l.h[k]);
+    ss += v[k] * v[k];
+  }
+  if (in) {
+    uint16_t* o = dst + (x * rows + r) * 2 * d;
+    *reinterpret_cast<uint4*>(o + sg * 8) = h.q;
+    *reinterpret_cast<uint4*>(o + d + sg * 8) = l.q;
+  }
+  if (norms != nullptr) {  // uniform
+    for (int m = 1; m < segs; m <<= 1) ss += __shfl_xor(ss, m);
+    if (in && sg == 0) norms[x * rows + r] = sqrtf(ss);
+  }
 }
 
 // Exact top-k selection (lowest index wins ties): hga_select.h.
@@ -403,14 +600,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(RouteParams p) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) load_row_raw<BF16, KS>(p, w, row_of_lane(w, 0, blk), xq[blk]);
       score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit, [&] {
-        fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
+        fill_rope_table<KS>(p, w, cs, reinterpret_cast<float2*>(keys));
         __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
-          rotate_split<KS>(p, row_of_lane(w, 0, blk), cs, xq[blk], ahi[blk], alo[blk]);
+        {
+          float ss;
+          rotate_split<KS>(p, row_of_lane(w, 0, blk), cs, xq[blk], ahi[blk], alo[blk], ss);
+        }
       });
     } else {
-      fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
+      fill_rope_table<KS>(p, w, cs, reinterpret_cast<float2*>(keys));
       __syncthreads();
       load_rows<BF16, KS, NB>(p, w, 0, cs, ahi, alo);
       score_stream<KS, NB>(n, wave, kScoreThreads / 64, rowp, ahi, alo, emit);
@@ -535,6 +735,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ int selc[kMaxSel];
   __shared__ int selg[kMaxSel];
   __shared__ SelScratch scr;
+  __shared__ uint32_t qmax2;  // largest squared norm of the unit's rotated rows (f32 bits)
   // staged split rows, two stages (the stage buffers are separate arrays so
   // that the compiler sees that reading one need not wait for loads into
   // the other)
@@ -559,18 +760,73 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
 
   Pack8 ahi[NB][KS], alo[NB][KS];
   int nselc = 0;
-  if (route) {
-    {
-      fill_rope_table(p, w, cs, reinterpret_cast<float2*>(keys));
+  if (route && n_mid <= p.Kc) {
+    // every middle chunk is chosen: no scores needed
+    nselc = n_mid;
+    for (int i = threadIdx.x; i < n_mid; i += blockDim.x) selc[i] = static_cast<int>(w.mid_lo) + i;
+    __syncthreads();
+    if (p.Kg > 0) {  // the group phase needs the query rows
+      fill_rope_table<KS>(p, w, cs, reinterpret_cast<float2*>(keys));
       __syncthreads();
       if (has_rows) load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
+      __syncthreads();
+    }
+  } else if (route) {
+    {
+      if (threadIdx.x == 0) qmax2 = 0u;
+      float n2 = 0.f;
+      if constexpr (BF16) {
+        // the raw rows are in flight while the RoPE table is built
+        uint4 raw[NB][KS];
+        if (has_rows) issue_rows16<KS, NB>(p, w, rg * kRows, raw);
+        fill_rope_table<KS>(p, w, cs, reinterpret_cast<float2*>(keys));
+        __syncthreads();
+        if (has_rows) n2 = rotate_rows16<KS, NB>(p, w, rg * kRows, cs, raw, ahi, alo);
+      } else {
+        fill_rope_table<KS>(p, w, cs, reinterpret_cast<float2*>(keys));
+        __syncthreads();
+        if (has_rows) n2 = load_rows<BF16, KS, NB>(p, w, rg * kRows, cs, ahi, alo);
+      }
+      if (has_rows && lane == 0) atomicMax(&qmax2, __float_as_uint(n2));  // n2 >= 0: bit order is value order
       for (int i = threadIdx.x; i < n_mid; i += blockDim.x) keys[i] = 0u;
       __syncthreads();
       const int64_t cbase = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.nchunk_cap;
+      const int64_t slab = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
+      const uint16_t* c0 = p.csplit + (slab * p.csplit_rows + w.mid_lo) * 2 * p.d;
+      if (RG > 1 && n_mid > kScreenMin) {
+        // Screened chunk scoring.  hi.hi scores s of every middle chunk
+        // bound the split scores to s -/+ E_m (E_m = kScreenEps Q |c_m|);
+        // lam = the K_c-th largest lower end; a chunk whose upper end is
+        // below lam is beaten by at least K_c chunks, so the split scores
+        // of the others (S, ascending) decide the same selection as
+        // scoring them all.  cs (the RoPE table, no longer needed) holds
+        // the upper ends and S.
+        screen_staged<KS, NB>(n_mid, [&](int c) { return c0 + static_cast<int64_t>(c) * 2 * p.d; },
+                              has_rows, tg, TG, ahi, alo, sh0, sl0, sh1, sl1, keys);
+        uint32_t* hik = reinterpret_cast<uint32_t*>(cs);
+        int* sidx = reinterpret_cast<int*>(cs) + kMaxCand;
+        const float qn = sqrtf(__uint_as_float(qmax2));
+        const float* cn = p.cnorm + slab * p.csplit_rows + w.mid_lo;
+        for (int i = threadIdx.x; i < n_mid; i += blockDim.x) {
+          const float sc = key_float(keys[i]);
+          const float e = kScreenEps * qn * cn[i] + kScreenAbs;
+          keys[i] = order_key(plus_zero(sc - e));
+          hik[i] = order_key(plus_zero(sc + e));
+        }
+        __syncthreads();
+        const uint32_t lam = block_kth(keys, n_mid, p.Kc, scr);
+        const int ns = block_compact_ge(hik, n_mid, lam, sidx, scr);
+        for (int i = threadIdx.x; i < ns; i += blockDim.x) keys[i] = 0u;
+        __syncthreads();
+        score_staged<KS, NB, true>(ns, [&](int i) { return c0 + static_cast<int64_t>(sidx[i]) * 2 * p.d; },
+                                   has_rows, tg, TG, ahi, alo, sh0, sl0, sh1, sl1, keys);
+        __syncthreads();
+        nselc = block_select(keys, ns, p.Kc, selc, scr);
+        for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] = sidx[selc[i]] + static_cast<int>(w.mid_lo);
+        __syncthreads();
+      } else {
       if (RG > 1) {
-        const int64_t slab = static_cast<int64_t>(w.b) * p.Hkv + w.kvh;
-        const uint16_t* c0 = p.csplit + (slab * p.csplit_rows + w.mid_lo) * 2 * p.d;
-        score_staged<KS, NB>(n_mid, [&](int c) { return c0 + static_cast<int64_t>(c) * 2 * p.d; },
+        score_staged<KS, NB, true>(n_mid, [&](int c) { return c0 + static_cast<int64_t>(c) * 2 * p.d; },
                              has_rows, tg, TG, ahi, alo, sh0, sl0, sh1, sl1, keys);
       } else if (has_rows) {
         const float* c0 = p.csum + (cbase + w.mid_lo) * p.d;
@@ -584,6 +840,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
       nselc = block_select(keys, n_mid, p.Kc, selc, scr);
       for (int i = threadIdx.x; i < nselc; i += blockDim.x) selc[i] += static_cast<int>(w.mid_lo);
       __syncthreads();
+      }
     }
   }
 
@@ -600,7 +857,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     };
     if (RG > 1) {
       const uint16_t* gs0 = p.gsplit + (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.gsplit_rows * 2 * p.d;
-      score_staged<KS, NB>(nc, [&](int c) {
+      score_staged<KS, NB, true>(nc, [&](int c) {
                              const int cr = c / p.r;
                              return gs0 + (static_cast<int64_t>(selc[cr]) * p.r + (c - cr * p.r)) * 2 * p.d;
                            },
@@ -700,15 +957,18 @@ bool use_split(const Geometry& g) {
   return !use_segmented(g) && g.Kc > 0 && rows > kRowsPerWave;
 }
 // Rows split: chunks [0, t_last] (a unit reads middle chunks before its own)
-// and their groups; independent of kv_cap (the sizing call has none).
+// and their groups; independent of kv_cap (the sizing call has none).  After
+// the two split tables, the norms of the chunk rows (f32).
 int64_t split_chunks(const Geometry& g) { return g.t0 + g.nqc; }
-size_t split_bytes(const Geometry& g, size_t& gsplit_off) {
+size_t split_bytes(const Geometry& g, size_t& gsplit_off, size_t& norm_off) {
   const size_t slabs = static_cast<size_t>(g.B) * g.Hkv;
   const size_t row = static_cast<size_t>(g.d) * 2 * 2;
   const size_t rc = static_cast<size_t>(split_chunks(g));
   const size_t c = slabs * rc * row;
   gsplit_off = (c + 255) / 256 * 256;
-  return gsplit_off + (g.Kg > 0 ? slabs * rc * static_cast<size_t>(g.r) * row : 0);
+  const size_t gend = gsplit_off + (g.Kg > 0 ? slabs * rc * static_cast<size_t>(g.r) * row : 0);
+  norm_off = (gend + 255) / 256 * 256;
+  return norm_off + slabs * rc * sizeof(float);
 }
 
 }  // namespace
@@ -722,8 +982,8 @@ bool route_supported(const Geometry& g) {
 
 size_t route_workspace(const Geometry& g) {
   if (use_split(g)) {
-    size_t goff = 0;
-    return split_bytes(g, goff);
+    size_t goff = 0, noff = 0;
+    return split_bytes(g, goff, noff);
   }
   if (!use_segmented(g) || g.Kc <= 0) return 0;
   const SegPlan sp = seg_plan(g);
@@ -772,30 +1032,33 @@ hipError_t launch_route(const Geometry& g, const void* q, const float* chunk_sum
   p.ws_stride = static_cast<int64_t>(sp.nseg) * g.Kc * (2 + (g.Kg > 0 ? g.r : 0));
   p.csplit = nullptr;
   p.gsplit = nullptr;
+  p.cnorm = nullptr;
   p.csplit_rows = p.gsplit_rows = 0;
   if (use_split(g)) {
     // split the summary rows the call can read: chunks before the last
     // query chunk and their groups
-    size_t goff = 0;
-    split_bytes(g, goff);
+    size_t goff = 0, noff = 0;
+    split_bytes(g, goff, noff);
     uint16_t* cs = static_cast<uint16_t*>(ws);
     uint16_t* gsp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + goff);
+    float* cn = reinterpret_cast<float*>(static_cast<char*>(ws) + noff);
     const int64_t slabs = static_cast<int64_t>(g.B) * g.Hkv;
     const int64_t rc = split_chunks(g);  // <= nchunk_cap (q_pos0 + n_q <= kv_cap)
     const int64_t n8 = slabs * rc * (g.d / 8);
     hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, stream,
-                       chunk_sum, cs, p.nchunk_cap, rc, slabs, g.d);
+                       chunk_sum, cs, cn, p.nchunk_cap, rc, slabs, g.d);
     p.csplit_rows = rc;
     p.gsplit_rows = rc * g.r;
     if (g.Kg > 0) {
       const int64_t g8 = slabs * rc * g.r * (g.d / 8);
       hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>((g8 + 255) / 256)), dim3(256), 0, stream,
-                         group_sum, gsp, p.ngroup_cap, rc * g.r, slabs, g.d);
+                         group_sum, gsp, nullptr, p.ngroup_cap, rc * g.r, slabs, g.d);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     p.csplit = cs;
     p.gsplit = gsp;
+    p.cnorm = cn;
   }
   if (g.bf16) {
     return g.d == 128 ? launch_route_t<true, 4>(p, units, seg, stream)

@@ -132,7 +132,8 @@ int32_t hga_max_granules(const hga_config* cfg);
  * segment winners of decode-shaped calls, or, for calls whose units have
  * more than 64 (query, head) rows, the summary rows the call can read split
  * into bf16 hi / lo halves (chunks up to the last query chunk and their
- * groups, 4 * d bytes per row). */
+ * groups, 4 * d bytes per row) and the norms of those chunk rows (4 bytes
+ * each). */
 size_t hga_route_workspace_bytes(const hga_config* cfg, int32_t batch,
                                  int64_t q_pos0, int64_t n_q);
 
@@ -154,7 +155,10 @@ size_t hga_route_workspace_bytes(const hga_config* cfg, int32_t batch,
  *               first token is <= the unit's last query (sorted, unique)
  * Scores are evaluated with split-bf16 matrix-core products (hi*hi + hi*lo +
  * lo*hi, f32 accumulation), about 1e-5 relative to an f64 evaluation; exact
- * ties go to the lowest index.
+ * ties go to the lowest index.  Units with more than 64 rows and 64 middle
+ * chunks screen the chunks with hi*hi alone first and take the split
+ * products only of the chunks that a proven bound on the difference leaves
+ * in contention: the selection is the same as scoring every chunk.
  *
  * chunk_sum must hold every chunk < the last query chunk; group_sum every
  * group of those chunks (group_sum / group_idx may be NULL iff K_g == 0).

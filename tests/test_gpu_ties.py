@@ -7,8 +7,9 @@ them exactly 0: they tie with each other at the K-th place (in the mixed
 cases the live chunks score above them).  The oracle's margin there is
 exactly 0, which parity.compare_routes does not accept as a near-tie: the
 GPU's chunk and group lists must equal the oracle's lowest-index choice.
-Covered: the fused prefill routing (rank select, <= 512 candidates), the
-block radix select (> 512 middle chunks) and the segmented decode scoring,
+Covered: the fused prefill routing (rank select, <= 512 candidates), with
+and without the screened chunk scoring, the block radix select (> 512
+middle chunks) and the segmented decode scoring,
 where each segment keeps its own winners and the merge must still prefer
 the lower index across segments.
 """
@@ -25,6 +26,14 @@ CASES = {
     # fused prefill routing: 64 query chunks x 4 KV heads, rank select
     "prefill_mixed": (W.QWEN3_PREFILL.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=0), (5, 9, 17, 22)),
     "prefill_all_zero": (W.QWEN3_PREFILL.scaled(n_ctx=4096, kv_cap=4096, n_q=4096, planted=0), ()),
+    # the same shape over 12288 tokens: units past query chunk 74 have more
+    # than 64 middle chunks, so their chunk scoring is screened (hi*hi, then
+    # the split products of the chunks left in contention: every tied zero
+    # chunk stays in contention)
+    "prefill_screened_mixed": (W.QWEN3_PREFILL.scaled(n_ctx=12288, kv_cap=12288, n_q=12288, planted=0),
+                               (5, 40, 90, 150)),
+    "prefill_screened_all_zero": (W.QWEN3_PREFILL.scaled(n_ctx=12288, kv_cap=12288, n_q=12288, planted=0),
+                                  ()),
     # one query chunk after 624 closed chunks: 614 middle chunks, radix select
     "radix_mixed": (W.QWEN3_PREFILL.scaled(n_ctx=40000, kv_cap=40000, q_pos0=39936, n_q=64, planted=0),
                     (100, 300, 500)),
