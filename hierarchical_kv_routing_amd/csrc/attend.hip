@@ -37,6 +37,8 @@
 #include <mutex>
 #include <tuple>
 
+#include <type_traits>
+
 #include "hga_device.h"
 
 // Scratch of hga_attend_noalloc (the split-key partials of few-unit calls),
@@ -57,7 +59,8 @@ constexpr int kTKf = 32;               // keys per LDS tile (f32 path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
-constexpr float kRescaleSum = 4096.0f; // move the reference when a lane's half sum exceeds 2^12
+constexpr float kRescaleSum = 4096.0f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f}; // move the reference when a lane's half sum exceeds 2^12
 
 struct AttendParams {
   const void* q;
@@ -320,42 +323,57 @@ constexpr int stage_bytes() {
 
 // 2^x of the 16 scores of a half (x already relative to the reference):
 // P as bf16 MFMA operands (pb[0]: keys 0..15, pb[1]: keys 16..31) and the
-// lane's partial row sum.
+// lane's partial row sum of those bf16 values.
 __device__ __forceinline__ float exp_pack(const f32x16& s, Pack8 (&pb)[2]) {
   float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; j += 2) {
     const float e0 = __builtin_amdgcn_exp2f(s[j]);
     const float e1 = __builtin_amdgcn_exp2f(s[j + 1]);
-    ps += e0 + e1;
     const f32x2 f = {e0, e1};
-    pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    const bf16x2 pk = __builtin_convertvector(f, bf16x2);
+    pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes2, ps, false);
   }
   return ps;
 }
 
-// Softmax of one 32-key half for one row: s[j] holds the score of key
-// 16*(j/8) + 8*hsub + (j%8) of the half (tokens tl[] when masked).  Scores
-// become 2^(s - ref).  The reference moves (and o, lsum are rescaled) only
-// when a lane's sum of the half's terms exceeds 2^12 (every term is then
-// bounded by 2^12), a wave-uniform branch taken rarely; the common case
-// costs one compare per half instead of a running maximum.
-template <int DB>
-__device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* tl, int hsub,
-                                             int cur0, int qpos, float& ref, float& lsum,
-                                             bool& started, f32x16 (&o)[DB], Pack8 (&pb)[2]) {
-  if (masked) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int tok = tl[16 * (j >> 3) + 8 * hsub + (j & 7)];
-      const bool ok = (tok >= 0) & ((tok < cur0) | (tok <= qpos));
-      s[j] = ok ? s[j] - ref : -INFINITY;
-    }
+// Softmax of one 32-key half for one row, in pieces that sit between
+// matrix-core products: s[j] holds the score of key 16*(j/8) + 8*hsub + (j%8)
+// of the half (tokens tl[] when masked).  sm_pair handles elements j and
+// j+1 (j even): the mask, s - ref, 2^x, the pair's bf16 P operand and the
+// lane's partial row sum (a dot product of the bf16 pair with (1, 1), so the
+// sum is the one of the P the products use).  sm_post: the reference moves
+// (and o, lsum are rescaled) only when a lane's sum of the half's terms
+// exceeds 2^12 (every term is then bounded by 2^12), a wave-uniform branch
+// taken rarely; the common case costs one compare per half instead of a
+// running maximum.  Then the half's sum joins the row sum.
+template <bool MASKED>
+__device__ __forceinline__ void sm_pair(f32x16& s, int j, const int* tl, int hsub, int cur0, int qpos,
+                                        float ref, float& ps, Pack8 (&pb)[2]) {
+  float x0 = s[j], x1 = s[j + 1];
+  if constexpr (MASKED) {
+    const int t0 = tl[16 * (j >> 3) + 8 * hsub + (j & 7)];
+    const int t1 = tl[16 * ((j + 1) >> 3) + 8 * hsub + ((j + 1) & 7)];
+    x0 = ((t0 >= 0) & ((t0 < cur0) | (t0 <= qpos))) ? x0 - ref : -INFINITY;
+    x1 = ((t1 >= 0) & ((t1 < cur0) | (t1 <= qpos))) ? x1 - ref : -INFINITY;
   } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] -= ref;
+    x0 -= ref;
+    x1 -= ref;
   }
-  float ps = exp_pack(s, pb);
+  s[j] = x0;
+  s[j + 1] = x1;
+  const float e0 = __builtin_amdgcn_exp2f(x0);
+  const float e1 = __builtin_amdgcn_exp2f(x1);
+  const f32x2 f = {e0, e1};
+  const bf16x2 pk = __builtin_convertvector(f, bf16x2);
+  pb[j >> 3].u[(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+  ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes2, ps, false);
+}
+
+template <int DB>
+__device__ __forceinline__ void sm_post(f32x16& s, float ps, float& ref, float& lsum, bool& started,
+                                        f32x16 (&o)[DB], Pack8 (&pb)[2]) {
   if (__builtin_amdgcn_ballot_w64(!started || ps > kRescaleSum) != 0) {  // wave-uniform, rare
     float mx = -INFINITY;
 #pragma unroll
@@ -363,7 +381,7 @@ __device__ __forceinline__ void softmax_half(f32x16& s, bool masked, const int* 
     const float mrow = fmaxf(mx, __shfl_xor(mx, 32));
     float delta = 0.f;
     if (!started) {
-      if (mrow > -INFINITY) {  // first visible keys of the row set the reference
+      if (mrow > -INFINITY) {
         delta = mrow;
         started = true;
       }
@@ -539,19 +557,35 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
       for (int j = 0; j < 16; ++j) o[rb][db][j] = 0.f;
   }
 
-  auto step = [&](int st) {
-    char* kl = smem + (st & 1) * SB;
-    char* vl = kl + kTK * KP;
-    int* tl = reinterpret_cast<int*>(vl + D * kVP);
-    store_stage<D, NW>(sr, kl, vl, tl);
-    const bool masked = sr.masked;
-    __syncthreads();
-    if (!rb_on[0]) {  // wave-uniform: this wave has no rows, only loads
-      load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, qend, sr);
+  // One stage, with its matrix-core products and the other work of the
+  // stage interleaved in a fixed order (scheduling barriers): S of the first
+  // key half beside the next stage's loads, S of the second half beside the
+  // softmax of the first, PV of the first beside the softmax of the second,
+  // PV of the second beside the next stage's LDS stores (into the buffer the
+  // previous stage used).  Operands are read three products ahead.
+  constexpr int NS = 2 * KS;      // S products: i -> half i / KS, slice i % KS
+  constexpr int NP = 2 * DB;      // PV products of a half: i -> kk = i / DB, db = i % DB
+  constexpr int AH = 3;
+  auto kop = [&](const char* kl, int i) {
+    return *reinterpret_cast<const bf16x8*>(kl + ((i / KS) * 32 + n) * KP + ((i % KS) * 16 + hsub * 8) * 2);
+  };
+  auto vop = [&](const char* vl, int h, int i) {
+    return *reinterpret_cast<const bf16x8*>(vl + ((i % DB) * 32 + n) * kVP + ((2 * h + i / DB) * 16 + hsub * 8) * 2);
+  };
+  auto step = [&](int st, auto mtag) {
+    constexpr bool masked = decltype(mtag)::value;
+    const char* kl = smem + (st & 1) * SB;
+    const char* vl = kl + kTK * KP;
+    const int* tl = reinterpret_cast<const int*>(vl + D * kVP);
+    char* kn = smem + ((st + 1) & 1) * SB;
+    char* vn = kn + kTK * KP;
+    int* tn = reinterpret_cast<int*>(vn + D * kVP);
+    const int knext = kbeg + (st + 1) * kTK;
+    if (!rb_on[0]) {  // wave-uniform: this wave has no rows, only loads and stores
+      load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, cur0, qend, sr);
+      store_stage<D, NW>(sr, kn, vn, tn);
       return;
     }
-    // S^T for the two 32-key halves; each K operand serves every row block.
-    // s[rb][h][j] holds key 32h + 16*(j/8) + 8*hsub + (j%8).
     f32x16 s[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -559,44 +593,99 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 16; ++j) s[rb][h][j] = 0.f;
+    bf16x8 a[AH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < AH; ++i) a[i] = kop(kl, i);
+    __builtin_amdgcn_sched_barrier(0);
+    // S of the first half, the next stage's loads after two products
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kl + (h * 32 + n) * KP + (ks * 16 + hsub * 8) * 2);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          if (rb_on[rb]) s[rb][h] = mfma32x32x16(a, qb[rb][ks].v, s[rb][h]);
-      }
-    }
-    // The next stage's loads go out behind the S products (past the last
-    // stage every key is absent: zeros, no memory traffic).
-    load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg + (st + 1) * kTK, kend, cur0, qend, sr);
-    // Per half: softmax (VALU) then O^T += V^T P^T; the second half's
-    // softmax is independent of the first half's PV products.
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      Pack8 pb[RB][2];
+    for (int i = 0; i < KS; ++i) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (rb_on[rb])
-          softmax_half<DB>(s[rb][h], masked, tl + 32 * h, hsub, cur0, qpos[rb], ref[rb], lsum[rb],
-                           started[rb], o[rb], pb[rb]);
+        if (rb_on[rb]) s[rb][0] = mfma32x32x16(a[i % AH], qb[rb][i].v, s[rb][0]);
+      if (i + AH < NS) a[i % AH] = kop(kl, i + AH);
+      if (i == 1) load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, cur0, qend, sr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // S of the second half, the softmax terms of the first
+    Pack8 pb[RB][2][2];
+    float ps[RB][2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+    for (int rb = 0; rb < RB; ++rb) ps[rb][0] = ps[rb][1] = 0.f;
+    constexpr int PPS = 8 / KS;  // element pairs per product
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              vl + (db * 32 + n) * kVP + ((2 * h + kk) * 16 + hsub * 8) * 2);
+    for (int i = KS; i < NS; ++i) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            if (rb_on[rb]) o[rb][db] = mfma32x32x16(a, pb[rb][kk].v, o[rb][db]);
-        }
-      }
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb]) s[rb][1] = mfma32x32x16(a[i % AH], qb[rb][i - KS].v, s[rb][1]);
+      if (i + AH < NS) a[i % AH] = kop(kl, i + AH);
+#pragma unroll
+      for (int q = 0; q < PPS; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb_on[rb])
+            sm_pair<masked>(s[rb][0], 2 * ((i - KS) * PPS + q), tl, hsub, cur0, qpos[rb], ref[rb], ps[rb][0],
+                            pb[rb][0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (rb_on[rb]) sm_post<DB>(s[rb][0], ps[rb][0], ref[rb], lsum[rb], started[rb], o[rb], pb[rb][0]);
+    // PV of the first half, the softmax terms of the second
+    constexpr int PPP = 8 / NP;
+#pragma unroll
+    for (int i = 0; i < AH; ++i) a[i] = vop(vl, 0, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb]) o[rb][i % DB] = mfma32x32x16(a[i % AH], pb[rb][0][i / DB].v, o[rb][i % DB]);
+      if (i + AH < NP) a[i % AH] = vop(vl, 0, i + AH);
+#pragma unroll
+      for (int q = 0; q < PPP; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb_on[rb])
+            sm_pair<masked>(s[rb][1], 2 * (i * PPP + q), tl + 32, hsub, cur0, qpos[rb], ref[rb], ps[rb][1],
+                            pb[rb][1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (rb_on[rb]) sm_post<DB>(s[rb][1], ps[rb][1], ref[rb], lsum[rb], started[rb], o[rb], pb[rb][1]);
+    // PV of the second half, the next stage's LDS stores after two products
+#pragma unroll
+    for (int i = 0; i < AH; ++i) a[i] = vop(vl, 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb_on[rb]) o[rb][i % DB] = mfma32x32x16(a[i % AH], pb[rb][1][i / DB].v, o[rb][i % DB]);
+      if (i + AH < NP) a[i % AH] = vop(vl, 1, i + AH);
+      if (i == 1) store_stage<D, NW>(sr, kn, vn, tn);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int st = 0; st < nstages; ++st) step(st);
+  if (nstages > 0) {
+    store_stage<D, NW>(sr, smem, smem + kTK * KP, reinterpret_cast<int*>(smem + kTK * KP + D * kVP));
+    __syncthreads();
+  }
+  // Masked stages (past the key range, absent keys, current-chunk keys) form
+  // a suffix of an item's stages, since tokens ascend along a list: a loop
+  // over the unmasked stages, then one over the rest (two stage bodies in
+  // sequence rather than a choice inside one loop, which the register
+  // allocator handles without spills).
+  int st = 0;
+  for (; st < nstages && !sr.masked; ++st) {
+    step(st, std::false_type{});
+    __syncthreads();  // stage st + 1 is in LDS; every read of stage st is done
+  }
+  for (; st < nstages; ++st) {
+    step(st, std::true_type{});
+    __syncthreads();
+  }
 
   // O^T register j of block db is d = db*32 + 8*(j/4) + 4*hsub + (j%4).
 #pragma unroll
