@@ -31,8 +31,9 @@ HGA_F32, HGA_BF16 = 0, 1
 # Every symbol include/hga.h declares.
 ABI_SYMBOLS = ("hga_build_summaries", "hga_max_granules", "hga_route_workspace_bytes",
                "hga_route", "hga_attend_workspace_bytes", "hga_attend", "hga_dense_causal",
-               "hga_host_tiered_buffer_bytes", "hga_attend_host_tiered",
-               "hga_decode_session_buffer_bytes", "hga_decode_session_create",
+               "hga_host_tiered_buffer_bytes", "hga_host_tiered_cache_slots", "hga_attend_host_tiered",
+               "hga_decode_session_cache_slots", "hga_decode_session_buffer_bytes",
+               "hga_decode_session_create",
                "hga_decode_session_destroy", "hga_decode_session_append",
                "hga_decode_session_step", "hga_attend_backward_workspace_bytes",
                "hga_attend_backward", "hga_attend_noalloc", "hga_attend_noalloc_max_scratch_bytes",
@@ -137,6 +138,8 @@ def lib() -> ctypes.CDLL:
         "hga_decode_step": (I32, [CP, I32, I32, P, I64, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "hga_host_tiered_buffer_bytes": (I32, [CP, I32, I32, I64, I64, I32, I64, I64,
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "hga_host_tiered_cache_slots": (I32, [CP, I32, I32, I64, I64, I32, I64, SZ, ctypes.POINTER(I64)]),
+        "hga_decode_session_cache_slots": (I32, [CP, I32, I32, I64, SZ, ctypes.POINTER(I64)]),
         "hga_attend_host_tiered": (I32, [CP, I32, I32, P, I64, I64, P, I64, P, P, P, P, P, SZ, P, SZ,
                                          I32, I64, I64, I32, P, P, ctypes.POINTER(hga_tier_stats)]),
         "hga_decode_session_buffer_bytes": (I32, [CP, I32, I32, I64, I64, ctypes.POINTER(SZ),
@@ -405,6 +408,32 @@ def host_tiered_buffer_bytes(cfg: Config, dtype, batch: int, q_pos0: int, n_q: i
                                             ctypes.byref(dev), ctypes.byref(host))
     _check(st, "hga_host_tiered_buffer_bytes")
     return dev.value, host.value
+
+
+def host_tiered_cache_slots(cfg: Config, dtype, batch: int, q_pos0: int, n_q: int,
+                            max_window_chunks: int, slots_per_window: int, headroom_bytes: int) -> int:
+    """Warm-tier granules that fit while headroom_bytes of the device's free
+    memory stay unused (0: the cold tier alone)."""
+    torch = _torch()
+    code = HGA_BF16 if dtype == torch.bfloat16 else HGA_F32
+    n = ctypes.c_int64(0)
+    st = lib().hga_host_tiered_cache_slots(ctypes.byref(cfg.c()), code, batch, q_pos0, n_q,
+                                           max_window_chunks, slots_per_window, headroom_bytes,
+                                           ctypes.byref(n))
+    _check(st, "hga_host_tiered_cache_slots")
+    return n.value
+
+
+def decode_session_cache_slots(cfg: Config, dtype, batch: int, kv_cap: int, headroom_bytes: int) -> int:
+    """Decode-session cache granules that fit while headroom_bytes of the
+    device's free memory stay unused."""
+    torch = _torch()
+    code = HGA_BF16 if dtype == torch.bfloat16 else HGA_F32
+    n = ctypes.c_int64(0)
+    st = lib().hga_decode_session_cache_slots(ctypes.byref(cfg.c()), code, batch, kv_cap, headroom_bytes,
+                                              ctypes.byref(n))
+    _check(st, "hga_decode_session_cache_slots")
+    return n.value
 
 
 def host_store(cfg: Config, k_rot, v):

@@ -370,6 +370,28 @@ hga_status tiered_cached(const hga::Geometry& g, const Layout& L, const void* q_
   return HGA_OK;
 }
 
+// The largest n in [lo, hi] with fits(n) (fits is monotone: true up to
+// some n), or lo - 1 when fits(lo) fails.
+template <typename Fits>
+int64_t largest_fitting(int64_t lo, int64_t hi, Fits fits) {
+  if (hi < lo || !fits(lo)) return lo - 1;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (fits(mid)) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Device memory that can be given to a warm tier while `headroom` bytes of
+// the current device's free memory stay unused.
+hga_status free_budget(size_t headroom, size_t& budget) {
+  size_t free_b = 0, total_b = 0;
+  const hipError_t e = hipMemGetInfo(&free_b, &total_b);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  budget = free_b > headroom ? free_b - headroom : 0;
+  return HGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +410,34 @@ hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, 
   const Layout L = make_layout(g, max_window_chunks, slots_per_window, cache_slots);
   *device_bytes = L.dev_total;
   *host_bytes = L.host_total;
+  return HGA_OK;
+}
+
+hga_status hga_host_tiered_cache_slots(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                       int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
+                                       int64_t slots_per_window, size_t headroom_bytes,
+                                       int64_t* cache_slots) {
+  if (cfg == nullptr || cache_slots == nullptr || cfg->chunk_size <= 0 || cfg->group_size <= 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  const int64_t cap = ((q_pos0 + n_q + cfg->chunk_size - 1) / cfg->chunk_size) * cfg->chunk_size;
+  hga::Geometry g;
+  hga_status st = tier_geometry(cfg, dtype, batch, q_pos0, n_q, cap > 0 ? cap : cfg->chunk_size,
+                                max_window_chunks, slots_per_window, 0, g);
+  if (st != HGA_OK) return st;
+  size_t budget = 0;
+  st = free_budget(headroom_bytes, budget);
+  if (st != HGA_OK) return st;
+  const int64_t lo = static_cast<int64_t>(g.B) * g.Hkv * g.gmax;         // a window's granules
+  const int64_t hi = static_cast<int64_t>(g.B) * g.Hkv * (g.kv_cap / g.gs);  // all of the call's
+  auto fits = [&](int64_t n) {
+    hga::Geometry gc;
+    if (tier_geometry(cfg, dtype, batch, q_pos0, n_q, g.kv_cap, max_window_chunks, slots_per_window, n, gc) !=
+        HGA_OK)
+      return false;
+    return make_layout(gc, max_window_chunks, slots_per_window, n).dev_total <= budget;
+  };
+  const int64_t n = largest_fitting(lo, std::max(lo, hi), fits);
+  *cache_slots = n >= lo ? n : 0;
   return HGA_OK;
 }
 
@@ -685,6 +735,27 @@ struct hga_decode_session {
 };
 
 extern "C" {
+
+hga_status hga_decode_session_cache_slots(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                          int64_t kv_cap, size_t headroom_bytes, int64_t* cache_slots) {
+  if (cfg == nullptr || cache_slots == nullptr) return HGA_ERR_INVALID_ARGUMENT;
+  hga::Geometry g;
+  hga_status st = session_geometry(cfg, dtype, batch, kv_cap, kv_cap - 1, g);
+  if (st != HGA_OK) return st;
+  size_t budget = 0;
+  st = free_budget(headroom_bytes, budget);
+  if (st != HGA_OK) return st;
+  const int64_t lo = static_cast<int64_t>(g.B) * g.Hkv * g.gmax;         // one step's granules
+  const int64_t hi = static_cast<int64_t>(g.B) * g.Hkv * (kv_cap / g.gs);  // the whole store
+  auto fits = [&](int64_t n) {
+    SessionLayout L;
+    return session_layout(cfg, dtype, batch, kv_cap, n, L) == HGA_OK && L.dev_total <= budget;
+  };
+  const int64_t n = largest_fitting(lo, std::max(lo, hi), fits);
+  if (n < lo) return HGA_ERR_WORKSPACE_TOO_SMALL;  // a session needs one step's granules
+  *cache_slots = n;
+  return HGA_OK;
+}
 
 hga_status hga_decode_session_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                            int64_t kv_cap, int64_t cache_slots,

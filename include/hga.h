@@ -339,6 +339,24 @@ hga_status hga_host_tiered_buffer_bytes(const hga_config* cfg, hga_dtype dtype, 
                                         int64_t slots_per_window, int64_t cache_slots,
                                         size_t* device_bytes, size_t* host_bytes);
 
+/*
+ * Warm-tier size under a VRAM headroom (the tiered store of the xllm-io
+ * page, section 3: the warm tier is bounded so that a configurable amount of
+ * device memory stays free).  The library allocates nothing, so the policy
+ * is a sizing call: *cache_slots receives the largest cache_slots whose
+ * dev_staging (hga_host_tiered_buffer_bytes with these arguments) leaves at
+ * least headroom_bytes of the current device's free memory (hipMemGetInfo,
+ * read now) unused, at most one slot per granule of the call's context, or 0
+ * when even the smallest warm tier (B * Hkv * hga_max_granules(cfg) slots)
+ * does not fit: the call then runs on the cold tier alone.  Recomputing it
+ * before a call shrinks or grows the tier with the memory other work holds.
+ * HGA_ERR_HIP when the device cannot be queried.
+ */
+hga_status hga_host_tiered_cache_slots(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                       int64_t q_pos0, int64_t n_q, int32_t max_window_chunks,
+                                       int64_t slots_per_window, size_t headroom_bytes,
+                                       int64_t* cache_slots);
+
 hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                   const void* q_raw, int64_t q_pos0, int64_t n_q,
                                   const void* kv_host, int64_t kv_cap,
@@ -425,6 +443,13 @@ hga_status hga_attend_backward(const hga_config* cfg, hga_dtype dtype, int32_t b
  * Calls on one session must not overlap.
  */
 typedef struct hga_decode_session hga_decode_session;
+
+/* The same sizing for a decode session's cache: the largest cache_slots
+ * whose dev_buffer (hga_decode_session_buffer_bytes) leaves headroom_bytes
+ * of the device's free memory unused, at most one slot per granule of
+ * kv_cap; HGA_ERR_WORKSPACE_TOO_SMALL when one step's granules do not fit. */
+hga_status hga_decode_session_cache_slots(const hga_config* cfg, hga_dtype dtype, int32_t batch,
+                                          int64_t kv_cap, size_t headroom_bytes, int64_t* cache_slots);
 
 hga_status hga_decode_session_buffer_bytes(const hga_config* cfg, hga_dtype dtype, int32_t batch,
                                            int64_t kv_cap, int64_t cache_slots,
