@@ -1240,23 +1240,19 @@ unsigned resident_grid(Kernel k, int threads, int64_t n) {
   return static_cast<unsigned>(n < v ? n : v);
 }
 
+// bf16 calls always run 8 waves per workgroup (make_plan).
 template <int D, int RB, bool POOL>
-void launch_mfma(int nw, int64_t nblocks, hipStream_t stream, const AttendParams& p) {
-  if (nw == 4) {
-    auto k = attend_mfma_kernel<D, 4, RB, POOL>;
-    hipLaunchKernelGGL(k, dim3(resident_grid(k, 256, nblocks)), dim3(256), 0, stream, p);
-  } else {
-    auto k = attend_mfma_kernel<D, 8, RB, POOL>;
-    hipLaunchKernelGGL(k, dim3(resident_grid(k, 512, nblocks)), dim3(512), 0, stream, p);
-  }
+void launch_mfma(int64_t nblocks, hipStream_t stream, const AttendParams& p) {
+  auto k = attend_mfma_kernel<D, 8, RB, POOL>;
+  hipLaunchKernelGGL(k, dim3(resident_grid(k, 512, nblocks)), dim3(512), 0, stream, p);
 }
 
 template <int D, int RB>
-void launch_mfma_pool(int nw, int64_t nblocks, hipStream_t stream, const AttendParams& p) {
+void launch_mfma_pool(int64_t nblocks, hipStream_t stream, const AttendParams& p) {
   if (p.pool_slot != nullptr)
-    launch_mfma<D, RB, true>(nw, nblocks, stream, p);
+    launch_mfma<D, RB, true>(nblocks, stream, p);
   else
-    launch_mfma<D, RB, false>(nw, nblocks, stream, p);
+    launch_mfma<D, RB, false>(nblocks, stream, p);
 }
 
 template <int D>
@@ -1275,7 +1271,7 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
   p.nblocks = groups * 8 * p.per_unit;
   const unsigned grid = static_cast<unsigned>(p.nblocks);
   if (g.bf16) {
-    launch_mfma_pool<D, 1>(pl.nw, p.nblocks, stream, p);
+    launch_mfma_pool<D, 1>(p.nblocks, stream, p);
   } else {
     hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(64), 0, stream, p);
   }
