@@ -27,7 +27,7 @@ Every timed region is preceded by half a second of dense matrix products, so
 that the GPU runs at its steady clock whatever --warmup is.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prefill|decode|smalllm|host|stream|backward|copy|peaks]
+       [--only prefill|decode|smalllm|tiny|host|stream|backward|copy|peaks]
 """
 from __future__ import annotations
 

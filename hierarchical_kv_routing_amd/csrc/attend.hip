@@ -30,8 +30,9 @@
 // out-of-range keys.  Few-unit calls (decode) split each unit's keys over
 // several workgroups and merge (m, l, O) partials in combine_kernel.
 //
-// f32 path (attend_f32_kernel): one wave per 64 rows, one lane per row,
-// K/V tiles in LDS, f32 vector ALU; exact to f32 rounding.
+// f32 path (attend_f32_kernel): four waves per 64 rows, four lanes per row
+// (each owns a quarter of d), K/V tiles in LDS, f32 vector ALU; a score is
+// the sum of the row's four lane partials; exact to f32 rounding.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -746,15 +747,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-// f32 inputs: one wave per 64 rows, one lane per row.
+// f32 inputs: 64 rows per workgroup, four consecutive lanes per row.  Lane
+// part q of a row owns the 16-byte chunks q, q + 4, q + 8, ... of d: the
+// four lanes of a row read 64 contiguous bytes of a K/V row per LDS read
+// (one broadcast read serves the wave's 16 rows), and since d/2 is a
+// multiple of 16 floats, the partner i + d/2 of each of a lane's RoPE
+// dimensions i < d/2 is in the lane's own chunks.  Each lane forms its
+// partial q.k over its d/4 dimensions; two DPP exchanges inside the quad
+// give every lane of the row the full score, so the softmax state (m, l) is
+// the same in the four lanes and each keeps O for its own dimensions.
+__device__ __forceinline__ float quad_sum(float x) {
+  // quad_perm [1,0,3,2], then [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttendParams p) {
   constexpr int TK = kTKf;
   constexpr int H = D / 2;
+  constexpr int NC = D / 16;  // 16-byte chunks per lane
+  static_assert(H % 16 == 0, "pair partners in the lane's own chunks");
   __shared__ __align__(16) float kt[TK][D];
   __shared__ __align__(16) float vt[TK][D];
   __shared__ int tk[TK];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int part = tid & 3;
   int64_t u;
   int item;
   if (!block_item(p, blockIdx.x, u, item)) return;
@@ -767,34 +786,46 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
   int kend = kbeg + p.keys_per_split;
   if (kend > w.nkeys) kend = w.nkeys;
 
-  const int row = r0 + lane;
+  const int row = r0 + (tid >> 2);
   const bool row_ok = row < w.R;
   const int qloc = row_ok ? row / p.G : 0;
   const int hl = row_ok ? row - qloc * p.G : 0;
   const int qpos = static_cast<int>(w.qlo) + qloc;
   const double qrot = static_cast<double>(rope_base(p.rope, w.qlo) + qloc);
-  float q[D];
+  // chunk c of the lane covers dimensions 4 * (part + 4 c) .. + 3
+  auto dim0 = [&](int c) { return 4 * (part + 4 * c); };
+  float q[NC][4];
   {
     const float* src = static_cast<const float*>(p.q) +
         ((static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl) * p.q_stride + (qpos - p.q_row0)) * D;
+    float4 raw[NC];
 #pragma unroll
-    for (int i = 0; i < H; ++i) {
-      const float a = row_ok ? src[i] : 0.f, b = row_ok ? src[i + H] : 0.f;
-      float c, s;
-      rope_cs(qrot, rope_freq(p.rope, i), c, s);
-      q[i] = (a * c - b * s) * p.scale_log2;
-      q[i + H] = (a * s + b * c) * p.scale_log2;
+    for (int c = 0; c < NC; ++c)
+      raw[c] = row_ok ? *reinterpret_cast<const float4*>(src + dim0(c)) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < NC / 2; ++c) {
+      const float a[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+      const float b[4] = {raw[c + NC / 2].x, raw[c + NC / 2].y, raw[c + NC / 2].z, raw[c + NC / 2].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float cs, sn;
+        rope_cs(qrot, rope_freq(p.rope, dim0(c) + e), cs, sn);
+        q[c][e] = (a[e] * cs - b[e] * sn) * p.scale_log2;
+        q[c + NC / 2][e] = (a[e] * sn + b[e] * cs) * p.scale_log2;
+      }
     }
   }
-  float o[D];
+  float o[NC][4];
 #pragma unroll
-  for (int i = 0; i < D; ++i) o[i] = 0.f;
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[c][e] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
   const int64_t slab = (static_cast<int64_t>(w.b) * p.Hkv + w.kvh) * p.kv_cap;
   const int cur0 = static_cast<int>(w.t * p.C);
   for (int kb = kbeg; kb < kend; kb += TK) {
     __syncthreads();
-    for (int idx = lane; idx < TK * D / 4; idx += 64) {
+    for (int idx = tid; idx < TK * D / 4; idx += 256) {
       const int s = idx / (D / 4), c4 = idx - s * (D / 4);
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       const int tok = kb + s < kend ? slot_token(p, w, kb + s) : -1;
@@ -807,7 +838,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
       reinterpret_cast<float4*>(&kt[s][0])[c4] = kk;
       reinterpret_cast<float4*>(&vt[s][0])[c4] = vv;
     }
-    if (lane < TK) tk[lane] = (kb + lane < kend) ? slot_token(p, w, kb + lane) : -1;
+    if (tid < TK) tk[tid] = (kb + tid < kend) ? slot_token(p, w, kb + tid) : -1;
     __syncthreads();
     float sc[TK];
     float mx = kNegBig;
@@ -815,7 +846,14 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     for (int s = 0; s < TK; ++s) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < D; ++i) acc = fmaf(q[i], kt[s][i], acc);
+      for (int c = 0; c < NC; ++c) {
+        const float4 kk = *reinterpret_cast<const float4*>(&kt[s][dim0(c)]);
+        acc = fmaf(q[c][0], kk.x, acc);
+        acc = fmaf(q[c][1], kk.y, acc);
+        acc = fmaf(q[c][2], kk.z, acc);
+        acc = fmaf(q[c][3], kk.w, acc);
+      }
+      acc = quad_sum(acc);
       const int tok = tk[s];
       const bool ok = tok >= 0 && (tok < cur0 || tok <= qpos);
       sc[s] = ok ? acc : -INFINITY;
@@ -825,13 +863,21 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     const float alpha = exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < D; ++i) o[i] *= alpha;
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[c][e] *= alpha;
 #pragma unroll
     for (int s = 0; s < TK; ++s) {
       const float e = exp2f(sc[s] - m_new);
       l_run += e;
 #pragma unroll
-      for (int i = 0; i < D; ++i) o[i] = fmaf(e, vt[s][i], o[i]);
+      for (int c = 0; c < NC; ++c) {
+        const float4 vv = *reinterpret_cast<const float4*>(&vt[s][dim0(c)]);
+        o[c][0] = fmaf(e, vv.x, o[c][0]);
+        o[c][1] = fmaf(e, vv.y, o[c][1]);
+        o[c][2] = fmaf(e, vv.z, o[c][2]);
+        o[c][3] = fmaf(e, vv.w, o[c][3]);
+      }
     }
     m_run = m_new;
   }
@@ -841,14 +887,19 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendParams p) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* out = static_cast<float*>(p.out) + orow * D;
 #pragma unroll
-    for (int i = 0; i < D; ++i) out[i] = o[i] * inv;
-    if (p.lse != nullptr) p.lse[orow] = (m_run + log2f(l_run)) * kLn2;
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<float4*>(out + dim0(c)) =
+          make_float4(o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv);
+    if (p.lse != nullptr && part == 0) p.lse[orow] = (m_run + log2f(l_run)) * kLn2;
   } else {
     const int64_t pr = (w.slot * p.splits + split) * p.Rcap + row;
 #pragma unroll
-    for (int i = 0; i < D; ++i) p.ws_o[pr * D + i] = o[i];
-    p.ws_ml[pr * 2] = m_run;
-    p.ws_ml[pr * 2 + 1] = l_run;
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<float4*>(p.ws_o + pr * D + dim0(c)) = make_float4(o[c][0], o[c][1], o[c][2], o[c][3]);
+    if (part == 0) {
+      p.ws_ml[pr * 2] = m_run;
+      p.ws_ml[pr * 2 + 1] = l_run;
+    }
   }
 }
 
@@ -1178,14 +1229,14 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
     pl.nw = 8;
     pl.slices = static_cast<int>((wblocks + pl.nw - 1) / pl.nw);
   } else {
-    pl.nw = 1;
+    pl.nw = 4;
     pl.slices = static_cast<int>((rows + 63) / 64);
   }
   const int64_t wgs = pl.units * pl.slices;
   const int64_t keys = max_keys(g, dense);
   pl.splits = 1;
   pl.kps = static_cast<int>(keys);
-  if (allow_split && wgs < 512 && keys > 256) {
+  if (allow_split && wgs < 512 && keys > (g.bf16 ? 256 : 64)) {
     int64_t sp, want;
     if (g.bf16) {
       // About one work item per CU (the bf16 kernel keeps one workgroup per
@@ -1194,7 +1245,8 @@ Plan make_plan(const Geometry& g, bool dense, bool allow_split) {
       sp = (keys + kTK - 1) / kTK;
       want = (device_cus() + wgs - 1) / wgs;
     } else {
-      sp = (keys + 127) / 128;
+      // f32: splits of about 64 keys, up to about 1024 workgroups
+      sp = (keys + 63) / 64;
       want = (1024 + wgs - 1) / wgs;
     }
     if (sp > want) sp = want;
@@ -1273,7 +1325,7 @@ hipError_t launch_attend_d(const Geometry& g, AttendParams& p, const Plan& pl, h
   if (g.bf16) {
     launch_mfma_pool<D, 1>(p.nblocks, stream, p);
   } else {
-    hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((attend_f32_kernel<D>), dim3(grid), dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
