@@ -19,6 +19,41 @@ namespace {
 
 constexpr int kSumWaves = 4;
 
+// sin and cos of a (double): reduction to r in [-pi, pi] (two-part 2*pi,
+// as rope_cs), Taylor series at x = r/16 (|x| < 0.2; terms through x^11
+// and x^12, below 1e-18), then four angle doublings; for the per-token step
+// of the rotation, where a relative error of 1e-15 is far below the f32
+// rounding that follows.
+__device__ __forceinline__ void sincos_step(double a, double& sn, double& cs) {
+  const double kTwoPiHi = 6.283185307179586;
+  const double kTwoPiLo = 2.4492935982947064e-16;
+  const double kInvTwoPi = 0.15915494309189535;
+  const double k = rint(a * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, a);
+  r = fma(-k, kTwoPiLo, r);
+  const double x = r * 0.0625;
+  const double x2 = x * x;
+  double sv = fma(x2, -1.0 / 39916800.0, 1.0 / 362880.0);
+  sv = fma(x2, sv, -1.0 / 5040.0);
+  sv = fma(x2, sv, 1.0 / 120.0);
+  sv = fma(x2, sv, -1.0 / 6.0);
+  sv = fma(x2 * x, sv, x);
+  double cv = fma(x2, 1.0 / 479001600.0, -1.0 / 3628800.0);
+  cv = fma(x2, cv, 1.0 / 40320.0);
+  cv = fma(x2, cv, -1.0 / 720.0);
+  cv = fma(x2, cv, 1.0 / 24.0);
+  cv = fma(x2, cv, -0.5);
+  cv = fma(x2, cv, 1.0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double s2 = 2.0 * sv * cv;
+    cv = fma(cv, cv, -sv * sv);
+    sv = s2;
+  }
+  sn = sv;
+  cs = cv;
+}
+
 struct SumParams {
   const void* k_raw;
   void* k_rot;
@@ -32,11 +67,11 @@ struct SumParams {
   RopeFreqs rope;
 };
 
-template <bool BF16>
+template <bool BF16, int D>
 __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int h = p.d >> 1;
+  constexpr int h = D / 2;
   const int64_t m = p.chunk_first + blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -47,6 +82,8 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
   const bool active = lane < h;
   const double freq = active ? rope_freq(p.rope, lane) : 0.0;
   const bool high = lane < p.n_hf;
+  double cs1, sn1;  // cos/sin of one position step of the pair
+  sincos_step(freq, sn1, cs1);
 
   float cx = 0.f, cy = 0.f;  // chunk partial sums of this wave (rotated or raw per pair kind)
   for (int g = wave; g < p.r; g += kSumWaves) {
@@ -56,21 +93,43 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
     const int64_t gw = rope_base(p.rope, g0);  // rotation position of token g0
     float sx = 0.f, sy = 0.f;
     if (active) {
-      for (int64_t j = g0; j < jend; ++j) {
-        const int64_t e = (slab + j) * p.d + lane;
-        const float x = load1<BF16>(p.k_raw, e);
-        const float y = load1<BF16>(p.k_raw, e + h);
-        float c, s;
-        rope_cs(static_cast<double>(gw + (j - g0)), freq, c, s);
-        const float rx = x * c - y * s;
-        const float ry = x * s + y * c;
-        if (p.k_rot != nullptr && j >= p.tok_begin) {
-          store1<BF16>(p.k_rot, e, rx);
-          store1<BF16>(p.k_rot, e + h, ry);
+      // cos/sin at the group's first position as rope_cs gives them; each
+      // later token's by one more rotation by theta, carried in double so
+      // that the g_s - 1 steps add no f32 roundings (every token's pair is
+      // within about one f32 ulp of the exact cos/sin, like rope_cs's)
+      float c0, s0;
+      rope_cs(static_cast<double>(gw), freq, c0, s0);
+      double c = c0, s = s0;
+      constexpr int kBatch = 8;  // token rows in flight per lane
+      for (int64_t j0 = g0; j0 < jend; j0 += kBatch) {
+        float xs[kBatch], ys[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          const int64_t e = (slab + (j0 + t < jend ? j0 + t : j0)) * D + lane;
+          xs[t] = load1<BF16>(p.k_raw, e);
+          ys[t] = load1<BF16>(p.k_raw, e + h);
         }
-        // high-frequency pairs average rotated keys, low-frequency pairs raw keys
-        sx += high ? rx : x;
-        sy += high ? ry : y;
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          const int64_t j = j0 + t;
+          if (j < jend) {
+            const float x = xs[t], y = ys[t];
+            const float cf = static_cast<float>(c), sf = static_cast<float>(s);
+            const float rx = x * cf - y * sf;
+            const float ry = x * sf + y * cf;
+            if (p.k_rot != nullptr && j >= p.tok_begin) {
+              const int64_t e = (slab + j) * D + lane;
+              store1<BF16>(p.k_rot, e, rx);
+              store1<BF16>(p.k_rot, e + h, ry);
+            }
+            // high-frequency pairs average rotated keys, low-frequency pairs raw keys
+            sx += high ? rx : x;
+            sy += high ? ry : y;
+            const double cn = c * cs1 - s * sn1;
+            s = s * cs1 + c * sn1;
+            c = cn;
+          }
+        }
       }
       const bool done = g1 <= p.tok_end && g1 > p.tok_begin;
       if (done && p.group_sum != nullptr) {
@@ -84,8 +143,8 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
           oy = mx * s + my * c;
         }
         const int64_t row = (static_cast<int64_t>(b) * p.Hkv + kvh) * (p.kv_cap / p.gs) + g0 / p.gs;
-        p.group_sum[row * p.d + lane] = ox;
-        p.group_sum[row * p.d + lane + h] = oy;
+        p.group_sum[row * D + lane] = ox;
+        p.group_sum[row * D + lane + h] = oy;
       }
     }
     cx += sx;
@@ -115,8 +174,8 @@ __global__ __launch_bounds__(kSumWaves * 64) void summarize_kernel(SumParams p) 
       oy = mx * s + my * c;
     }
     const int64_t row = (static_cast<int64_t>(b) * p.Hkv + kvh) * (p.kv_cap / p.C) + m;
-    p.chunk_sum[row * p.d + lane] = ox;
-    p.chunk_sum[row * p.d + lane + h] = oy;
+    p.chunk_sum[row * D + lane] = ox;
+    p.chunk_sum[row * D + lane + h] = oy;
   }
 }
 
@@ -147,10 +206,14 @@ hipError_t launch_summarize(const Geometry& g, const void* k_raw, int64_t tok_be
   const int64_t chunk_last = (tok_end - 1) / g.C;
   dim3 grid(static_cast<unsigned>(chunk_last - p.chunk_first + 1), g.Hkv, g.B);
   dim3 block(kSumWaves * 64);
-  if (g.bf16)
-    hipLaunchKernelGGL(summarize_kernel<true>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(summarize_kernel<false>, grid, block, 0, stream, p);
+  // head_dim is 64 or 128 (checked with the configuration)
+  if (g.bf16) {
+    if (g.d == 128) hipLaunchKernelGGL((summarize_kernel<true, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((summarize_kernel<true, 64>), grid, block, 0, stream, p);
+  } else {
+    if (g.d == 128) hipLaunchKernelGGL((summarize_kernel<false, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((summarize_kernel<false, 64>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
