@@ -203,7 +203,6 @@ struct StageRegs {
   static constexpr int kPer = (kItems + NW * 64 - 1) / (NW * 64);
   uint4 k0[kPer], k1[kPer], v0[kPer], v1[kPer];
   int t0[kPer], t1[kPer];
-  bool masked;
 };
 
 // Buffer resource over `bytes` bytes from `base`: a load whose offset is
@@ -230,13 +229,40 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // offset kNoRow (zeros) and token -1.  No branches: the stage's first key kb
 // is a multiple of g_s, so a key's table entry is the stage's first entry
 // plus a per-thread constant.
+//
+// fast (a uniform flag): every key of the stage is valid and before the
+// current chunk, and g_s >= 2, so the two keys of a pair share a granule.
+// Then a thread reads one table entry for its K pair and one for its V
+// pair, forms the offsets without any validity test, and leaves the token
+// slots unset (only masked stages read tokens, and those are never fast).
 template <int D, int NW>
 __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffer_rsrc_t kr,
                                            __amdgpu_buffer_rsrc_t vr, const int2* gtab, int gfirst,
-                                           int kb, int kend, int cur0, int qend, StageRegs<D, NW>& r) {
+                                           int kb, int kend, int qend, bool fast, StageRegs<D, NW>& r) {
   constexpr int SL = StageRegs<D, NW>::SL;
   const int lg = p.lg_gs, gm = (1 << lg) - 1;
   const int gbase = (kb >> lg) - gfirst;
+  if (fast) {
+    const int* gx = reinterpret_cast<const int*>(gtab) + 2 * gbase;
+#pragma unroll
+    for (int i = 0; i < StageRegs<D, NW>::kPer; ++i) {
+      const int idx = threadIdx.x + i * NW * 64;
+      if (idx < StageRegs<D, NW>::kItems) {
+        const int kpk = idx / SL, slk = idx - kpk * SL;
+        const int kpv = idx & 31, slv = idx >> 5;
+        const int ek = gx[2 * ((2 * kpk) >> lg)];
+        const int ev = gx[2 * ((2 * kpv) >> lg)];
+        const uint32_t ok = static_cast<uint32_t>(ek + ((2 * kpk) & gm)) * (D * 2) + slk * 16;
+        const uint32_t ov = static_cast<uint32_t>(ev + ((2 * kpv) & gm)) * (D * 2) + slv * 16;
+        r.k0[i] = load16(kr, ok);
+        r.k1[i] = load16(kr, ok + D * 2);
+        r.v0[i] = load16(vr, ov);
+        r.v1[i] = load16(vr, ov + D * 2);
+        r.t0[i] = r.t1[i] = 0;
+      }
+    }
+    return;
+  }
   const int rem = kend - kb;  // keys of the stage before kend
   // Table entries as single 64-bit LDS reads, all issued before any is used.
   auto entry = [&](int s) {
@@ -275,14 +301,6 @@ __device__ __forceinline__ void load_stage(const AttendParams& p, __amdgpu_buffe
       r.v1[i] = load16(vr, o1);
     }
   }
-  // Tokens ascend along a list, so the stage needs masks iff it runs past the
-  // end of the key range or its last key is absent or in the current chunk.
-  int last = (rem < kTK ? rem : kTK) - 1;
-  last = last > 0 ? last : 0;  // a stage past the end (rem <= 0) is masked anyway
-  const int2 e = gtab[gbase + (last >> lg)];
-  const int tl = e.x >= 0 ? e.y + (last & gm) : -1;
-  // the same value on every lane: make it a scalar so branches on it are uniform
-  r.masked = __builtin_amdgcn_readfirstlane(static_cast<int>((kb + kTK > kend) || tl < 0 || tl >= cur0)) != 0;
 }
 
 template <int D, int NW>
@@ -462,8 +480,13 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
 
   // Granule table of the item's key range (rows and tokens of each granule's
   // first key), read once so that stage loads need no dependent global load.
+  // Each wave also finds its first table entry that is absent or in the
+  // current chunk (wfb[wave]): tokens ascend along a list, so every key
+  // before the first such entry (and before kend) is valid and unmasked.
   int2* gtab = reinterpret_cast<int2*>(smem + kMain);
+  int* wfb = reinterpret_cast<int*>(smem + kMain + kTab * 8);
   const int gfirst = kbeg >> p.lg_gs;
+  int fb = kTab;
   if (kend > kbeg) {
     const int ng = ((kend - 1) >> p.lg_gs) - gfirst + 1;  // <= kTab (make_plan)
     const int64_t gcap = p.kv_cap >> p.lg_gs;
@@ -481,8 +504,12 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
         }
       }
       gtab[i] = t;
+      if ((t.x < 0 || t.y >= cur0) && i < fb) fb = i;
     }
   }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) fb = min(fb, __shfl_xor(fb, m));
+  if (lane == 0) wfb[wave] = fb;
 
   // RoPE table for the queries of this workgroup's rows.
   const int rend = (r0 + kRows) < w.R ? (r0 + kRows) : w.R;
@@ -507,10 +534,21 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
     kr = buffer_rsrc(static_cast<const char*>(p.k) + slab, bytes);
     vr = buffer_rsrc(static_cast<const char*>(p.v) + slab, bytes);
   }
-  // The first stage's loads go out before the query rows are rotated.
+  // Stages [0, nu) hold only valid keys before the current chunk (no masks);
+  // their loads take the fast path when g_s >= 2 (nfast).
   const int nstages = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+  int nu;
+  {
+    int f = wfb[0];
+#pragma unroll
+    for (int x = 1; x < NW; ++x) f = min(f, wfb[x]);
+    const int good = min(f << p.lg_gs, kend - kbeg);
+    nu = __builtin_amdgcn_readfirstlane(good > 0 ? good / kTK : 0);
+  }
+  const int nfast = p.lg_gs >= 1 ? nu : 0;
+  // The first stage's loads go out before the query rows are rotated.
   StageRegs<D, NW> sr;
-  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, cur0, qend, sr);
+  if (nstages > 0) load_stage<D, NW>(p, kr, vr, gtab, gfirst, kbeg, kend, qend, nfast > 0, sr);
 
   // Rotate, scale by softmax_scale * log2(e) and round the query rows to
   // bf16 MFMA operands.
@@ -573,8 +611,9 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   auto vop = [&](const char* vl, int h, int i) {
     return *reinterpret_cast<const bf16x8*>(vl + ((i % DB) * 32 + n) * kVP + ((2 * h + i / DB) * 16 + hsub * 8) * 2);
   };
-  auto step = [&](int st, auto mtag) {
+  auto step = [&](int st, auto mtag, auto ftag) {
     constexpr bool masked = decltype(mtag)::value;
+    constexpr bool fast = decltype(ftag)::value;  // the next stage's loads take the fast path
     const char* kl = smem + (st & 1) * SB;
     const char* vl = kl + kTK * KP;
     const int* tl = reinterpret_cast<const int*>(vl + D * kVP);
@@ -583,7 +622,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
     int* tn = reinterpret_cast<int*>(vn + D * kVP);
     const int knext = kbeg + (st + 1) * kTK;
     if (!rb_on[0]) {  // wave-uniform: this wave has no rows, only loads and stores
-      load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, cur0, qend, sr);
+      load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, qend, fast, sr);
       store_stage<D, NW>(sr, kn, vn, tn);
       return;
     }
@@ -605,7 +644,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
       for (int rb = 0; rb < RB; ++rb)
         if (rb_on[rb]) s[rb][0] = mfma32x32x16(a[i % AH], qb[rb][i].v, s[rb][0]);
       if (i + AH < NS) a[i % AH] = kop(kl, i + AH);
-      if (i == 1) load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, cur0, qend, sr);
+      if (i == 1) load_stage<D, NW>(p, kr, vr, gtab, gfirst, knext, kend, qend, fast, sr);
       __builtin_amdgcn_sched_barrier(0);
     }
     // S of the second half, the softmax terms of the first
@@ -678,13 +717,20 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   // over the unmasked stages, then one over the rest (two stage bodies in
   // sequence rather than a choice inside one loop, which the register
   // allocator handles without spills).
+  // The unmasked stages whose successor is also fast-loaded run a body with
+  // only the fast load path (a body with both paths would merge their load
+  // registers, which makes the loads wait).
   int st = 0;
-  for (; st < nstages && !sr.masked; ++st) {
-    step(st, std::false_type{});
+  for (; st + 1 < nfast; ++st) {
+    step(st, std::false_type{}, std::true_type{});
     __syncthreads();  // stage st + 1 is in LDS; every read of stage st is done
   }
+  for (; st < nu; ++st) {
+    step(st, std::false_type{}, std::false_type{});
+    __syncthreads();
+  }
   for (; st < nstages; ++st) {
-    step(st, std::true_type{});
+    step(st, std::true_type{}, std::false_type{});
     __syncthreads();
   }
 
@@ -740,7 +786,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
 // workgroup dispatch separates one item from the next.
 template <int D, int NW, int RB, bool POOL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_mfma_kernel(AttendParams p) {
-  __shared__ __align__(16) char smem[attend_main_bytes<D>() + kTab * 8];
+  __shared__ __align__(16) char smem[attend_main_bytes<D>() + kTab * 8 + 64];
   for (int64_t bx = blockIdx.x; bx < p.nblocks; bx += gridDim.x) {
     attend_item<D, NW, RB, POOL>(p, bx, smem);
     __syncthreads();  // the next item rewrites the LDS tables
