@@ -735,6 +735,12 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
   }
 
   // O^T register j of block db is d = db*32 + 8*(j/4) + 4*hsub + (j%4).
+  // Unsplit items stage their bf16 rows in LDS (the stage buffers are free
+  // once the last stage's barrier has passed) and write whole rows, 16 bytes
+  // per lane: a lane's own pieces of a row are 8 bytes at 16-byte strides,
+  // which would touch 32 rows' cache lines per store instruction.
+  constexpr int OP = D * 2 + 16;  // bytes per staged output row
+  static_assert(kRows * OP <= kMain, "the output tile fits the stage buffers");
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if (!rb_on[rb]) continue;
@@ -744,7 +750,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
         (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + hl[rb]) * p.q_stride + (qpos[rb] - p.q_row0);
     if (p.splits == 1) {
       const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-      uint16_t* out = static_cast<uint16_t*>(p.out) + orow * D;
+      char* ot = smem + (row[rb] - r0) * OP;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -755,7 +761,7 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
           uint2 pk;
           pk.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f0, bf16x2));
           pk.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f1, bf16x2));
-          *reinterpret_cast<uint2*>(out + d0) = pk;
+          *reinterpret_cast<uint2*>(ot + d0 * 2) = pk;
         }
       }
       if (p.lse != nullptr && hsub == 0)
@@ -776,6 +782,20 @@ __device__ __forceinline__ void attend_item(const AttendParams& p, int64_t bx, c
         p.ws_ml[pr * 2] = started[rb] ? ref[rb] : kNegBig;
         p.ws_ml[pr * 2 + 1] = lrow;
       }
+    }
+  }
+  if (p.splits == 1) {  // uniform
+    __syncthreads();
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+    const int nrows = (w.R - r0) < kRows ? (w.R - r0) : kRows;
+    for (int i = threadIdx.x; i < nrows * CPR; i += NW * 64) {
+      const int lr = i / CPR, c = i - lr * CPR;
+      const int r = r0 + lr;
+      const int qi = r / p.G;
+      const int64_t orow = (static_cast<int64_t>(w.b) * p.Hq + w.kvh * p.G + (r - qi * p.G)) * p.q_stride +
+                           (w.qlo + qi - p.q_row0);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow * D + c * 8) =
+          *reinterpret_cast<const uint4*>(smem + lr * OP + c * 16);
     }
   }
 }
