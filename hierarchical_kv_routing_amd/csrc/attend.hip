@@ -1166,8 +1166,7 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
       mx = fmaxf(mx, sv[t][i]);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xor32_max(xor16_max(mx));
   // P (f32, rows x keys) and the wave's V rows into its LDS regions.
   float ls = 0.f;
 #pragma unroll
@@ -1180,8 +1179,7 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendParams p) {
     ls += (e4.x + e4.y) + (e4.z + e4.w);
     *reinterpret_cast<float4*>(&pw[wave][n][t * 16 + sub * 4]) = e4;
   }
-  ls += __shfl_xor(ls, 16);
-  ls += __shfl_xor(ls, 32);
+  ls = xor32_sum(xor16_sum(ls));
   char* vw = vbuf + wave * kDecWaveKeys * VP;
 #pragma unroll
   for (int j = 0; j < kDecWaveKeys; ++j) {

@@ -159,13 +159,9 @@ __device__ __forceinline__ void score_rows(int n, RowPtr row, const float (&qv)[
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = a0[i] + a1[i];  // row 4 kg + i of the tile, query row l%16
-      v = fmaxf(v, __shfl_xor(v, 8));
-      v = fmaxf(v, __shfl_xor(v, 4));
-      v = fmaxf(v, __shfl_xor(v, 2));
-      v = fmaxf(v, __shfl_xor(v, 1));
+      const float v = row16_max(a0[i] + a1[i]);  // row 4 kg + i of the tile, max over query rows l%16
       const int c = tile * 16 + 4 * kg + i;
-      if (m == 0 && c < n) emit(c, v);
+      if (m == 0 && c < n) emit(c, plus_zero(v));
     }
   };
   float4 x0[S], x1[S];
@@ -256,6 +252,8 @@ __device__ __forceinline__ void attend_wave(const Pack8 (&qb)[D / 32], const Wav
     *reinterpret_cast<uint4*>(vw + (j * KV::RPI + lane / KV::CPR) * VP + (lane % KV::CPR) * 16) = kv.vq[j];
   float sv[2][4];
   mx = kNegBigD;
+  // key k of the wave is present iff bit k of the ballot is set (lane k names it)
+  const uint64_t present = __ballot(kv.tok >= 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -263,13 +261,12 @@ __device__ __forceinline__ void attend_wave(const Pack8 (&qb)[D / 32], const Wav
     for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(kv.ka[t][ks].v, qb[ks].v, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kt = __shfl(kv.tok, t * 16 + sub * 4 + i);
-      sv[t][i] = kt >= 0 ? acc[i] : -INFINITY;
+      const bool on = (present >> (t * 16 + sub * 4 + i)) & 1ull;
+      sv[t][i] = on ? acc[i] : -INFINITY;
       mx = fmaxf(mx, sv[t][i]);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xor32_max(xor16_max(mx));
   Pack8 pa;
   ls = 0.f;
 #pragma unroll
@@ -280,8 +277,7 @@ __device__ __forceinline__ void attend_wave(const Pack8 (&qb)[D / 32], const Wav
     pa.u[2 * t] = pack_bf16x2(e0, e1);
     pa.u[2 * t + 1] = pack_bf16x2(e2, e3);
   }
-  ls += __shfl_xor(ls, 16);
-  ls += __shfl_xor(ls, 32);
+  ls = xor32_sum(xor16_sum(ls));
   // the wave's own LDS rows: a wave-local wait suffices
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();

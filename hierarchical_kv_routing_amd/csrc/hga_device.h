@@ -154,6 +154,39 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // -0 -> +0, so that equal values get equal order keys.
 __device__ __forceinline__ float plus_zero(float f) { return f == 0.f ? 0.f : f; }
 
+// Cross-lane reductions without the LDS crossbar.  row16_max: the max over
+// the 16 lanes of each DPP row (lanes 16r .. 16r + 15), in every lane of
+// the row (rotations by 8, 4, 2, 1 within the row).  xor16_* / xor32_*:
+// each lane combined with lane ^ 16 / lane ^ 32 (gfx950's permlane swaps;
+// with both operands the same register, the two results hold the two
+// partners, so their max or sum is the pair's in every lane).
+template <int N>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_row_ror<8>(v));
+  v = fmaxf(v, dpp_row_ror<4>(v));
+  v = fmaxf(v, dpp_row_ror<2>(v));
+  return fmaxf(v, dpp_row_ror<1>(v));
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Matrix-core wrappers (gfx950 double-rate bf16 forms).
 //   16x16x32: A[m][k] m = lane%16; B[k][n] n = lane%16; each lane brings 8
 //             k-values (the same k slots for A and B);
