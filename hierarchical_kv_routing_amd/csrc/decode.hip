@@ -521,7 +521,20 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(DecodeParams 
   score_rows<D>(n, [&](int c) { return cbase + static_cast<int64_t>(c) * D; }, qv, setup,
                 [&](int c, float s) { ss.keys[c] = order_key(s); });
   __syncthreads();
-  const int nl = block_select(ss.keys, n, p.Kc, ss.sel, ss.scr);
+  int nl;
+  if (p.Kc < n && n <= 256) {  // one wave selects (ballot radix), no block-wide passes
+    if (tid < 64) {
+      auto key = [&](int i) { return ss.keys[i]; };
+      if (n <= 64) wave_select<1>(key, n, p.Kc, ss.sel);
+      else if (n <= 128) wave_select<2>(key, n, p.Kc, ss.sel);
+      else if (n <= 192) wave_select<3>(key, n, p.Kc, ss.sel);
+      else wave_select<4>(key, n, p.Kc, ss.sel);
+    }
+    __syncthreads();
+    nl = p.Kc;
+  } else {
+    nl = block_select(ss.keys, n, p.Kc, ss.sel, ss.scr);
+  }
   uint32_t* dk = useg + static_cast<int64_t>(idx) * p.Kc;
   uint32_t* di = dk + ncand;
   if (p.Kg > 0) {
@@ -622,9 +635,49 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(DecodePar
   fill_cs<D>(p, sm.cs);
   if (tid == 0) sm.nselc = sm.nselg = 0;
   lds_barrier();
-  if (routing) {
+  const int want = routing ? static_cast<int>(std::min<int64_t>(p.Kc, n_mid)) : 0;
+  if (routing && ncand <= 64 && (p.Kg <= 0 || std::min(want, ncand) * p.r <= 64)) {
+    // wave 0 makes both selections (ballot radix select, no block-wide
+    // passes): at most 64 segment winners and 64 groups of the chosen chunks
     auto& ms = sm.u.merge;
-    const int want = static_cast<int>(std::min<int64_t>(p.Kc, n_mid));
+    if (wave == 0) {
+      const int nselc = want < ncand ? want : ncand;
+      if (want < ncand) {
+        wave_select<1>([&](int i) { return ms.keys[i]; }, ncand, want, ms.pos);
+      } else if (lane < ncand) {
+        ms.pos[lane] = lane;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+      __builtin_amdgcn_wave_barrier();
+      if (lane < nselc) sm.selc[lane] = ms.offs[ms.pos[lane]] + static_cast<int>(p.sink_hi);
+      int nselg = 0;
+      if (p.Kg > 0) {
+        const int nc = nselc * p.r;
+        auto gkey = [&](int c) {
+          const int i = c / p.r;
+          return ms.gks[ms.pos[i] * p.r + (c - i * p.r)];
+        };
+        nselg = p.Kg < nc ? p.Kg : nc;
+        if (p.Kg < nc) {
+          wave_select<1>(gkey, nc, p.Kg, sm.selg);
+        } else if (lane < nc) {
+          sm.selg[lane] = lane;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < nselg) {
+          const int c = sm.selg[lane];
+          const int i = c / p.r;
+          sm.selg[lane] = sm.selc[i] * p.r + (c - i * p.r);
+        }
+      }
+      if (lane == 0) {
+        sm.nselc = nselc;
+        sm.nselg = nselg;
+      }
+    }
+  } else if (routing) {
+    auto& ms = sm.u.merge;
     const int nselc = block_select(ms.keys, ncand, want, ms.pos, ms.scr);
     for (int i = tid; i < nselc; i += NTH) sm.selc[i] = ms.offs[ms.pos[i]] + static_cast<int>(p.sink_hi);
     int nselg = 0;

@@ -110,6 +110,66 @@ __device__ __forceinline__ int rank_select(const uint32_t* keys, int n, int k, i
   return k;
 }
 
+// Top-k (0 < k < n <= 64*S) by one wave, no barrier: the k-th largest key
+// by a most-significant-bit-first search over wave ballots (key i held by
+// lane i % 64 of slot i / 64; per bit, the alive keys with the bit set are
+// counted from the ballots), the keys above it all taken, then the
+// lowest-index keys equal to it; indices written to out[] ascending.  Same
+// result as block_select.  key(i) gives the order key of candidate i.
+template <int S, typename KeyAt>
+__device__ __forceinline__ void wave_select(KeyAt key, int n, int k, int* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v[S];
+  uint64_t alive[S], sel[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int i = s * 64 + lane;
+    v[s] = i < n ? key(i) : 0u;
+    alive[s] = __ballot(i < n);
+    sel[s] = 0ull;
+  }
+  int need = k, na = n;  // na: alive keys
+  for (int b = 31; b >= 0 && need < na; --b) {
+    uint64_t on[S];
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      on[s] = alive[s] & __ballot((v[s] >> b) & 1u);
+      cnt += __popcll(on[s]);
+    }
+    if (cnt >= need) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) alive[s] = on[s];
+      na = cnt;
+    } else {
+      need -= cnt;
+      na -= cnt;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        sel[s] |= on[s];
+        alive[s] &= ~on[s];
+      }
+    }
+  }
+  // need == na: every alive key is taken; need < na only when the alive
+  // keys are all equal (every bit decided), and the lowest indices go first
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    while (need > 0 && alive[s] != 0ull) {
+      const uint64_t low = alive[s] & (~alive[s] + 1ull);
+      sel[s] |= low;
+      alive[s] ^= low;
+      --need;
+    }
+  }
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if ((sel[s] >> lane) & 1ull) out[base + __popcll(sel[s] & ((1ull << lane) - 1ull))] = s * 64 + lane;
+    base += __popcll(sel[s]);
+  }
+}
+
 // Top-k selection for small inputs without the radix passes: n <= 128 with
 // k <= 64 (one wave sorts everything), or n <= 128 * waves with k <= 16 (each
 // wave sorts 128 keys and keeps its top k, one wave sorts the survivors).
