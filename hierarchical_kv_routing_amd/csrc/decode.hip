@@ -572,7 +572,6 @@ struct FinishSmem {
   } u;
   float2 cs[D / 2];
   int selc[256], selg[256];
-  int routed[kDsMaxRouted];
   int nselc, nselg;
 };
 
@@ -705,21 +704,25 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(DecodePar
   __syncthreads();
   const int nselc = sm.nselc, nselg = sm.nselg;
   const int nrouted = p.Kg > 0 ? nselg : nselc * p.r;
-  for (int j = tid; j < nrouted; j += NTH)
-    sm.routed[j] = p.Kg > 0 ? sm.selg[j] : sm.selc[j / p.r] * p.r + (j - (j / p.r) * p.r);
+  // routed tokens, 256 keys per round: token of routed key k, from the
+  // selections in LDS; the first round's K/V loads go out before the lists
+  // are written and the query is rotated
+  const int64_t nkeys = static_cast<int64_t>(nrouted) * p.gs;
+  auto tok_of = [&](int64_t k) -> int {
+    if (k >= nkeys) return -1;
+    const int j = static_cast<int>(k >> p.lg_gs);
+    const int g = p.Kg > 0 ? sm.selg[j] : sm.selc[j / p.r] * p.r + (j - (j / p.r) * p.r);
+    return g * p.gs + static_cast<int>(k & (p.gs - 1));
+  };
+  WaveKV<D> kv;
+  load_wave_kv<D>(p, slab, tok_of(wave * kDsWaveKeys + (lane & 31)), kv);
   if (p.gran != nullptr) write_lists(p, u, sm.selc, nselc, sm.selg, nselg);
-  __syncthreads();
   Pack8 qb[D / 32];
   rotate_query<D>(p, sm.cs, xq, qb);
-  // routed tokens, 256 keys per round
   auto& sa = sm.u.attn;
-  reset_running<D, 8>(sa);
-  const int64_t nkeys = static_cast<int64_t>(nrouted) * p.gs;
+  reset_running<D, 8>(sa);  // fold_round's first barrier orders it before any read
   for (int64_t k0 = 0; k0 < nkeys; k0 += 8 * kDsWaveKeys) {
-    const int64_t k = k0 + wave * kDsWaveKeys + (lane & 31);
-    const int tok = k < nkeys ? sm.routed[k >> p.lg_gs] * p.gs + static_cast<int>(k & (p.gs - 1)) : -1;
-    WaveKV<D> kv;
-    load_wave_kv<D>(p, slab, tok, kv);
+    if (k0 > 0) load_wave_kv<D>(p, slab, tok_of(k0 + wave * kDsWaveKeys + (lane & 31)), kv);
     fold_round<D, 8>(qb, kv, R, sa);
   }
   // merge with the window partials: output rows and LSE
