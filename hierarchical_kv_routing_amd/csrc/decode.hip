@@ -573,6 +573,7 @@ struct FinishSmem {
   float2 cs[D / 2];
   int selc[256], selg[256];
   int nselc, nselg;
+  float wpart[win_floats(D)];  // the window partials, parked once the selection is done
 };
 
 template <int D, int RP>
@@ -708,6 +709,12 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(DecodePar
   // selections in LDS; the first round's K/V loads go out before the lists
   // are written and the query is rotated
   const int64_t nkeys = static_cast<int64_t>(nrouted) * p.gs;
+  // the window partials (loaded first, in registers since) into their LDS region
+#pragma unroll
+  for (int k = 0; k < kDsWinRegs; ++k) {
+    const int64_t i = tid + static_cast<int64_t>(k) * NTH;
+    if (i < nwf) sm.wpart[i] = wreg[k];
+  }
   auto tok_of = [&](int64_t k) -> int {
     if (k >= nkeys) return -1;
     const int j = static_cast<int>(k >> p.lg_gs);
@@ -720,20 +727,63 @@ __global__ __launch_bounds__(kFinishThreads) void decode_finish_kernel(DecodePar
   Pack8 qb[D / 32];
   rotate_query<D>(p, sm.cs, xq, qb);
   auto& sa = sm.u.attn;
+  constexpr int SS = RP * (D + 2);  // floats per window partial
+  if (nkeys <= 8 * kDsWaveKeys) {
+    // One round: the eight waves' partials and the window partials are
+    // merged in one pass; each wave's O rows overwrite its own V tile once
+    // its products have read it.
+    float mx, ls;
+    f32x4 ot[D / 16];
+    attend_wave<D, 8>(qb, kv, sa, mx, ls, ot);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's V reads are done
+    __builtin_amdgcn_wave_barrier();
+    float* wo = reinterpret_cast<float*>(sa.vbuf + wave * kDsWaveKeys * vpitch<D>());  // [16][D]
+    const int n = lane & 15, sub = lane >> 4;
+    if (sub == 0) {
+      sa.wm[wave][n] = mx;
+      sa.wl[wave][n] = ls;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = sub * 4 + i;
+        if (rr < R) wo[rr * D + c * 16 + n] = ot[c][i];
+      }
+    __syncthreads();
+    for (int i = tid; i < R * D; i += NTH) {
+      const int rr = i / D, d = i - rr * D;
+      float m = kNegBigD;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) m = fmaxf(m, sa.wm[x][rr]);
+      for (int s = 0; s < p.nwin; ++s) m = fmaxf(m, sm.wpart[s * SS + RP * D + 2 * rr]);
+      float l = 0.f, acc = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float sc = exp2f(sa.wm[x][rr] - m);
+        l += sa.wl[x][rr] * sc;
+        acc += reinterpret_cast<const float*>(sa.vbuf + x * kDsWaveKeys * vpitch<D>())[rr * D + d] * sc;
+      }
+      for (int s = 0; s < p.nwin; ++s) {
+        const float sc = exp2f(sm.wpart[s * SS + RP * D + 2 * rr] - m);
+        l += sm.wpart[s * SS + RP * D + 2 * rr + 1] * sc;
+        acc += sm.wpart[s * SS + rr * D + d] * sc;
+      }
+      const int64_t orow = static_cast<int64_t>(b) * p.Hq + kvh * p.G + rr;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      store1<true>(p.out, orow * D + d, acc * inv);
+      if (p.lse != nullptr && d == 0) p.lse[orow] = (m + log2f(l)) * kLn2D;
+    }
+    return;
+  }
   reset_running<D, 8>(sa);  // fold_round's first barrier orders it before any read
   for (int64_t k0 = 0; k0 < nkeys; k0 += 8 * kDsWaveKeys) {
     if (k0 > 0) load_wave_kv<D>(p, slab, tok_of(k0 + wave * kDsWaveKeys + (lane & 31)), kv);
     fold_round<D, 8>(qb, kv, R, sa);
   }
-  // merge with the window partials: output rows and LSE
-  float* win = reinterpret_cast<float*>(sa.vbuf);  // free once the rounds are done
-#pragma unroll
-  for (int k = 0; k < kDsWinRegs; ++k) {
-    const int64_t i = tid + static_cast<int64_t>(k) * NTH;
-    if (i < nwf) win[i] = wreg[k];
-  }
-  __syncthreads();
-  constexpr int SS = RP * (D + 2);  // floats per window partial
+  // merge with the window partials: output rows and LSE (fold_round ended
+  // with a barrier, which also made the parked partials visible)
+  const float* win = sm.wpart;
   for (int i = tid; i < R * D; i += NTH) {
     const int rr = i / D, d = i - rr * D;
     float m = sa.run_m[rr];
