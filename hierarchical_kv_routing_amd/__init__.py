@@ -569,8 +569,10 @@ class DecodeSession:
             group_sum.data_ptr() if group_sum is not None else None, ctypes.c_void_p(s.cuda_stream))
         _check(st, "hga_decode_session_append")
 
-    def step(self, q, pos: int, chunk_sum, group_sum, out, lse=None, stream=None) -> dict:
-        """One query per sequence at position pos: q, out [B][Hq][1][d]."""
+    def step(self, q, pos: int, chunk_sum, group_sum, out, lse=None, stream=None, stats=True):
+        """One query per sequence at position pos: q, out [B][Hq][1][d].
+        With stats, waits for the step and returns its cache counts;
+        without, only enqueues it and returns None."""
         torch = _torch()
         cfg = self.cfg
         shape = (self.batch, cfg.n_q_heads, 1, cfg.head_dim)
@@ -580,14 +582,16 @@ class DecodeSession:
         _dev(chunk_sum, "chunk_sum")
         _dev(group_sum, "group_sum")
         cs = stream if stream is not None else torch.cuda.current_stream(q.device)
-        stats = hga_tier_stats()
+        rec = hga_tier_stats() if stats else None
         st = lib().hga_decode_session_step(
             self._h, q.data_ptr(), pos, chunk_sum.data_ptr(),
             group_sum.data_ptr() if group_sum is not None else None, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, ctypes.c_void_p(cs.cuda_stream),
-            ctypes.byref(stats))
+            ctypes.byref(rec) if rec is not None else None)
         _check(st, "hga_decode_session_step")
-        return {f: getattr(stats, f) for f, _ in hga_tier_stats._fields_}
+        if rec is None:
+            return None
+        return {f: getattr(rec, f) for f, _ in hga_tier_stats._fields_}
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value is not None:

@@ -627,43 +627,212 @@ hga_status hga_attend_host_tiered(const hga_config* cfg, hga_dtype dtype, int32_
 // step moves only the granules its routes need; a device cache keeps
 // granules across steps (consecutive steps re-route mostly the same ones).
 //
-// A session holds, across steps, the device cache's slot map and LRU order
-// (host memory) and carves the caller's device / host buffers:
+// A session carves the caller's device / host buffers:
 //   device: route outputs, route and attention workspaces, the granule
-//           cache, a landing buffer for one step's misses, the per-entry
-//           cache slots, and the raw and rotated keys of the current chunk;
-//   host:   the granule lists, the landing staging and the slot arrays.
+//           cache and its directory (slot of every (sequence, KV head,
+//           granule), owner, token count and last-use step of every slot,
+//           a replacement hand), the per-entry cache slots and one step's
+//           miss list, and the raw and rotated keys of the current chunk;
+//   host:   the step's hit / miss counts, read back only when asked.
 // append() rotates a new token's key on the device (and builds the chunk /
 // group summaries a token closes, from the current chunk's raw keys), then
-// copies its rotated key and value into the host store.  step() routes the
-// step's queries, copies the lists to the host (a synchronisation), looks up
-// the cache (a granule copied when it held fewer tokens than the step needs,
-// i.e. the granule being filled, counts as a miss) and sends the miss list
-// to the device, where a gather kernel reads the missing granules straight
-// from the pinned store over the host link (no host-side packing) into their
-// cache slots; then the decode attention runs over the cache.
+// copies its rotated key and value into the host store.  step() enqueues,
+// with no host wait: the routing of the step's queries; one workgroup that
+// looks every listed granule up in the directory (a granule cached while
+// it held fewer tokens than the step needs, i.e. the granule being filled,
+// counts as a miss), gives each granule without a slot a victim slot (the
+// next slots from the hand that this step does not use, in ring order) and
+// writes the miss list; a gather kernel that reads the missing granules
+// straight from the pinned store over the host link (no host-side packing)
+// into their cache slots; then the decode attention over the cache.
 // ---------------------------------------------------------------------------
 namespace {
 
 struct SessionLayout {
-  int64_t units = 0, per_step = 0;
+  int64_t units = 0, per_step = 0, keys = 0;
   size_t granule_bytes = 0, row_bytes = 0;
-  // the slot map and the miss list (sources, then destinations) are
-  // contiguous on both sides: one host-to-device copy
   size_t cidx = 0, gidx = 0, gran = 0, gcnt = 0, rws = 0, aws = 0, cache = 0, idx = 0,
-         win_raw = 0, win_rot = 0, dev_total = 0;
-  size_t hgran = 0, hcnt = 0, hidx = 0, host_total = 0;
+         win_raw = 0, win_rot = 0, dir = 0, dev_total = 0;
+  size_t hstate = 0, host_total = 0;
   size_t rws_bytes = 0, aws_bytes = 0, idx_bytes = 0, slots_off = 0, src_off = 0, dst_off = 0;
+  // directory block: slot_of [keys], owner / fill / stamp [cache_slots],
+  // victim [per_step] (int32 each), state [16] int32 (hand, misses, hits)
+  size_t slot_of_off = 0, owner_off = 0, fill_off = 0, stamp_off = 0, victim_off = 0, state_off = 0,
+         dir_bytes = 0;
 };
 
+constexpr int kDirThreads = 1024;
+
+struct DirParams {
+  const int32_t* gran;   // [units][gmax] the step's granule lists
+  const int32_t* gcnt;   // [units]
+  int32_t* slot_of;      // [units * ngran] cache slot of a (unit, granule) or -1
+  int32_t* owner;        // [cache_slots] key held by a slot or -1
+  int32_t* fill;         // [cache_slots] tokens of the slot's granule copy
+  int32_t* stamp;        // [cache_slots] last step that used the slot (-1: never)
+  int32_t* victim;       // [per_step] scratch: the step's victim slots
+  int32_t* slots;        // [units][gmax] out: cache slot per list entry, -1 past the count
+  int64_t* src;          // [per_step] out: store granule of each miss
+  int32_t* dst;          // [per_step] out: its cache slot
+  int32_t* state;        // [0] hand, [1] misses, [2] hits, [3] slots missing (0 unless a bug)
+  int64_t units, gmax, ngran, cache_slots, pos;
+  int32_t gs, step;
+};
+
+// Exclusive rank of this thread's flag among the workgroup's set flags, in
+// thread order, and their total; every thread of the workgroup calls it.
+__device__ int block_rank(bool flag, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wave_tot[wv] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < kDirThreads / 64; ++w) {
+    const int c = wave_tot[w];
+    before += w < wv ? c : 0;
+    tot += c;
+  }
+  __syncthreads();  // wave_tot is rewritten by the next call
+  total = tot;
+  return before + in_wave;
+}
+
+// The decode session's cache directory, one workgroup per step: entries
+// whose granule has a slot mark it used in this step; the entries without
+// one take, in entry order, the next slots from the hand (ring order) that
+// this step does not use, evicting their owners; an entry is a miss when
+// its slot is new or holds fewer tokens than the step needs.  Slots used in
+// the step (every fixed-window granule, every step) are never victims, and
+// one step's entries fit the cache (cache_slots >= per_step), so the victim
+// search ends within one pass over the slots.
+__global__ __launch_bounds__(kDirThreads) void directory_kernel(DirParams p) {
+  __shared__ int wave_tot[kDirThreads / 64];
+  __shared__ int s_need, s_hits;
+  __shared__ long long s_hand;
+  const int tid = threadIdx.x;
+  const int64_t n = p.units * p.gmax;
+  if (tid == 0) {
+    s_need = 0;
+    s_hits = 0;
+    s_hand = p.state[0];
+  }
+  __syncthreads();
+  // 1. lookups; a found slot is marked used in this step
+  int need = 0;
+  for (int64_t e = tid; e < n; e += kDirThreads) {
+    const int64_t x = e / p.gmax;
+    int32_t sl = -2;  // no entry
+    const int64_t gid = p.gran[e];
+    if (e - x * p.gmax < p.gcnt[x] && gid >= 0 && gid < p.ngran) {
+      sl = p.slot_of[x * p.ngran + gid];
+      if (sl >= 0) p.stamp[sl] = p.step;
+      else ++need;
+    }
+    p.slots[e] = sl;
+  }
+  atomicAdd(&s_need, need);
+  __syncthreads();
+  const int R = s_need;
+  const int64_t hand = s_hand;
+  // 2. R victims: the slots this step does not use, from the hand on
+  int found = 0;
+  for (int64_t base = 0; found < R && base < p.cache_slots; base += kDirThreads) {
+    const int64_t j = base + tid;
+    int32_t slot = -1;
+    bool fr = false;
+    if (j < p.cache_slots) {
+      slot = static_cast<int32_t>((hand + j) % p.cache_slots);
+      fr = p.stamp[slot] != p.step;
+    }
+    int tot = 0;
+    const int r = found + block_rank(fr, wave_tot, tot);
+    if (fr && r < R) {
+      p.victim[r] = slot;
+      if (r == R - 1) s_hand = (slot + 1) % p.cache_slots;
+    }
+    found += tot;
+  }
+  const int have = found < R ? found : R;
+  // 3. new slots (in entry order), misses, the per-entry slots
+  int new_base = 0, miss_base = 0, hits = 0;
+  for (int64_t e0 = 0; e0 < n; e0 += kDirThreads) {
+    const int64_t e = e0 + tid;
+    int32_t sl = -2, last = 0;
+    int64_t k = 0;
+    if (e < n) {
+      sl = p.slots[e];
+      if (sl != -2) {
+        const int64_t x = e / p.gmax, gid = p.gran[e];
+        k = x * p.ngran + gid;
+        const int64_t left = p.pos + 1 - gid * p.gs;  // tokens this step needs
+        last = static_cast<int32_t>(left < p.gs ? left : p.gs);
+      }
+    }
+    const bool fresh = sl == -1;
+    int tot = 0;
+    const int r = new_base + block_rank(fresh, wave_tot, tot);
+    new_base += tot;
+    if (fresh) {
+      if (r < have) {
+        sl = p.victim[r];
+        const int32_t prev = p.owner[sl];
+        if (prev >= 0) p.slot_of[prev] = -1;
+        p.owner[sl] = static_cast<int32_t>(k);
+        p.slot_of[k] = sl;
+        p.stamp[sl] = p.step;
+      } else {
+        sl = -2;  // unreachable while cache_slots >= per_step; counted below
+      }
+    }
+    const bool miss = sl >= 0 && (fresh || p.fill[sl] < last);
+    const int m = miss_base + block_rank(miss, wave_tot, tot);
+    miss_base += tot;
+    if (miss) {
+      p.fill[sl] = last;
+      p.src[m] = k;
+      p.dst[m] = sl;
+    }
+    hits += (sl >= 0 && !miss) ? 1 : 0;
+    if (e < n) p.slots[e] = sl >= 0 ? sl : -1;
+  }
+  atomicAdd(&s_hits, hits);
+  __syncthreads();
+  if (tid == 0) {
+    p.state[0] = static_cast<int32_t>(s_hand);
+    p.state[1] = miss_base;
+    p.state[2] = s_hits;
+    p.state[3] = R - have;
+  }
+}
+
+// Empty directory: no granule has a slot, no slot an owner or a use.
+__global__ __launch_bounds__(256) void directory_init(int32_t* slot_of, int64_t keys, int32_t* owner,
+                                                      int32_t* fill, int32_t* stamp, int64_t slots,
+                                                      int32_t* state) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < keys; i += stride) slot_of[i] = -1;
+  for (int64_t i = i0; i < slots; i += stride) {
+    owner[i] = -1;
+    fill[i] = 0;
+    stamp[i] = -1;
+  }
+  if (i0 < 16) state[i0] = 0;
+}
+
 // Reads granule src[j] of the pinned host store (through its device
-// mapping, over the host link) into cache slot dst[j]; one workgroup per
-// granule, 16-byte words.
+// mapping, over the host link) into cache slot dst[j] for j < *count (the
+// directory's miss count); workgroups stride over the misses, 16-byte words.
 __global__ __launch_bounds__(256) void fetch_granules(const uint4* store, const int64_t* src,
-                                                      const int32_t* dst, uint4* cache, int64_t words) {
-  const uint4* in = store + src[blockIdx.x] * words;
-  uint4* out = cache + static_cast<int64_t>(dst[blockIdx.x]) * words;
-  for (int64_t i = threadIdx.x; i < words; i += blockDim.x) out[i] = in[i];
+                                                      const int32_t* dst, const int32_t* count,
+                                                      uint4* cache, int64_t words) {
+  const int32_t n = *count;
+  for (int32_t j = blockIdx.x; j < n; j += gridDim.x) {
+    const uint4* in = store + src[j] * words;
+    uint4* out = cache + static_cast<int64_t>(dst[j]) * words;
+    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) out[i] = in[i];
+  }
 }
 
 // Geometry of a decode call at position pos (one query per sequence).
@@ -706,12 +875,20 @@ hga_status session_layout(const hga_config* cfg, hga_dtype dtype, int32_t batch,
   L.idx = off; off = align_up(off + L.idx_bytes);
   L.win_raw = off; off = align_up(off + u * g.C * L.row_bytes);
   L.win_rot = off; off = align_up(off + u * g.C * L.row_bytes);
+  // the directory keys (unit, granule) and slots as int32
+  L.keys = L.units * (kv_cap / g.gs);
+  if (L.keys >= 2147483647 || cache_slots >= 2147483647) return HGA_ERR_UNSUPPORTED;
+  L.slot_of_off = 0;
+  L.owner_off = align_up(static_cast<size_t>(L.keys) * 4);
+  L.fill_off = align_up(L.owner_off + static_cast<size_t>(cache_slots) * 4);
+  L.stamp_off = align_up(L.fill_off + static_cast<size_t>(cache_slots) * 4);
+  L.victim_off = align_up(L.stamp_off + static_cast<size_t>(cache_slots) * 4);
+  L.state_off = align_up(L.victim_off + static_cast<size_t>(L.per_step) * 4);
+  L.dir_bytes = align_up(L.state_off + 16 * 4);
+  L.dir = off; off = align_up(off + L.dir_bytes);
   L.dev_total = off;
-  size_t h = 0;
-  L.hgran = h; h = align_up(h + u * g.gmax * 4);
-  L.hcnt = h; h = align_up(h + u * 4);
-  L.hidx = h; h = align_up(h + L.idx_bytes);
-  L.host_total = h;
+  L.hstate = 0;
+  L.host_total = align_up(16 * 4);
   return HGA_OK;
 }
 
@@ -727,11 +904,9 @@ struct hga_decode_session {
   char* host;
   char* store;
   const uint4* store_dev;        // the store's device mapping
-  Lru lru;
-  std::vector<int64_t> slot_of;  // (sequence, KV head, granule) -> cache slot or -1
-  std::vector<int32_t> fill;     // cache slot -> tokens of its granule copy
+  int32_t steps = 0;             // steps enqueued (the directory's use stamps)
+  bool dir_ready = false;        // directory cleared on the device
   int64_t next_pos;              // position append() expects next
-  explicit hga_decode_session(int64_t slots) : lru(slots) {}
 };
 
 extern "C" {
@@ -795,7 +970,7 @@ hga_status hga_decode_session_create(const hga_config* cfg, hga_dtype dtype, int
   }
   hga_decode_session* s = nullptr;
   try {
-    s = new hga_decode_session(cache_slots);
+    s = new hga_decode_session();
     s->cfg = *cfg;
     s->dtype = dtype;
     s->batch = batch;
@@ -807,8 +982,6 @@ hga_status hga_decode_session_create(const hga_config* cfg, hga_dtype dtype, int
     s->host = static_cast<char*>(host_buffer);
     s->store = static_cast<char*>(kv_host);
     s->store_dev = static_cast<const uint4*>(store_dev);
-    s->slot_of.assign(static_cast<size_t>(L.units * s->ngran), -1);
-    s->fill.assign(static_cast<size_t>(cache_slots), 0);
     s->next_pos = first_pos;
   } catch (...) {
     delete s;
@@ -876,85 +1049,74 @@ hga_status hga_decode_session_step(hga_decode_session* s, const void* q_raw, int
   char* host = s->host;
   int32_t* d_gran = reinterpret_cast<int32_t*>(dev + L.gran);
   int32_t* d_gcnt = reinterpret_cast<int32_t*>(dev + L.gcnt);
-  hipError_t e = hga::launch_route(g, q_raw, chunk_sum, group_sum, reinterpret_cast<int32_t*>(dev + L.cidx),
-                                   g.Kg > 0 ? reinterpret_cast<int32_t*>(dev + L.gidx) : nullptr, d_gran,
-                                   d_gcnt, dev + L.rws, cs);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(host + L.hgran, d_gran, static_cast<size_t>(L.per_step) * 4,
-                       hipMemcpyDeviceToHost, cs);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(host + L.hcnt, d_gcnt, static_cast<size_t>(L.units) * 4, hipMemcpyDeviceToHost, cs);
-  // also orders every earlier step's gathers and attention, and every
-  // append's store copies, before the host rewrites the index block
-  if (e == hipSuccess) e = hipStreamSynchronize(cs);
-  if (e != hipSuccess) return hga::hip_fail(e);
-
-  const int32_t* h_gran = reinterpret_cast<const int32_t*>(host + L.hgran);
-  const int32_t* h_gcnt = reinterpret_cast<const int32_t*>(host + L.hcnt);
-  char* hidx = host + L.hidx;
-  int32_t* h_slots = reinterpret_cast<int32_t*>(hidx + L.slots_off);
-  int64_t* h_src = reinterpret_cast<int64_t*>(hidx + L.src_off);
-  int32_t* h_dst = reinterpret_cast<int32_t*>(hidx + L.dst_off);
-  int64_t miss = 0, hits = 0;
-  for (int64_t x = 0; x < L.units; ++x) {
-    const int32_t cnt = h_gcnt[x];
-    for (int32_t i = 0; i < g.gmax; ++i) {
-      if (i >= cnt) {
-        h_slots[x * g.gmax + i] = -1;
-        continue;
-      }
-      const int64_t gid = h_gran[x * g.gmax + i];
-      const int64_t k = x * s->ngran + gid;
-      const int64_t last = std::min<int64_t>(g.gs, pos + 1 - gid * g.gs);  // tokens this step needs
-      int64_t sl = s->slot_of[static_cast<size_t>(k)];
-      if (sl >= 0 && s->fill[static_cast<size_t>(sl)] >= last) {
-        ++hits;
-      } else {
-        if (sl < 0) {
-          sl = s->lru.victim();  // untouched in this step (per_step <= cache_slots)
-          const int64_t prev = s->lru.owner(sl);
-          if (prev >= 0) s->slot_of[static_cast<size_t>(prev)] = -1;
-          s->lru.set_owner(sl, k);
-          s->slot_of[static_cast<size_t>(k)] = sl;
-        }
-        s->fill[static_cast<size_t>(sl)] = static_cast<int32_t>(last);
-        h_src[miss] = k;
-        h_dst[miss] = static_cast<int32_t>(sl);
-        ++miss;
-      }
-      s->lru.touch(sl);
-      h_slots[x * g.gmax + i] = static_cast<int32_t>(sl);
-    }
+  char* dir = dev + L.dir;
+  int32_t* d_state = reinterpret_cast<int32_t*>(dir + L.state_off);
+  hipError_t e = hipSuccess;
+  if (!s->dir_ready) {
+    hipLaunchKernelGGL(directory_init, dim3(256), dim3(256), 0, cs,
+                       reinterpret_cast<int32_t*>(dir + L.slot_of_off), L.keys,
+                       reinterpret_cast<int32_t*>(dir + L.owner_off), reinterpret_cast<int32_t*>(dir + L.fill_off),
+                       reinterpret_cast<int32_t*>(dir + L.stamp_off), s->cache_slots, d_state);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hga::hip_fail(e);
+    s->dir_ready = true;
   }
-  const double lookup_s =
-      std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
-  // the index block to the device, then the misses straight from the store
-  e = hipMemcpyAsync(dev + L.idx, hidx, L.idx_bytes, hipMemcpyHostToDevice, cs);
+  e = hga::launch_route(g, q_raw, chunk_sum, group_sum, reinterpret_cast<int32_t*>(dev + L.cidx),
+                        g.Kg > 0 ? reinterpret_cast<int32_t*>(dev + L.gidx) : nullptr, d_gran, d_gcnt,
+                        dev + L.rws, cs);
+  if (e != hipSuccess) return hga::hip_fail(e);
+  int32_t* d_slots = reinterpret_cast<int32_t*>(dev + L.idx + L.slots_off);
+  int64_t* d_src = reinterpret_cast<int64_t*>(dev + L.idx + L.src_off);
+  int32_t* d_dst = reinterpret_cast<int32_t*>(dev + L.idx + L.dst_off);
+  DirParams dp;
+  dp.gran = d_gran;
+  dp.gcnt = d_gcnt;
+  dp.slot_of = reinterpret_cast<int32_t*>(dir + L.slot_of_off);
+  dp.owner = reinterpret_cast<int32_t*>(dir + L.owner_off);
+  dp.fill = reinterpret_cast<int32_t*>(dir + L.fill_off);
+  dp.stamp = reinterpret_cast<int32_t*>(dir + L.stamp_off);
+  dp.victim = reinterpret_cast<int32_t*>(dir + L.victim_off);
+  dp.slots = d_slots;
+  dp.src = d_src;
+  dp.dst = d_dst;
+  dp.state = d_state;
+  dp.units = L.units;
+  dp.gmax = g.gmax;
+  dp.ngran = s->ngran;
+  dp.cache_slots = s->cache_slots;
+  dp.pos = pos;
+  dp.gs = static_cast<int32_t>(g.gs);
+  dp.step = s->steps;
+  s->steps = s->steps == 2147483647 ? 0 : s->steps + 1;
+  hipLaunchKernelGGL(directory_kernel, dim3(1), dim3(kDirThreads), 0, cs, dp);
+  e = hipGetLastError();
   if (e != hipSuccess) return hga::hip_fail(e);
   const size_t gb = L.granule_bytes;
   char* cache = dev + L.cache;
-  if (miss > 0) {
-    hipLaunchKernelGGL(fetch_granules, dim3(static_cast<unsigned>(miss)), dim3(256), 0, cs, s->store_dev,
-                       reinterpret_cast<const int64_t*>(dev + L.idx + L.src_off),
-                       reinterpret_cast<const int32_t*>(dev + L.idx + L.dst_off),
-                       reinterpret_cast<uint4*>(cache), static_cast<int64_t>(gb / 16));
-    e = hipGetLastError();
-    if (e != hipSuccess) return hga::hip_fail(e);
-  }
+  const unsigned fetch_groups = static_cast<unsigned>(std::min<int64_t>(L.per_step, 1024));
+  hipLaunchKernelGGL(fetch_granules, dim3(fetch_groups), dim3(256), 0, cs, s->store_dev, d_src, d_dst,
+                     d_state + 1, reinterpret_cast<uint4*>(cache), static_cast<int64_t>(gb / 16));
+  e = hipGetLastError();
+  if (e != hipSuccess) return hga::hip_fail(e);
   hga::AttendExtra ex;
-  ex.pool_slot = reinterpret_cast<const int32_t*>(dev + L.idx + L.slots_off);
+  ex.pool_slot = d_slots;
   ex.pool_slots = s->cache_slots;
   ex.allow_split = true;
   e = hga::launch_attend(g, q_raw, cache, cache, d_gran, d_gcnt, false, out, lse, dev + L.aws, cs, &ex);
   if (e != hipSuccess) return hga::hip_fail(e);
   if (stats != nullptr) {
+    // the only wait of a step, and only when its counts are asked for
+    int32_t* h_state = reinterpret_cast<int32_t*>(host + L.hstate);
+    e = hipMemcpyAsync(h_state, d_state, 16 * 4, hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess) e = hipStreamSynchronize(cs);
+    if (e != hipSuccess) return hga::hip_fail(e);
     stats->windows = 1;
-    stats->granules_copied = miss;
-    stats->bytes_h2d = static_cast<int64_t>(static_cast<size_t>(miss) * gb + L.idx_bytes);
-    stats->pack_seconds = lookup_s;
+    stats->granules_copied = h_state[1];
+    stats->bytes_h2d = static_cast<int64_t>(static_cast<size_t>(h_state[1]) * gb);
+    stats->pack_seconds = 0.0;
     stats->host_seconds =
         std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
-    stats->granules_hit = hits;
+    stats->granules_hit = h_state[2];
   }
   return HGA_OK;
 }

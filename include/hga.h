@@ -411,7 +411,11 @@ hga_status hga_attend_backward(const hga_config* cfg, hga_dtype dtype, int32_t b
  * store, RAM-cached decode): the token K/V history stays in the pinned
  * granule-major host store (layout of hga_attend_host_tiered), summaries and
  * routing on the device, and a device cache of cache_slots granules keeps
- * what earlier steps brought over (least recently used evicted first).
+ * what earlier steps brought over.  Its directory lives on the device: a
+ * granule without a slot takes the next slot, in ring order from a
+ * replacement hand, that the step does not use (so the always-visible
+ * windows, used every step, stay cached; the oldest-filled routed granules
+ * go first).
  *
  * A session (host object) owns the cache bookkeeping; the caller owns and
  * allocates every buffer: kv_host (pinned, hipHostMalloc, mapped into the
@@ -433,13 +437,16 @@ hga_status hga_attend_backward(const hga_config* cfg, hga_dtype dtype, int32_t b
  * hga_decode_session_step: one query per sequence at position pos (<= the
  *   last appended position): q_raw [B][Hq][1][d], out [B][Hq][1][d], lse
  *   [B][Hq][1] (may be NULL).  Same outputs as hga_route + hga_attend with
- *   q_pos0 = pos, n_q = 1 over the device-resident cache.  Host-blocking: it
- *   waits for the route's granule lists, looks the granules up in the cache,
- *   then enqueues on compute_stream the gather of the misses from the store
- *   and the attention.  A granule cached while it held fewer tokens than the
- *   step needs is fetched again.  stats (may be NULL): granules fetched
+ *   q_pos0 = pos, n_q = 1 over the device-resident cache.  Asynchronous:
+ *   it enqueues on compute_stream the route, the cache lookup (one
+ *   workgroup), the gather of the misses from the store and the attention,
+ *   and returns without waiting.  A granule cached while it held fewer
+ *   tokens than the step needs is fetched again.  stats (may be NULL; then
+ *   the call waits for the step to finish): granules fetched
  *   (granules_copied) / found (granules_hit), bytes over the host link,
- *   pack_seconds = host lookup time, host_seconds = whole call.
+ *   pack_seconds = 0 (no host lookup), host_seconds = whole call.
+ *   The device buffer holds the cache and its directory between calls:
+ *   leave it untouched while the session lives.
  * Calls on one session must not overlap.
  */
 typedef struct hga_decode_session hga_decode_session;

@@ -79,7 +79,7 @@ def _oracle_steps(w, q, k, v, routes, outs, lses, steps):
         P.check_attention(run, qs, k, v, units, name=f"stream:{w.name}:step{s}")
 
 
-def _session_run(run, w, cache_slots, dev, poison=False):
+def _session_run(run, w, cache_slots, dev, poison=False, with_stats=True):
     import torch
     cfg = run.cfg
     # store and summary tables hold only the prefix; the session appends the rest
@@ -106,7 +106,7 @@ def _session_run(run, w, cache_slots, dev, poison=False):
         q = run.q[:, :, s:s + 1].contiguous()
         out = torch.full_like(q, float("nan"))
         lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
-        stats.append(sess.step(q, pos, csum, gsum, out, lse))
+        stats.append(sess.step(q, pos, csum, gsum, out, lse, stats=with_stats))
         outs.append(out)
         lses.append(lse)
     torch.cuda.synchronize()
@@ -114,7 +114,7 @@ def _session_run(run, w, cache_slots, dev, poison=False):
     return outs, lses, stats, csum, gsum, store
 
 
-def _check_session(w, cache_slots, poison=False, seed=0):
+def _check_session(w, cache_slots, poison=False, seed=0, with_stats=True):
     """Session outputs vs the device path at every step, then its summaries
     and host store vs a prefill build; returns the per-step stats."""
     import torch
@@ -122,7 +122,8 @@ def _check_session(w, cache_slots, poison=False, seed=0):
     q, k, v = P.make_inputs_parallel(w, seed)
     run = P.DeviceRun(w, q, k, v, route=False, attend=False)
     ref_out, ref_lse, ref_routes = _reference(run, w, dev)
-    outs, lses, stats, csum, gsum, store = _session_run(run, w, cache_slots, dev, poison=poison)
+    outs, lses, stats, csum, gsum, store = _session_run(run, w, cache_slots, dev, poison=poison,
+                                                        with_stats=with_stats)
     bad = [s for s in range(w.n_q)
            if not (torch.equal(outs[s], ref_out[s]) and torch.equal(lses[s], ref_lse[s]))]
     detail = []
@@ -132,7 +133,8 @@ def _check_session(w, cache_slots, poison=False, seed=0):
         rows = torch.nonzero(do.amax(dim=-1) > 0).tolist()
         detail.append(f"step {s}: max|dO| {do.max().item():.3g} max|dlse| {dl.max().item():.3g} "
                       f"nan {int(torch.isnan(outs[s]).sum())} rows {rows[:8]} "
-                      f"copied {stats[s]['granules_copied']} hits {stats[s]['granules_hit']}")
+                      + (f"copied {stats[s]['granules_copied']} hits {stats[s]['granules_hit']}"
+                         if stats[s] is not None else ""))
     assert not bad, f"steps differing from the device path: {bad[:10]}; " + "; ".join(detail)
     end = w.q_pos0 + w.n_q
     n_closed = end // run.cfg.chunk_size
@@ -177,6 +179,18 @@ def test_stream_decode_equals_device_path(cache):
         # (the synthetic queries are independent, so routes change a lot)
         assert np.mean(copied[1:]) < 0.5 * copied[0]
         assert min(hits[1:]) > 0
+
+
+@pytest.mark.parametrize("cache", ["roomy", "smallest"])
+def test_stream_decode_unsynchronised(cache):
+    """Steps enqueued back to back with no host wait between them (no stats
+    asked): the cache lookup, the gathers and the attention stay ordered on
+    the stream, and every step equals the device path bit for bit."""
+    w = _workload()
+    print(f"[gpu] stream decode unsynchronised ({cache}): {w}", flush=True)
+    need = w.batch * w.n_kv_heads * H.max_granules(H.Config.from_workload(w))
+    stats = _check_session(w, 4 * need if cache == "roomy" else need, with_stats=False)
+    assert all(st is None for st in stats)
 
 
 @pytest.mark.parametrize("i", range(N_STREAM))
