@@ -679,39 +679,47 @@ struct DirParams {
   int32_t gs, step;
 };
 
-// Exclusive rank of this thread's flag among the workgroup's set flags, in
-// thread order, and their total; every thread of the workgroup calls it.
-__device__ int block_rank(bool flag, int* wave_tot, int& total) {
+constexpr int kDirPer = 4;  // list entries per thread per pass
+
+// Exclusive prefix, in thread order, of every thread's count c over the
+// workgroup, and their total; every thread of the workgroup calls it.
+__device__ int block_scan(int c, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[wv] = __popcll(m);
+  int incl = c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    incl += lane >= o ? t : 0;
+  }
+  if (lane == 63) wave_tot[wv] = incl;
   __syncthreads();
   int before = 0, tot = 0;
   for (int w = 0; w < kDirThreads / 64; ++w) {
-    const int c = wave_tot[w];
-    before += w < wv ? c : 0;
-    tot += c;
+    const int x = wave_tot[w];
+    before += w < wv ? x : 0;
+    tot += x;
   }
   __syncthreads();  // wave_tot is rewritten by the next call
   total = tot;
-  return before + in_wave;
+  return before + incl - c;
 }
 
 // The decode session's cache directory, one workgroup per step: entries
 // whose granule has a slot mark it used in this step; the entries without
-// one take, in entry order, the next slots from the hand (ring order) that
-// this step does not use, evicting their owners; an entry is a miss when
-// its slot is new or holds fewer tokens than the step needs.  Slots used in
-// the step (every fixed-window granule, every step) are never victims, and
-// one step's entries fit the cache (cache_slots >= per_step), so the victim
-// search ends within one pass over the slots.
+// one take, in pass / thread / entry order, the next slots from the hand
+// (ring order) that this step does not use, evicting their owners; an
+// entry is a miss when its slot is new or holds fewer tokens than the step
+// needs.  Slots used in the step (every fixed-window granule, every step)
+// are never victims, and one step's entries fit the cache (cache_slots >=
+// per_step), so the victim search ends within one pass over the slots.
+// Each thread takes kDirPer entries per pass (entry e0 + j * kDirThreads +
+// tid) so that their loads are in flight together.
 __global__ __launch_bounds__(kDirThreads) void directory_kernel(DirParams p) {
   __shared__ int wave_tot[kDirThreads / 64];
   __shared__ int s_need, s_hits;
   __shared__ long long s_hand;
   const int tid = threadIdx.x;
   const int64_t n = p.units * p.gmax;
+  const int64_t pass = static_cast<int64_t>(kDirPer) * kDirThreads;
   if (tid == 0) {
     s_need = 0;
     s_hits = 0;
@@ -720,16 +728,27 @@ __global__ __launch_bounds__(kDirThreads) void directory_kernel(DirParams p) {
   __syncthreads();
   // 1. lookups; a found slot is marked used in this step
   int need = 0;
-  for (int64_t e = tid; e < n; e += kDirThreads) {
-    const int64_t x = e / p.gmax;
-    int32_t sl = -2;  // no entry
-    const int64_t gid = p.gran[e];
-    if (e - x * p.gmax < p.gcnt[x] && gid >= 0 && gid < p.ngran) {
-      sl = p.slot_of[x * p.ngran + gid];
-      if (sl >= 0) p.stamp[sl] = p.step;
-      else ++need;
+  for (int64_t e0 = 0; e0 < n; e0 += pass) {
+    int64_t key[kDirPer];
+    int32_t sl[kDirPer];
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      const int64_t e = e0 + j * kDirThreads + tid;
+      key[j] = -1;
+      if (e < n) {
+        const int64_t x = e / p.gmax, gid = p.gran[e];
+        if (e - x * p.gmax < p.gcnt[x] && gid >= 0 && gid < p.ngran) key[j] = x * p.ngran + gid;
+      }
     }
-    p.slots[e] = sl;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) sl[j] = key[j] >= 0 ? p.slot_of[key[j]] : -2;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      const int64_t e = e0 + j * kDirThreads + tid;
+      if (sl[j] >= 0) p.stamp[sl[j]] = p.step;
+      need += sl[j] == -1 ? 1 : 0;
+      if (e < n) p.slots[e] = sl[j];
+    }
   }
   atomicAdd(&s_need, need);
   __syncthreads();
@@ -746,7 +765,7 @@ __global__ __launch_bounds__(kDirThreads) void directory_kernel(DirParams p) {
       fr = p.stamp[slot] != p.step;
     }
     int tot = 0;
-    const int r = found + block_rank(fr, wave_tot, tot);
+    const int r = found + block_scan(fr ? 1 : 0, wave_tot, tot);
     if (fr && r < R) {
       p.victim[r] = slot;
       if (r == R - 1) s_hand = (slot + 1) % p.cache_slots;
@@ -754,47 +773,81 @@ __global__ __launch_bounds__(kDirThreads) void directory_kernel(DirParams p) {
     found += tot;
   }
   const int have = found < R ? found : R;
-  // 3. new slots (in entry order), misses, the per-entry slots
+  // 3. new slots, misses, the per-entry slots
   int new_base = 0, miss_base = 0, hits = 0;
-  for (int64_t e0 = 0; e0 < n; e0 += kDirThreads) {
-    const int64_t e = e0 + tid;
-    int32_t sl = -2, last = 0;
-    int64_t k = 0;
-    if (e < n) {
-      sl = p.slots[e];
-      if (sl != -2) {
+  for (int64_t e0 = 0; e0 < n; e0 += pass) {
+    int32_t sl[kDirPer], last[kDirPer], fill[kDirPer];
+    int64_t key[kDirPer];
+    int fresh = 0;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      const int64_t e = e0 + j * kDirThreads + tid;
+      sl[j] = e < n ? p.slots[e] : -2;
+    }
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      const int64_t e = e0 + j * kDirThreads + tid;
+      key[j] = 0;
+      last[j] = 0;
+      if (sl[j] != -2) {
         const int64_t x = e / p.gmax, gid = p.gran[e];
-        k = x * p.ngran + gid;
+        key[j] = x * p.ngran + gid;
         const int64_t left = p.pos + 1 - gid * p.gs;  // tokens this step needs
-        last = static_cast<int32_t>(left < p.gs ? left : p.gs);
+        last[j] = static_cast<int32_t>(left < p.gs ? left : p.gs);
       }
+      fresh += sl[j] == -1 ? 1 : 0;
     }
-    const bool fresh = sl == -1;
     int tot = 0;
-    const int r = new_base + block_rank(fresh, wave_tot, tot);
+    int r = new_base + block_scan(fresh, wave_tot, tot);
     new_base += tot;
-    if (fresh) {
-      if (r < have) {
-        sl = p.victim[r];
-        const int32_t prev = p.owner[sl];
-        if (prev >= 0) p.slot_of[prev] = -1;
-        p.owner[sl] = static_cast<int32_t>(k);
-        p.slot_of[k] = sl;
-        p.stamp[sl] = p.step;
-      } else {
-        sl = -2;  // unreachable while cache_slots >= per_step; counted below
+    int32_t prev[kDirPer];
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      fill[j] = 0;
+      prev[j] = -1;
+      if (sl[j] == -1) {
+        if (r < have) {
+          sl[j] = p.victim[r];
+          key[j] = ~key[j];  // marks a new slot (keys are >= 0)
+        } else {
+          sl[j] = -2;  // unreachable while cache_slots >= per_step
+        }
+        ++r;
+      } else if (sl[j] >= 0) {
+        fill[j] = p.fill[sl[j]];
       }
     }
-    const bool miss = sl >= 0 && (fresh || p.fill[sl] < last);
-    const int m = miss_base + block_rank(miss, wave_tot, tot);
-    miss_base += tot;
-    if (miss) {
-      p.fill[sl] = last;
-      p.src[m] = k;
-      p.dst[m] = sl;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j)
+      if (key[j] < 0) prev[j] = p.owner[sl[j]];
+    int misses = 0;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      if (key[j] < 0) {
+        key[j] = ~key[j];
+        if (prev[j] >= 0) p.slot_of[prev[j]] = -1;
+        p.owner[sl[j]] = static_cast<int32_t>(key[j]);
+        p.slot_of[key[j]] = sl[j];
+        p.stamp[sl[j]] = p.step;
+        fill[j] = -1;  // a new slot is a miss
+      }
+      misses += (sl[j] >= 0 && fill[j] < last[j]) ? 1 : 0;
     }
-    hits += (sl >= 0 && !miss) ? 1 : 0;
-    if (e < n) p.slots[e] = sl >= 0 ? sl : -1;
+    int m = miss_base + block_scan(misses, wave_tot, tot);
+    miss_base += tot;
+#pragma unroll
+    for (int j = 0; j < kDirPer; ++j) {
+      const int64_t e = e0 + j * kDirThreads + tid;
+      if (sl[j] >= 0 && fill[j] < last[j]) {
+        p.fill[sl[j]] = last[j];
+        p.src[m] = key[j];
+        p.dst[m] = sl[j];
+        ++m;
+      } else if (sl[j] >= 0) {
+        ++hits;
+      }
+      if (e < n) p.slots[e] = sl[j] >= 0 ? sl[j] : -1;
+    }
   }
   atomicAdd(&s_hits, hits);
   __syncthreads();
