@@ -25,7 +25,7 @@ def test_qwen3_prefill_32k_full():
     print(f"[gpu] qwen3 32k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
     assert near <= len(units) // 50
     last = w.n_q // w.chunk_size - 1
-    att = sorted(set(P.sample_units(w, 64)) | {(0, h, last) for h in range(w.n_kv_heads)})
+    att = sorted(set(P.sample_units(w, 256)) | {(0, h, last) for h in range(w.n_kv_heads)})
     m, r, l = P.check_attention(run, q, k, v, att, name="fullsize:" + w.name)
     print(f"[gpu] qwen3 32k attention on {len(att)} units: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
@@ -43,7 +43,7 @@ def test_smalllm_prefill_4k_full():
     exact, near = P.compare_routes(run, orc, units, name="fullsize:" + w.name)
     print(f"[gpu] smalllm 4k routes: exact={exact} near_tie={near} of {len(units)}", flush=True)
     assert near <= len(units) // 50
-    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 64), name="fullsize:" + w.name)
+    m, r, l = P.check_attention(run, q, k, v, P.sample_units(w, 256), name="fullsize:" + w.name)
     print(f"[gpu] smalllm 4k attention: max_abs={m:.3g} rel_l2={r:.3g}", flush=True)
 
 
@@ -83,9 +83,9 @@ def test_host_tiered_128k_full(base):
     print(f"[gpu] host tier 128k {base}: {stats}", flush=True)
     same = bool(torch.equal(out, run.out))
     assert same, "host tier differs from the device-resident path"
-    # 32 units spread over the query chunks and KV heads, with the last chunk
+    # 64 units spread over the query chunks and KV heads, with the last chunk
     nqc = w.n_q // w.chunk_size
-    units = sorted({(0, i % w.n_kv_heads, int(t)) for i, t in enumerate(np.linspace(11, nqc - 1, 32))}
+    units = sorted({(0, i % w.n_kv_heads, int(t)) for i, t in enumerate(np.linspace(11, nqc - 1, 64))}
                    | {(0, 3, nqc - 1)})
     orc = P.oracle_route(run, q, k, units)
     exact, near = P.compare_routes(run, orc, units, name=f"fullsize:{base}")
