@@ -1105,6 +1105,11 @@ hga_status hga_decode_session_step(hga_decode_session* s, const void* q_raw, int
   char* dir = dev + L.dir;
   int32_t* d_state = reinterpret_cast<int32_t*>(dir + L.state_off);
   hipError_t e = hipSuccess;
+  if (s->steps == 2147483647) {
+    // use stamps would repeat: start again from an empty cache
+    s->steps = 0;
+    s->dir_ready = false;
+  }
   if (!s->dir_ready) {
     hipLaunchKernelGGL(directory_init, dim3(256), dim3(256), 0, cs,
                        reinterpret_cast<int32_t*>(dir + L.slot_of_off), L.keys,
@@ -1139,8 +1144,7 @@ hga_status hga_decode_session_step(hga_decode_session* s, const void* q_raw, int
   dp.cache_slots = s->cache_slots;
   dp.pos = pos;
   dp.gs = static_cast<int32_t>(g.gs);
-  dp.step = s->steps;
-  s->steps = s->steps == 2147483647 ? 0 : s->steps + 1;
+  dp.step = s->steps++;
   hipLaunchKernelGGL(directory_kernel, dim3(1), dim3(kDirThreads), 0, cs, dp);
   e = hipGetLastError();
   if (e != hipSuccess) return hga::hip_fail(e);
